@@ -1,0 +1,58 @@
+"""Planted mistakes in a patched copy of the oracle (CPU only) must each be
+caught by at least one pin: evidence that the pins constrain the oracle."""
+import os
+import subprocess
+
+import pytest
+
+import tests.test_oracle_pins as P
+from oracle import build as B
+from oracle import oracle as O
+
+# (name, exact source text, planted replacement, pins that must catch it)
+MUTANTS = [
+    ("argmax ties keep the higher index", "if (x > best) {", "if (x >= best) {",
+     [P.test_argmax_planted_first_maximum_config1, P.test_argmax_matches_numpy_first_occurrence]),
+    ("top-k ties ordered by descending id", "return a < b;", "return a > b;",
+     [P.test_topk_matches_lexsort]),
+    ("logsumexp drops the factored maximum", "return M + std::log(s);", "return std::log(s);",
+     [P.test_lse_closed_forms]),
+    ("logsumexp ignores the temperature", "s += std::exp(static_cast<double>(R.at(r, i)) / T - M);",
+     "s += std::exp(static_cast<double>(R.at(r, i)) - M);", [P.test_lse_matches_scipy]),
+    ("top-p cut on the tempered distribution",
+     "Z0 += (e[j] = std::exp(static_cast<double>(R.at(r, cand[j])) - z0));",
+     "Z0 += (e[j] = std::exp((static_cast<double>(R.at(r, cand[j])) - z0) / T));",
+     [P.test_sample_filter_order_worked_example]),
+    ("accept test with p and q transposed", "if (!(lhs <= pt)) {", "if (!(static_cast<double>(u_acc[b * G + i]) * pt <= qt)) {",
+     [P.test_mrs_is_lossless_and_hits_the_ceiling]),
+    ("residual with the wrong sign", "std::max(p_of(L, x) - q_of(L, x), 0.0)", "std::max(q_of(L, x) - p_of(L, x), 0.0)",
+     [P.test_mrs_is_lossless_and_hits_the_ceiling]),
+    ("coupling sum with max instead of min", "s += std::min(p_of(i, x), q_of(i, x));", "s += std::max(p_of(i, x), q_of(i, x));",
+     [P.test_spec_invariants_config4_like]),
+    ("bonus draw from the wrong target row", "w[x] = p_of(G, x);", "w[x] = p_of(G - 1, x);",
+     [P.test_bonus_draw_comes_from_the_last_target_row]),
+    ("draw from the last crossing instead of the first", "if (target < c) {", "if (target < c && j + 1 == w.size()) {",
+     [P.test_sample_u_grid_frequencies_and_support]),
+]
+
+
+@pytest.mark.parametrize("name,find,repl,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, find, repl, pins):
+    src = open(B.SRC).read()
+    assert src.count(find) == 1, f"mutation anchor not unique: {find}"
+    mut = tmp_path / "mutant.cpp"
+    mut.write_text(src.replace(find, repl))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-fPIC", "-shared", "-pthread", str(mut), "-o", str(so)], check=True)
+    saved = O._lib
+    O._lib = O.load(str(so))
+    try:
+        caught = 0
+        for pin in pins:
+            try:
+                pin(O)
+            except AssertionError:
+                caught += 1
+        assert caught >= 1, f"no pin caught the planted mistake: {name}"
+    finally:
+        O._lib = saved
