@@ -1,0 +1,202 @@
+"""Benchmark of the vocab-row selection path on one MI355X.
+
+Step = one vsel_topk call (first-maximum argmax + exact top-84 (value, id) +
+log-sum-exp, fused in one pass) over a batch of 1,024 bfloat16 logit rows of
+202,048 entries at a padded stride of 202,112.  Inputs are resident in HBM
+and rotate over three copies (1.24 GB, well past the 256 MB Infinity Cache),
+so every step streams its rows from HBM.
+
+Prints one JSON line (rank 0).  `roofline` prices the fused kernel against
+the 8 TB/s HBM peak with its algorithmic bytes (valid input elements plus the
+outputs); `cpu_baseline` times the CPU oracle on a bounded sample of the same
+rows; `extra` holds the latency-bound configurations in microseconds per call.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+ROWS, V, LD, K = 1024, 202_048, 202_112, 84
+
+
+def algorithmic_bytes(rows, vocab, elem, k):
+    # valid input elements + top-k values and ids + argmax + log-sum-exp
+    return rows * (vocab * elem + k * 8 + 4 + 4)
+
+
+def time_calls(fn, n, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(n):
+        fn(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / n  # microseconds per call
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the selection path has no multi-GPU leg); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vocab_row_reductions_amd as vsel
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    print(f"bench: generating {ROWS} x {V} bf16 rows (ld {LD})", file=sys.stderr, flush=True)
+    bits, _ = W.decode_batch_bf16(rows=ROWS, vocab=V, ld=LD)
+    base = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    bufs = [base] + [base.clone() for _ in range(2)]
+    out = dict(vals=torch.empty((ROWS, K), dtype=torch.float32, device=dev),
+               ids=torch.empty((ROWS, K), dtype=torch.int32, device=dev),
+               argmax=torch.empty(ROWS, dtype=torch.int32, device=dev),
+               lse=torch.empty(ROWS, dtype=torch.float32, device=dev))
+
+    def step(i):
+        vsel.vsel_topk(bufs[i % 3], K, vocab=V, out=out)
+
+    for _ in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us_per_launch = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    rows_per_s = ROWS / (ms_per_step / 1e3)
+    abytes = algorithmic_bytes(ROWS, V, 2, K)
+    achieved = abytes / (us_per_launch * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "large-batch decode selection: 1024 rows x 202048 bf16 logits, ld 202112, "
+                               "fused argmax + top-k k=84 + logsumexp, inputs rotated over 3 HBM copies",
+                   "rows": ROWS, "vocab": V, "ld": LD, "k": K},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "topk_kernel<bf16, lse>", "us_per_launch": us_per_launch,
+                     "algorithmic_bytes_per_launch": abytes},
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        n = min(args.cpu_rows, ROWS)
+        cores = len(os.sched_getaffinity(0))
+        O.topk(bits[:2], K, vocab=V, nthreads=cores)
+        t = time.perf_counter()
+        O.topk(bits[:n], K, vocab=V, nthreads=cores)
+        dt = time.perf_counter() - t
+        result["cpu_baseline"] = {"value": n / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+                                  "sample": f"first {n} of the {ROWS} rows, same fused outputs (top-84, argmax, "
+                                            f"float64 logsumexp), {dt:.2f} s"}
+
+    if not args.no_extra:
+        result["extra"] = extras(torch, vsel, W, dev, stream, bufs, out)
+
+    print(json.dumps(result), flush=True)
+
+
+def extras(torch, vsel, W, dev, stream, bufs, out):
+    """Microseconds per call for the other configurations (cold: inputs rotated
+    over >= 1 GB of copies; warm: one buffer, as right after the LM head)."""
+    ex = {}
+    ex["topk_k84_us"] = time_calls(lambda i: vsel.vsel_topk(bufs[i % 3], K, vocab=V, out=out), 50, 5, stream)
+    out64 = dict(vals=torch.empty((ROWS, 64), dtype=torch.float32, device=dev),
+                 ids=torch.empty((ROWS, 64), dtype=torch.int32, device=dev),
+                 argmax=torch.empty(ROWS, dtype=torch.int32, device=dev),
+                 lse=torch.empty(ROWS, dtype=torch.float32, device=dev))
+    ex["topk_k64_us"] = time_calls(lambda i: vsel.vsel_topk(bufs[i % 3], 64, vocab=V, out=out64), 50, 5, stream)
+    ex["topk_k64_gbs"] = algorithmic_bytes(ROWS, V, 2, 64) / (ex["topk_k64_us"] * 1e-6) / 1e9
+    ex["argmax_only_bf16_1024rows_us"] = time_calls(lambda i: vsel.vsel_argmax(bufs[i % 3], vocab=V), 50, 5, stream)
+
+    def cold_copies(x, total=1 << 30):
+        n = max(1, -(-total // (x.numel() * x.element_size())))
+        return [x] + [x.clone() for _ in range(n - 1)]
+
+    # config 1: one row argmax
+    row, _ = W.greedy_single_row()
+    r1 = cold_copies(torch.from_numpy(row).to(dev), 1 << 28)
+    ex["argmax_1x202048_warm_us"] = time_calls(lambda i: vsel.vsel_argmax(r1[0]), 200, 10, stream)
+    ex["argmax_1x202048_cold_us"] = time_calls(lambda i: vsel.vsel_argmax(r1[i % len(r1)]), 200, 10, stream)
+    del r1
+    # config 2: verify rows, k = 84
+    for rows in (3, 49):
+        x = W.verify_topk_rows(rows=rows)
+        xs = cold_copies(torch.from_numpy(x).to(dev))
+        ex[f"topk_{rows}x248320_k84_warm_us"] = time_calls(lambda i: vsel.vsel_topk(xs[0], 84), 100, 5, stream)
+        ex[f"topk_{rows}x248320_k84_cold_us"] = time_calls(lambda i: vsel.vsel_topk(xs[i % len(xs)], 84), 100, 5, stream)
+        del xs
+    # config 3: sampling
+    x, u = W.sampling_rows()
+    xs = cold_copies(torch.from_numpy(x).to(dev))
+    ud = torch.from_numpy(u).to(dev)
+    ex["sample_64x202048_warm_us"] = time_calls(lambda i: vsel.vsel_sample(xs[0], 0.7, 20, 0.95, ud), 100, 5, stream)
+    ex["sample_64x202048_cold_us"] = time_calls(lambda i: vsel.vsel_sample(xs[i % len(xs)], 0.7, 20, 0.95, ud), 100, 5, stream)
+    del xs
+    # config 4: speculative acceptance
+    d = W.speculative_batch()
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    tg, dr = g(d["target"]), g(d["draft"])
+    args = (g(d["tokens"].view(np.int32)), g(d["u_acc"]), g(d["u_res"]), g(d["u_bon"]), 32, 8, 1.0)
+    so = vsel.vsel_spec_accept(tg, dr, *args)
+    ex["spec_accept_32x8_warm_us"] = time_calls(lambda i: vsel.vsel_spec_accept(tg, dr, *args, out=so), 50, 5, stream)
+    L = so["len_mrs"].cpu().numpy()
+    tested = int(np.minimum(L + 1, 8).sum())
+    ex["spec_accept_32x8_per_position_acceptance"] = float(L.sum() / tested)
+    ex["spec_accept_32x8_mean_summin"] = float(so["summin"].float().mean().item())
+    # fp32 variant of the headline batch (one buffer pair, 827 MB each)
+    x32 = bufs[0][:, :V].float().contiguous()
+    x32b = [x32, x32.clone()]
+    o32 = dict(vals=torch.empty((ROWS, K), dtype=torch.float32, device=dev),
+               ids=torch.empty((ROWS, K), dtype=torch.int32, device=dev),
+               argmax=torch.empty(ROWS, dtype=torch.int32, device=dev),
+               lse=torch.empty(ROWS, dtype=torch.float32, device=dev))
+    us32 = time_calls(lambda i: vsel.vsel_topk(x32b[i % 2], K, out=o32), 30, 3, stream)
+    ex["topk_fp32_1024x202048_k84_us"] = us32
+    ex["topk_fp32_1024x202048_k84_gbs"] = algorithmic_bytes(ROWS, V, 4, K) / (us32 * 1e-6) / 1e9
+    del x32b, x32
+    # a plain device-to-device copy of the same batch (read + write), for context
+    src = bufs[0]
+    dst = torch.empty_like(src)
+    cu = time_calls(lambda i: dst.copy_(bufs[i % 3]), 30, 3, stream)
+    ex["torch_copy_bf16_batch_us"] = cu
+    ex["torch_copy_bf16_batch_gbs"] = 2 * src.numel() * 2 / (cu * 1e-6) / 1e9
+    return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ex.items()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,89 @@
+"""Host-side checks of the C ABI (no kernel is launched): the library loads,
+exports every entry point include/vsel.h declares, sizes workspaces and
+rejects bad arguments synchronously."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsel.h")
+
+
+@pytest.fixture(scope="module")
+def vsel():
+    import vocab_row_reductions_amd as v
+    return v
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsel_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for op in ("vsel_argmax", "vsel_topk", "vsel_sample", "vsel_spec_accept", "vsel_workspace_bytes"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(vsel):
+    lib = C.CDLL(vsel.library_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libvsel.so does not export {name}"
+
+
+def test_version_and_status_strings(vsel):
+    assert vsel.lib.vsel_version() >> 16 >= 1
+    assert vsel.lib.vsel_status_string(0) == b"ok"
+    assert b"invalid" in vsel.lib.vsel_status_string(1)
+
+
+def test_workspace_sizes(vsel):
+    wb = vsel.workspace_bytes
+    for op, k in ((vsel.OP_ARGMAX, 0), (vsel.OP_TOPK, 84), (vsel.OP_SAMPLE, 20), (vsel.OP_SAMPLE, 0),
+                  (vsel.OP_SPEC, 8)):
+        n = wb(op, vsel.F32, 32, 202048, k)
+        assert n > 0 and n % 256 == 0
+    assert wb(vsel.OP_TOPK, vsel.BF16, 1024, 202048, 84) > 0
+    # rejected shapes size to 0
+    assert wb(vsel.OP_TOPK, vsel.F32, 4, 100, 101) == 0          # k > vocab
+    assert wb(vsel.OP_TOPK, vsel.F32, 4, 5000, 1025) == 0        # k > K_MAX
+    assert wb(vsel.OP_ARGMAX, vsel.F32, 0, 100, 0) == 0          # no rows
+    assert wb(vsel.OP_ARGMAX, 7, 4, 100, 0) == 0                 # unknown dtype
+    assert wb(99, vsel.F32, 4, 100, 0) == 0                      # unknown op
+
+
+def test_invalid_arguments_return_einval_before_launch(vsel):
+    L = vsel.lib
+    fake = C.c_void_p(4096)   # never dereferenced: every call below fails validation first
+    ws = C.c_void_p(1 << 20)
+    EINVAL, EWS = 1, 2
+    assert L.vsel_argmax(None, 0, 4, 100, 100, fake, None, ws, 1 << 20, None) == EINVAL
+    assert L.vsel_argmax(fake, 0, 0, 100, 100, fake, None, ws, 1 << 20, None) == EINVAL
+    assert L.vsel_argmax(fake, 0, 4, 100, 99, fake, None, ws, 1 << 20, None) == EINVAL       # ld < vocab
+    assert L.vsel_argmax(fake, 0, 4, 1 << 31, 1 << 31, fake, None, ws, 1 << 20, None) == EINVAL
+    assert L.vsel_argmax(C.c_void_p(4097), 1, 4, 100, 100, fake, None, ws, 1 << 20, None) == EINVAL
+    assert L.vsel_argmax(fake, 0, 4, 100, 100, fake, None, ws, 16, None) == EWS                # too small
+    assert L.vsel_argmax(fake, 0, 4, 100, 100, fake, None, C.c_void_p((1 << 20) + 8), 1 << 20, None) == EWS
+    assert L.vsel_topk(fake, 0, 4, 100, 100, 0, fake, fake, None, None, ws, 1 << 20, None) == EINVAL
+    assert L.vsel_topk(fake, 0, 4, 100, 100, 101, fake, fake, None, None, ws, 1 << 20, None) == EINVAL
+    assert L.vsel_topk(fake, 0, 4, 5000, 5000, 1025, fake, fake, None, None, ws, 1 << 20, None) == EINVAL
+    assert L.vsel_topk(fake, 0, 4, 100, 100, 5, None, fake, None, None, ws, 1 << 20, None) == EINVAL
+    bad_sample = [(-0.5, 20, 0.9), (0.7, -1, 0.9), (0.7, 20, 0.0), (0.7, 20, 1.5), (0.7, 0, 0.9),
+                  (0.7, 1025, 0.9), (float("nan"), 20, 0.9), (float("inf"), 20, 0.9)]
+    for T, k, p in bad_sample:
+        assert L.vsel_sample(fake, 0, 4, 100, 100, T, k, p, fake, fake, None, ws, 1 << 20, None) == EINVAL
+    args = dict(batch=2, gamma=3, vocab=100, T=1.0)
+    def spec(**kw):
+        a = {**args, **kw}
+        return L.vsel_spec_accept(fake, a.get("ld_t", 100), fake, a.get("ld_d", 100), a["batch"], a["gamma"],
+                                  a["vocab"], a["T"], fake, fake, fake, fake, fake, fake, None, None, None,
+                                  ws, 1 << 20, None)
+    assert spec(gamma=0) == EINVAL
+    assert spec(batch=0) == EINVAL
+    assert spec(T=-1.0) == EINVAL
+    assert spec(ld_t=99) == EINVAL
+    assert spec(ld_d=50) == EINVAL

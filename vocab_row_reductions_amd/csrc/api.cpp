@@ -1,0 +1,514 @@
+// api.cpp -- the C ABI of include/vsel.h: argument checks, workspace
+// layout, segment planning and kernel dispatch.  Host code only.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/vsel.h"
+#include "internal.hpp"
+
+using namespace vsel;
+
+namespace {
+
+constexpr int64_t kMinSegment = 2048;      // elements per workgroup, at least
+constexpr int64_t kSegOverhead = 4096;     // fixed cost of a segment, in elements streamed
+constexpr int64_t kMaxSplitWork = 8192;    // rows x segments never exceeds max(rows, this)
+constexpr size_t kTicketFloor = 65536;     // counters live in the first 64 KiB (or more)
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int32_t S;
+  int64_t seg_len;
+};
+
+// Upper bound on segments per row.  It depends on the shape only, so the
+// workspace can be sized without the device: no segment shorter than
+// kMinSegment, a row's k-record sets must fit one workgroup's merge buffer,
+// and the split never multiplies the work items past kMaxSplitWork.
+int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap) {
+  int64_t b = std::max<int64_t>(1, cdiv(V, kMinSegment));
+  if (k > 0) b = std::min<int64_t>(b, std::max<int64_t>(1, cap / k));
+  return std::min<int64_t>(b, std::max<int64_t>(1, cdiv(kMaxSplitWork, rows)));
+}
+
+// Segments per row for a grid that runs `resident` workgroups at once:
+// minimise rounds x (segment length + fixed cost), so that the chip is full
+// and no launch ends with a nearly empty last round.
+Plan plan_segments(int64_t rows, int64_t V, int64_t k, int64_t resident, int cap) {
+  const int64_t sb = seg_bound(rows, V, k, cap);
+  Plan best{1, cdiv(V, 8) * 8};
+  int64_t best_cost = INT64_MAX;
+  for (int64_t S = 1; S <= sb; ++S) {
+    const int64_t seg = cdiv(cdiv(V, S), 8) * 8;
+    const int64_t Sx = cdiv(V, seg);
+    if (Sx != S) continue;
+    const int64_t cost = cdiv(rows * Sx, std::max<int64_t>(1, resident)) * (seg + kSegOverhead);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = Plan{(int32_t)Sx, seg};
+    }
+  }
+  return best;
+}
+
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int64_t resident_scan(int dtype, bool lse) {
+  const int b = scan_blocks_per_cu(dtype, lse);
+  return (int64_t)(b > 0 ? b : 4) * device_cus();
+}
+int64_t resident_topk(int dtype, bool lse, int cap) {
+  const int b = topk_blocks_per_cu(dtype, lse, cap);
+  return (int64_t)(b > 0 ? b : 2) * device_cus();
+}
+
+Plan plan_scan(int dtype, bool lse, int64_t rows, int64_t V) {
+  return plan_segments(rows, V, 0, resident_scan(dtype, lse), kCapLarge);
+}
+Plan plan_scan_bound(int64_t rows, int64_t V) {
+  const int64_t sb = seg_bound(rows, V, 0, kCapLarge);
+  return Plan{(int32_t)sb, cdiv(cdiv(V, sb), 8) * 8};
+}
+
+// Top-k: the small candidate buffer whenever it can hold the merge, which
+// keeps four workgroups per CU.
+struct TopkPlan {
+  Plan p;
+  int cap;
+};
+TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k) {
+  if (2 * k <= kCapSmall) return TopkPlan{plan_segments(rows, V, k, resident_topk(dtype, lse, kCapSmall), kCapSmall), kCapSmall};
+  return TopkPlan{plan_segments(rows, V, k, resident_topk(dtype, lse, kCapLarge), kCapLarge), kCapLarge};
+}
+Plan plan_topk_bound(int64_t rows, int64_t V, int64_t k) {
+  const int64_t sb = seg_bound(rows, V, k, kCapLarge);
+  return Plan{(int32_t)sb, 0};
+}
+
+// Sequential bump allocator over the workspace; the first region holds every
+// counter the call uses (zero between calls).
+struct Layout {
+  size_t off = 0;
+  size_t tick_bytes = 0;
+  void reserve_tickets(size_t n) {
+    tick_bytes = align_up(std::max(kTicketFloor, n * sizeof(uint32_t)));
+    off = tick_bytes;
+  }
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool elem_ok(int dtype) { return dtype == VSEL_F32 || dtype == VSEL_BF16; }
+size_t elem_size(int dtype) { return dtype == VSEL_F32 ? 4 : 2; }
+bool rows_ok(int64_t rows, int64_t V, int64_t ld) {
+  return rows >= 1 && V >= 1 && V < (int64_t(1) << 31) && ld >= V && rows <= (int64_t(1) << 24);
+}
+bool aligned16(const void* p, int64_t ld, size_t es) {
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * (int64_t)es) % 16 == 0);
+}
+bool aligned_elem(const void* p, size_t es) { return reinterpret_cast<uintptr_t>(p) % es == 0; }
+
+// ---- layouts (the same functions size the workspace and place the buffers)
+struct ScanWs {
+  size_t tickets, p_key, p_m, p_s;
+};
+ScanWs scan_layout(Layout& L, int64_t rows, const Plan& p, bool own_tickets = true) {
+  ScanWs w{};
+  if (own_tickets) L.reserve_tickets((size_t)rows);
+  w.tickets = 0;
+  const size_t n = (size_t)(rows * p.S);
+  w.p_key = L.take(n * 8);
+  w.p_m = L.take(n * 4);
+  w.p_s = L.take(n * 8);
+  return w;
+}
+
+struct TopkWs {
+  size_t tickets, rec_key, rec_bits, rec_cnt, p_m, p_s;
+};
+TopkWs topk_layout(Layout& L, int64_t rows, int64_t k, const Plan& p) {
+  TopkWs w{};
+  L.reserve_tickets((size_t)rows);
+  const size_t n = (size_t)(rows * p.S);
+  const size_t nr = p.S > 1 ? n * (size_t)k : 0;
+  w.rec_key = L.take(nr * 8);
+  w.rec_bits = L.take(nr * 4);
+  w.rec_cnt = L.take(n * 4);
+  w.p_m = L.take(n * 4);
+  w.p_s = L.take(n * 8);
+  return w;
+}
+
+struct StatsWs {
+  size_t amax, mx, lse, bad;
+};
+StatsWs stats_layout(Layout& L, int64_t nrows) {
+  StatsWs w{};
+  w.amax = L.take((size_t)nrows * 4);
+  w.mx = L.take((size_t)nrows * 4);
+  w.lse = L.take((size_t)nrows * 8);
+  w.bad = L.take((size_t)nrows * 4);
+  return w;
+}
+
+// Sampling over the whole row (top_k == 0): row scan, then the draw.
+struct RowDrawWs {
+  ScanWs scan;
+  StatsWs st;
+  size_t dtickets, p_w;
+};
+RowDrawWs rowdraw_layout(Layout& L, int64_t rows, const Plan& ps, const Plan& pd) {
+  RowDrawWs w{};
+  L.reserve_tickets((size_t)(2 * rows));
+  w.scan = scan_layout(L, rows, ps, false);
+  w.scan.tickets = 0;
+  w.dtickets = (size_t)rows * 4;
+  w.st = stats_layout(L, rows);
+  w.p_w = L.take((size_t)(rows * pd.S) * 8);
+  return w;
+}
+
+struct SpecWs {
+  ScanWs scan;
+  StatsWs st;
+  size_t tk_pos, tk_seq, tk_row, tk_draw;
+  size_t p_summin, acc, draw_L, p_lse, lse64, p_w;
+};
+SpecWs spec_layout(Layout& L, int64_t B, int64_t G, const Plan& ps, const Plan& pp) {
+  SpecWs w{};
+  const int64_t nrows = B * (2 * G + 1);
+  const size_t nt = (size_t)(nrows + B * G + B + 2 * B + B);
+  L.reserve_tickets(nt);
+  w.scan.tickets = 0;
+  w.tk_pos = (size_t)nrows * 4;
+  w.tk_seq = w.tk_pos + (size_t)(B * G) * 4;
+  w.tk_row = w.tk_seq + (size_t)B * 4;
+  w.tk_draw = w.tk_row + (size_t)(2 * B) * 4;
+  w.scan = scan_layout(L, nrows, ps, false);
+  w.scan.tickets = 0;
+  w.st = stats_layout(L, nrows);
+  w.p_summin = L.take((size_t)(B * G * pp.S) * 8);
+  w.acc = L.take((size_t)(B * G) * 4);
+  w.draw_L = L.take((size_t)B * 4);
+  w.p_lse = L.take((size_t)(2 * B * pp.S) * 8);
+  w.lse64 = L.take((size_t)(2 * B) * 8);
+  w.p_w = L.take((size_t)(B * pp.S) * 8);
+  return w;
+}
+
+bool ws_ok(void* ws, size_t have, size_t need) {
+  return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) % kWsAlign == 0) && have >= need;
+}
+
+vsel_status launched(hipError_t e) { return e == hipSuccess ? VSEL_OK : VSEL_EDEVICE; }
+
+ScanArgs scan_args(const void* x, int dtype, int64_t rows, int64_t V, int64_t ld, const Plan& p, double T) {
+  ScanArgs a{};
+  a.x1 = x;
+  a.x2 = nullptr;
+  a.ld1 = ld;
+  a.ld2 = ld;
+  a.rows1 = rows;
+  a.rows2 = 0;
+  a.V = V;
+  a.seg_len = p.seg_len;
+  a.S = p.S;
+  a.vec1 = aligned16(x, ld, elem_size(dtype)) ? 1 : 0;
+  a.vec2 = 0;
+  a.T = T > 0 ? T : 1.0;
+  a.lse_c = (float)(1.4426950408889634 / a.T);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vsel_version(void) { return (1 << 16) | 0; }
+
+const char* vsel_status_string(int s) {
+  switch (s) {
+    case VSEL_OK: return "ok";
+    case VSEL_EINVAL: return "invalid argument";
+    case VSEL_EWORKSPACE: return "workspace too small or misaligned";
+    case VSEL_EDEVICE: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int32_t k) {
+  if (!elem_ok(dtype)) return 0;
+  Layout L;
+  switch (op) {
+    case VSEL_OP_ARGMAX: {
+      if (!rows_ok(rows, vocab, vocab)) return 0;
+      scan_layout(L, rows, plan_scan_bound(rows, vocab));
+      return L.off;
+    }
+    case VSEL_OP_TOPK: {
+      if (!rows_ok(rows, vocab, vocab) || k < 1 || k > VSEL_K_MAX || k > vocab) return 0;
+      topk_layout(L, rows, k, plan_topk_bound(rows, vocab, k));
+      return L.off;
+    }
+    case VSEL_OP_SAMPLE: {
+      if (!rows_ok(rows, vocab, vocab) || k < 0 || k > VSEL_K_MAX) return 0;
+      Layout a;
+      scan_layout(a, rows, plan_scan_bound(rows, vocab));
+      size_t need = a.off;
+      if (k == 0) {
+        Layout b;
+        rowdraw_layout(b, rows, plan_scan_bound(rows, vocab), plan_scan_bound(rows, vocab));
+        need = std::max(need, b.off);
+      } else if (k > 1) {
+        const int64_t kk = std::min<int64_t>(k, vocab);
+        Layout b;
+        topk_layout(b, rows, kk, plan_topk_bound(rows, vocab, kk));
+        need = std::max(need, b.off);
+      }
+      return need;
+    }
+    case VSEL_OP_SPEC_ACCEPT: {
+      const int64_t B = rows, G = k;
+      if (B < 1 || G < 1 || !rows_ok(B * (2 * G + 1), vocab, vocab)) return 0;
+      spec_layout(L, B, G, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
+      return L.off;
+    }
+    default:
+      return 0;
+  }
+}
+
+vsel_status vsel_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                        uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !out_idx || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
+      !aligned_elem(logits, elem_size(dtype)))
+    return VSEL_EINVAL;
+  Layout L;
+  const ScanWs w = scan_layout(L, rows, plan_scan_bound(rows, vocab));
+  if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+  const Plan p = plan_scan(dtype, false, rows, vocab);
+  ScanArgs a = scan_args(logits, dtype, rows, vocab, ld, p, 1.0);
+  a.out_idx = out_idx;
+  a.out_val = out_val;
+  a.tickets = at<uint32_t>(ws, w.tickets);
+  a.p_key = at<uint64_t>(ws, w.p_key);
+  a.p_m = at<float>(ws, w.p_m);
+  a.p_s = at<double>(ws, w.p_s);
+  return launched(launch_scan(dtype, false, a, (hipStream_t)stream));
+}
+
+static vsel_status topk_common(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                               int32_t k, bool want_lse, TopkArgs& a, void* ws, size_t ws_bytes,
+                               void* stream) {
+  Layout L;
+  const TopkWs w = topk_layout(L, rows, k, plan_topk_bound(rows, vocab, k));
+  if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+  const TopkPlan tp = plan_topk(dtype, want_lse, rows, vocab, k);
+  const Plan& p = tp.p;
+  a.x = logits;
+  a.ld = ld;
+  a.rows = rows;
+  a.V = vocab;
+  a.seg_len = p.seg_len;
+  a.S = p.S;
+  a.k = k;
+  a.vec = aligned16(logits, ld, elem_size(dtype)) ? 1 : 0;
+  a.tickets = at<uint32_t>(ws, w.tickets);
+  a.rec_key = at<uint64_t>(ws, w.rec_key);
+  a.rec_bits = at<uint32_t>(ws, w.rec_bits);
+  a.rec_cnt = at<uint32_t>(ws, w.rec_cnt);
+  a.p_m = at<float>(ws, w.p_m);
+  a.p_s = at<double>(ws, w.p_s);
+  return launched(launch_topk(dtype, want_lse, tp.cap, a, (hipStream_t)stream));
+}
+
+vsel_status vsel_topk(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld, int32_t k,
+                      float* out_vals, uint32_t* out_ids, uint32_t* out_argmax, float* out_lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!logits || !out_vals || !out_ids || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
+      !aligned_elem(logits, elem_size(dtype)) || k < 1 || k > VSEL_K_MAX || k > vocab)
+    return VSEL_EINVAL;
+  TopkArgs a{};
+  a.mode = 0;
+  a.out_vals = out_vals;
+  a.out_ids = out_ids;
+  a.out_argmax = out_argmax;
+  a.out_lse = out_lse;
+  return topk_common(logits, dtype, rows, vocab, ld, k, out_lse != nullptr, a, ws, ws_bytes, stream);
+}
+
+vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                        float temperature, int32_t top_k, float top_p, const float* u, uint32_t* out_token,
+                        float* out_logprob, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !u || !out_token || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
+      !aligned_elem(logits, elem_size(dtype)))
+    return VSEL_EINVAL;
+  if (!(temperature >= 0.0f) || std::isinf(temperature) || top_k < 0 || top_k > VSEL_K_MAX ||
+      !(top_p > 0.0f && top_p <= 1.0f))
+    return VSEL_EINVAL;
+  if (top_k == 0 && top_p < 1.0f) return VSEL_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (temperature == 0.0f || top_k == 1) {
+    // Greedy: the argmax, nothing drawn; log-probability 0.
+    Layout L;
+    const ScanWs w = scan_layout(L, rows, plan_scan_bound(rows, vocab));
+    if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+    const Plan p = plan_scan(dtype, false, rows, vocab);
+    ScanArgs a = scan_args(logits, dtype, rows, vocab, ld, p, 1.0);
+    a.out_idx = out_token;
+    a.tickets = at<uint32_t>(ws, w.tickets);
+    a.p_key = at<uint64_t>(ws, w.p_key);
+    a.p_m = at<float>(ws, w.p_m);
+    a.p_s = at<double>(ws, w.p_s);
+    a.out_logp0 = out_logprob;
+    return launched(launch_scan(dtype, false, a, s));
+  }
+
+  if (top_k == 0) {
+    Layout L;
+    const Plan bnd = plan_scan_bound(rows, vocab);
+    const RowDrawWs w = rowdraw_layout(L, rows, bnd, bnd);
+    if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+    const Plan ps = plan_scan(dtype, false, rows, vocab);
+    const Plan pd = ps;
+    ScanArgs a = scan_args(logits, dtype, rows, vocab, ld, ps, temperature);
+    a.tickets = at<uint32_t>(ws, w.scan.tickets);
+    a.p_key = at<uint64_t>(ws, w.scan.p_key);
+    a.p_m = at<float>(ws, w.scan.p_m);
+    a.p_s = at<double>(ws, w.scan.p_s);
+    a.st_amax = at<uint32_t>(ws, w.st.amax);
+    a.st_max = at<float>(ws, w.st.mx);
+    a.st_bad = at<uint32_t>(ws, w.st.bad);
+    hipError_t e = launch_scan(dtype, false, a, s);
+    if (e != hipSuccess) return VSEL_EDEVICE;
+    DrawArgs d{};
+    d.x = logits;
+    d.ld = ld;
+    d.rows = rows;
+    d.V = vocab;
+    d.seg_len = pd.seg_len;
+    d.S = pd.S;
+    d.vec = a.vec1;
+    d.T = temperature;
+    d.u = u;
+    d.st_max = a.st_max;
+    d.st_bad = a.st_bad;
+    d.out_token = out_token;
+    d.out_logp = out_logprob;
+    d.tickets = at<uint32_t>(ws, w.dtickets);
+    d.p_w = at<double>(ws, w.p_w);
+    return launched(launch_draw_rows(dtype, d, s));
+  }
+
+  const int32_t k = (int32_t)std::min<int64_t>(top_k, vocab);
+  TopkArgs a{};
+  a.mode = 1;
+  a.temperature = temperature;
+  a.top_p = top_p;
+  a.u = u;
+  a.out_token = out_token;
+  a.out_logp = out_logprob;
+  return topk_common(logits, dtype, rows, vocab, ld, k, false, a, ws, ws_bytes, stream);
+}
+
+vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
+                             int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
+                             const float* u_accept, const float* u_resid, const float* u_bonus,
+                             int32_t* out_len_mrs, uint32_t* out_tok_mrs, int32_t* out_len_aa,
+                             uint32_t* out_tok_aa, float* out_summin, void* ws, size_t ws_bytes, void* stream) {
+  if (!target || !draft || !draft_tokens || !u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs)
+    return VSEL_EINVAL;
+  if (batch < 1 || gamma < 1 || vocab < 1 || vocab >= (int64_t(1) << 31) || ld_t < vocab || ld_d < vocab)
+    return VSEL_EINVAL;
+  if (!rows_ok(batch * (2 * (int64_t)gamma + 1), vocab, vocab)) return VSEL_EINVAL;
+  if (!(temperature >= 0.0f) || std::isinf(temperature)) return VSEL_EINVAL;
+  if (!aligned_elem(target, 4) || !aligned_elem(draft, 4)) return VSEL_EINVAL;
+  const int64_t B = batch, G = gamma;
+  Layout L;
+  const SpecWs w = spec_layout(L, B, G, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
+  if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+  const Plan ps = plan_scan(VSEL_F32, temperature > 0.0f, B * (2 * G + 1), vocab);
+  const Plan pp = plan_scan(VSEL_F32, true, B * G, vocab);
+  hipStream_t s = (hipStream_t)stream;
+
+  ScanArgs a = scan_args(target, VSEL_F32, B * (G + 1), vocab, ld_t, ps, temperature);
+  a.x2 = draft;
+  a.ld2 = ld_d;
+  a.rows2 = B * G;
+  a.vec2 = aligned16(draft, ld_d, 4) ? 1 : 0;
+  a.tickets = at<uint32_t>(ws, w.scan.tickets);
+  a.p_key = at<uint64_t>(ws, w.scan.p_key);
+  a.p_m = at<float>(ws, w.scan.p_m);
+  a.p_s = at<double>(ws, w.scan.p_s);
+  a.st_amax = at<uint32_t>(ws, w.st.amax);
+  a.st_max = at<float>(ws, w.st.mx);
+  a.st_lse = at<double>(ws, w.st.lse);
+  a.st_bad = at<uint32_t>(ws, w.st.bad);
+  hipError_t e = launch_scan(VSEL_F32, temperature > 0.0f, a, s);
+  if (e != hipSuccess) return VSEL_EDEVICE;
+
+  SpecArgs p{};
+  p.tgt = target;
+  p.dft = draft;
+  p.ld_t = ld_t;
+  p.ld_d = ld_d;
+  p.B = B;
+  p.gamma = gamma;
+  p.V = vocab;
+  p.T = temperature;
+  p.inv_T = temperature > 0 ? 1.0f / temperature : 0.0f;
+  p.lse_c = a.lse_c;
+  p.tokens = draft_tokens;
+  p.u_acc = u_accept;
+  p.u_res = u_resid;
+  p.u_bon = u_bonus;
+  p.len_mrs = out_len_mrs;
+  p.tok_mrs = out_tok_mrs;
+  p.len_aa = out_len_aa;
+  p.tok_aa = out_tok_aa;
+  p.summin = out_summin;
+  p.seg_len = pp.seg_len;
+  p.S = pp.S;
+  p.vec_t = a.vec1;
+  p.vec_d = a.vec2;
+  p.st_amax = a.st_amax;
+  p.st_max = a.st_max;
+  p.st_lse = a.st_lse;
+  p.st_bad = a.st_bad;
+  p.tk_pos = at<uint32_t>(ws, w.tk_pos);
+  p.tk_seq = at<uint32_t>(ws, w.tk_seq);
+  p.tk_row = at<uint32_t>(ws, w.tk_row);
+  p.tk_draw = at<uint32_t>(ws, w.tk_draw);
+  p.p_summin = at<double>(ws, w.p_summin);
+  p.acc = at<uint32_t>(ws, w.acc);
+  p.draw_L = at<int32_t>(ws, w.draw_L);
+  p.p_lse = at<double>(ws, w.p_lse);
+  p.lse64 = at<double>(ws, w.lse64);
+  p.p_w = at<double>(ws, w.p_w);
+  return launched(launch_spec(p, s));
+}
+
+}  // extern "C"

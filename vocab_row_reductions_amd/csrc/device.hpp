@@ -1,0 +1,452 @@
+// device.hpp -- device building blocks shared by the vsel kernels (gfx950).
+//
+// Row layout: a workgroup of NT = 256 threads (4 wave64) walks a segment of
+// one row in tiles.  A tile is G 16-byte groups per lane; lane l of the
+// workgroup owns groups j*NT + l (j = 0..G-1) of the tile, so consecutive
+// lanes load consecutive 16-byte words (fully coalesced) and every lane sees
+// its own elements in increasing index order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsel {
+
+constexpr int NT = 256;
+constexpr int NWAVE = NT / 64;
+constexpr uint32_t kFail = 0xFFFFFFFFu;
+constexpr uint32_t kNegInfBits = 0xFF800000u;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Elements per 16-byte group.
+template <typename DT> struct Elem;
+template <> struct Elem<float> { static constexpr int E = 4; };
+template <> struct Elem<uint16_t> { static constexpr int E = 8; };  // bfloat16 bit patterns
+
+struct Group { uint32_t w[4]; };
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// float32 bit pattern of element e of a group (bfloat16 widens exactly).
+template <typename DT> __device__ __forceinline__ uint32_t gbits(const Group& g, int e);
+template <> __device__ __forceinline__ uint32_t gbits<float>(const Group& g, int e) { return g.w[e]; }
+template <> __device__ __forceinline__ uint32_t gbits<uint16_t>(const Group& g, int e) {
+  return (e & 1) ? (g.w[e >> 1] & 0xFFFF0000u) : (g.w[e >> 1] << 16);
+}
+
+// float32 bit pattern of element i of a row.
+template <typename DT> __device__ __forceinline__ uint32_t gbits_at(const DT* row, int64_t i);
+template <> __device__ __forceinline__ uint32_t gbits_at<float>(const float* row, int64_t i) { return __float_as_uint(row[i]); }
+template <> __device__ __forceinline__ uint32_t gbits_at<uint16_t>(const uint16_t* row, int64_t i) { return (uint32_t)row[i] << 16; }
+
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Load one full tile starting at tb (uniform): group j of this lane is
+// elements (j*NT + threadIdx.x)*E .. +E-1.  Plain loads, issued back to back.
+template <typename DT, int NG, bool VEC>
+__device__ __forceinline__ void load_tile_full(Group (&g)[NG], const DT* __restrict__ tb) {
+  constexpr int E = Elem<DT>::E;
+  const uint32_t tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const uint32_t o = (uint32_t)(j * NT + tid) * E;
+    if constexpr (VEC) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + o));
+      g[j].w[0] = v.x; g[j].w[1] = v.y; g[j].w[2] = v.z; g[j].w[3] = v.w;
+    } else if constexpr (E == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[j].w[e] = __float_as_uint(tb[o + e]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g[j].w[q] = (uint32_t)tb[o + 2 * q] | ((uint32_t)tb[o + 2 * q + 1] << 16);
+    }
+  }
+}
+
+// Load one tile: group j of this lane covers elements
+// t0 + (j*NT + threadIdx.x)*E .. +E-1, for whole groups below e_full (a
+// multiple of E past e_begin); groups at or past e_full read as -inf.
+// Addresses are a uniform tile base plus small 32-bit lane offsets, and all
+// loads of the tile are issued back to back.  VEC rows (start and stride
+// 16-byte aligned, e_begin a multiple of 8 elements) use 16-byte loads: an
+// out-of-range group re-reads the tile's first group and is masked.  Other
+// rows use element loads, clamped the same way.
+template <typename DT, int NG, bool VEC>
+__device__ __forceinline__ void load_tile(Group (&g)[NG], const DT* __restrict__ row, int64_t t0, int64_t e_full) {
+  constexpr int E = Elem<DT>::E;
+  constexpr uint32_t pad = (E == 4) ? kNegInfBits : 0xFF80FF80u;
+  constexpr int64_t TILE = (int64_t)NT * NG * E;
+  const uint32_t tid = threadIdx.x;
+  const DT* __restrict__ tb = row + t0;                        // uniform
+  const uint32_t lim = (uint32_t)min(e_full - t0, TILE);     // uniform, whole groups left (>= E)
+  if (lim == (uint32_t)TILE) {                                 // full tile: plain loads
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const uint32_t o = (uint32_t)(j * NT + tid) * E;
+      if constexpr (VEC) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + o));
+        g[j].w[0] = v.x; g[j].w[1] = v.y; g[j].w[2] = v.z; g[j].w[3] = v.w;
+      } else if constexpr (E == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[j].w[e] = __float_as_uint(tb[o + e]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[j].w[q] = (uint32_t)tb[o + 2 * q] | ((uint32_t)tb[o + 2 * q + 1] << 16);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const uint32_t o = (uint32_t)(j * NT + tid) * E;
+    const bool full = o < lim;
+    const uint32_t src = full ? o : 0u;
+    if constexpr (VEC) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + src));
+      g[j].w[0] = full ? v.x : pad;
+      g[j].w[1] = full ? v.y : pad;
+      g[j].w[2] = full ? v.z : pad;
+      g[j].w[3] = full ? v.w : pad;
+    } else if constexpr (E == 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t v = __float_as_uint(tb[src + e]);
+        g[j].w[e] = full ? v : pad;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t v = (uint32_t)tb[src + 2 * q] | ((uint32_t)tb[src + 2 * q + 1] << 16);
+        g[j].w[q] = full ? v : pad;
+      }
+    }
+  }
+}
+
+// Walk the whole groups of [e_begin, e_full) of a row: full tiles of NG
+// groups per lane, then the remaining groups one per lane at a time (masked
+// past e_full).  fn(g, t0) gets each tile (a Group[NG] or Group[1]) and its
+// first element index; all threads call it for every tile.
+template <typename DT, int NG, bool VEC, class Fn>
+__device__ __forceinline__ void walk_groups(const DT* __restrict__ xr, int64_t e_begin, int64_t e_full, Fn&& fn) {
+  constexpr int E = Elem<DT>::E;
+  constexpr int64_t TILE = (int64_t)NT * NG * E;
+  const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
+  for (int64_t t0 = e_begin; t0 < e_tiles; t0 += TILE) {
+    Group g[NG];
+    load_tile_full<DT, NG, VEC>(g, xr + t0);
+    fn(g, t0);
+  }
+  for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
+    Group g1[1];
+    load_tile<DT, 1, VEC>(g1, xr, t0, e_full);
+    fn(g1, t0);
+  }
+}
+
+// Order-preserving unsigned image of a float's bits: larger float -> larger
+// key; -0.0 is folded onto +0.0 first so the two tie as floats do.
+__device__ __forceinline__ uint32_t fkey(uint32_t u) {
+  u = (u == 0x80000000u) ? 0u : u;
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k & 0x80000000u) ? (k ^ 0x80000000u) : ~k; }
+
+// Composite key: value first, then the lower id wins.  Distinct per element,
+// and never 0 for a real element (its value key is >= the key of -inf).
+__device__ __forceinline__ uint64_t comp_key(uint32_t bits, uint32_t id) {
+  return ((uint64_t)fkey(bits) << 32) | (uint32_t)(~id);
+}
+
+// Float threshold for a composite threshold T: every element with composite
+// >= T has value >= the returned float.
+__device__ __forceinline__ float thr_float(uint64_t T) {
+  uint32_t k = (uint32_t)(T >> 32);
+  return (k <= 0x007FFFFFu) ? -__builtin_inff() : __uint_as_float(key_bits(k));
+}
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((int)(uint32_t)v, m), hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+  return __longlong_as_double((long long)shfl_xor_u64((uint64_t)__double_as_longlong(v), m));
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) { uint64_t o = shfl_xor_u64(v, m); v = o > v ? o : v; }
+  return v;
+}
+__device__ __forceinline__ float wave_max_nan(float v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v = fmax_nan(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += shfl_xor_f64(v, m);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- log-sum-exp
+// (m, s): m is the running maximum (NaN-propagating, so a NaN or +inf element
+// poisons it), s = sum exp2((x - m) * c) in float64 with c = log2(e)/T.
+struct LSE { float m; double s; };
+
+__device__ __forceinline__ LSE lse_merge(LSE a, LSE b, float c) {
+  float M = fmax_nan(a.m, b.m);
+  double sa = (a.m == M) ? a.s : a.s * exp2((double)(a.m - M) * (double)c);
+  double sb = (b.m == M) ? b.s : b.s * exp2((double)(b.m - M) * (double)c);
+  if (M != M) return LSE{M, __builtin_nan("")};
+  return LSE{M, sa + sb};
+}
+__device__ __forceinline__ LSE wave_lse(LSE v, float c) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    LSE o{__shfl_xor(v.m, m), shfl_xor_f64(v.s, m)};
+    v = lse_merge(v, o, c);
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- workgroup scratch
+struct SelShared {
+  uint32_t hist[256];
+  uint32_t cnt;        // records in the candidate buffer
+  uint32_t overflow;   // a tile's candidates did not fit
+  uint32_t cnt2;
+  uint32_t digit, rem, bcnt;
+  uint32_t last;       // this workgroup finishes the row
+  uint32_t wtau[NWAVE];
+  float wm[NWAVE];
+  double ws[NWAVE];
+  uint64_t wk[NWAVE];
+  uint64_t wk2[NWAVE];
+};
+
+// One MSB-first radix step: after `hist` holds the counts of the next 8-bit
+// digit among keys matching the prefix, find the digit d holding the rem-th
+// largest key.  Wave 0 scans the 256 bins from the top; all threads then read
+// (digit, rem within the bucket, bucket count) from sh.
+__device__ __forceinline__ void radix_pick(SelShared& sh, uint32_t rem) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int lane = tid;
+    uint32_t c[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) c[b] = sh.hist[255 - 4 * lane - b];
+    uint32_t local = c[0] + c[1] + c[2] + c[3];
+    uint32_t incl = wave_incl_scan_u32(local, lane);
+    uint32_t cum = incl - local;
+    if (cum < rem && rem <= incl) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (cum + c[b] >= rem) {
+          sh.digit = 255 - 4 * lane - b;
+          sh.rem = rem - cum;
+          sh.bcnt = c[b];
+          break;
+        }
+        cum += c[b];
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t wave_and_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v &= shfl_xor_u64(v, m);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_or_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v |= shfl_xor_u64(v, m);
+  return v;
+}
+
+// k-th largest of the distinct 64-bit keys produced by `each(f)` (which
+// calls f(key) for every key this thread contributes); at least k keys exist.
+// Returns T such that exactly k keys are >= T.  MSB-first 8-bit digits; a
+// digit on which all keys agree (from the AND / OR of all keys) costs no
+// histogram pass.  All threads must call.
+template <class Each>
+__device__ uint64_t radix_select(SelShared& sh, uint32_t k, Each each) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t all_and = ~0ull, all_or = 0ull;
+  each([&](uint64_t K) {
+    all_and &= K;
+    all_or |= K;
+  });
+  all_and = wave_and_u64(all_and);
+  all_or = wave_or_u64(all_or);
+  __syncthreads();
+  if (lane == 0) {
+    sh.wk[wave] = all_and;
+    sh.wk2[wave] = all_or;
+  }
+  __syncthreads();
+  all_and = sh.wk[0];
+  all_or = sh.wk2[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) {
+    all_and &= sh.wk[q];
+    all_or |= sh.wk2[q];
+  }
+  const uint64_t varies = all_and ^ all_or;
+  uint64_t prefix = 0;
+  uint32_t rem = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (((varies >> shift) & 0xFFull) == 0) {  // every key has the same digit here
+      prefix |= all_and & (0xFFull << shift);
+      continue;
+    }
+    for (int i = tid; i < 256; i += NT) sh.hist[i] = 0;
+    __syncthreads();
+    const uint64_t hmask = (shift == 56) ? 0ull : (~0ull << (shift + 8));
+    each([&](uint64_t K) {
+      if ((K & hmask) == prefix) atomicAdd(&sh.hist[(uint32_t)(K >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    radix_pick(sh, rem);
+    __syncthreads();
+    prefix |= (uint64_t)sh.digit << shift;
+    const uint32_t bc = sh.bcnt;
+    rem = sh.rem;
+    if (bc == rem) break;  // the whole bucket qualifies
+  }
+  __syncthreads();
+  return prefix;
+}
+
+// Shrink the LDS candidate buffer (n > k records) to its k largest keys and
+// return the new threshold (the k-th largest key).  The compaction is done
+// in place by wave 0, 64 records at a time: a record's destination (the
+// number of winners before it) never lies beyond what the wave has already
+// read.  All threads must call.
+template <int CAP>
+__device__ uint64_t select_compact(SelShared& sh, uint64_t* key, uint32_t* bits, uint32_t n, uint32_t k) {
+  const int tid = threadIdx.x;
+  const uint64_t T = radix_select(sh, k, [&](auto f) {
+    for (uint32_t i = tid; i < n; i += NT) f(key[i]);
+  });
+  if (tid < 64) {
+    uint32_t base = 0;
+    for (uint32_t c0 = 0; c0 < n; c0 += 64) {
+      const uint32_t i = c0 + tid;
+      const uint64_t K = i < n ? key[i] : 0ull;
+      const uint32_t b = i < n ? bits[i] : 0u;
+      const bool win = i < n && K >= T;
+      const uint64_t m = __ballot(win);
+      if (win) {
+        const uint32_t d =
+            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        key[d] = K;
+        bits[d] = b;
+      }
+      base += (uint32_t)__popcll(m);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) sh.cnt = k;
+  __syncthreads();
+  return T;
+}
+
+// Sort key[0..n) (with bits) in descending key order; n <= CAP.
+template <int CAP>
+__device__ void sort_desc(uint64_t* key, uint32_t* bits, uint32_t n) {
+  const int tid = threadIdx.x;
+  uint32_t P = 1;
+  while (P < n) P <<= 1;
+  for (uint32_t i = n + tid; i < P; i += NT) { key[i] = 0ull; bits[i] = 0u; }
+  for (uint32_t size = 2; size <= P; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (uint32_t i = tid; i < P / 2; i += NT) {
+        uint32_t lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        uint64_t a = key[lo], b = key[hi];
+        bool desc = (lo & size) == 0;
+        if (desc ? (a < b) : (a > b)) {
+          key[lo] = b; key[hi] = a;
+          uint32_t t = bits[lo]; bits[lo] = bits[hi]; bits[hi] = t;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Cross-workgroup data (segment partials, tickets) moves only through
+// device-scope atomic loads and stores.  On gfx950 these are coherent across
+// the XCDs' separate L2s by themselves, so no whole-cache writeback or
+// invalidate is needed (an agent-scope fence would cost one per workgroup).
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) { st_dev(reinterpret_cast<uint32_t*>(p), (uint32_t)v); }
+__device__ __forceinline__ void st_dev(float* p, float v) { st_dev(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
+__device__ __forceinline__ void st_dev(double* p, double v) {
+  st_dev(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v));
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __uint_as_float(ld_dev(reinterpret_cast<const uint32_t*>(p)));
+}
+__device__ __forceinline__ double ld_dev(const double* p) {
+  return __longlong_as_double((long long)ld_dev(reinterpret_cast<const uint64_t*>(p)));
+}
+
+// Last-workgroup-done ticket.  Every thread has written its partial results
+// with st_dev; waiting for its outstanding memory operations makes them
+// complete at device scope before the workgroup's arrival is counted.
+// Returns true in exactly one of the `n` workgroups sharing `ticket` (the
+// last to arrive), which may then read every partial with ld_dev; it resets
+// the ticket to 0 for the next call.  All threads must call.
+__device__ __forceinline__ bool last_done(SelShared& sh, uint32_t* ticket, uint32_t n) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.last = (old == n - 1) ? 1u : 0u;
+    if (old == n - 1) st_dev(ticket, 0u);
+  }
+  __syncthreads();
+  return sh.last != 0;
+}
+
+// Work index of this workgroup, remapped so that consecutive work items run
+// on the same XCD (workgroups are dealt round-robin over the 8 XCDs), which
+// keeps the segments of one row and their partials in one L2.
+__device__ __forceinline__ uint32_t work_index() {
+  const uint32_t b = blockIdx.x, n = gridDim.x;
+  if ((n & 7u) == 0) return (b & 7u) * (n >> 3) + (b >> 3);
+  return b;
+}
+
+// (row, segment) of this workgroup's work item, computed in 32 bits and kept
+// uniform.
+struct Item {
+  uint32_t row, seg;
+};
+__device__ __forceinline__ Item work_item(int32_t S) {
+  const uint32_t w = work_index();
+  const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(w / (uint32_t)S);
+  return Item{row, (uint32_t)__builtin_amdgcn_readfirstlane(w - row * (uint32_t)S)};
+}
+
+}  // namespace vsel

@@ -1,0 +1,145 @@
+// internal.hpp -- kernel argument blocks and launcher entry points of the
+// vsel library (not part of the public C ABI in include/vsel.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vsel {
+
+constexpr size_t kWsAlign = 256;
+constexpr int kCapSmall = 2048;  // LDS candidate records per workgroup (about 35 KiB of LDS in all)
+constexpr int kCapLarge = 4096;  // for large k or many segments per row
+
+inline size_t align_up(size_t x, size_t a = kWsAlign) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- row scan
+// One pass over each row: first-maximum argmax, the maximum value, the
+// latch for nonfinite rows and (optionally) log-sum-exp at temperature T.
+// Rows [0, rows1) come from x1 (stride ld1), rows [rows1, rows1+rows2) from x2.
+struct ScanArgs {
+  const void* x1;
+  const void* x2;
+  int64_t ld1, ld2;
+  int64_t rows1, rows2;
+  int64_t V;
+  int64_t seg_len;     // elements per segment, a multiple of 8
+  int32_t S;           // segments per row
+  int32_t vec1, vec2;  // 16-byte aligned rows
+  float lse_c;         // log2(e) / T
+  double T;            // temperature of the log-sum-exp
+  // user outputs (argmax op)
+  uint32_t* out_idx;
+  float* out_val;
+  float* out_logp0;    // greedy sampling: 0, or NaN for a fail-closed row
+  // row-stat outputs (spec / sample), any may be null
+  uint32_t* st_amax;
+  float* st_max;
+  double* st_lse;
+  uint32_t* st_bad;
+  // workspace
+  uint32_t* tickets;
+  uint64_t* p_key;
+  float* p_m;
+  double* p_s;
+};
+
+// ---------------------------------------------------------------- top-k
+struct TopkArgs {
+  const void* x;
+  int64_t ld;
+  int64_t rows;
+  int64_t V;
+  int64_t seg_len;
+  int32_t S;
+  int32_t k;
+  int32_t vec;
+  int32_t mode;   // 0: top-k outputs, 1: sampling tail
+  float* out_vals;
+  uint32_t* out_ids;
+  uint32_t* out_argmax;
+  float* out_lse;
+  // sampling
+  float temperature;
+  float top_p;
+  const float* u;
+  uint32_t* out_token;
+  float* out_logp;
+  // workspace (used when S > 1)
+  uint32_t* tickets;
+  uint64_t* rec_key;
+  uint32_t* rec_bits;
+  uint32_t* rec_cnt;
+  float* p_m;
+  double* p_s;
+};
+
+// ---------------------------------------------------------------- speculative acceptance
+struct SpecArgs {
+  const float* tgt;
+  const float* dft;
+  int64_t ld_t, ld_d;
+  int64_t B;
+  int32_t gamma;
+  int64_t V;
+  float T;
+  float inv_T;
+  float lse_c;
+  const uint32_t* tokens;
+  const float* u_acc;
+  const float* u_res;
+  const float* u_bon;
+  int32_t* len_mrs;
+  uint32_t* tok_mrs;
+  int32_t* len_aa;
+  uint32_t* tok_aa;
+  float* summin;
+  int64_t seg_len;
+  int32_t S;
+  int32_t vec_t, vec_d;
+  // row stats from the scan pass: target rows then draft rows
+  const uint32_t* st_amax;
+  const float* st_max;
+  const double* st_lse;
+  const uint32_t* st_bad;
+  // workspace
+  uint32_t* tk_pos;     // [B*gamma] per-position tickets
+  uint32_t* tk_seq;     // [B]       per-sequence tickets
+  uint32_t* tk_row;     // [B*2]     per draw-row tickets
+  uint32_t* tk_draw;    // [B]       per-sequence draw tickets
+  double* p_summin;     // [B*gamma*S]
+  uint32_t* acc;        // [B*gamma]
+  int32_t* draw_L;      // [B]: -1 none, 0..gamma-1 residual at L, gamma bonus
+  double* p_lse;        // [B*2*S] float64 partial sums for the draw rows
+  double* lse64;        // [B*2]
+  double* p_w;          // [B*S] partial draw masses
+};
+
+// Plain full-row draw for vsel_sample with top_k == 0.
+struct DrawArgs {
+  const void* x;
+  int64_t ld;
+  int64_t rows;
+  int64_t V;
+  int64_t seg_len;
+  int32_t S;
+  int32_t vec;
+  float T;
+  const float* u;
+  const float* st_max;
+  const uint32_t* st_bad;
+  uint32_t* out_token;
+  float* out_logp;
+  uint32_t* tickets;
+  double* p_w;
+};
+
+hipError_t launch_scan(int dtype, bool want_lse, const ScanArgs& a, hipStream_t s);
+hipError_t launch_topk(int dtype, bool want_lse, int cap, const TopkArgs& a, hipStream_t s);
+// Workgroups of a kernel variant that fit on one CU at once (0 if unknown).
+int scan_blocks_per_cu(int dtype, bool want_lse);
+int topk_blocks_per_cu(int dtype, bool want_lse, int cap);
+hipError_t launch_spec(const SpecArgs& a, hipStream_t s);
+hipError_t launch_draw_rows(int dtype, const DrawArgs& a, hipStream_t s);
+
+}  // namespace vsel

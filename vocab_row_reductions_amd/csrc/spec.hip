@@ -1,0 +1,512 @@
+// spec.hip -- speculative-decoding acceptance on the device, and the
+// full-row categorical draw.
+//
+// Modified rejection sampling ("speculative-acceptance.md", "Modified
+// rejection sampling"; the exact CPU acceptance of "Chapter 21", section
+// 21.9) needs, per verified position, two full-vocabulary reductions (the
+// pages' MLX version pays them as extra passes plus a host sync per
+// position).  Here the whole batch runs in four launches on one stream and
+// nothing returns to the host:
+//   1. row scan (scan.hip) over all target and draft rows: argmax, maximum,
+//      latch, log-sum-exp at T;
+//   2. coupling pass, one workgroup per (position, segment): p = exp(z/T -
+//      lse_p), q = exp(d/T - lse_q), sum of min(p, q) (the acceptance ceiling
+//      of "The acceptance ceiling").  The last workgroup of a position decides
+//      u * q(t) <= p(t) in float64; the last position of a sequence finds the
+//      first rejection L for both rules and writes every emitted token except
+//      the draw;
+//   3. float64 log-sum-exp of the draw rows of sequences that rejected (the
+//      residual mixes p and q, so both must be exact to float64 precision);
+//   4. the draw: float64 masses of each segment of the draw row (residual
+//      max(p - q, 0), or p for the bonus token), then the last workgroup
+//      picks the segment whose prefix crosses u * W and rescans it in id
+//      order.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace vsel {
+
+constexpr int PG = 4;  // 16-byte groups per lane per tile (float32 rows)
+
+__device__ __forceinline__ double block_sum_f64(SelShared& sh, double v) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  v = wave_sum_f64(v);
+  __syncthreads();
+  if (lane == 0) sh.ws[wave] = v;
+  __syncthreads();
+  double t = sh.ws[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) t += sh.ws[q];
+  return t;
+}
+
+// Exclusive prefix sum over the workgroup (thread order), float64.
+__device__ __forceinline__ double block_excl_scan_f64(SelShared& sh, double v, double* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    double o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) sh.ws[wave] = incl;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int q = 0; q < NWAVE; ++q) {
+    if (q < wave) base += sh.ws[q];
+    tot += sh.ws[q];
+  }
+  *total = tot;
+  return base + incl - v;
+}
+
+// ---------------------------------------------------------------- pass 2
+template <bool VEC>
+__global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
+  constexpr int E = 4, TILE = NT * PG * E;
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t pos = it.row;
+  const int seg = (int)it.seg;
+  const int64_t G = a.gamma;
+  if (pos >= a.B * G) return;
+  const int64_t b = pos / G, i = pos % G;
+  const int64_t trow = b * (G + 1) + i, drow = b * G + i;
+  const int64_t nT = a.B * (G + 1);
+  const float* __restrict__ zr = a.tgt + trow * a.ld_t;
+  const float* __restrict__ dr = a.dft + drow * a.ld_d;
+  const bool bad = a.st_bad[trow] || a.st_bad[nT + drow];
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+
+  double tot = 0.0;
+  if (a.T > 0.0f && !bad) {
+    const float c = a.lse_c;
+    const double Lp = a.st_lse[trow] * (double)kLog2e, Lq = a.st_lse[nT + drow] * (double)kLog2e;
+    const float Lp_hi = (float)Lp, Lq_hi = (float)Lq;
+    const float fp = (float)exp2(-(Lp - (double)Lp_hi)), fq = (float)exp2(-(Lq - (double)Lq_hi));
+    auto pair = [&](const auto& gz, const auto& gd) {
+      constexpr int NGP = (int)(sizeof(gz) / sizeof(Group));
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NGP; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
+          const float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          acc += fminf(p, q);
+        }
+      tot += (double)acc;
+    };
+    const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
+    const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
+    for (int64_t t0 = e_begin; t0 < e_tiles; t0 += TILE) {
+      Group gz[PG], gd[PG];
+      load_tile_full<float, PG, VEC>(gz, zr + t0);
+      load_tile_full<float, PG, VEC>(gd, dr + t0);
+      pair(gz, gd);
+    }
+    for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
+      Group gz[1], gd[1];
+      load_tile<float, 1, VEC>(gz, zr, t0, e_full);
+      load_tile<float, 1, VEC>(gd, dr, t0, e_full);
+      pair(gz, gd);
+    }
+    if (tid == 0)
+      for (int64_t x = e_full; x < e_end; ++x) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
+        const float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        tot += (double)fminf(p, q);
+      }
+  }
+  tot = block_sum_f64(sh, tot);
+  if (a.S > 1) {
+    if (tid == 0) st_dev(&a.p_summin[pos * a.S + seg], tot);
+    if (!last_done(sh, a.tk_pos + pos, (uint32_t)a.S)) return;
+    if (tid == 0) {
+      tot = 0.0;
+      for (int sg = 0; sg < a.S; ++sg) tot += ld_dev(&a.p_summin[pos * a.S + sg]);
+    }
+  }
+  // Position decision (one thread): coupling sum and the accept test.
+  if (tid == 0) {
+    const uint32_t t = a.tokens[pos];
+    uint32_t flag;
+    if (bad || t >= (uint64_t)a.V) {
+      flag = 2u;  // the sequence fails closed
+    } else if (a.T == 0.0f) {
+      flag = (t == a.st_amax[trow]) ? 1u : 0u;
+      tot = (a.st_amax[trow] == a.st_amax[nT + drow]) ? 1.0 : 0.0;
+    } else {
+      const double Td = a.T;
+      const double pt = exp((double)zr[t] / Td - a.st_lse[trow]);
+      const double qt = exp((double)dr[t] / Td - a.st_lse[nT + drow]);
+      flag = ((double)a.u_acc[pos] * qt <= pt) ? 1u : 0u;
+    }
+    st_dev(&a.acc[pos], flag);
+    if (a.summin) st_dev(&a.summin[pos], bad ? __builtin_nanf("") : (float)tot);
+  }
+  if (!last_done(sh, a.tk_seq + b, (uint32_t)G)) return;
+  if (tid != 0) return;
+
+  // Sequence decision.
+  uint32_t* tm = a.tok_mrs + b * (G + 1);
+  uint32_t* ta = a.tok_aa ? a.tok_aa + b * (G + 1) : nullptr;
+  bool fail = a.st_bad[b * (G + 1) + G] != 0;
+  for (int64_t q = 0; q < G; ++q) fail |= ld_dev(&a.acc[b * G + q]) == 2u;
+  for (int64_t q = 0; q <= G; ++q) {
+    tm[q] = kFail;
+    if (ta) ta[q] = kFail;
+  }
+  if (fail) {
+    a.len_mrs[b] = -1;
+    if (a.len_aa) a.len_aa[b] = -1;
+    if (a.summin)
+      for (int64_t q = 0; q < G; ++q) st_dev(&a.summin[b * G + q], __builtin_nanf(""));
+    a.draw_L[b] = -1;
+    return;
+  }
+  int64_t Laa = G;
+  for (int64_t q = 0; q < G; ++q)
+    if (a.tokens[b * G + q] != a.st_amax[b * (G + 1) + q]) {
+      Laa = q;
+      break;
+    }
+  if (a.len_aa) a.len_aa[b] = (int32_t)Laa;
+  if (ta) {
+    for (int64_t q = 0; q < Laa; ++q) ta[q] = a.tokens[b * G + q];
+    ta[Laa] = a.st_amax[b * (G + 1) + Laa];
+  }
+  if (a.T == 0.0f) {
+    a.len_mrs[b] = (int32_t)Laa;
+    for (int64_t q = 0; q < Laa; ++q) tm[q] = a.tokens[b * G + q];
+    tm[Laa] = a.st_amax[b * (G + 1) + Laa];
+    a.draw_L[b] = -1;
+    return;
+  }
+  int64_t L = G;
+  for (int64_t q = 0; q < G; ++q)
+    if (ld_dev(&a.acc[b * G + q]) == 0u) {
+      L = q;
+      break;
+    }
+  a.len_mrs[b] = (int32_t)L;
+  for (int64_t q = 0; q < L; ++q) tm[q] = a.tokens[b * G + q];
+  a.draw_L[b] = (int32_t)L;
+}
+
+// ---------------------------------------------------------------- pass 3
+template <bool VEC>
+__global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
+  constexpr int E = 4;
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t item = it.row;  // b*2 + which
+  const int seg = (int)it.seg;
+  if (item >= a.B * 2) return;
+  const int64_t b = item >> 1;
+  const int which = (int)(item & 1);
+  const int64_t G = a.gamma;
+  const int32_t L = a.draw_L[b];
+  if (L < 0 || L >= G) return;  // no residual draw for this sequence
+  const int64_t nT = a.B * (G + 1);
+  const int64_t srow = which == 0 ? b * (G + 1) + L : nT + b * G + L;
+  const float* __restrict__ xr = which == 0 ? a.tgt + (b * (G + 1) + L) * a.ld_t : a.dft + (b * G + L) * a.ld_d;
+  const double m = a.st_max[srow];
+  const double Td = a.T;
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  double s = 0.0;
+  const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
+  walk_groups<float, PG, VEC>(xr, e_begin, e_full, [&](const auto& g, int64_t) {
+    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+#pragma unroll
+    for (int j = 0; j < NGP; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += exp(((double)__uint_as_float(g[j].w[e]) - m) / Td);
+  });
+  if (tid == 0)
+    for (int64_t x = e_full; x < e_end; ++x) s += exp(((double)xr[x] - m) / Td);
+  s = block_sum_f64(sh, s);
+  if (a.S > 1) {
+    if (tid == 0) st_dev(&a.p_lse[item * a.S + seg], s);
+    if (!last_done(sh, a.tk_row + item, (uint32_t)a.S)) return;
+    if (tid == 0) {
+      s = 0.0;
+      for (int sg = 0; sg < a.S; ++sg) s += ld_dev(&a.p_lse[item * a.S + sg]);
+    }
+  }
+  if (tid == 0) a.lse64[item] = m / Td + log(s);
+}
+
+// ---------------------------------------------------------------- pass 4 (and the full-row draw)
+// Weight of element x of the draw: residual max(p - q, 0) with float64
+// log-sum-exps, or exp((z - m) / T) (p up to a constant factor, which the
+// inverse CDF over u * W does not see).
+struct DrawRow {
+  const float* z;
+  const float* d;  // null: plain p
+  double lp, lq, m, T;
+  __device__ __forceinline__ double weight(int64_t x) const {
+    if (d) {
+      const double p = exp((double)z[x] / T - lp), q = exp((double)d[x] / T - lq);
+      return p > q ? p - q : 0.0;
+    }
+    return exp(((double)z[x] - m) / T);
+  }
+};
+
+// Float64 mass of one segment (coalesced, lane-strided).
+__device__ __forceinline__ double segment_mass(const DrawRow& r, int64_t e_begin, int64_t e_end) {
+  double s = 0.0;
+  for (int64_t x = e_begin + threadIdx.x; x < e_end; x += NT) s += r.weight(x);
+  return s;
+}
+
+// Last workgroup: choose the segment whose prefix of masses crosses u*W,
+// rescan it in id order and return the token (valid in thread 0).
+__device__ uint32_t draw_finish(SelShared& sh, const DrawRow& r, const double* pw, int S, int64_t seg_len,
+                                int64_t V, double u, double* W_out) {
+  const int tid = threadIdx.x;
+  __shared__ int s_seg;
+  __shared__ double s_in;
+  __shared__ uint32_t s_tok;
+  if (tid == 0) {
+    double W = 0.0;
+    for (int sg = 0; sg < S; ++sg) W += ld_dev(&pw[sg]);
+    const double target = u * W;
+    double cum = 0.0;
+    int pick = -1;
+    for (int sg = 0; sg < S; ++sg) {
+      if (target < cum + ld_dev(&pw[sg])) {
+        pick = sg;
+        break;
+      }
+      cum += ld_dev(&pw[sg]);
+    }
+    double tin = target - cum;
+    if (pick < 0) {  // rounding at the very top: the last segment with mass
+      for (int sg = S - 1; sg >= 0; --sg)
+        if (ld_dev(&pw[sg]) > 0.0) {
+          pick = sg;
+          break;
+        }
+      if (pick < 0) pick = 0;
+      tin = ld_dev(&pw[pick]);
+    }
+    s_seg = pick;
+    s_in = tin;
+    s_tok = kFail;
+    *W_out = W;
+  }
+  __syncthreads();
+  const int64_t e_begin = (int64_t)s_seg * seg_len, e_end = min(V, e_begin + seg_len);
+  const int64_t len = e_end - e_begin;
+  const int64_t per = (len + NT - 1) / NT;
+  const int64_t lo = min(e_end, e_begin + tid * per), hi = min(e_end, lo + per);
+  double local = 0.0;
+  for (int64_t x = lo; x < hi; ++x) local += r.weight(x);
+  double total;
+  const double excl = block_excl_scan_f64(sh, local, &total);
+  const double tin = s_in;
+  if (tin >= excl && tin < excl + local) {
+    double c = excl;
+    for (int64_t x = lo; x < hi; ++x) {
+      c += r.weight(x);
+      if (tin < c) {
+        s_tok = (uint32_t)x;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0 && s_tok == kFail) {  // rounding: the last element with weight in the segment
+    for (int64_t x = e_end - 1; x >= e_begin; --x)
+      if (r.weight(x) > 0.0) {
+        s_tok = (uint32_t)x;
+        break;
+      }
+    if (s_tok == kFail) s_tok = (uint32_t)e_begin;
+  }
+  __syncthreads();
+  return s_tok;
+}
+
+__global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t b = it.row;
+  const int seg = (int)it.seg;
+  if (b >= a.B) return;
+  const int64_t G = a.gamma;
+  const int32_t L = a.draw_L[b];
+  if (L < 0) return;
+  DrawRow r;
+  r.T = a.T;
+  double u;
+  if (L < G) {
+    r.z = a.tgt + (b * (G + 1) + L) * a.ld_t;
+    r.d = a.dft + (b * G + L) * a.ld_d;
+    r.lp = a.lse64[b * 2];
+    r.lq = a.lse64[b * 2 + 1];
+    r.m = 0.0;
+    u = a.u_res[b * G + L];
+  } else {
+    r.z = a.tgt + (b * (G + 1) + G) * a.ld_t;
+    r.d = nullptr;
+    r.lp = r.lq = 0.0;
+    r.m = a.st_max[b * (G + 1) + G];
+    u = a.u_bon[b];
+  }
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  double s = block_sum_f64(sh, segment_mass(r, e_begin, e_end));
+  if (tid == 0) st_dev(&a.p_w[b * a.S + seg], s);
+  if (!last_done(sh, a.tk_draw + b, (uint32_t)a.S)) return;
+  double* pw = a.p_w + b * a.S;
+  // Degenerate residual (p <= q everywhere): draw from p instead.
+  __shared__ int s_degen;
+  if (tid == 0) {
+    double W = 0.0;
+    for (int sg = 0; sg < a.S; ++sg) W += ld_dev(&pw[sg]);
+    s_degen = (r.d != nullptr && !(W > 0.0)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (s_degen) {
+    r.d = nullptr;
+    r.m = a.st_max[b * (G + 1) + L];
+    for (int sg = 0; sg < a.S; ++sg) {
+      const int64_t eb = (int64_t)sg * a.seg_len, ee = min(a.V, eb + a.seg_len);
+      const double ms = block_sum_f64(sh, segment_mass(r, eb, ee));
+      if (tid == 0) st_dev(&pw[sg], ms);
+      __syncthreads();
+    }
+  }
+  double W;
+  const uint32_t tok = draw_finish(sh, r, pw, a.S, a.seg_len, a.V, u, &W);
+  if (tid == 0) a.tok_mrs[b * (G + 1) + L] = tok;
+}
+
+template <typename DT>
+__global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows) return;
+  if (a.st_bad[row]) {
+    if (seg == 0 && tid == 0) {
+      a.out_token[row] = kFail;
+      if (a.out_logp) a.out_logp[row] = __builtin_nanf("");
+    }
+    return;
+  }
+  // Weights exp((z - m) / T) of the row, widened to float32 then float64.
+  const DT* xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const double m = a.st_max[row], Td = a.T;
+  auto wt = [&](int64_t x) { return exp(((double)__uint_as_float(gbits_at<DT>(xr, x)) - m) / Td); };
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  double s = 0.0;
+  for (int64_t x = e_begin + tid; x < e_end; x += NT) s += wt(x);
+  s = block_sum_f64(sh, s);
+  if (tid == 0) st_dev(&a.p_w[row * a.S + seg], s);
+  if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
+  const double* pw = a.p_w + row * a.S;
+  __shared__ int s_seg;
+  __shared__ double s_in, s_W;
+  __shared__ uint32_t s_tok;
+  if (tid == 0) {
+    double W = 0.0;
+    for (int sg = 0; sg < a.S; ++sg) W += ld_dev(&pw[sg]);
+    const double target = (double)a.u[row] * W;
+    double cum = 0.0;
+    int pick = -1;
+    for (int sg = 0; sg < a.S; ++sg) {
+      if (target < cum + ld_dev(&pw[sg])) {
+        pick = sg;
+        break;
+      }
+      cum += ld_dev(&pw[sg]);
+    }
+    double tin = target - cum;
+    if (pick < 0) {
+      for (int sg = a.S - 1; sg >= 0; --sg)
+        if (ld_dev(&pw[sg]) > 0.0) {
+          pick = sg;
+          break;
+        }
+      if (pick < 0) pick = 0;
+      tin = ld_dev(&pw[pick]);
+    }
+    s_seg = pick;
+    s_in = tin;
+    s_W = W;
+    s_tok = kFail;
+  }
+  __syncthreads();
+  const int64_t eb = (int64_t)s_seg * a.seg_len, ee = min(a.V, eb + a.seg_len);
+  const int64_t per = (ee - eb + NT - 1) / NT;
+  const int64_t lo = min(ee, eb + tid * per), hi = min(ee, lo + per);
+  double local = 0.0;
+  for (int64_t x = lo; x < hi; ++x) local += wt(x);
+  double total;
+  const double excl = block_excl_scan_f64(sh, local, &total);
+  const double tin = s_in;
+  if (tin >= excl && tin < excl + local) {
+    double c = excl;
+    for (int64_t x = lo; x < hi; ++x) {
+      c += wt(x);
+      if (tin < c) {
+        s_tok = (uint32_t)x;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t tok = s_tok;
+    if (tok == kFail) {
+      for (int64_t x = ee - 1; x >= eb; --x)
+        if (wt(x) > 0.0) {
+          tok = (uint32_t)x;
+          break;
+        }
+      if (tok == kFail) tok = (uint32_t)eb;
+    }
+    a.out_token[row] = tok;
+    if (a.out_logp)
+      a.out_logp[row] = (float)(((double)__uint_as_float(gbits_at<DT>(xr, tok)) - m) / Td - log(s_W));
+  }
+}
+
+hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
+  const bool vec = a.vec_t && a.vec_d;
+  const unsigned npos = (unsigned)(a.B * a.gamma * a.S);
+  if (vec)
+    hipLaunchKernelGGL(coupling_kernel<true>, dim3(npos), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(coupling_kernel<false>, dim3(npos), dim3(NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.T == 0.0f) return e;
+  if (vec)
+    hipLaunchKernelGGL(draw_lse_kernel<true>, dim3((unsigned)(a.B * 2 * a.S)), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(draw_lse_kernel<false>, dim3((unsigned)(a.B * 2 * a.S)), dim3(NT), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.S)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_draw_rows(int dtype, const DrawArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.rows * a.S));
+  if (dtype == 0)
+    hipLaunchKernelGGL(row_draw_kernel<float>, grid, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(row_draw_kernel<uint16_t>, grid, dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace vsel
