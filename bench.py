@@ -49,6 +49,28 @@ def time_calls(fn, n, warmup, stream):
     return ev0.elapsed_time(ev1) * 1e3 / n  # microseconds per call
 
 
+def time_graph(fn, n, stream):
+    """Device microseconds per call: n calls captured in one graph, replayed."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / (reps * n)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,37 +169,53 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
         n = max(1, -(-total // (x.numel() * x.element_size())))
         return [x] + [x.clone() for _ in range(n - 1)]
 
+    # Latency-bound configurations: eager microseconds per call (includes the
+    # Python binding and the launch) and device microseconds per call (graph
+    # replay); cold = inputs rotated over >= 256 MB of copies, warm = one buffer.
+    def lat(name, fn_warm, fn_cold, n=100):
+        ex[name + "_eager_us"] = time_calls(fn_warm, n, 5, stream)
+        ex[name + "_device_warm_us"] = time_graph(fn_warm, 20, stream)
+        ex[name + "_device_cold_us"] = time_graph(fn_cold, 20, stream)
+
     # config 1: one row argmax
     row, _ = W.greedy_single_row()
     r1 = cold_copies(torch.from_numpy(row).to(dev), 1 << 28)
-    ex["argmax_1x202048_warm_us"] = time_calls(lambda i: vsel.vsel_argmax(r1[0]), 200, 10, stream)
-    ex["argmax_1x202048_cold_us"] = time_calls(lambda i: vsel.vsel_argmax(r1[i % len(r1)]), 200, 10, stream)
+    o1 = torch.empty(1, dtype=torch.int32, device=dev)
+    lat("argmax_1x202048", lambda i: vsel.vsel_argmax(r1[0], out_idx=o1, want_val=False),
+        lambda i: vsel.vsel_argmax(r1[i % len(r1)], out_idx=o1, want_val=False))
     del r1
     # config 2: verify rows, k = 84
     for rows in (3, 49):
         x = W.verify_topk_rows(rows=rows)
-        xs = cold_copies(torch.from_numpy(x).to(dev))
-        ex[f"topk_{rows}x248320_k84_warm_us"] = time_calls(lambda i: vsel.vsel_topk(xs[0], 84), 100, 5, stream)
-        ex[f"topk_{rows}x248320_k84_cold_us"] = time_calls(lambda i: vsel.vsel_topk(xs[i % len(xs)], 84), 100, 5, stream)
+        xs = cold_copies(torch.from_numpy(x).to(dev), 1 << 28)
+        o2 = dict(vals=torch.empty((rows, 84), dtype=torch.float32, device=dev),
+                  ids=torch.empty((rows, 84), dtype=torch.int32, device=dev),
+                  argmax=torch.empty(rows, dtype=torch.int32, device=dev), lse=None)
+        lat(f"topk_{rows}x248320_k84", lambda i: vsel.vsel_topk(xs[0], 84, out=o2),
+            lambda i: vsel.vsel_topk(xs[i % len(xs)], 84, out=o2))
         del xs
     # config 3: sampling
     x, u = W.sampling_rows()
-    xs = cold_copies(torch.from_numpy(x).to(dev))
+    xs = cold_copies(torch.from_numpy(x).to(dev), 1 << 28)
     ud = torch.from_numpy(u).to(dev)
-    ex["sample_64x202048_warm_us"] = time_calls(lambda i: vsel.vsel_sample(xs[0], 0.7, 20, 0.95, ud), 100, 5, stream)
-    ex["sample_64x202048_cold_us"] = time_calls(lambda i: vsel.vsel_sample(xs[i % len(xs)], 0.7, 20, 0.95, ud), 100, 5, stream)
+    ot = torch.empty(64, dtype=torch.int32, device=dev)
+    ol = torch.empty(64, dtype=torch.float32, device=dev)
+    lat("sample_64x202048", lambda i: vsel.vsel_sample(xs[0], 0.7, 20, 0.95, ud, out_token=ot, out_logprob=ol),
+        lambda i: vsel.vsel_sample(xs[i % len(xs)], 0.7, 20, 0.95, ud, out_token=ot, out_logprob=ol))
     del xs
-    # config 4: speculative acceptance
+    # config 4: speculative acceptance (target + draft rows: 440 MB, already past the Infinity Cache)
     d = W.speculative_batch()
     g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     tg, dr = g(d["target"]), g(d["draft"])
     args = (g(d["tokens"].view(np.int32)), g(d["u_acc"]), g(d["u_res"]), g(d["u_bon"]), 32, 8, 1.0)
     so = vsel.vsel_spec_accept(tg, dr, *args)
-    ex["spec_accept_32x8_warm_us"] = time_calls(lambda i: vsel.vsel_spec_accept(tg, dr, *args, out=so), 50, 5, stream)
+    ex["spec_accept_32x8_eager_us"] = time_calls(lambda i: vsel.vsel_spec_accept(tg, dr, *args, out=so), 50, 5, stream)
+    ex["spec_accept_32x8_device_us"] = time_graph(lambda i: vsel.vsel_spec_accept(tg, dr, *args, out=so), 10, stream)
     L = so["len_mrs"].cpu().numpy()
     tested = int(np.minimum(L + 1, 8).sum())
     ex["spec_accept_32x8_per_position_acceptance"] = float(L.sum() / tested)
     ex["spec_accept_32x8_mean_summin"] = float(so["summin"].float().mean().item())
+    del tg, dr
     # fp32 variant of the headline batch (one buffer pair, 827 MB each)
     x32 = bufs[0][:, :V].float().contiguous()
     x32b = [x32, x32.clone()]

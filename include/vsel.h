@@ -140,7 +140,8 @@ vsel_status vsel_topk(const void* logits, int dtype, int64_t rows, int64_t vocab
  *      the last kept candidate with w_j > 0.
  *   out_logprob = log(w_j / W), the log-probability under the distribution
  *   actually drawn from.
- *   temperature >= 0, 0 <= top_k <= VSEL_K_MAX, 0 < top_p <= 1
+ *   temperature >= 0, 0 <= top_k <= VSEL_K_MAX, 0 < top_p <= 1; with
+ *   top_k == 0, vocab <= 67,108,864 (256 segments of 1,024 chunks of 256)
  *   u           [rows] float32 in [0, 1)
  *   out_token   [rows] uint32 (VSEL_NONFINITE for a fail-closed row)
  *   out_logprob [rows] float32 or NULL
@@ -165,6 +166,7 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
  * acceptance ceiling of any distribution-preserving rule ("The acceptance
  * ceiling"), for every position.  temperature == 0 is greedy: both rules are
  * argmax-against-argmax and summin_i is 1 where the two argmaxes agree, else 0.
+ *   1 <= gamma <= 256; temperature >= 0 and finite; vocab <= 67,108,864
  *   target_logits [batch*(gamma+1), ld_t] float32; row b*(gamma+1)+i is verify
  *                 position i of sequence b (row b*(gamma+1)+gamma: bonus row)
  *   draft_logits  [batch*gamma, ld_d] float32

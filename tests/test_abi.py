@@ -83,6 +83,7 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
                                   a["vocab"], a["T"], fake, fake, fake, fake, fake, fake, None, None, None,
                                   ws, 1 << 20, None)
     assert spec(gamma=0) == EINVAL
+    assert spec(gamma=257) == EINVAL
     assert spec(batch=0) == EINVAL
     assert spec(T=-1.0) == EINVAL
     assert spec(ld_t=99) == EINVAL

@@ -30,7 +30,7 @@ struct Plan {
 // kMinSegment, a row's k-record sets must fit one workgroup's merge buffer,
 // and the split never multiplies the work items past kMaxSplitWork.
 int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap) {
-  int64_t b = std::max<int64_t>(1, cdiv(V, kMinSegment));
+  int64_t b = std::min<int64_t>(kMaxSegments, std::max<int64_t>(1, cdiv(V, kMinSegment)));
   if (k > 0) b = std::min<int64_t>(b, std::max<int64_t>(1, cap / k));
   return std::min<int64_t>(b, std::max<int64_t>(1, cdiv(kMaxSplitWork, rows)));
 }
@@ -38,12 +38,13 @@ int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap) {
 // Segments per row for a grid that runs `resident` workgroups at once:
 // minimise rounds x (segment length + fixed cost), so that the chip is full
 // and no launch ends with a nearly empty last round.
-Plan plan_segments(int64_t rows, int64_t V, int64_t k, int64_t resident, int cap) {
+// Segment lengths are multiples of `granule` elements (a multiple of 8).
+Plan plan_segments(int64_t rows, int64_t V, int64_t k, int64_t resident, int cap, int64_t granule = 8) {
   const int64_t sb = seg_bound(rows, V, k, cap);
-  Plan best{1, cdiv(V, 8) * 8};
+  Plan best{1, cdiv(V, granule) * granule};
   int64_t best_cost = INT64_MAX;
   for (int64_t S = 1; S <= sb; ++S) {
-    const int64_t seg = cdiv(cdiv(V, S), 8) * 8;
+    const int64_t seg = cdiv(cdiv(V, S), granule) * granule;
     const int64_t Sx = cdiv(V, seg);
     if (Sx != S) continue;
     const int64_t cost = cdiv(rows * Sx, std::max<int64_t>(1, resident)) * (seg + kSegOverhead);
@@ -84,15 +85,29 @@ Plan plan_scan_bound(int64_t rows, int64_t V) {
   return Plan{(int32_t)sb, cdiv(cdiv(V, sb), 8) * 8};
 }
 
+// Draws: segments a multiple of kChunk elements, at most kChunksPerSeg
+// chunks each, at most kMaxSegments per row.
+constexpr int64_t kMaxDrawVocab = (int64_t)kMaxSegments * kChunk * kChunksPerSeg;
+Plan plan_draw(int64_t rows, int64_t V, int64_t resident) {
+  const Plan p = plan_segments(rows, V, 0, resident, kCapLarge);
+  int64_t seg = cdiv(p.seg_len, kChunk) * kChunk;
+  seg = std::min<int64_t>(seg, (int64_t)kChunk * kChunksPerSeg);
+  seg = std::max<int64_t>(seg, cdiv(cdiv(V, kMaxSegments), kChunk) * kChunk);
+  return Plan{(int32_t)cdiv(V, seg), seg};
+}
+
 // Top-k: the small candidate buffer whenever it can hold the merge, which
 // keeps four workgroups per CU.
 struct TopkPlan {
   Plan p;
   int cap;
 };
+// Top-k segments are whole tiles (kTopkTile elements of 16 bytes per lane
+// x 8 groups), so only a row's last segment ends in a partial tile.
 TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k) {
-  if (2 * k <= kCapSmall) return TopkPlan{plan_segments(rows, V, k, resident_topk(dtype, lse, kCapSmall), kCapSmall), kCapSmall};
-  return TopkPlan{plan_segments(rows, V, k, resident_topk(dtype, lse, kCapLarge), kCapLarge), kCapLarge};
+  const int64_t tile = (int64_t)kTopkGroups * 256 * (dtype == VSEL_F32 ? 4 : 8);
+  const int cap = (2 * k <= kCapSmall) ? kCapSmall : kCapLarge;
+  return TopkPlan{plan_segments(rows, V, k, resident_topk(dtype, lse, cap), cap, tile), cap};
 }
 Plan plan_topk_bound(int64_t rows, int64_t V, int64_t k) {
   const int64_t sb = seg_bound(rows, V, k, kCapLarge);
@@ -177,16 +192,17 @@ StatsWs stats_layout(Layout& L, int64_t nrows) {
 struct RowDrawWs {
   ScanWs scan;
   StatsWs st;
-  size_t dtickets, p_w;
+  size_t dtickets, p_w, p_c;
 };
-RowDrawWs rowdraw_layout(Layout& L, int64_t rows, const Plan& ps, const Plan& pd) {
+RowDrawWs rowdraw_layout(Layout& L, int64_t rows, int64_t V, const Plan& ps) {
   RowDrawWs w{};
   L.reserve_tickets((size_t)(2 * rows));
   w.scan = scan_layout(L, rows, ps, false);
   w.scan.tickets = 0;
   w.dtickets = (size_t)rows * 4;
   w.st = stats_layout(L, rows);
-  w.p_w = L.take((size_t)(rows * pd.S) * 8);
+  w.p_w = L.take((size_t)(rows * kMaxSegments) * 8);
+  w.p_c = L.take((size_t)(rows * cdiv(V, kChunk)) * 8);
   return w;
 }
 
@@ -194,9 +210,9 @@ struct SpecWs {
   ScanWs scan;
   StatsWs st;
   size_t tk_pos, tk_seq, tk_row, tk_draw;
-  size_t p_summin, acc, draw_L, p_lse, lse64, p_w;
+  size_t p_summin, acc, draw_L, p_lse, lse64, p_w, p_c;
 };
-SpecWs spec_layout(Layout& L, int64_t B, int64_t G, const Plan& ps, const Plan& pp) {
+SpecWs spec_layout(Layout& L, int64_t B, int64_t G, int64_t V, const Plan& ps, const Plan& pp) {
   SpecWs w{};
   const int64_t nrows = B * (2 * G + 1);
   const size_t nt = (size_t)(nrows + B * G + B + 2 * B + B);
@@ -214,7 +230,8 @@ SpecWs spec_layout(Layout& L, int64_t B, int64_t G, const Plan& ps, const Plan& 
   w.draw_L = L.take((size_t)B * 4);
   w.p_lse = L.take((size_t)(2 * B * pp.S) * 8);
   w.lse64 = L.take((size_t)(2 * B) * 8);
-  w.p_w = L.take((size_t)(B * pp.S) * 8);
+  w.p_w = L.take((size_t)(B * kMaxSegments) * 8);
+  w.p_c = L.take((size_t)(B * cdiv(V, kChunk)) * 8);
   return w;
 }
 
@@ -279,7 +296,8 @@ size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int3
       size_t need = a.off;
       if (k == 0) {
         Layout b;
-        rowdraw_layout(b, rows, plan_scan_bound(rows, vocab), plan_scan_bound(rows, vocab));
+        if (vocab > kMaxDrawVocab) return 0;
+        rowdraw_layout(b, rows, vocab, plan_scan_bound(rows, vocab));
         need = std::max(need, b.off);
       } else if (k > 1) {
         const int64_t kk = std::min<int64_t>(k, vocab);
@@ -291,8 +309,9 @@ size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int3
     }
     case VSEL_OP_SPEC_ACCEPT: {
       const int64_t B = rows, G = k;
-      if (B < 1 || G < 1 || !rows_ok(B * (2 * G + 1), vocab, vocab)) return 0;
-      spec_layout(L, B, G, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
+      if (B < 1 || G < 1 || G > kMaxSegments || vocab > kMaxDrawVocab || !rows_ok(B * (2 * G + 1), vocab, vocab))
+        return 0;
+      spec_layout(L, B, G, vocab, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
       return L.off;
     }
     default:
@@ -388,12 +407,12 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
   }
 
   if (top_k == 0) {
+    if (vocab > kMaxDrawVocab) return VSEL_EINVAL;
     Layout L;
-    const Plan bnd = plan_scan_bound(rows, vocab);
-    const RowDrawWs w = rowdraw_layout(L, rows, bnd, bnd);
+    const RowDrawWs w = rowdraw_layout(L, rows, vocab, plan_scan_bound(rows, vocab));
     if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
     const Plan ps = plan_scan(dtype, false, rows, vocab);
-    const Plan pd = ps;
+    const Plan pd = plan_draw(rows, vocab, resident_scan(dtype, false));
     ScanArgs a = scan_args(logits, dtype, rows, vocab, ld, ps, temperature);
     a.tickets = at<uint32_t>(ws, w.scan.tickets);
     a.p_key = at<uint64_t>(ws, w.scan.p_key);
@@ -419,7 +438,9 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
     d.out_token = out_token;
     d.out_logp = out_logprob;
     d.tickets = at<uint32_t>(ws, w.dtickets);
+    d.nchunk = cdiv(vocab, kChunk);
     d.p_w = at<double>(ws, w.p_w);
+    d.p_c = at<double>(ws, w.p_c);
     return launched(launch_draw_rows(dtype, d, s));
   }
 
@@ -441,14 +462,15 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
                              uint32_t* out_tok_aa, float* out_summin, void* ws, size_t ws_bytes, void* stream) {
   if (!target || !draft || !draft_tokens || !u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs)
     return VSEL_EINVAL;
-  if (batch < 1 || gamma < 1 || vocab < 1 || vocab >= (int64_t(1) << 31) || ld_t < vocab || ld_d < vocab)
+  if (batch < 1 || gamma < 1 || gamma > kMaxSegments || vocab < 1 || vocab >= (int64_t(1) << 31) || ld_t < vocab ||
+      ld_d < vocab)
     return VSEL_EINVAL;
   if (!rows_ok(batch * (2 * (int64_t)gamma + 1), vocab, vocab)) return VSEL_EINVAL;
   if (!(temperature >= 0.0f) || std::isinf(temperature)) return VSEL_EINVAL;
-  if (!aligned_elem(target, 4) || !aligned_elem(draft, 4)) return VSEL_EINVAL;
+  if (!aligned_elem(target, 4) || !aligned_elem(draft, 4) || vocab > kMaxDrawVocab) return VSEL_EINVAL;
   const int64_t B = batch, G = gamma;
   Layout L;
-  const SpecWs w = spec_layout(L, B, G, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
+  const SpecWs w = spec_layout(L, B, G, vocab, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
   if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
   const Plan ps = plan_scan(VSEL_F32, temperature > 0.0f, B * (2 * G + 1), vocab);
   const Plan pp = plan_scan(VSEL_F32, true, B * G, vocab);
@@ -507,7 +529,12 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   p.draw_L = at<int32_t>(ws, w.draw_L);
   p.p_lse = at<double>(ws, w.p_lse);
   p.lse64 = at<double>(ws, w.lse64);
+  const Plan pd = plan_draw(B, vocab, resident_scan(VSEL_F32, true));
+  p.dseg = pd.seg_len;
+  p.dS = pd.S;
+  p.nchunk = cdiv(vocab, kChunk);
   p.p_w = at<double>(ws, w.p_w);
+  p.p_c = at<double>(ws, w.p_c);
   return launched(launch_spec(p, s));
 }
 

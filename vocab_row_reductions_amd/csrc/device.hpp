@@ -429,6 +429,55 @@ __device__ __forceinline__ bool last_done(SelShared& sh, uint32_t* ticket, uint3
   return sh.last != 0;
 }
 
+// ---------------------------------------------------------------- merges
+// Reductions over per-segment partials, loaded in parallel (one thread per
+// segment) so that their device-scope load latencies overlap.  S <= NT.
+__device__ __forceinline__ double block_sum_f64(SelShared& sh, double v) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  v = wave_sum_f64(v);
+  __syncthreads();
+  if (lane == 0) sh.ws[wave] = v;
+  __syncthreads();
+  double t = sh.ws[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) t += sh.ws[q];
+  return t;
+}
+
+// Sum of p[0..S) (all threads get it; fixed order for a given S).
+__device__ __forceinline__ double merge_sum(SelShared& sh, const double* p, int S) {
+  const int tid = threadIdx.x;
+  return block_sum_f64(sh, tid < S ? ld_dev(&p[tid]) : 0.0);
+}
+
+// Combined (key max, log-sum-exp) of S partials (all threads get them).
+__device__ __forceinline__ void merge_key_lse(SelShared& sh, const uint64_t* pk, const float* pm, const double* ps,
+                                              int S, float c, uint64_t& P, LSE& r) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t k = 0;
+  LSE v{-__builtin_inff(), 0.0};
+  if (tid < S) {
+    if (pk) k = ld_dev(&pk[tid]);
+    v = LSE{ld_dev(&pm[tid]), ld_dev(&ps[tid])};
+  }
+  k = wave_max_u64(k);
+  v = wave_lse(v, c);
+  __syncthreads();
+  if (lane == 0) {
+    sh.wk[wave] = k;
+    sh.wm[wave] = v.m;
+    sh.ws[wave] = v.s;
+  }
+  __syncthreads();
+  P = sh.wk[0];
+  r = LSE{sh.wm[0], sh.ws[0]};
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) {
+    P = sh.wk[q] > P ? sh.wk[q] : P;
+    r = lse_merge(r, LSE{sh.wm[q], sh.ws[q]}, c);
+  }
+}
+
 // Work index of this workgroup, remapped so that consecutive work items run
 // on the same XCD (workgroups are dealt round-robin over the 8 XCDs), which
 // keeps the segments of one row and their partials in one L2.

@@ -10,6 +10,10 @@ namespace vsel {
 constexpr size_t kWsAlign = 256;
 constexpr int kCapSmall = 2048;  // LDS candidate records per workgroup (about 35 KiB of LDS in all)
 constexpr int kCapLarge = 4096;  // for large k or many segments per row
+constexpr int kMaxSegments = 256;  // segments per row, at most (one thread each in a merge)
+constexpr int kTopkGroups = 8;       // 16-byte groups per lane per top-k tile
+constexpr int kChunk = 256;          // draw chunk: elements per float64 chunk mass (one per thread)
+constexpr int kChunksPerSeg = 1024;  // chunks per draw segment, at most
 
 inline size_t align_up(size_t x, size_t a = kWsAlign) { return (x + a - 1) / a * a; }
 
@@ -112,7 +116,12 @@ struct SpecArgs {
   int32_t* draw_L;      // [B]: -1 none, 0..gamma-1 residual at L, gamma bonus
   double* p_lse;        // [B*2*S] float64 partial sums for the draw rows
   double* lse64;        // [B*2]
-  double* p_w;          // [B*S] partial draw masses
+  // the draw: segments of dseg elements (a multiple of kChunk), dS per row
+  int64_t dseg;
+  int32_t dS;
+  int64_t nchunk;       // chunks per row, ceil(V / kChunk)
+  double* p_w;          // [B*dS] segment masses
+  double* p_c;          // [B*nchunk] chunk masses
 };
 
 // Plain full-row draw for vsel_sample with top_k == 0.
@@ -131,7 +140,9 @@ struct DrawArgs {
   uint32_t* out_token;
   float* out_logp;
   uint32_t* tickets;
-  double* p_w;
+  int64_t nchunk;       // chunks per row, ceil(V / kChunk); seg_len is a multiple of kChunk
+  double* p_w;          // [rows*S] segment masses
+  double* p_c;          // [rows*nchunk] chunk masses
 };
 
 hipError_t launch_scan(int dtype, bool want_lse, const ScanArgs& a, hipStream_t s);

@@ -133,16 +133,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
       st_dev(&a.p_s[slot], r.s);
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
-    if (tid == 0) {
-      P = 0;
-      r = LSE{-__builtin_inff(), 0.0};
-      for (int sg = 0; sg < a.S; ++sg) {
-        const int64_t sl = row * a.S + sg;
-        const uint64_t pk = ld_dev(&a.p_key[sl]);
-        P = pk > P ? pk : P;
-        r = lse_merge(r, LSE{ld_dev(&a.p_m[sl]), ld_dev(&a.p_s[sl])}, c);
-      }
-    }
+    const int64_t s0 = row * a.S;
+    merge_key_lse(sh, a.p_key + s0, a.p_m + s0, a.p_s + s0, a.S, c, P, r);
   }
   if (tid != 0) return;
 

@@ -28,18 +28,6 @@ namespace vsel {
 
 constexpr int PG = 4;  // 16-byte groups per lane per tile (float32 rows)
 
-__device__ __forceinline__ double block_sum_f64(SelShared& sh, double v) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  v = wave_sum_f64(v);
-  __syncthreads();
-  if (lane == 0) sh.ws[wave] = v;
-  __syncthreads();
-  double t = sh.ws[0];
-#pragma unroll
-  for (int q = 1; q < NWAVE; ++q) t += sh.ws[q];
-  return t;
-}
-
 // Exclusive prefix sum over the workgroup (thread order), float64.
 __device__ __forceinline__ double block_excl_scan_f64(SelShared& sh, double v, double* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -125,10 +113,7 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
   if (a.S > 1) {
     if (tid == 0) st_dev(&a.p_summin[pos * a.S + seg], tot);
     if (!last_done(sh, a.tk_pos + pos, (uint32_t)a.S)) return;
-    if (tid == 0) {
-      tot = 0.0;
-      for (int sg = 0; sg < a.S; ++sg) tot += ld_dev(&a.p_summin[pos * a.S + sg]);
-    }
+    tot = merge_sum(sh, a.p_summin + pos * a.S, a.S);
   }
   // Position decision (one thread): coupling sum and the accept test.
   if (tid == 0) {
@@ -149,13 +134,15 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     if (a.summin) st_dev(&a.summin[pos], bad ? __builtin_nanf("") : (float)tot);
   }
   if (!last_done(sh, a.tk_seq + b, (uint32_t)G)) return;
+  if (tid < G) sh.hist[tid] = ld_dev(&a.acc[b * G + tid]);
+  __syncthreads();
   if (tid != 0) return;
 
   // Sequence decision.
   uint32_t* tm = a.tok_mrs + b * (G + 1);
   uint32_t* ta = a.tok_aa ? a.tok_aa + b * (G + 1) : nullptr;
   bool fail = a.st_bad[b * (G + 1) + G] != 0;
-  for (int64_t q = 0; q < G; ++q) fail |= ld_dev(&a.acc[b * G + q]) == 2u;
+  for (int64_t q = 0; q < G; ++q) fail |= sh.hist[q] == 2u;
   for (int64_t q = 0; q <= G; ++q) {
     tm[q] = kFail;
     if (ta) ta[q] = kFail;
@@ -188,7 +175,7 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
   }
   int64_t L = G;
   for (int64_t q = 0; q < G; ++q)
-    if (ld_dev(&a.acc[b * G + q]) == 0u) {
+    if (sh.hist[q] == 0u) {
       L = q;
       break;
     }
@@ -233,68 +220,115 @@ __global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
   if (a.S > 1) {
     if (tid == 0) st_dev(&a.p_lse[item * a.S + seg], s);
     if (!last_done(sh, a.tk_row + item, (uint32_t)a.S)) return;
-    if (tid == 0) {
-      s = 0.0;
-      for (int sg = 0; sg < a.S; ++sg) s += ld_dev(&a.p_lse[item * a.S + sg]);
-    }
+    s = merge_sum(sh, a.p_lse + item * a.S, a.S);
   }
   if (tid == 0) a.lse64[item] = m / Td + log(s);
 }
 
 // ---------------------------------------------------------------- pass 4 (and the full-row draw)
-// Weight of element x of the draw: residual max(p - q, 0) with float64
-// log-sum-exps, or exp((z - m) / T) (p up to a constant factor, which the
-// inverse CDF over u * W does not see).
-struct DrawRow {
-  const float* z;
-  const float* d;  // null: plain p
+// An inverse-CDF draw in id order over W = sum of weights, in three levels:
+// segment masses, 256-element chunk masses, then one element per thread.
+// Every mass is a float64 sum; a segment's mass is the in-order sum of its
+// chunk masses, so the levels agree up to the last bits of the final scan.
+
+// Source of a draw: weight w(x) >= 0 of row element x.
+//   residual: max(p - q, 0), p = exp(z/T - lp), q = exp(d/T - lq)
+//   plain:    exp((z - m) / T), proportional to p (u*W does not see the scale)
+template <typename DT>
+struct DrawSrc {
+  const DT* z;
+  const float* d;  // null: plain
   double lp, lq, m, T;
-  __device__ __forceinline__ double weight(int64_t x) const {
+  int64_t V;
+  __device__ __forceinline__ float zv(int64_t x) const { return __uint_as_float(gbits_at<DT>(z, x)); }
+  __device__ __forceinline__ double w(float zx, float dx) const {
     if (d) {
-      const double p = exp((double)z[x] / T - lp), q = exp((double)d[x] / T - lq);
+      const double p = exp((double)zx / T - lp), q = exp((double)dx / T - lq);
       return p > q ? p - q : 0.0;
     }
-    return exp(((double)z[x] - m) / T);
+    return exp(((double)zx - m) / T);
   }
 };
 
-// Float64 mass of one segment (coalesced, lane-strided).
-__device__ __forceinline__ double segment_mass(const DrawRow& r, int64_t e_begin, int64_t e_end) {
-  double s = 0.0;
-  for (int64_t x = e_begin + threadIdx.x; x < e_end; x += NT) s += r.weight(x);
-  return s;
+// Chunk masses of segment [e_begin, e_end): each wave takes 4 chunks per
+// step (16 loads per lane in flight), reduces each chunk's 256 weights (4 per
+// lane) in float64, and writes the masses to `cm` (LDS) and `pc` (global,
+// indexed from the segment's first chunk).  Returns the segment mass in
+// thread 0: the in-order sum of its chunk masses.
+template <typename DT>
+__device__ double chunk_masses(const DrawSrc<DT>& r, int64_t e_begin, int64_t e_end, double* cm, double* pc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int CW = 4;  // chunks per wave per step
+  const int nch = (int)((e_end - e_begin + kChunk - 1) / kChunk);
+  for (int q0 = 0; q0 < nch; q0 += NWAVE * CW) {
+    float zz[CW][4], dd[CW][4];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int q = q0 + wave * CW + j;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t x = e_begin + (int64_t)q * kChunk + lane * 4 + e;
+        const bool in = q < nch && x < e_end;
+        const int64_t xs = in ? x : e_begin;
+        const float zx = r.zv(xs);
+        const float dx = r.d ? r.d[xs] : 0.0f;
+        zz[j][e] = in ? zx : -__builtin_inff();  // weight 0
+        dd[j][e] = in ? dx : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int q = q0 + wave * CW + j;
+      double s = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += r.w(zz[j][e], dd[j][e]);
+      s = wave_sum_f64(s);
+      if (lane == 0 && q < nch) {
+        cm[q] = s;
+        st_dev(&pc[q], s);
+      }
+    }
+  }
+  __syncthreads();
+  double tot = 0.0;
+  if (tid == 0)
+    for (int q = 0; q < nch; ++q) tot += cm[q];
+  return tot;
 }
 
-// Last workgroup: choose the segment whose prefix of masses crosses u*W,
-// rescan it in id order and return the token (valid in thread 0).
-__device__ uint32_t draw_finish(SelShared& sh, const DrawRow& r, const double* pw, int S, int64_t seg_len,
-                                int64_t V, double u, double* W_out) {
+// The draw itself (one workgroup): segment, then chunk, then element.  pw
+// (LDS) holds the S segment masses, pc (global) the row's chunk masses.
+// Returns the token in every thread; *W_out (thread 0) is the total mass.
+template <typename DT>
+__device__ uint32_t draw_pick(SelShared& sh, const DrawSrc<DT>& r, const double* pw, const double* pc, int S,
+                              int64_t seg_len, double u, double* W_out) {
   const int tid = threadIdx.x;
-  __shared__ int s_seg;
+  __shared__ double cm[kChunksPerSeg];
+  __shared__ int s_seg, s_ch;
   __shared__ double s_in;
   __shared__ uint32_t s_tok;
   if (tid == 0) {
     double W = 0.0;
-    for (int sg = 0; sg < S; ++sg) W += ld_dev(&pw[sg]);
+    for (int sg = 0; sg < S; ++sg) W += pw[sg];
     const double target = u * W;
     double cum = 0.0;
     int pick = -1;
     for (int sg = 0; sg < S; ++sg) {
-      if (target < cum + ld_dev(&pw[sg])) {
+      if (target < cum + pw[sg]) {
         pick = sg;
         break;
       }
-      cum += ld_dev(&pw[sg]);
+      cum += pw[sg];
     }
     double tin = target - cum;
     if (pick < 0) {  // rounding at the very top: the last segment with mass
       for (int sg = S - 1; sg >= 0; --sg)
-        if (ld_dev(&pw[sg]) > 0.0) {
+        if (pw[sg] > 0.0) {
           pick = sg;
           break;
         }
       if (pick < 0) pick = 0;
-      tin = ld_dev(&pw[pick]);
+      tin = pw[pick];
     }
     s_seg = pick;
     s_in = tin;
@@ -302,33 +336,50 @@ __device__ uint32_t draw_finish(SelShared& sh, const DrawRow& r, const double* p
     *W_out = W;
   }
   __syncthreads();
-  const int64_t e_begin = (int64_t)s_seg * seg_len, e_end = min(V, e_begin + seg_len);
-  const int64_t len = e_end - e_begin;
-  const int64_t per = (len + NT - 1) / NT;
-  const int64_t lo = min(e_end, e_begin + tid * per), hi = min(e_end, lo + per);
-  double local = 0.0;
-  for (int64_t x = lo; x < hi; ++x) local += r.weight(x);
-  double total;
-  const double excl = block_excl_scan_f64(sh, local, &total);
-  const double tin = s_in;
-  if (tin >= excl && tin < excl + local) {
-    double c = excl;
-    for (int64_t x = lo; x < hi; ++x) {
-      c += r.weight(x);
-      if (tin < c) {
-        s_tok = (uint32_t)x;
+  const int64_t e_begin = (int64_t)s_seg * seg_len, e_end = min(r.V, e_begin + seg_len);
+  const int nch = (int)((e_end - e_begin + kChunk - 1) / kChunk);
+  for (int q = tid; q < nch; q += NT) cm[q] = ld_dev(&pc[e_begin / kChunk + q]);
+  __syncthreads();
+  if (tid == 0) {
+    const double tin = s_in;
+    double cum = 0.0;
+    int pick = -1;
+    for (int q = 0; q < nch; ++q) {
+      if (tin < cum + cm[q]) {
+        pick = q;
         break;
       }
+      cum += cm[q];
     }
+    double t2 = tin - cum;
+    if (pick < 0) {
+      for (int q = nch - 1; q >= 0; --q)
+        if (cm[q] > 0.0) {
+          pick = q;
+          break;
+        }
+      if (pick < 0) pick = 0;
+      t2 = cm[pick];
+    }
+    s_ch = pick;
+    s_in = t2;
   }
   __syncthreads();
-  if (tid == 0 && s_tok == kFail) {  // rounding: the last element with weight in the segment
-    for (int64_t x = e_end - 1; x >= e_begin; --x)
-      if (r.weight(x) > 0.0) {
-        s_tok = (uint32_t)x;
+  const int64_t c0 = e_begin + (int64_t)s_ch * kChunk;
+  const int64_t x = c0 + tid;
+  const double wx = x < e_end ? r.w(r.zv(x), r.d ? r.d[x] : 0.0f) : 0.0;
+  double total;
+  const double excl = block_excl_scan_f64(sh, wx, &total);
+  const double t2 = s_in;
+  if (excl <= t2 && t2 < excl + wx) s_tok = (uint32_t)x;
+  __syncthreads();
+  if (tid == 0 && s_tok == kFail) {  // rounding: the chunk's last element with weight
+    for (int64_t y = min(e_end, c0 + kChunk) - 1; y >= c0; --y)
+      if (r.w(r.zv(y), r.d ? r.d[y] : 0.0f) > 0.0) {
+        s_tok = (uint32_t)y;
         break;
       }
-    if (s_tok == kFail) s_tok = (uint32_t)e_begin;
+    if (s_tok == kFail) s_tok = (uint32_t)c0;
   }
   __syncthreads();
   return s_tok;
@@ -336,16 +387,18 @@ __device__ uint32_t draw_finish(SelShared& sh, const DrawRow& r, const double* p
 
 __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   __shared__ SelShared sh;
+  __shared__ double cmw[kChunksPerSeg];
   const int tid = threadIdx.x;
-  const Item it = work_item(a.S);
+  const Item it = work_item(a.dS);
   const int64_t b = it.row;
   const int seg = (int)it.seg;
   if (b >= a.B) return;
   const int64_t G = a.gamma;
   const int32_t L = a.draw_L[b];
   if (L < 0) return;
-  DrawRow r;
+  DrawSrc<float> r;
   r.T = a.T;
+  r.V = a.V;
   double u;
   if (L < G) {
     r.z = a.tgt + (b * (G + 1) + L) * a.ld_t;
@@ -361,37 +414,41 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
     r.m = a.st_max[b * (G + 1) + G];
     u = a.u_bon[b];
   }
-  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
-  double s = block_sum_f64(sh, segment_mass(r, e_begin, e_end));
-  if (tid == 0) st_dev(&a.p_w[b * a.S + seg], s);
-  if (!last_done(sh, a.tk_draw + b, (uint32_t)a.S)) return;
-  double* pw = a.p_w + b * a.S;
+  double* pc = a.p_c + b * a.nchunk;
+  const int64_t e_begin = (int64_t)seg * a.dseg, e_end = min(a.V, e_begin + a.dseg);
+  const double ms = chunk_masses(r, e_begin, e_end, cmw, pc + e_begin / kChunk);
+  if (tid == 0) st_dev(&a.p_w[b * a.dS + seg], ms);
+  if (!last_done(sh, a.tk_draw + b, (uint32_t)a.dS)) return;
+  __shared__ double pw[kMaxSegments];
+  if (tid < a.dS) pw[tid] = ld_dev(&a.p_w[b * a.dS + tid]);
+  __syncthreads();
   // Degenerate residual (p <= q everywhere): draw from p instead.
   __shared__ int s_degen;
   if (tid == 0) {
     double W = 0.0;
-    for (int sg = 0; sg < a.S; ++sg) W += ld_dev(&pw[sg]);
+    for (int sg = 0; sg < a.dS; ++sg) W += pw[sg];
     s_degen = (r.d != nullptr && !(W > 0.0)) ? 1 : 0;
   }
   __syncthreads();
   if (s_degen) {
     r.d = nullptr;
     r.m = a.st_max[b * (G + 1) + L];
-    for (int sg = 0; sg < a.S; ++sg) {
-      const int64_t eb = (int64_t)sg * a.seg_len, ee = min(a.V, eb + a.seg_len);
-      const double ms = block_sum_f64(sh, segment_mass(r, eb, ee));
-      if (tid == 0) st_dev(&pw[sg], ms);
+    for (int sg = 0; sg < a.dS; ++sg) {
+      const int64_t eb = (int64_t)sg * a.dseg, ee = min(a.V, eb + a.dseg);
+      const double m2 = chunk_masses(r, eb, ee, cmw, pc + eb / kChunk);
+      if (tid == 0) pw[sg] = m2;
       __syncthreads();
     }
   }
   double W;
-  const uint32_t tok = draw_finish(sh, r, pw, a.S, a.seg_len, a.V, u, &W);
+  const uint32_t tok = draw_pick(sh, r, pw, pc, a.dS, a.dseg, u, &W);
   if (tid == 0) a.tok_mrs[b * (G + 1) + L] = tok;
 }
 
 template <typename DT>
 __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
   __shared__ SelShared sh;
+  __shared__ double cmw[kChunksPerSeg];
   const int tid = threadIdx.x;
   const Item it = work_item(a.S);
   const int64_t row = it.row;
@@ -404,81 +461,26 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
     }
     return;
   }
-  // Weights exp((z - m) / T) of the row, widened to float32 then float64.
-  const DT* xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
-  const double m = a.st_max[row], Td = a.T;
-  auto wt = [&](int64_t x) { return exp(((double)__uint_as_float(gbits_at<DT>(xr, x)) - m) / Td); };
+  DrawSrc<DT> r;
+  r.z = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  r.d = nullptr;
+  r.lp = r.lq = 0.0;
+  r.m = a.st_max[row];
+  r.T = a.T;
+  r.V = a.V;
+  double* pc = a.p_c + row * a.nchunk;
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
-  double s = 0.0;
-  for (int64_t x = e_begin + tid; x < e_end; x += NT) s += wt(x);
-  s = block_sum_f64(sh, s);
-  if (tid == 0) st_dev(&a.p_w[row * a.S + seg], s);
+  const double ms = chunk_masses(r, e_begin, e_end, cmw, pc + e_begin / kChunk);
+  if (tid == 0) st_dev(&a.p_w[row * a.S + seg], ms);
   if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
-  const double* pw = a.p_w + row * a.S;
-  __shared__ int s_seg;
-  __shared__ double s_in, s_W;
-  __shared__ uint32_t s_tok;
-  if (tid == 0) {
-    double W = 0.0;
-    for (int sg = 0; sg < a.S; ++sg) W += ld_dev(&pw[sg]);
-    const double target = (double)a.u[row] * W;
-    double cum = 0.0;
-    int pick = -1;
-    for (int sg = 0; sg < a.S; ++sg) {
-      if (target < cum + ld_dev(&pw[sg])) {
-        pick = sg;
-        break;
-      }
-      cum += ld_dev(&pw[sg]);
-    }
-    double tin = target - cum;
-    if (pick < 0) {
-      for (int sg = a.S - 1; sg >= 0; --sg)
-        if (ld_dev(&pw[sg]) > 0.0) {
-          pick = sg;
-          break;
-        }
-      if (pick < 0) pick = 0;
-      tin = ld_dev(&pw[pick]);
-    }
-    s_seg = pick;
-    s_in = tin;
-    s_W = W;
-    s_tok = kFail;
-  }
+  __shared__ double pw[kMaxSegments];
+  if (tid < a.S) pw[tid] = ld_dev(&a.p_w[row * a.S + tid]);
   __syncthreads();
-  const int64_t eb = (int64_t)s_seg * a.seg_len, ee = min(a.V, eb + a.seg_len);
-  const int64_t per = (ee - eb + NT - 1) / NT;
-  const int64_t lo = min(ee, eb + tid * per), hi = min(ee, lo + per);
-  double local = 0.0;
-  for (int64_t x = lo; x < hi; ++x) local += wt(x);
-  double total;
-  const double excl = block_excl_scan_f64(sh, local, &total);
-  const double tin = s_in;
-  if (tin >= excl && tin < excl + local) {
-    double c = excl;
-    for (int64_t x = lo; x < hi; ++x) {
-      c += wt(x);
-      if (tin < c) {
-        s_tok = (uint32_t)x;
-        break;
-      }
-    }
-  }
-  __syncthreads();
+  double W;
+  const uint32_t tok = draw_pick(sh, r, pw, pc, a.S, a.seg_len, (double)a.u[row], &W);
   if (tid == 0) {
-    uint32_t tok = s_tok;
-    if (tok == kFail) {
-      for (int64_t x = ee - 1; x >= eb; --x)
-        if (wt(x) > 0.0) {
-          tok = (uint32_t)x;
-          break;
-        }
-      if (tok == kFail) tok = (uint32_t)eb;
-    }
     a.out_token[row] = tok;
-    if (a.out_logp)
-      a.out_logp[row] = (float)(((double)__uint_as_float(gbits_at<DT>(xr, tok)) - m) / Td - log(s_W));
+    if (a.out_logp) a.out_logp[row] = (float)(((double)r.zv(tok) - r.m) / r.T - log(W));
   }
 }
 
@@ -496,7 +498,7 @@ hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
   else
     hipLaunchKernelGGL(draw_lse_kernel<false>, dim3((unsigned)(a.B * 2 * a.S)), dim3(NT), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.S)), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@
 
 namespace vsel {
 
-constexpr int TG = 8;               // 16-byte groups per lane per tile
+constexpr int TG = kTopkGroups;     // 16-byte groups per lane per tile
 constexpr uint32_t kRankMax = 256;  // winners ordered by rank up to this many
 
 constexpr uint32_t kStage = 128;    // staged groups per wave per tile
@@ -341,20 +341,37 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       st_dev(&a.p_s[slot], r.s);
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
-    uint32_t off = 0;
-    r = LSE{-__builtin_inff(), 0.0};
-    for (int sg = 0; sg < a.S; ++sg) {
-      const int64_t sl = row * a.S + sg;
-      const uint32_t cs = ld_dev(&a.rec_cnt[sl]);
-      for (uint32_t i = tid; i < cs; i += NT) {
-        s_key[off + i] = ld_dev(&a.rec_key[sl * k + i]);
-        s_bits[off + i] = ld_dev(&a.rec_bits[sl * k + i]);
+    const int64_t s0 = row * a.S;
+    // record counts of all segments at once, then their offsets (wave 0)
+    if (tid < a.S) sh.hist[tid] = ld_dev(&a.rec_cnt[s0 + tid]);
+    uint64_t unusedP;
+    merge_key_lse(sh, nullptr, a.p_m + s0, a.p_s + s0, a.S, c, unusedP, r);
+    if (tid < 64) {
+      uint32_t cv[4], loc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cv[q] = (4 * tid + q < a.S) ? sh.hist[4 * tid + q] : 0u;
+        loc += cv[q];
       }
-      off += cs;
-      r = lse_merge(r, LSE{ld_dev(&a.p_m[sl]), ld_dev(&a.p_s[sl])}, c);
+      uint32_t run = wave_incl_scan_u32(loc, tid) - loc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * tid + q < a.S) sh.hist[4 * tid + q] = run;
+        run += cv[q];
+      }
+      if (tid == 63) sh.cnt2 = run;
     }
     __syncthreads();
-    n = off;
+    n = sh.cnt2;
+    for (int sg = 0; sg < a.S; ++sg) {
+      const uint32_t off = sh.hist[sg];
+      const uint32_t cs = (sg + 1 < a.S ? sh.hist[sg + 1] : n) - off;
+      for (uint32_t i = tid; i < cs; i += NT) {
+        s_key[off + i] = ld_dev(&a.rec_key[(s0 + sg) * k + i]);
+        s_bits[off + i] = ld_dev(&a.rec_bits[(s0 + sg) * k + i]);
+      }
+    }
+    __syncthreads();
     if (n > k) {
       select_compact<CAP>(sh, s_key, s_bits, n, k);
       n = k;
