@@ -101,10 +101,11 @@ def test_edge_shapes_and_k(g, oracle, V, k, dtype):
         compare(g, oracle, x, k, ld=ld)
 
 
-def test_adversarial_rows(g, oracle):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_adversarial_rows(g, oracle, dtype):
     V = 50000
     rng = np.random.default_rng(9)
-    x = rng.normal(0, 1, (10, V)).astype(np.float32)
+    x = rng.normal(0, 1, (11, V)).astype(np.float32)
     x[0, :] = 1.5                                   # all equal: every element ties
     x[1, :] = np.arange(V, dtype=np.float32)        # ascending: the threshold keeps rising
     x[2, :] = -np.arange(V, dtype=np.float32)       # descending
@@ -117,7 +118,10 @@ def test_adversarial_rows(g, oracle):
     x[7, ::2] = -0.0                                # signed zeros tie
     x[8, :] = np.round(x[8, :])                     # few distinct values
     x[9, 40000:] = 100.0                            # the winners all in the last segment
-    for k in (1, 84, 300, 1024):
+    x[10, :] = rng.normal(0, 1e30, V)               # huge magnitudes: the exp offset moves far
+    if dtype == "bf16":
+        x = W.f32_to_bf16_bits(x)
+    for k in (1, 20, 84, 128, 129, 300, 1024):
         compare(g, oracle, x, k)
 
 

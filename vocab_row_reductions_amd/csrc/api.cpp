@@ -104,10 +104,18 @@ struct TopkPlan {
 };
 // Top-k segments are whole tiles (kTopkTile elements of 16 bytes per lane
 // x 8 groups), so only a row's last segment ends in a partial tile.
-TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k) {
+// The per-wave variant takes k <= kWaveTopkMax on 16-byte-aligned rows.
+TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k, bool wave) {
   const int64_t tile = (int64_t)kTopkGroups * 256 * (dtype == VSEL_F32 ? 4 : 8);
-  const int cap = (2 * k <= kCapSmall) ? kCapSmall : kCapLarge;
-  return TopkPlan{plan_segments(rows, V, k, resident_topk(dtype, lse, cap), cap, tile), cap};
+  const int cap = (wave || 2 * k <= kCapSmall) ? kCapSmall : kCapLarge;
+  int64_t resident = 0;
+  if (wave) {
+    const int b = topk_wave_blocks_per_cu(dtype, lse);
+    resident = (int64_t)(b > 0 ? b : 2) * device_cus();
+  } else {
+    resident = resident_topk(dtype, lse, cap);
+  }
+  return TopkPlan{plan_segments(rows, V, k, resident, cap, tile), cap};
 }
 Plan plan_topk_bound(int64_t rows, int64_t V, int64_t k) {
   const int64_t sb = seg_bound(rows, V, k, kCapLarge);
@@ -344,7 +352,9 @@ static vsel_status topk_common(const void* logits, int dtype, int64_t rows, int6
   Layout L;
   const TopkWs w = topk_layout(L, rows, k, plan_topk_bound(rows, vocab, k));
   if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
-  const TopkPlan tp = plan_topk(dtype, want_lse, rows, vocab, k);
+  const bool vec = aligned16(logits, ld, elem_size(dtype));
+  const bool wave = vec && k <= kWaveTopkMax;
+  const TopkPlan tp = plan_topk(dtype, want_lse, rows, vocab, k, wave);
   const Plan& p = tp.p;
   a.x = logits;
   a.ld = ld;
@@ -353,13 +363,14 @@ static vsel_status topk_common(const void* logits, int dtype, int64_t rows, int6
   a.seg_len = p.seg_len;
   a.S = p.S;
   a.k = k;
-  a.vec = aligned16(logits, ld, elem_size(dtype)) ? 1 : 0;
+  a.vec = vec ? 1 : 0;
   a.tickets = at<uint32_t>(ws, w.tickets);
   a.rec_key = at<uint64_t>(ws, w.rec_key);
   a.rec_bits = at<uint32_t>(ws, w.rec_bits);
   a.rec_cnt = at<uint32_t>(ws, w.rec_cnt);
   a.p_m = at<float>(ws, w.p_m);
   a.p_s = at<double>(ws, w.p_s);
+  if (wave) return launched(launch_topk_wave(dtype, want_lse, a, (hipStream_t)stream));
   return launched(launch_topk(dtype, want_lse, tp.cap, a, (hipStream_t)stream));
 }
 

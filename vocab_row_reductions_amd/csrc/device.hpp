@@ -326,7 +326,8 @@ __device__ uint64_t radix_select(SelShared& sh, uint32_t k, Each each) {
 }
 
 // Shrink the LDS candidate buffer (n > k records) to its k largest keys and
-// return the new threshold (the k-th largest key).  The compaction is done
+// return the new threshold (the k-th largest key).  `bits` (the records'
+// element bits) may be null for a keys-only buffer.  The compaction is done
 // in place by wave 0, 64 records at a time: a record's destination (the
 // number of winners before it) never lies beyond what the wave has already
 // read.  All threads must call.
@@ -341,14 +342,14 @@ __device__ uint64_t select_compact(SelShared& sh, uint64_t* key, uint32_t* bits,
     for (uint32_t c0 = 0; c0 < n; c0 += 64) {
       const uint32_t i = c0 + tid;
       const uint64_t K = i < n ? key[i] : 0ull;
-      const uint32_t b = i < n ? bits[i] : 0u;
+      const uint32_t b = (bits && i < n) ? bits[i] : 0u;
       const bool win = i < n && K >= T;
       const uint64_t m = __ballot(win);
       if (win) {
         const uint32_t d =
             base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         key[d] = K;
-        bits[d] = b;
+        if (bits) bits[d] = b;
       }
       base += (uint32_t)__popcll(m);
     }
@@ -381,6 +382,51 @@ __device__ void sort_desc(uint64_t* key, uint32_t* bits, uint32_t n) {
     }
   }
   __syncthreads();
+}
+
+// Temperature sampling with top-p on sorted candidates (one thread, float64):
+// untempered nucleus cut, then the tempered inverse-CDF draw with u.
+__device__ inline void sample_tail(const uint64_t* key, const uint32_t* bits, uint32_t n, float temperature,
+                            float top_p, float u, uint32_t* tok, float* logp) {
+  const double T = temperature;
+  const double z0 = __uint_as_float(bits[0]);
+  uint32_t keep = n;
+  if (top_p < 1.0f) {
+    double Z0 = 0.0;
+    for (uint32_t j = 0; j < n; ++j) Z0 += exp((double)__uint_as_float(bits[j]) - z0);
+    double cum = 0.0;
+    keep = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      cum += exp((double)__uint_as_float(bits[j]) - z0) / Z0;
+      if (cum >= (double)top_p) {
+        keep = j + 1;
+        break;
+      }
+    }
+    if (keep == 0) keep = n;
+  }
+  double W = 0.0;
+  for (uint32_t j = 0; j < keep; ++j) W += exp(((double)__uint_as_float(bits[j]) - z0) / T);
+  const double target = (double)u * W;
+  double c = 0.0;
+  int pick = -1;
+  for (uint32_t j = 0; j < keep; ++j) {
+    c += exp(((double)__uint_as_float(bits[j]) - z0) / T);
+    if (target < c) {
+      pick = (int)j;
+      break;
+    }
+  }
+  if (pick < 0) {
+    for (int j = (int)keep - 1; j >= 0; --j)
+      if (exp(((double)__uint_as_float(bits[j]) - z0) / T) > 0.0) {
+        pick = j;
+        break;
+      }
+    if (pick < 0) pick = 0;
+  }
+  *tok = ~(uint32_t)key[pick];
+  *logp = (float)(((double)__uint_as_float(bits[pick]) - z0) / T - log(W));
 }
 
 // Cross-workgroup data (segment partials, tickets) moves only through

@@ -147,6 +147,11 @@ struct DrawArgs {
 
 hipError_t launch_scan(int dtype, bool want_lse, const ScanArgs& a, hipStream_t s);
 hipError_t launch_topk(int dtype, bool want_lse, int cap, const TopkArgs& a, hipStream_t s);
+// Per-wave filtering variant of the top-k kernel: k <= kWaveTopkMax, rows
+// whose start and stride are 16-byte aligned, merge buffer of kCapSmall.
+constexpr int kWaveTopkMax = 128;
+hipError_t launch_topk_wave(int dtype, bool want_lse, const TopkArgs& a, hipStream_t s);
+int topk_wave_blocks_per_cu(int dtype, bool want_lse);
 // Workgroups of a kernel variant that fit on one CU at once (0 if unknown).
 int scan_blocks_per_cu(int dtype, bool want_lse);
 int topk_blocks_per_cu(int dtype, bool want_lse, int cap);

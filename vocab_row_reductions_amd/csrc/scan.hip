@@ -25,8 +25,8 @@ constexpr int SG = 8;  // 16-byte groups per lane per tile
 __device__ __forceinline__ void lse_push(LSE& st, float x, float c) {
   const float mn = fmax_nan(st.m, x);
   const float ms = (mn == -__builtin_inff()) ? 0.0f : mn;
-  const double scale = (st.m == mn) ? 1.0 : (double)__builtin_amdgcn_exp2f(st.m * c - ms * c);
-  st.s = st.s * scale + (double)__builtin_amdgcn_exp2f(x * c - ms * c);
+  const double scale = (st.m == mn) ? 1.0 : (double)__builtin_amdgcn_exp2f((st.m - ms) * c);
+  st.s = st.s * scale + (double)__builtin_amdgcn_exp2f((x - ms) * c);
   st.m = mn;
 }
 
@@ -55,8 +55,11 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
   LSE st{-__builtin_inff(), 0.0};
   auto tile = [&](const auto& g, int64_t t0) {
     constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
-    float mt = st.m, off = 0.0f, stile = 0.0f;
-    if constexpr (WANT_LSE) off = ((mt == -__builtin_inff()) ? 0.0f : mt) * c;
+    // exponents as (x - ob) * c with the offset ob in input units: exact for
+    // the maximum itself at any magnitude (x * c - ob * c would carry the
+    // rounding of both products)
+    float mt = st.m, ob = 0.0f, stile = 0.0f;
+    if constexpr (WANT_LSE) ob = (mt == -__builtin_inff()) ? 0.0f : mt;
 #pragma unroll
     for (int j = 0; j < NGP; ++j) {
       float x[E];
@@ -76,13 +79,13 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
         const float mn = fmax_nan(mt, m0);
         if (!(mn == mt)) {
           const float ms = (mn == -__builtin_inff()) ? 0.0f : mn;
-          stile *= __builtin_amdgcn_exp2f(mt * c - ms * c);
-          off = ms * c;
+          stile *= __builtin_amdgcn_exp2f((mt - ms) * c);
+          ob = ms;
           mt = mn;
         }
         float acc = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[e], c, -off));
+        for (int e = 0; e < E; ++e) acc += __builtin_amdgcn_exp2f((x[e] - ob) * c);
         stile += acc;
       } else {
         mt = fmax_nan(mt, m0);
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
     }
     if constexpr (WANT_LSE) {
       // st.m < mt here unless equal; an empty state (st.m = -inf) scales to 0
-      const double scale = (st.m == mt) ? 1.0 : (double)__builtin_amdgcn_exp2f(st.m * c - mt * c);
+      const double scale = (st.m == mt) ? 1.0 : (double)__builtin_amdgcn_exp2f((st.m - mt) * c);
       st.s = st.s * scale + (double)stile;
     }
     st.m = mt;

@@ -38,51 +38,6 @@ struct WaveStage {
   uint32_t e0[kStage];
 };
 
-// Temperature sampling with top-p on sorted candidates (one thread, float64):
-// untempered nucleus cut, then the tempered inverse-CDF draw with u.
-__device__ void sample_tail(const uint64_t* key, const uint32_t* bits, uint32_t n, float temperature,
-                            float top_p, float u, uint32_t* tok, float* logp) {
-  const double T = temperature;
-  const double z0 = __uint_as_float(bits[0]);
-  uint32_t keep = n;
-  if (top_p < 1.0f) {
-    double Z0 = 0.0;
-    for (uint32_t j = 0; j < n; ++j) Z0 += exp((double)__uint_as_float(bits[j]) - z0);
-    double cum = 0.0;
-    keep = 0;
-    for (uint32_t j = 0; j < n; ++j) {
-      cum += exp((double)__uint_as_float(bits[j]) - z0) / Z0;
-      if (cum >= (double)top_p) {
-        keep = j + 1;
-        break;
-      }
-    }
-    if (keep == 0) keep = n;
-  }
-  double W = 0.0;
-  for (uint32_t j = 0; j < keep; ++j) W += exp(((double)__uint_as_float(bits[j]) - z0) / T);
-  const double target = (double)u * W;
-  double c = 0.0;
-  int pick = -1;
-  for (uint32_t j = 0; j < keep; ++j) {
-    c += exp(((double)__uint_as_float(bits[j]) - z0) / T);
-    if (target < c) {
-      pick = (int)j;
-      break;
-    }
-  }
-  if (pick < 0) {
-    for (int j = (int)keep - 1; j >= 0; --j)
-      if (exp(((double)__uint_as_float(bits[j]) - z0) / T) > 0.0) {
-        pick = j;
-        break;
-      }
-    if (pick < 0) pick = 0;
-  }
-  *tok = ~(uint32_t)key[pick];
-  *logp = (float)(((double)__uint_as_float(bits[pick]) - z0) / T - log(W));
-}
-
 // Append one candidate to the workgroup buffer (or flag the overflow).
 template <int CAP>
 __device__ __forceinline__ void append(SelShared& sh, uint64_t* key, uint32_t* bits, uint64_t K, uint32_t b) {
@@ -157,8 +112,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     // stile is folded into the float64 lane sum at the end of the tile.
     float gm[NGP];
     float tmax = -__builtin_inff();
-    float mt = st.m, off = 0.0f, stile = 0.0f;
-    if constexpr (WANT_LSE) off = ((mt == -__builtin_inff()) ? 0.0f : mt) * c;
+    // exponents as (x - ob) * c with the offset ob in input units: exact for
+    // the maximum itself at any magnitude (x * c - ob * c would carry the
+    // rounding of both products)
+    float mt = st.m, ob = 0.0f, stile = 0.0f;
+    if constexpr (WANT_LSE) ob = (mt == -__builtin_inff()) ? 0.0f : mt;
 #pragma unroll
     for (int j = 0; j < NGP; ++j) {
       float x[E];
@@ -173,13 +131,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         const float mn = fmax_nan(mt, m0);
         if (!(mn == mt)) {  // the running maximum moved (or became NaN)
           const float ms = (mn == -__builtin_inff()) ? 0.0f : mn;
-          stile *= __builtin_amdgcn_exp2f(mt * c - ms * c);
-          off = ms * c;
+          stile *= __builtin_amdgcn_exp2f((mt - ms) * c);
+          ob = ms;
           mt = mn;
         }
         float acc = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[e], c, -off));
+        for (int e = 0; e < E; ++e) acc += __builtin_amdgcn_exp2f((x[e] - ob) * c);
         stile += acc;
       }
     }
@@ -189,7 +147,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       asm volatile("" ::"v"(stile), "v"(mt));
       // fold: st.s is relative to st.m, stile to mt >= st.m
       // st.m < mt here unless equal; an empty state (st.m = -inf) scales to 0
-      const double scale = (st.m == mt) ? 1.0 : (double)__builtin_amdgcn_exp2f(st.m * c - mt * c);
+      const double scale = (st.m == mt) ? 1.0 : (double)__builtin_amdgcn_exp2f((st.m - mt) * c);
       st.s = st.s * scale + (double)stile;
       st.m = mt;
     } else {
@@ -298,8 +256,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         if constexpr (WANT_LSE) {
           const float mn = fmax_nan(st.m, x);
           const float ms = (mn == -__builtin_inff()) ? 0.0f : mn;
-          const double scale = (st.m == mn) ? 1.0 : (double)__builtin_amdgcn_exp2f(st.m * c - ms * c);
-          st.s = st.s * scale + (double)__builtin_amdgcn_exp2f(x * c - ms * c);
+          const double scale = (st.m == mn) ? 1.0 : (double)__builtin_amdgcn_exp2f((st.m - ms) * c);
+          st.s = st.s * scale + (double)__builtin_amdgcn_exp2f((x - ms) * c);
           st.m = mn;
         } else {
           st.m = fmax_nan(st.m, x);

@@ -1,0 +1,643 @@
+// topk_wave.hip -- fused per-row top-k + argmax + log-sum-exp (and the
+// sampling tail) for k <= 128 on 16-byte-aligned rows, one pass over the row.
+//
+// Same result as topk_kernel; a different schedule.  The selection of PR #49
+// ("Change": top_k + get_rows on each device's share) is fused with the
+// argmax and the log-sum-exp, and the four waves of a workgroup filter their
+// share of each tile independently, with no workgroup barrier while the row
+// streams:
+//   * log-sum-exp with a lazy offset: every element costs one FMA, one exp2
+//     and one add against the lane's current offset, and the offset moves
+//     (rescaling the lane's sums) only when a group maximum passes it by 2^64
+//     -- the first group, and then almost never;
+//   * each 16-byte group is tested once through its maximum against the
+//     wave's threshold T (a lower bound of the segment's k-th largest
+//     composite key); the wave compacts its passing groups into an LDS
+//     staging list (ballot + mbcnt) and, every 64 staged groups, opens them
+//     and appends the elements that reach T to its own LDS candidate list;
+//   * a wave-level radix select cuts the list to k and raises T whenever the
+//     list grows past a few k records;
+//   * at the segment's end the four lists merge (workgroup select), segments
+//     of a row merge in the row's last workgroup, and the winners are written
+//     in (value desc, id asc) order.  A record is only its composite key; the
+//     value comes back from the key, except for +-0 winners whose sign bit
+//     the key folds away: those are read again from the row.
+// The first tile's threshold is the one workgroup-wide step: the
+// ceil(k/4)-th largest lane maximum of each wave, minimum over the waves,
+// so at least k distinct elements reach it.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace vsel {
+
+constexpr int WTG = kTopkGroups;      // 16-byte groups per lane per tile
+constexpr uint32_t kWCap = 512;       // candidate records per wave
+constexpr uint32_t kWStage = 128;     // staged groups per wave
+constexpr uint32_t kFlushAt = 64;     // open the staged groups at a tile end from this many
+constexpr float kLazyLog2 = 64.0f;    // the exp2 offset moves when a maximum passes it by this
+constexpr uint32_t kRank = NT;        // records ordered by rank directly, one per thread
+
+struct WaveArea {
+  uint32_t w[kWStage][4];
+  uint32_t e0[kWStage];
+  uint32_t hist[256];
+};
+
+// Order the wave's LDS accesses around cross-lane communication (the LDS
+// unit executes one wave's operations in order; this keeps the compiler from
+// moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// k-th largest of the n > k distinct keys wb[0..n), by one wave (MSB-first
+// 8-bit digits; digits on which all keys agree cost nothing).  Compacts the
+// list in place to exactly the k keys >= the returned threshold.
+__device__ __forceinline__ uint64_t wave_select(uint64_t* wb, uint32_t n, uint32_t k, uint32_t* hist) {
+  const uint32_t lane = threadIdx.x & 63u;
+  uint64_t a_and = ~0ull, a_or = 0ull;
+  for (uint32_t i = lane; i < n; i += 64) {
+    const uint64_t K = wb[i];
+    a_and &= K;
+    a_or |= K;
+  }
+  a_and = wave_and_u64(a_and);
+  a_or = wave_or_u64(a_or);
+  const uint64_t varies = a_and ^ a_or;
+  uint64_t prefix = 0;
+  uint32_t rem = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (((varies >> shift) & 0xFFull) == 0) {
+      prefix |= a_and & (0xFFull << shift);
+      continue;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
+    wave_lds_sync();
+    const uint64_t hmask = (shift == 56) ? 0ull : (~0ull << (shift + 8));
+    for (uint32_t i = lane; i < n; i += 64) {
+      const uint64_t K = wb[i];
+      if ((K & hmask) == prefix) atomicAdd(&hist[(uint32_t)(K >> shift) & 255u], 1u);
+    }
+    wave_lds_sync();
+    uint32_t c[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) c[b] = hist[255 - 4 * lane - b];
+    wave_lds_sync();
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan_u32(local, (int)lane);
+    uint32_t cum = incl - local;
+    const bool mine = cum < rem && rem <= incl;
+    uint32_t d = 0, r2 = 0, bc = 0;
+    if (mine) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (cum + c[b] >= rem) {
+          d = 255 - 4 * lane - b;
+          r2 = rem - cum;
+          bc = c[b];
+          break;
+        }
+        cum += c[b];
+      }
+    }
+    const int src = __builtin_ctzll(__ballot(mine));  // exactly one lane
+    d = (uint32_t)__builtin_amdgcn_readlane((int)d, src);
+    r2 = (uint32_t)__builtin_amdgcn_readlane((int)r2, src);
+    bc = (uint32_t)__builtin_amdgcn_readlane((int)bc, src);
+    prefix |= (uint64_t)d << shift;
+    rem = r2;
+    if (bc == rem) break;  // the whole bucket qualifies
+  }
+  // In place: a winner's destination never lies past the chunk being read.
+  uint32_t base = 0;
+  for (uint32_t c0 = 0; c0 < n; c0 += 64) {
+    const uint32_t i = c0 + lane;
+    const uint64_t K = i < n ? wb[i] : 0ull;
+    const bool win = i < n && K >= prefix;
+    const uint64_t m = __ballot(win);
+    wave_lds_sync();
+    if (win) wb[base + lane_rank(m)] = K;
+    base += (uint32_t)__popcll(m);
+  }
+  wave_lds_sync();
+  return prefix;
+}
+
+// 2^a in float64 for a finite a, to float precision (the fraction through
+// the hardware exp2, the integer part exactly through ldexp); saturates far
+// outside the float64 range.
+__device__ __forceinline__ double exp2_split(double a) {
+  a = fmin(fmax(a, -1100.0), 1100.0);
+  const double n = floor(a);
+  return ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
+}
+
+template <typename DT, bool WANT_LSE>
+__global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
+  constexpr int E = Elem<DT>::E;
+  constexpr int64_t TILE = (int64_t)NT * WTG * E;
+  constexpr uint32_t kBlockCap = NWAVE * kWCap;  // the lists, then the row's merge buffer
+  __shared__ uint64_t s_key[kBlockCap];
+  __shared__ WaveArea area_all[NWAVE];
+  __shared__ uint32_t wcount[NWAVE];
+  __shared__ uint64_t s_T;  // largest threshold any wave has found (valid for all)
+  __shared__ SelShared sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows) return;
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const int64_t e_begin = (int64_t)seg * a.seg_len;
+  const int64_t e_end = min(a.V, e_begin + a.seg_len);
+  const uint32_t k = (uint32_t)a.k;
+  const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
+  const uint32_t e_full32 = (uint32_t)e_full;
+  const float c = kLog2e;
+  const uint32_t select_at = min(max(2u * k, 192u), kWCap - 64u);
+
+  if (tid == 0) s_T = 1;  // ordered before every read by the first barrier below
+  WaveArea& area = area_all[wave];
+  uint64_t* wb = s_key + wave * kWCap;
+  uint32_t wcnt = 0;  // records in this wave's list
+  uint32_t sn = 0;    // staged groups (may pass kWStage: the tile then overflows)
+  uint64_t T = 1;     // every real element's composite key is above 1
+  float tf = -__builtin_inff();
+
+  // Lane log-sum-exp with a lazy offset om (in input units): LS is the
+  // lane's sum of 2^((x - om) c) in float64.  Terms are exp2(fma(x, c, noff))
+  // with noff = -fl(om c); these carry the factor 2^delta of that rounding,
+  // delta = om c - fl(om c), which corr = 2^-delta removes when a tile is
+  // folded in.  Past |om| = 2^25 the rounding could reach the exponent
+  // range, and the lane takes its terms exactly as exp2((x - om) c) instead
+  // (huge).  trig: a tile maximum above it moves the offset.
+  float lm = -__builtin_inff(), om = -__builtin_inff(), trig = -__builtin_inff(), noff = 0.0f, ls = 0.0f;
+  double LS = 0.0, corr = 1.0;
+  bool huge = false;
+  // Move the offset to m (finite, above the current one), rescaling LS.
+  auto set_offset = [&](float m) {
+    LS = (om == -__builtin_inff()) ? 0.0 : LS * exp2_split(((double)om - (double)m) * (double)c);
+    om = m;
+    const float oc = m * c;
+    noff = -oc;
+    trig = m + kLazyLog2 / c;
+    corr = exp2_split((double)oc - (double)m * (double)c);
+    huge = !(__builtin_fabsf(m) <= 0x1p25f);
+  };
+
+  auto group_max = [&](const Group& g, float (&x)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = __uint_as_float(gbits<DT>(g, e));
+    float m0 = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) m0 = fmax_nan(m0, x[e]);
+    return m0;
+  };
+
+  auto stage = [&](const Group& g, float gm, uint32_t e0) {
+    const bool pass = gm >= tf;
+    const uint64_t bm = __ballot(pass);
+    if (bm) {
+      const uint32_t p = sn + lane_rank(bm);
+      if (pass && p < kWStage) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) area.w[p][i] = g.w[i];
+        area.e0[p] = e0;
+      }
+      sn += (uint32_t)__popcll(bm);
+    }
+  };
+
+  // Maximum and log-sum-exp terms of one group against the lane's current
+  // offset (no branch); returns the group maximum.
+  auto lse_group = [&](const Group& g) {
+    float x[E];
+    const float gm = group_max(g, x);
+    if constexpr (WANT_LSE) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[e], c, noff));
+      ls += acc;
+    }
+    return gm;
+  };
+
+  // After a tile's terms are in ls: a lane whose tile maximum passed its
+  // trigger moves its offset to that maximum; it, and a lane past the
+  // fast-path range, recompute the tile's terms (the ones just added may
+  // have overflowed).
+  auto lse_check = [&](auto& g, float tmax) {
+    lm = fmax_nan(lm, tmax);
+    if constexpr (WANT_LSE) {
+      constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+      const bool up = tmax > trig && tmax < __builtin_inff();
+      if (__ballot(up || huge)) {
+        if (up) set_offset(tmax);
+        if (up || huge) {
+          // fresh words (not the values unpacked above, which would then
+          // stay live through the whole tile)
+          auto fresh = [&](int j, float (&x)[E]) {
+            uint32_t w0 = g[j].w[0], w1 = g[j].w[1], w2 = g[j].w[2], w3 = g[j].w[3];
+            asm volatile("" : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+            Group gf;
+            gf.w[0] = w0; gf.w[1] = w1; gf.w[2] = w2; gf.w[3] = w3;
+            (void)group_max(gf, x);
+          };
+          ls = 0.0f;
+          if (huge) {
+            for (int j = 0; j < NGP; ++j) {
+              float x[E];
+              fresh(j, x);
+#pragma unroll
+              for (int e = 0; e < E; ++e) ls += __builtin_amdgcn_exp2f((x[e] - om) * c);
+            }
+          } else {
+            for (int j = 0; j < NGP; ++j) {
+              float x[E];
+              fresh(j, x);
+#pragma unroll
+              for (int e = 0; e < E; ++e) ls += __builtin_amdgcn_exp2f(fmaf(x[e], c, noff));
+            }
+          }
+        }
+      }
+    }
+  };
+
+  auto fold = [&]() {
+    if constexpr (WANT_LSE) {
+      LS += huge ? (double)ls : (double)ls * corr;
+      ls = 0.0f;
+    }
+  };
+
+  // Append every element of the staged groups that reaches T to the wave's
+  // list, one element of 64 staged groups per step; the list is cut to k
+  // (raising T) whenever a step would overflow it, and after the last step
+  // when it holds more than select_at records.
+  auto flush = [&]() {
+    wave_lds_sync();
+    const uint32_t nsteps = (sn + 63u) / 64u * (uint32_t)E;
+    for (uint32_t step = 0; step <= nsteps; ++step) {
+      bool pass = false;
+      uint64_t K = 0;
+      if (step < nsteps) {
+        const uint32_t e = step % (uint32_t)E;
+        const uint32_t q = (step / (uint32_t)E) * 64u + (uint32_t)lane;
+        if (q < sn) {
+          const uint32_t word = area.w[q][E == 8 ? (e >> 1) : e];
+          const uint32_t b = (E == 8) ? ((e & 1u) ? (word & 0xFFFF0000u) : (word << 16)) : word;
+          const uint32_t id = area.e0[q] + e;
+          K = comp_key(b, id);
+          pass = id < e_full32 && K >= T;
+        }
+      }
+      uint64_t m = __ballot(pass);
+      const bool cut = (step < nsteps) ? (wcnt + (uint32_t)__popcll(m) > kWCap) : (wcnt > select_at);
+      if (cut) {
+        T = wave_select(wb, wcnt, k, area.hist);
+        wcnt = k;
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)T);
+        pass = pass && K >= T;
+        m = __ballot(pass);
+      }
+      if (pass) wb[wcnt + lane_rank(m)] = K;
+      wcnt += (uint32_t)__popcll(m);
+    }
+    sn = 0;
+    tf = thr_float(T);
+    wave_lds_sync();
+  };
+
+  // First tile: threshold from the lane maxima m (needs k <= 4 waves x 64),
+  // and the lane's first exp2 offset.
+  auto first_threshold = [&](float m, int64_t t0) {
+    if constexpr (WANT_LSE) {
+      if (m > -__builtin_inff() && m < __builtin_inff()) set_offset(m);
+    }
+    const bool real = t0 + (int64_t)tid * E < e_full;
+    const uint32_t lk = real ? fkey(__float_as_uint(m)) : 0u;
+    const uint32_t kw = (k + NWAVE - 1) / NWAVE;
+    uint32_t tw = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = tw | (1u << b);
+      if ((uint32_t)__popcll(__ballot(lk >= cand)) >= kw) tw = cand;
+    }
+    if (lane == 0) sh.wtau[wave] = tw;
+    __syncthreads();
+    uint32_t tau = sh.wtau[0];
+#pragma unroll
+    for (int q = 1; q < NWAVE; ++q) tau = min(tau, sh.wtau[q]);
+    const uint64_t Tn = (uint64_t)tau << 32;
+    if (Tn > T) T = Tn;
+    tf = thr_float(T);
+  };
+  // Lane maximum of a tile, for the first threshold; the asm keeps the
+  // compiler from sharing these unpacked values with the pass that follows.
+  auto first_tile = [&](auto& g, int64_t t0) {
+    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < NGP; ++j) {
+      float x[E];
+      m = fmax_nan(m, group_max(g[j], x));
+    }
+#pragma unroll
+    for (int j = 0; j < NGP; ++j) asm volatile("" : "+v"(g[j].w[0]), "+v"(g[j].w[1]), "+v"(g[j].w[2]), "+v"(g[j].w[3]));
+    first_threshold(m, t0);
+  };
+
+  // Streaming loop.  Every flush happens at the top of the loop, so the
+  // flush (and the select inside it) is one piece of code and no tile data
+  // is live across it.  A tile whose passing groups did not fit the staging
+  // list is taken again from memory, one group per lane at a time, after
+  // the groups staged before it are opened (its log-sum-exp terms are
+  // already in).
+  const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
+  int64_t t0 = e_begin;
+  int64_t ov_t0 = 0;
+  int ovj = WTG;  // next group of an overflowed tile to take again (WTG: none)
+  bool first = true, want_flush = false;
+  for (;;) {
+    if (want_flush) {
+      flush();
+      want_flush = false;
+    }
+    if (ovj < WTG) {
+      const uint32_t o = (uint32_t)(ovj * NT + tid) * E;
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + ov_t0 + o));
+      Group g1;
+      g1.w[0] = v.x; g1.w[1] = v.y; g1.w[2] = v.z; g1.w[3] = v.w;
+      float x[E];
+      stage(g1, group_max(g1, x), (uint32_t)ov_t0 + o);
+      ++ovj;
+      want_flush = true;
+      continue;
+    }
+    if (t0 < e_tiles) {
+      Group g[WTG];
+      load_tile_full<DT, WTG, true>(g, xr + t0);
+      if (first) {
+        first_tile(g, t0);
+        first = false;
+      } else {
+        // another wave may have raised the threshold
+        const uint64_t Ts = __hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (Ts > T) {
+          T = Ts;
+          tf = thr_float(T);
+        }
+      }
+      const uint32_t sn0 = sn;
+      float gm[WTG];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < WTG; ++j) {
+        gm[j] = lse_group(g[j]);
+        tmax = fmax_nan(tmax, gm[j]);
+      }
+      // finish the exp2 terms before the branches below (otherwise the
+      // compiler keeps many groups unpacked at once)
+      if constexpr (WANT_LSE) asm volatile("" ::"v"(ls), "v"(tmax));
+      lse_check(g, tmax);
+#pragma unroll
+      for (int j = 0; j < WTG; ++j) stage(g[j], gm[j], (uint32_t)t0 + (uint32_t)(j * NT + tid) * E);
+      fold();
+      if (sn > kWStage) {
+        sn = sn0;  // open the earlier groups, then take this tile again
+        ov_t0 = t0;
+        ovj = 0;
+        want_flush = true;
+      } else if (sn >= kFlushAt) {
+        want_flush = true;
+      }
+      t0 += TILE;
+      continue;
+    }
+    if (t0 < e_full) {
+      // the row's last partial tile: one group per lane at a time (at most
+      // 63 staged groups wait, so these never overflow the staging list)
+      Group g1[1];
+      load_tile<DT, 1, true>(g1, xr, t0, e_full);
+      if (first) {
+        first_tile(g1, t0);
+        first = false;
+      }
+      const float gm1 = lse_group(g1[0]);
+      lse_check(g1, gm1);
+      stage(g1[0], gm1, (uint32_t)t0 + (uint32_t)tid * E);
+      fold();
+      if (sn >= kFlushAt) want_flush = true;
+      t0 += (int64_t)NT * E;
+      continue;
+    }
+    if (sn) {
+      want_flush = true;
+      continue;
+    }
+    break;
+  }
+
+  // The row's last few elements (fewer than one group): lanes of wave 0.
+  if (e_full < e_end && wave == 0) {
+    const int64_t i = e_full + lane;
+    const bool has = i < e_end;
+    const uint32_t b = has ? gbits_at<DT>(xr, i) : kNegInfBits;
+    const float x = __uint_as_float(b);
+    lm = fmax_nan(lm, x);
+    if constexpr (WANT_LSE) {
+      if (x > trig && x < __builtin_inff()) set_offset(x);
+      LS += huge ? (double)__builtin_amdgcn_exp2f((x - om) * c)
+                 : (double)__builtin_amdgcn_exp2f(fmaf(x, c, noff)) * corr;
+    }
+    // room: after the last flush the list holds at most select_at <= kWCap - 64
+    const uint64_t K = comp_key(b, (uint32_t)i);
+    const bool pass = has && K >= T;
+    const uint64_t m = __ballot(pass);
+    if (pass) wb[wcnt + lane_rank(m)] = K;
+    wcnt += (uint32_t)__popcll(m);
+  }
+  // Lane log-sum-exp state relative to the lane maximum, then the workgroup's.
+  LSE r{lm, 0.0};
+  if constexpr (WANT_LSE) {
+    if (lm != lm || lm == __builtin_inff()) r.s = __builtin_nan("");
+    else if (lm != -__builtin_inff()) r.s = LS * exp2_split(((double)om - (double)lm) * (double)c);
+  }
+  r = wave_lse(r, c);
+  if (lane == 0) {
+    sh.wm[wave] = r.m;
+    sh.ws[wave] = r.s;
+    atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)T);
+  }
+  __syncthreads();
+  // Keep only the records that reach the final shared threshold (at least k
+  // in all: it is some wave's k-th largest, or the first tile's bound).
+  {
+    const uint64_t Tb = s_T > T ? s_T : T;
+    uint32_t base = 0;
+    for (uint32_t c0 = 0; c0 < wcnt; c0 += 64) {
+      const uint32_t i = c0 + lane;
+      const uint64_t K = i < wcnt ? wb[i] : 0ull;
+      const bool keep = i < wcnt && K >= Tb;
+      const uint64_t m = __ballot(keep);
+      wave_lds_sync();
+      if (keep) wb[base + lane_rank(m)] = K;
+      base += (uint32_t)__popcll(m);
+    }
+    wcnt = base;
+  }
+  if (lane == 0) wcount[wave] = wcnt;
+  __syncthreads();
+  r = LSE{sh.wm[0], sh.ws[0]};
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) r = lse_merge(r, LSE{sh.wm[q], sh.ws[q]}, c);
+  // Gather the four lists at the front of s_key: every record goes through
+  // registers first (a destination may overlap another wave's list).
+  uint32_t off = 0, n = 0;
+#pragma unroll
+  for (int q = 0; q < NWAVE; ++q) {
+    if (q < wave) off += wcount[q];
+    n += wcount[q];
+  }
+  {
+    constexpr uint32_t kPer = kWCap / 64;
+    uint64_t held[kPer];
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; ++q) {
+      const uint32_t i = q * 64 + lane;
+      held[q] = i < wcnt ? wb[i] : 0ull;
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; ++q) {
+      const uint32_t i = q * 64 + lane;
+      if (i < wcnt) s_key[off + i] = held[q];
+    }
+  }
+  __syncthreads();
+  // Winners in (value desc, id asc) order at okey: more than kRank records
+  // are first cut to k by the radix select; then each record's rank among
+  // the rest is its place (ranks >= k drop out).
+  uint64_t* okey = s_key + kBlockCap / 2;
+  auto rank_order = [&](uint32_t& nn) {
+    if (nn > kRank) {
+      select_compact<kBlockCap>(sh, s_key, nullptr, nn, k);
+      nn = k;
+    }
+    if ((uint32_t)tid < nn) {
+      const uint64_t K = s_key[tid];
+      uint32_t r0 = 0;
+      for (uint32_t j = 0; j < nn; ++j) r0 += s_key[j] > K ? 1u : 0u;
+      if (r0 < k) okey[r0] = K;
+    }
+    __syncthreads();
+    nn = min(nn, k);
+  };
+  rank_order(n);
+
+  if (a.S > 1) {
+    const int64_t slot = row * a.S + seg;
+    for (uint32_t i = tid; i < n; i += NT) st_dev(&a.rec_key[slot * k + i], okey[i]);
+    if (tid == 0) {
+      st_dev(&a.rec_cnt[slot], n);
+      st_dev(&a.p_m[slot], r.m);
+      st_dev(&a.p_s[slot], r.s);
+    }
+    if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
+    const int64_t s0 = row * a.S;
+    if (tid < a.S) sh.hist[tid] = ld_dev(&a.rec_cnt[s0 + tid]);
+    uint64_t unusedP;
+    merge_key_lse(sh, nullptr, a.p_m + s0, a.p_s + s0, a.S, c, unusedP, r);
+    if (tid < 64) {
+      uint32_t cv[4], loc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cv[q] = (4 * tid + q < a.S) ? sh.hist[4 * tid + q] : 0u;
+        loc += cv[q];
+      }
+      uint32_t run = wave_incl_scan_u32(loc, tid) - loc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (4 * tid + q < a.S) sh.hist[4 * tid + q] = run;
+        run += cv[q];
+      }
+      if (tid == 63) sh.cnt2 = run;
+    }
+    __syncthreads();
+    n = sh.cnt2;
+    for (int sg = 0; sg < a.S; ++sg) {
+      const uint32_t o = sh.hist[sg];
+      const uint32_t cs = (sg + 1 < a.S ? sh.hist[sg + 1] : n) - o;
+      for (uint32_t i = tid; i < cs; i += NT) s_key[o + i] = ld_dev(&a.rec_key[(s0 + sg) * k + i]);
+    }
+    __syncthreads();
+    rank_order(n);
+  }
+
+  const bool bad = (r.m != r.m) || (r.m == __builtin_inff());
+  const bool none = bad || r.m == -__builtin_inff();
+  // A winner's bits from its key; +-0 (one key) from the row itself.
+  auto win_bits = [&](uint64_t K) -> uint32_t {
+    const uint32_t hk = (uint32_t)(K >> 32);
+    return (hk == 0x80000000u) ? gbits_at<DT>(xr, (int64_t)(~(uint32_t)K)) : key_bits(hk);
+  };
+  if (a.mode == 0) {
+    for (uint32_t j = tid; j < k; j += NT) {
+      const bool ok = !bad && j < n;
+      const uint64_t K = ok ? okey[j] : 0ull;
+      a.out_ids[row * k + j] = ok ? ~(uint32_t)K : kFail;
+      a.out_vals[row * k + j] = ok ? __uint_as_float(win_bits(K)) : __builtin_nanf("");
+    }
+    if (tid == 0) {
+      if (a.out_argmax) a.out_argmax[row] = (none || n == 0) ? kFail : ~(uint32_t)okey[0];
+      if (a.out_lse)
+        a.out_lse[row] = bad ? __builtin_nanf("")
+                             : (r.m == -__builtin_inff() ? -__builtin_inff() : (float)((double)r.m + log(r.s)));
+    }
+  } else {
+    uint32_t* obits = area_all[0].e0;  // free now; n <= k <= kWStage
+    if (!none)
+      for (uint32_t j = tid; j < n; j += NT) obits[j] = win_bits(okey[j]);
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t tok = kFail;
+      float lp = __builtin_nanf("");
+      if (!none && n > 0) sample_tail(okey, obits, n, a.temperature, a.top_p, a.u[row], &tok, &lp);
+      a.out_token[row] = tok;
+      if (a.out_logp) a.out_logp[row] = lp;
+    }
+  }
+}
+
+template <typename DT, bool L>
+static hipError_t go_wave(const TopkArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((topk_wave_kernel<DT, L>), dim3((unsigned)(a.rows * a.S)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_wave(int dtype, bool want_lse, const TopkArgs& a, hipStream_t s) {
+  if (dtype == 0) return want_lse ? go_wave<float, true>(a, s) : go_wave<float, false>(a, s);
+  return want_lse ? go_wave<uint16_t, true>(a, s) : go_wave<uint16_t, false>(a, s);
+}
+
+template <typename DT, bool L>
+static int occ_wave() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, topk_wave_kernel<DT, L>, NT, 0) != hipSuccess) return 0;
+  return n;
+}
+
+int topk_wave_blocks_per_cu(int dtype, bool want_lse) {
+  if (dtype == 0) return want_lse ? occ_wave<float, true>() : occ_wave<float, false>();
+  return want_lse ? occ_wave<uint16_t, true>() : occ_wave<uint16_t, false>();
+}
+
+}  // namespace vsel
