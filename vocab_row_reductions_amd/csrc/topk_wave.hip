@@ -56,11 +56,12 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// k-th largest of the n > k distinct keys wb[0..n), by one wave (MSB-first
-// 8-bit digits; digits on which all keys agree cost nothing).  Compacts the
-// list in place to exactly the k keys >= the returned threshold.
-__device__ __forceinline__ uint64_t wave_select(uint64_t* wb, uint32_t n, uint32_t k, uint32_t* hist) {
+// Threshold with exactly `rank` of the n > rank distinct keys wb[0..n) at
+// or above it, by one wave (MSB-first 8-bit digits; digits on which all
+// keys agree cost nothing).
+__device__ __forceinline__ uint64_t wave_kth(const uint64_t* wb, uint32_t n, uint32_t rank, uint32_t* hist) {
   const uint32_t lane = threadIdx.x & 63u;
+  wave_lds_sync();  // the list was just written by other lanes
   uint64_t a_and = ~0ull, a_or = 0ull;
   for (uint32_t i = lane; i < n; i += 64) {
     const uint64_t K = wb[i];
@@ -71,7 +72,7 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t* wb, uint32_t n, uint32
   a_or = wave_or_u64(a_or);
   const uint64_t varies = a_and ^ a_or;
   uint64_t prefix = 0;
-  uint32_t rem = k;
+  uint32_t rem = rank;
   for (int shift = 56; shift >= 0; shift -= 8) {
     if (((varies >> shift) & 0xFFull) == 0) {
       prefix |= a_and & (0xFFull << shift);
@@ -115,19 +116,43 @@ __device__ __forceinline__ uint64_t wave_select(uint64_t* wb, uint32_t n, uint32
     rem = r2;
     if (bc == rem) break;  // the whole bucket qualifies
   }
-  // In place: a winner's destination never lies past the chunk being read.
+  return prefix;
+}
+
+// Keep the keys of wb[0..n) at or above T, in place (a key's destination
+// never lies past the chunk being read); returns their number.
+__device__ __forceinline__ uint32_t wave_cut(uint64_t* wb, uint32_t n, uint64_t T) {
+  const uint32_t lane = threadIdx.x & 63u;
+  wave_lds_sync();
   uint32_t base = 0;
   for (uint32_t c0 = 0; c0 < n; c0 += 64) {
     const uint32_t i = c0 + lane;
     const uint64_t K = i < n ? wb[i] : 0ull;
-    const bool win = i < n && K >= prefix;
-    const uint64_t m = __ballot(win);
+    const bool keep = i < n && K >= T;
+    const uint64_t m = __ballot(keep);
     wave_lds_sync();
-    if (win) wb[base + lane_rank(m)] = K;
+    if (keep) wb[base + lane_rank(m)] = K;
     base += (uint32_t)__popcll(m);
   }
   wave_lds_sync();
-  return prefix;
+  return base;
+}
+
+// One full tile of NG 16-byte groups per lane through a buffer resource
+// based at the tile (scalar base, per-lane offset, per-group scalar offset:
+// no vector address arithmetic); reads past the tile would return zero.
+template <typename DT, int NG>
+__device__ __forceinline__ void load_tile_buf(Group (&g)[NG], const DT* __restrict__ tb) {
+  constexpr int E = Elem<DT>::E;
+  constexpr int kTileBytes = NT * NG * 16;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)tb, 0, kTileBytes, 0x00020000);
+  const int vo = (int)threadIdx.x * 16;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, j * NT * 16, 2 /* nontemporal */);
+    g[j].w[0] = v.x; g[j].w[1] = v.y; g[j].w[2] = v.z; g[j].w[3] = v.w;
+  }
+  (void)E;
 }
 
 // 2^a in float64 for a finite a, to float precision (the fraction through
@@ -139,15 +164,53 @@ __device__ __forceinline__ double exp2_split(double a) {
   return ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
 }
 
+// Log-sum-exp states (m, s) of the workgroup's lanes merged: the maximum
+// first (NaN-propagating), then one rescale per lane and float64 sums, so
+// no step pays more than one exp2.  Every thread must call; every thread
+// gets the result.
+__device__ __forceinline__ LSE block_lse(LSE v, float c, float* sm, double* ss) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float M = wave_max_nan(v.m);
+  if (lane == 0) sm[wave] = M;
+  __syncthreads();
+  M = sm[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) M = fmax_nan(M, sm[q]);
+  double t = 0.0;
+  if (M != M || M == __builtin_inff()) t = __builtin_nan("");
+  else if (v.m != -__builtin_inff()) t = v.s * exp2_split(((double)v.m - (double)M) * (double)c);
+  t = wave_sum_f64(t);
+  if (lane == 0) ss[wave] = t;
+  __syncthreads();
+  double S = ss[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) S += ss[q];
+  return LSE{M, S};
+}
+
+// LDS use (about 33 KB) allows four workgroups per CU, i.e. four waves per
+// SIMD; the attribute lets the compiler use the 128 VGPRs that occupancy
+// leaves instead of spilling to reach a higher one.
 template <typename DT, bool WANT_LSE>
-__global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_wave_kernel(TopkArgs a) {
   constexpr int E = Elem<DT>::E;
   constexpr int64_t TILE = (int64_t)NT * WTG * E;
   constexpr uint32_t kBlockCap = NWAVE * kWCap;  // the lists, then the row's merge buffer
   __shared__ uint64_t s_key[kBlockCap];
   __shared__ WaveArea area_all[NWAVE];
   __shared__ uint32_t wcount[NWAVE];
-  __shared__ uint64_t s_T;  // largest threshold any wave has found (valid for all)
+  // Shared threshold.  Wave w publishes in s_slot[w] a key with at least
+  // ceil(k/4) of its own elements at or above it; the four waves' elements
+  // are distinct, so at least k elements reach the smallest slot, which
+  // makes min(s_slot) (and s_T, the largest such minimum seen) a valid
+  // lower bound of the segment's k-th largest key for every wave.
+  __shared__ uint64_t s_slot[NWAVE];
+  __shared__ uint64_t s_T;
+  // Histogram of the maxima of staged groups (distinct elements): bin b
+  // counts maxima whose value key is at least hbase + (b << 16) (the last
+  // bin: and above).  The lower edge of the highest bin at which the count
+  // from the top reaches k is a valid threshold for every wave.
+  __shared__ uint32_t s_hist[256];
   __shared__ SelShared sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -165,6 +228,9 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
   const uint32_t select_at = min(max(2u * k, 192u), kWCap - 64u);
 
   if (tid == 0) s_T = 1;  // ordered before every read by the first barrier below
+  if (lane == 0) s_slot[wave] = 1;  // each wave its own slot, before it publishes
+  s_hist[tid] = 0u;                   // ordered before use by the first barrier below
+  uint32_t hbase = 0;                 // value key of the first threshold
   WaveArea& area = area_all[wave];
   uint64_t* wb = s_key + wave * kWCap;
   uint32_t wcnt = 0;  // records in this wave's list
@@ -202,7 +268,10 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
     return m0;
   };
 
-  auto stage = [&](const Group& g, float gm, uint32_t e0) {
+  // count: add the group's maximum to the histogram (a group seen for the
+  // first time, and a real one -- pad groups start at or past e_full).
+  // full: the group is known to be real (a full tile).
+  auto stage = [&](const Group& g, float gm, uint32_t e0, bool count, bool full) {
     const bool pass = gm >= tf;
     const uint64_t bm = __ballot(pass);
     if (bm) {
@@ -212,7 +281,42 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
         for (int i = 0; i < 4; ++i) area.w[p][i] = g.w[i];
         area.e0[p] = e0;
       }
+      if (count && pass && (full || e0 < e_full32)) {
+        const uint32_t hk = fkey(__float_as_uint(gm));
+        if (hk >= hbase) atomicAdd(&s_hist[min(255u, (hk - hbase) >> 16)], 1u);
+      }
       sn += (uint32_t)__popcll(bm);
+    }
+  };
+
+  // The histogram's threshold, published in s_T (one wave a tile does
+  // this): lane l reads bins 255-4l .. 252-4l, a wave prefix sum counts
+  // from the top.
+  auto hist_threshold = [&]() {
+    uint32_t c4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) c4[b] = __hip_atomic_load(&s_hist[255 - 4 * lane - b], __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t local = c4[0] + c4[1] + c4[2] + c4[3];
+    const uint32_t incl = wave_incl_scan_u32(local, lane);
+    uint32_t cum = incl - local;
+    const bool mine = cum < k && k <= incl;
+    uint32_t bin = 0;
+    if (mine) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (cum + c4[b] >= k) {
+          bin = 255 - 4 * lane - b;
+          break;
+        }
+        cum += c4[b];
+      }
+    }
+    const uint64_t who = __ballot(mine);
+    if (who) {
+      bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, __builtin_ctzll(who));
+      const uint64_t Th = (uint64_t)(hbase + (bin << 16)) << 32;
+      if (lane == 0) atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)Th);
     }
   };
 
@@ -222,9 +326,9 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
     float x[E];
     const float gm = group_max(g, x);
     if constexpr (WANT_LSE) {
-      float acc = 0.0f;
+      float acc = __builtin_amdgcn_exp2f(fmaf(x[0], c, noff));
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[e], c, noff));
+      for (int e = 1; e < E; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[e], c, noff));
       ls += acc;
     }
     return gm;
@@ -279,42 +383,91 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
     }
   };
 
+  // Make room in the wave's list: publish the wave's ceil(k/4)-th largest
+  // key, take the shared threshold, drop what falls below it, and only if
+  // the list is still long cut it to the wave's own k largest.
+  auto shrink = [&]() {
+    const uint32_t q = (k + NWAVE - 1) / NWAVE;
+    if (wcnt > q) {
+      const uint64_t Tq = wave_kth(wb, wcnt, q, area.hist);
+      if (lane == 0) {
+        const uint64_t mine = max(Tq, __hip_atomic_load(&s_slot[wave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        __hip_atomic_store(&s_slot[wave], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        uint64_t mn = mine;
+#pragma unroll
+        for (int q2 = 0; q2 < NWAVE; ++q2)
+          mn = min(mn, __hip_atomic_load(&s_slot[q2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)mn);
+      }
+      wave_lds_sync();
+    }
+    const uint64_t Ts = __hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (Ts > T) T = Ts;
+    wcnt = wave_cut(wb, wcnt, T);
+    if (wcnt > select_at) {
+      T = wave_kth(wb, wcnt, k, area.hist);
+      wcnt = wave_cut(wb, wcnt, T);
+    }
+    tf = thr_float(T);
+  };
+
   // Append every element of the staged groups that reaches T to the wave's
-  // list, one element of 64 staged groups per step; the list is cut to k
-  // (raising T) whenever a step would overflow it, and after the last step
-  // when it holds more than select_at records.
+  // list.  Each lane opens one staged group per step (64 groups a step) and
+  // a wave prefix sum of the lanes' counts places the appends.  A step that
+  // would overflow the list goes element by element instead (at most 64
+  // appends each), shrinking the list whenever one would not fit: shrink
+  // leaves at most select_at <= kWCap - 64 records, so every such append
+  // fits and the flush always progresses.  (One call site of shrink only:
+  // a second inlined copy makes the compiler put locals in scratch.)
   auto flush = [&]() {
     wave_lds_sync();
-    const uint32_t nsteps = (sn + 63u) / 64u * (uint32_t)E;
-    for (uint32_t step = 0; step <= nsteps; ++step) {
-      bool pass = false;
-      uint64_t K = 0;
-      if (step < nsteps) {
-        const uint32_t e = step % (uint32_t)E;
-        const uint32_t q = (step / (uint32_t)E) * 64u + (uint32_t)lane;
-        if (q < sn) {
-          const uint32_t word = area.w[q][E == 8 ? (e >> 1) : e];
-          const uint32_t b = (E == 8) ? ((e & 1u) ? (word & 0xFFFF0000u) : (word << 16)) : word;
-          const uint32_t id = area.e0[q] + e;
-          K = comp_key(b, id);
-          pass = id < e_full32 && K >= T;
+    for (uint32_t q0 = 0; q0 < sn; q0 += 64) {
+      const uint32_t q = q0 + (uint32_t)lane;
+      const bool has = q < sn;
+      Group gg;
+      uint32_t e0 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gg.w[i] = has ? area.w[q][i] : 0u;
+      if (has) e0 = area.e0[q];
+      uint32_t pm = 0;  // this lane's elements that reach T
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t id = e0 + (uint32_t)e;
+        const bool pass = has && id < e_full32 && comp_key(gbits<DT>(gg, e), id) >= T;
+        pm |= pass ? (1u << e) : 0u;
+      }
+      const uint32_t cnt = (uint32_t)__popc(pm);
+      const uint32_t incl = wave_incl_scan_u32(cnt, lane);
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      if (wcnt + total <= kWCap) {
+        uint32_t pos = wcnt + incl - cnt;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (pm & (1u << e)) wb[pos++] = comp_key(gbits<DT>(gg, e), e0 + (uint32_t)e);
+        wcnt += total;
+      } else {
+        for (int e = 0; e < E; ++e) {
+          // element e without indexing the group by a runtime value (that
+          // would put it in scratch memory): select the word, then the half
+          const int wi = (E == 8) ? (e >> 1) : e;
+          const uint32_t wd = wi == 0 ? gg.w[0] : wi == 1 ? gg.w[1] : wi == 2 ? gg.w[2] : gg.w[3];
+          const uint32_t b = (E == 8) ? ((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16)) : wd;
+          const uint64_t K = comp_key(b, e0 + (uint32_t)e);
+          bool pass = ((pm >> e) & 1u) && K >= T;
+          uint64_t m = __ballot(pass);
+          if (wcnt + (uint32_t)__popcll(m) > kWCap) {
+            shrink();
+            pass = pass && K >= T;
+            m = __ballot(pass);
+          }
+          if (pass) wb[wcnt + lane_rank(m)] = K;
+          wcnt += (uint32_t)__popcll(m);
         }
       }
-      uint64_t m = __ballot(pass);
-      const bool cut = (step < nsteps) ? (wcnt + (uint32_t)__popcll(m) > kWCap) : (wcnt > select_at);
-      if (cut) {
-        T = wave_select(wb, wcnt, k, area.hist);
-        wcnt = k;
-        if (lane == 0) atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)T);
-        pass = pass && K >= T;
-        m = __ballot(pass);
-      }
-      if (pass) wb[wcnt + lane_rank(m)] = K;
-      wcnt += (uint32_t)__popcll(m);
     }
     sn = 0;
-    tf = thr_float(T);
     wave_lds_sync();
+    tf = thr_float(T);
   };
 
   // First tile: threshold from the lane maxima m (needs k <= 4 waves x 64),
@@ -331,13 +484,18 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
       const uint32_t cand = tw | (1u << b);
       if ((uint32_t)__popcll(__ballot(lk >= cand)) >= kw) tw = cand;
     }
-    if (lane == 0) sh.wtau[wave] = tw;
+    if (lane == 0) {
+      sh.wtau[wave] = tw;
+      s_slot[wave] = (uint64_t)tw << 32;  // this wave has ceil(k/4) elements there
+    }
     __syncthreads();
     uint32_t tau = sh.wtau[0];
 #pragma unroll
     for (int q = 1; q < NWAVE; ++q) tau = min(tau, sh.wtau[q]);
     const uint64_t Tn = (uint64_t)tau << 32;
     if (Tn > T) T = Tn;
+    hbase = tau;
+    if (tid == 0) atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)Tn);
     tf = thr_float(T);
   };
   // Lane maximum of a tile, for the first threshold; the asm keeps the
@@ -366,6 +524,7 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
   int64_t ov_t0 = 0;
   int ovj = WTG;  // next group of an overflowed tile to take again (WTG: none)
   bool first = true, want_flush = false;
+  uint32_t tix = 0;  // full tiles so far (the histogram scan rotates over the waves)
   for (;;) {
     if (want_flush) {
       flush();
@@ -377,25 +536,20 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
       Group g1;
       g1.w[0] = v.x; g1.w[1] = v.y; g1.w[2] = v.z; g1.w[3] = v.w;
       float x[E];
-      stage(g1, group_max(g1, x), (uint32_t)ov_t0 + o);
+      stage(g1, group_max(g1, x), (uint32_t)ov_t0 + o, false, true);  // counted the first time
       ++ovj;
       want_flush = true;
       continue;
     }
     if (t0 < e_tiles) {
       Group g[WTG];
-      load_tile_full<DT, WTG, true>(g, xr + t0);
+      load_tile_buf<DT, WTG>(g, xr + t0);
       if (first) {
         first_tile(g, t0);
         first = false;
-      } else {
-        // another wave may have raised the threshold
-        const uint64_t Ts = __hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (Ts > T) {
-          T = Ts;
-          tf = thr_float(T);
-        }
       }
+      // the shared threshold, read early (used after the exp2 work)
+      const uint64_t Ts = __hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       const uint32_t sn0 = sn;
       float gm[WTG];
       float tmax = -__builtin_inff();
@@ -408,9 +562,14 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
       // compiler keeps many groups unpacked at once)
       if constexpr (WANT_LSE) asm volatile("" ::"v"(ls), "v"(tmax));
       lse_check(g, tmax);
+      if (Ts > T) {
+        T = Ts;
+        tf = thr_float(T);
+      }
 #pragma unroll
-      for (int j = 0; j < WTG; ++j) stage(g[j], gm[j], (uint32_t)t0 + (uint32_t)(j * NT + tid) * E);
+      for (int j = 0; j < WTG; ++j) stage(g[j], gm[j], (uint32_t)t0 + (uint32_t)(j * NT + tid) * E, true, true);
       fold();
+      if ((tix++ & (NWAVE - 1)) == (uint32_t)wave) hist_threshold();
       if (sn > kWStage) {
         sn = sn0;  // open the earlier groups, then take this tile again
         ov_t0 = t0;
@@ -433,7 +592,7 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
       }
       const float gm1 = lse_group(g1[0]);
       lse_check(g1, gm1);
-      stage(g1[0], gm1, (uint32_t)t0 + (uint32_t)tid * E);
+      stage(g1[0], gm1, (uint32_t)t0 + (uint32_t)tid * E, true, false);
       fold();
       if (sn >= kFlushAt) want_flush = true;
       t0 += (int64_t)NT * E;
@@ -471,13 +630,8 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
     if (lm != lm || lm == __builtin_inff()) r.s = __builtin_nan("");
     else if (lm != -__builtin_inff()) r.s = LS * exp2_split(((double)om - (double)lm) * (double)c);
   }
-  r = wave_lse(r, c);
-  if (lane == 0) {
-    sh.wm[wave] = r.m;
-    sh.ws[wave] = r.s;
-    atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)T);
-  }
-  __syncthreads();
+  if (lane == 0) atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)T);
+  r = block_lse(r, c, sh.wm, sh.ws);  // (its barriers also publish s_T)
   // Keep only the records that reach the final shared threshold (at least k
   // in all: it is some wave's k-th largest, or the first tile's bound).
   {
@@ -496,9 +650,6 @@ __global__ __launch_bounds__(NT) void topk_wave_kernel(TopkArgs a) {
   }
   if (lane == 0) wcount[wave] = wcnt;
   __syncthreads();
-  r = LSE{sh.wm[0], sh.ws[0]};
-#pragma unroll
-  for (int q = 1; q < NWAVE; ++q) r = lse_merge(r, LSE{sh.wm[q], sh.ws[q]}, c);
   // Gather the four lists at the front of s_key: every record goes through
   // registers first (a destination may overlap another wave's list).
   uint32_t off = 0, n = 0;
