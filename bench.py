@@ -130,7 +130,7 @@ def main():
                    "rows": ROWS, "vocab": V, "ld": LD, "k": K},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "topk_kernel<bf16, lse>", "us_per_launch": us_per_launch,
+                     "kernel": "topk_wave_kernel<bf16, lse>", "us_per_launch": us_per_launch,
                      "algorithmic_bytes_per_launch": abytes},
     }
 

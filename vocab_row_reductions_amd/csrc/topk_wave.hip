@@ -35,7 +35,12 @@ constexpr uint32_t kWCap = 512;       // candidate records per wave
 constexpr uint32_t kWStage = 128;     // staged groups per wave
 constexpr uint32_t kFlushAt = 64;     // open the staged groups at a tile end from this many
 constexpr float kLazyLog2 = 64.0f;    // the exp2 offset moves when a maximum passes it by this
-constexpr uint32_t kRank = NT;        // records ordered by rank directly, one per thread
+constexpr uint32_t kRank = NT;
+#ifndef PRIO_Q1
+#define PRIO_Q1 (ntiles / 4)
+#define PRIO_Q2 (ntiles / 2)
+#define PRIO_Q3 (ntiles - ntiles / 4)
+#endif        // records ordered by rank directly, one per thread
 
 struct WaveArea {
   uint32_t w[kWStage][4];
@@ -50,6 +55,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// A value every lane of the wave holds, kept in scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
@@ -206,10 +218,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   // lower bound of the segment's k-th largest key for every wave.
   __shared__ uint64_t s_slot[NWAVE];
   __shared__ uint64_t s_T;
-  // Histogram of the maxima of staged groups (distinct elements): bin b
-  // counts maxima whose value key is at least hbase + (b << 16) (the last
-  // bin: and above).  The lower edge of the highest bin at which the count
-  // from the top reaches k is a valid threshold for every wave.
+  // Histogram of lane maxima (one per lane and tile, so distinct
+  // elements) that reach the threshold: bin b counts maxima whose value key
+  // is at least hbase + (b << 16) (the last bin: and above).  The lower edge
+  // of the highest bin at which the count from the top reaches k is a valid
+  // threshold for every wave.
   __shared__ uint32_t s_hist[256];
   __shared__ SelShared sh;
 
@@ -268,10 +281,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     return m0;
   };
 
-  // count: add the group's maximum to the histogram (a group seen for the
-  // first time, and a real one -- pad groups start at or past e_full).
-  // full: the group is known to be real (a full tile).
-  auto stage = [&](const Group& g, float gm, uint32_t e0, bool count, bool full) {
+  auto stage = [&](const Group& g, float gm, uint32_t e0) {
     const bool pass = gm >= tf;
     const uint64_t bm = __ballot(pass);
     if (bm) {
@@ -280,10 +290,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 #pragma unroll
         for (int i = 0; i < 4; ++i) area.w[p][i] = g.w[i];
         area.e0[p] = e0;
-      }
-      if (count && pass && (full || e0 < e_full32)) {
-        const uint32_t hk = fkey(__float_as_uint(gm));
-        if (hk >= hbase) atomicAdd(&s_hist[min(255u, (hk - hbase) >> 16)], 1u);
       }
       sn += (uint32_t)__popcll(bm);
     }
@@ -318,6 +324,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       const uint64_t Th = (uint64_t)(hbase + (bin << 16)) << 32;
       if (lane == 0) atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)Th);
     }
+  };
+
+  // Add a lane maximum (a real element, seen for the first time) that
+  // reaches the threshold to the histogram.
+  auto count_max = [&](float m) {
+    const uint32_t hk = fkey(__float_as_uint(m));
+    if (m >= tf && hk >= hbase) atomicAdd(&s_hist[min(255u, (hk - hbase) >> 16)], 1u);
   };
 
   // Maximum and log-sum-exp terms of one group against the lane's current
@@ -401,7 +414,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       }
       wave_lds_sync();
     }
-    const uint64_t Ts = __hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t Ts = uniform_u64(__hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
     if (Ts > T) T = Ts;
     wcnt = wave_cut(wb, wcnt, T);
     if (wcnt > select_at) {
@@ -520,6 +533,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   // the groups staged before it are opened (its log-sum-exp terms are
   // already in).
   const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
+  // Fair progress: the SIMD arbiter favours older waves, so without help
+  // the first of the workgroups sharing a CU races ahead and the last one
+  // ends alone, too few waves in flight to keep HBM busy.  A wave starts at
+  // the highest issue priority and drops one level per stage of its tiles,
+  // so waves that are ahead yield to those behind.
+  const uint32_t ntiles = (uint32_t)((e_tiles - e_begin) / TILE);
+  const uint32_t q1 = PRIO_Q1, q2 = PRIO_Q2, q3 = PRIO_Q3;
+  __builtin_amdgcn_s_setprio(3);
   int64_t t0 = e_begin;
   int64_t ov_t0 = 0;
   int ovj = WTG;  // next group of an overflowed tile to take again (WTG: none)
@@ -536,7 +557,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       Group g1;
       g1.w[0] = v.x; g1.w[1] = v.y; g1.w[2] = v.z; g1.w[3] = v.w;
       float x[E];
-      stage(g1, group_max(g1, x), (uint32_t)ov_t0 + o, false, true);  // counted the first time
+      stage(g1, group_max(g1, x), (uint32_t)ov_t0 + o);
       ++ovj;
       want_flush = true;
       continue;
@@ -549,7 +570,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         first = false;
       }
       // the shared threshold, read early (used after the exp2 work)
-      const uint64_t Ts = __hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const uint64_t Ts = uniform_u64(__hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
       const uint32_t sn0 = sn;
       float gm[WTG];
       float tmax = -__builtin_inff();
@@ -567,9 +588,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         tf = thr_float(T);
       }
 #pragma unroll
-      for (int j = 0; j < WTG; ++j) stage(g[j], gm[j], (uint32_t)t0 + (uint32_t)(j * NT + tid) * E, true, true);
+      for (int j = 0; j < WTG; ++j) stage(g[j], gm[j], (uint32_t)t0 + (uint32_t)(j * NT + tid) * E);
+      count_max(tmax);
       fold();
       if ((tix++ & (NWAVE - 1)) == (uint32_t)wave) hist_threshold();
+      if (tix == q1) __builtin_amdgcn_s_setprio(2);
+      else if (tix == q2) __builtin_amdgcn_s_setprio(1);
+      else if (tix == q3) __builtin_amdgcn_s_setprio(0);
       if (sn > kWStage) {
         sn = sn0;  // open the earlier groups, then take this tile again
         ov_t0 = t0;
@@ -592,7 +617,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       }
       const float gm1 = lse_group(g1[0]);
       lse_check(g1, gm1);
-      stage(g1[0], gm1, (uint32_t)t0 + (uint32_t)tid * E, true, false);
+      stage(g1[0], gm1, (uint32_t)t0 + (uint32_t)tid * E);
+      if (t0 + (int64_t)tid * E < e_full) count_max(gm1);  // real groups only
       fold();
       if (sn >= kFlushAt) want_flush = true;
       t0 += (int64_t)NT * E;
