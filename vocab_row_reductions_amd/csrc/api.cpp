@@ -35,19 +35,29 @@ int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap) {
   return std::min<int64_t>(b, std::max<int64_t>(1, cdiv(kMaxSplitWork, rows)));
 }
 
-// Segments per row for a grid that runs `resident` workgroups at once:
-// minimise rounds x (segment length + fixed cost), so that the chip is full
-// and no launch ends with a nearly empty last round.
+// Segments per row for a grid that runs `resident` workgroups at once.
+// About kSatPerCu streaming workgroups per CU already saturate HBM; beyond
+// that, splitting rows only adds merge work.  So a round of n workgroups
+// costs (segment length + a fixed per-segment cost) x max(1, n / sat): a
+// short round is bound by the workgroups' own speed, a full one by HBM.
 // Segment lengths are multiples of `granule` elements (a multiple of 8).
+constexpr int64_t kSatPerCu = 4;
+int device_cus();
 Plan plan_segments(int64_t rows, int64_t V, int64_t k, int64_t resident, int cap, int64_t granule = 8) {
   const int64_t sb = seg_bound(rows, V, k, cap);
+  const int64_t sat = kSatPerCu * device_cus();
   Plan best{1, cdiv(V, granule) * granule};
-  int64_t best_cost = INT64_MAX;
+  double best_cost = 1e300;
   for (int64_t S = 1; S <= sb; ++S) {
     const int64_t seg = cdiv(cdiv(V, S), granule) * granule;
     const int64_t Sx = cdiv(V, seg);
     if (Sx != S) continue;
-    const int64_t cost = cdiv(rows * Sx, std::max<int64_t>(1, resident)) * (seg + kSegOverhead);
+    const int64_t n = rows * Sx, res = std::max<int64_t>(1, resident);
+    double cost = 0.0;
+    for (int64_t left = n; left > 0; left -= res) {
+      const int64_t in_round = std::min(left, res);
+      cost += (double)(seg + kSegOverhead) * std::max(1.0, (double)in_round / (double)sat);
+    }
     if (cost < best_cost) {
       best_cost = cost;
       best = Plan{(int32_t)Sx, seg};

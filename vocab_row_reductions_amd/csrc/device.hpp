@@ -429,6 +429,67 @@ __device__ inline void sample_tail(const uint64_t* key, const uint32_t* bits, ui
   *logp = (float)(((double)__uint_as_float(bits[pick]) - z0) / T - log(W));
 }
 
+// A value every lane of the wave holds, kept in scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// One full tile of NG 16-byte groups per lane through a buffer resource
+// based at the tile (scalar base, per-lane offset, per-group scalar offset:
+// no vector address arithmetic); reads past the tile would return zero.
+template <typename DT, int NG>
+__device__ __forceinline__ void load_tile_buf(Group (&g)[NG], const DT* __restrict__ tb) {
+  constexpr int E = Elem<DT>::E;
+  constexpr int kTileBytes = NT * NG * 16;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)tb, 0, kTileBytes, 0x00020000);
+  const int vo = (int)threadIdx.x * 16;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, j * NT * 16, 2 /* nontemporal */);
+    g[j].w[0] = v.x; g[j].w[1] = v.y; g[j].w[2] = v.z; g[j].w[3] = v.w;
+  }
+  (void)E;
+}
+
+// 2^a in float64 for a finite a, to float precision (the fraction through
+// the hardware exp2, the integer part exactly through ldexp); saturates far
+// outside the float64 range.
+__device__ __forceinline__ double exp2_split(double a) {
+  a = fmin(fmax(a, -1100.0), 1100.0);
+  const double n = floor(a);
+  return ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
+}
+
+// Log-sum-exp states (m, s) of the workgroup's lanes merged: the maximum
+// first (NaN-propagating), then one rescale per lane and float64 sums, so
+// no step pays more than one exp2.  Every thread must call; every thread
+// gets the result.
+__device__ __forceinline__ LSE block_lse(LSE v, float c, float* sm, double* ss) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float M = wave_max_nan(v.m);
+  if (lane == 0) sm[wave] = M;
+  __syncthreads();
+  M = sm[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) M = fmax_nan(M, sm[q]);
+  double t = 0.0;
+  if (M != M || M == __builtin_inff()) t = __builtin_nan("");
+  else if (v.m != -__builtin_inff()) t = v.s * exp2_split(((double)v.m - (double)M) * (double)c);
+  t = wave_sum_f64(t);
+  if (lane == 0) ss[wave] = t;
+  __syncthreads();
+  double S = ss[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) S += ss[q];
+  return LSE{M, S};
+}
+
 // Cross-workgroup data (segment partials, tickets) moves only through
 // device-scope atomic loads and stores.  On gfx950 these are coherent across
 // the XCDs' separate L2s by themselves, so no whole-cache writeback or

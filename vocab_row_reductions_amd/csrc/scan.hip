@@ -18,21 +18,13 @@
 
 namespace vsel {
 
-constexpr int SG = 8;  // 16-byte groups per lane per tile
-
-// One element of the log-sum-exp, for the few elements past the last whole
-// group (one lane).
-__device__ __forceinline__ void lse_push(LSE& st, float x, float c) {
-  const float mn = fmax_nan(st.m, x);
-  const float ms = (mn == -__builtin_inff()) ? 0.0f : mn;
-  const double scale = (st.m == mn) ? 1.0 : (double)__builtin_amdgcn_exp2f((st.m - ms) * c);
-  st.s = st.s * scale + (double)__builtin_amdgcn_exp2f((x - ms) * c);
-  st.m = mn;
-}
+constexpr int SG = 8;            // 16-byte groups per lane per tile
+constexpr float kLazyScan = 64.0f; // the exp2 offset moves when a maximum passes it by this
 
 template <typename DT, bool WANT_LSE, bool VEC>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
   constexpr int E = Elem<DT>::E;
+  constexpr int64_t TILE = (int64_t)NT * SG * E;
   __shared__ SelShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const Item it = work_item(a.S);
@@ -47,86 +39,185 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
   const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
   const float c = a.lse_c;
 
-  // Lane state: its first maximum (elements arrive in index order) and the
-  // log-sum-exp pair.  A group is searched for its first maximum only when
-  // its maximum beats the lane's best so far.
+  // First maximum without a search per group: each lane keeps its best
+  // group (strictly greater, so the earliest of equal maxima -- a lane's
+  // elements arrive in index order), that group's position and its words;
+  // the first element equal to the maximum is found once, at the end.
   float best = -__builtin_inff();
-  uint32_t bidx = 0;
-  LSE st{-__builtin_inff(), 0.0};
-  auto tile = [&](const auto& g, int64_t t0) {
-    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
-    // exponents as (x - ob) * c with the offset ob in input units: exact for
-    // the maximum itself at any magnitude (x * c - ob * c would carry the
-    // rounding of both products)
-    float mt = st.m, ob = 0.0f, stile = 0.0f;
-    if constexpr (WANT_LSE) ob = (mt == -__builtin_inff()) ? 0.0f : mt;
+  uint32_t bpos = 0, tail_idx = 0;
+  bool from_tail = false;
+  Group bw;
 #pragma unroll
-    for (int j = 0; j < NGP; ++j) {
-      float x[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = __uint_as_float(gbits<DT>(g[j], e));
-      float m0 = x[0];
-#pragma unroll
-      for (int e = 1; e < E; ++e) m0 = fmax_nan(m0, x[e]);
-      if (m0 > best) {
-        uint32_t f = E - 1;
-#pragma unroll
-        for (int e = E - 2; e >= 0; --e) f = (x[e] == m0) ? (uint32_t)e : f;
-        best = m0;
-        bidx = (uint32_t)t0 + (uint32_t)(j * NT + tid) * E + f;
-      }
-      if constexpr (WANT_LSE) {
-        const float mn = fmax_nan(mt, m0);
-        if (!(mn == mt)) {
-          const float ms = (mn == -__builtin_inff()) ? 0.0f : mn;
-          stile *= __builtin_amdgcn_exp2f((mt - ms) * c);
-          ob = ms;
-          mt = mn;
-        }
-        float acc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc += __builtin_amdgcn_exp2f((x[e] - ob) * c);
-        stile += acc;
-      } else {
-        mt = fmax_nan(mt, m0);
-      }
-    }
-    if constexpr (WANT_LSE) {
-      // st.m < mt here unless equal; an empty state (st.m = -inf) scales to 0
-      const double scale = (st.m == mt) ? 1.0 : (double)__builtin_amdgcn_exp2f((st.m - mt) * c);
-      st.s = st.s * scale + (double)stile;
-    }
-    st.m = mt;
+  for (int i = 0; i < 4; ++i) bw.w[i] = 0u;
+
+  // Log-sum-exp with a lazy offset om (input units), as in the fused top-k
+  // kernel: LS is the lane's sum of 2^((x - om) c) in float64; terms are
+  // exp2(fma(x, c, noff)) with noff = -fl(om c), corrected by corr = 2^-delta
+  // for that rounding when folded in; past |om| = 2^25 the lane takes exact
+  // exp2((x - om) c) terms (huge).  A tile maximum above trig moves om.
+  float lm = -__builtin_inff(), om = -__builtin_inff(), trig = -__builtin_inff(), noff = 0.0f, ls = 0.0f;
+  double LS = 0.0, corr = 1.0;
+  bool huge = false;
+  auto set_offset = [&](float m) {
+    LS = (om == -__builtin_inff()) ? 0.0 : LS * exp2_split(((double)om - (double)m) * (double)c);
+    om = m;
+    const float oc = m * c;
+    noff = -oc;
+    trig = m + kLazyScan / c;
+    corr = exp2_split((double)oc - (double)m * (double)c);
+    huge = !(__builtin_fabsf(m) <= 0x1p25f);
   };
-  walk_groups<DT, SG, VEC>(xr, e_begin, e_full, tile);
+
+  auto group = [&](const Group& g, uint32_t pos) {
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = __uint_as_float(gbits<DT>(g, e));
+    float m0 = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) m0 = fmax_nan(m0, x[e]);
+    const bool upd = m0 > best;
+    best = upd ? m0 : best;
+    bpos = upd ? pos : bpos;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bw.w[i] = upd ? g.w[i] : bw.w[i];
+    if constexpr (WANT_LSE) {
+      float acc = __builtin_amdgcn_exp2f(fmaf(x[0], c, noff));
+#pragma unroll
+      for (int e = 1; e < E; ++e) acc += __builtin_amdgcn_exp2f(fmaf(x[e], c, noff));
+      ls += acc;
+    }
+    return m0;
+  };
+
+  // After a tile's terms are in ls: a lane whose tile maximum passed its
+  // trigger moves its offset there; it, and a lane past the fast-path range,
+  // recompute the tile's terms.
+  auto lse_check = [&](auto& g, float tmax) {
+    lm = fmax_nan(lm, tmax);
+    if constexpr (WANT_LSE) {
+      constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+      const bool up = tmax > trig && tmax < __builtin_inff();
+      if (__ballot(up || huge)) {
+        if (up) set_offset(tmax);
+        if (up || huge) {
+          auto fresh = [&](int j, float (&x)[E]) {
+            uint32_t w0 = g[j].w[0], w1 = g[j].w[1], w2 = g[j].w[2], w3 = g[j].w[3];
+            asm volatile("" : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+            Group gf;
+            gf.w[0] = w0; gf.w[1] = w1; gf.w[2] = w2; gf.w[3] = w3;
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = __uint_as_float(gbits<DT>(gf, e));
+          };
+          ls = 0.0f;
+          if (huge) {
+            for (int j = 0; j < NGP; ++j) {
+              float x[E];
+              fresh(j, x);
+#pragma unroll
+              for (int e = 0; e < E; ++e) ls += __builtin_amdgcn_exp2f((x[e] - om) * c);
+            }
+          } else {
+            for (int j = 0; j < NGP; ++j) {
+              float x[E];
+              fresh(j, x);
+#pragma unroll
+              for (int e = 0; e < E; ++e) ls += __builtin_amdgcn_exp2f(fmaf(x[e], c, noff));
+            }
+          }
+        }
+      }
+    }
+  };
+  auto fold = [&]() {
+    if constexpr (WANT_LSE) {
+      LS += huge ? (double)ls : (double)ls * corr;
+      ls = 0.0f;
+    }
+  };
+  // Before the first tile's terms: start the offset at the lane's maximum
+  // of that tile (the asm keeps these unpacked values from being shared
+  // with the pass that follows).
+  auto seed = [&](auto& g) {
+    if constexpr (WANT_LSE) {
+      constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < NGP; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmax_nan(m, __uint_as_float(gbits<DT>(g[j], e)));
+#pragma unroll
+      for (int j = 0; j < NGP; ++j) asm volatile("" : "+v"(g[j].w[0]), "+v"(g[j].w[1]), "+v"(g[j].w[2]), "+v"(g[j].w[3]));
+      if (m > -__builtin_inff() && m < __builtin_inff()) set_offset(m);
+    }
+  };
+
+  const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
+  bool first = true;
+  for (int64_t t0 = e_begin; t0 < e_tiles; t0 += TILE) {
+    Group g[SG];
+    if constexpr (VEC) load_tile_buf<DT, SG>(g, xr + t0);
+    else load_tile_full<DT, SG, false>(g, xr + t0);
+    if (first) {
+      seed(g);
+      first = false;
+    }
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < SG; ++j) tmax = fmax_nan(tmax, group(g[j], (uint32_t)t0 + (uint32_t)(j * NT + tid) * E));
+    if constexpr (WANT_LSE) asm volatile("" ::"v"(ls), "v"(tmax));
+    lse_check(g, tmax);
+    fold();
+  }
+  // the row's last partial tile: one group per lane at a time (pads -inf)
+  for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
+    Group g1[1];
+    load_tile<DT, 1, VEC>(g1, xr, t0, e_full);
+    if (first) {
+      seed(g1);
+      first = false;
+    }
+    const float m1 = group(g1[0], (uint32_t)t0 + (uint32_t)tid * E);
+    lse_check(g1, m1);
+    fold();
+  }
+  // the row's last few elements (fewer than one group): one lane
   if (e_full < e_end && tid == 0) {
     for (int64_t i = e_full; i < e_end; ++i) {
       const float x = __uint_as_float(gbits_at<DT>(xr, i));
       if (x > best) {
         best = x;
-        bidx = (uint32_t)i;
+        tail_idx = (uint32_t)i;
+        from_tail = true;
       }
-      if constexpr (WANT_LSE) lse_push(st, x, c);
-      else st.m = fmax_nan(st.m, x);
+      lm = fmax_nan(lm, x);
+      if constexpr (WANT_LSE) {
+        if (x > trig && x < __builtin_inff()) set_offset(x);
+        LS += huge ? (double)__builtin_amdgcn_exp2f((x - om) * c)
+                   : (double)__builtin_amdgcn_exp2f(fmaf(x, c, noff)) * corr;
+      }
     }
+  }
+  // the lane's first maximum inside its best group
+  uint32_t bidx = tail_idx;
+  if (!from_tail) {
+    uint32_t f = E - 1;
+#pragma unroll
+    for (int e = E - 2; e >= 0; --e) f = (__uint_as_float(gbits<DT>(bw, e)) == best) ? (uint32_t)e : f;
+    bidx = bpos + f;
   }
 
   uint64_t P = (best > -__builtin_inff()) ? (((uint64_t)fkey(__float_as_uint(best)) << 32) | (uint32_t)~bidx) : 0ull;
   P = wave_max_u64(P);
-  LSE r = wave_lse(st, c);
-  if (lane == 0) {
-    sh.wk[wave] = P;
-    sh.wm[wave] = r.m;
-    sh.ws[wave] = r.s;
+  if (lane == 0) sh.wk[wave] = P;
+  LSE r{lm, 0.0};
+  if constexpr (WANT_LSE) {
+    if (lm != lm || lm == __builtin_inff()) r.s = __builtin_nan("");
+    else if (lm != -__builtin_inff()) r.s = LS * exp2_split(((double)om - (double)lm) * (double)c);
   }
-  __syncthreads();
+  r = block_lse(r, c, sh.wm, sh.ws);  // its barriers also publish sh.wk
   P = sh.wk[0];
-  r = LSE{sh.wm[0], sh.ws[0]};
 #pragma unroll
-  for (int q = 1; q < NWAVE; ++q) {
-    P = sh.wk[q] > P ? sh.wk[q] : P;
-    r = lse_merge(r, LSE{sh.wm[q], sh.ws[q]}, c);
-  }
+  for (int q = 1; q < NWAVE; ++q) P = sh.wk[q] > P ? sh.wk[q] : P;
 
   if (a.S > 1) {
     const int64_t slot = row * a.S + seg;
