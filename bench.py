@@ -25,6 +25,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048, 1 GPU"
+
+# HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
+# (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
+# known size), valid for the kernel sources they were taken on.
+TRAFFIC_BYTES = 414_936_948
+TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
+                   "vocab_row_reductions_amd/csrc/internal.hpp")
+TRAFFIC_SHA256 = "28db74d6df6983ad7ad3b480779ef226d20a0265c7ca1ab59e985efc219c46e2"
+
+
+def measured_traffic():
+    """Bytes per launch from the counter runs, or None if the kernel changed since."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return TRAFFIC_BYTES if h.hexdigest() == TRAFFIC_SHA256 else None
 HBM_PEAK_GBS = 8000.0
 ROWS, V, LD, K = 1024, 202_048, 202_112, 84
 
@@ -129,7 +147,7 @@ def main():
                                "fused argmax + top-k k=84 + logsumexp, inputs rotated over 3 HBM copies",
                    "rows": ROWS, "vocab": V, "ld": LD, "k": K},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "topk_wave_kernel<bf16, lse>", "us_per_launch": us_per_launch,
                      "algorithmic_bytes_per_launch": abytes},
     }
