@@ -171,20 +171,53 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
   return __longlong_as_double((long long)shfl_xor_u64((uint64_t)__double_as_longlong(v), m));
 }
+// Wave all-reductions without LDS: four DPP steps inside each row of 16
+// lanes (swap neighbours, swap pairs, mirror the half-row, mirror the row),
+// after which every lane of a row holds the row's result; the four rows are
+// combined through readlane.  Every lane of the wave must be active.
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  return ((uint64_t)lane_u32((uint32_t)(v >> 32), l) << 32) | lane_u32((uint32_t)v, l);
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) { uint64_t o = shfl_xor_u64(v, m); v = o > v ? o : v; }
-  return v;
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<kDppXor1>(v));
+  v = mx(v, dpp_u64<kDppXor2>(v));
+  v = mx(v, dpp_u64<kDppHalfMirror>(v));
+  v = mx(v, dpp_u64<kDppMirror>(v));
+  return mx(mx(lane_u64(v, 0), lane_u64(v, 16)), mx(lane_u64(v, 32), lane_u64(v, 48)));
 }
 __device__ __forceinline__ float wave_max_nan(float v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) v = fmax_nan(v, __shfl_xor(v, m));
-  return v;
+  auto f = [](uint32_t u) { return __uint_as_float(u); };
+  v = fmax_nan(v, f(dpp_u32<kDppXor1>(__float_as_uint(v))));
+  v = fmax_nan(v, f(dpp_u32<kDppXor2>(__float_as_uint(v))));
+  v = fmax_nan(v, f(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmax_nan(v, f(dpp_u32<kDppMirror>(__float_as_uint(v))));
+  const uint32_t u = __float_as_uint(v);
+  return fmax_nan(fmax_nan(f(lane_u32(u, 0)), f(lane_u32(u, 16))), fmax_nan(f(lane_u32(u, 32)), f(lane_u32(u, 48))));
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) v += shfl_xor_f64(v, m);
-  return v;
+  auto d = [](uint64_t u) { return __longlong_as_double((long long)u); };
+  auto u = [](double x) { return (uint64_t)__double_as_longlong(x); };
+  v += d(dpp_u64<kDppXor1>(u(v)));
+  v += d(dpp_u64<kDppXor2>(u(v)));
+  v += d(dpp_u64<kDppHalfMirror>(u(v)));
+  v += d(dpp_u64<kDppMirror>(u(v)));
+  return (d(lane_u64(u(v), 0)) + d(lane_u64(u(v), 16))) + (d(lane_u64(u(v), 32)) + d(lane_u64(u(v), 48)));
 }
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
 #pragma unroll

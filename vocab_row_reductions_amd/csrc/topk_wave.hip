@@ -36,11 +36,8 @@ constexpr uint32_t kWStage = 128;     // staged groups per wave
 constexpr uint32_t kFlushAt = 64;     // open the staged groups at a tile end from this many
 constexpr float kLazyLog2 = 64.0f;    // the exp2 offset moves when a maximum passes it by this
 constexpr uint32_t kRank = NT;
-#ifndef PRIO_Q1
-#define PRIO_Q1 (ntiles / 4)
-#define PRIO_Q2 (ntiles / 2)
-#define PRIO_Q3 (ntiles - ntiles / 4)
-#endif        // records ordered by rank directly, one per thread
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+        // records ordered by rank directly, one per thread
 
 struct WaveArea {
   uint32_t w[kWStage][4];
@@ -147,7 +144,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   constexpr int E = Elem<DT>::E;
   constexpr int64_t TILE = (int64_t)NT * WTG * E;
   constexpr uint32_t kBlockCap = NWAVE * kWCap;  // the lists, then the row's merge buffer
-  __shared__ uint64_t s_key[kBlockCap];
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[kBlockCap];
   __shared__ WaveArea area_all[NWAVE];
   __shared__ uint32_t wcount[NWAVE];
   // Shared threshold.  Wave w publishes in s_slot[w] a key with at least
@@ -475,10 +472,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   // Fair progress: the SIMD arbiter favours older waves, so without help
   // the first of the workgroups sharing a CU races ahead and the last one
   // ends alone, too few waves in flight to keep HBM busy.  A wave starts at
-  // the highest issue priority and drops one level per stage of its tiles,
-  // so waves that are ahead yield to those behind.
+  // the highest issue priority and drops one level per quarter of its
+  // tiles, so waves that are ahead yield to those behind; the quarters of a
+  // younger workgroup end one tile later per step of age.  (Workgroups are
+  // dealt to the CUs in turn, so in a grid of four per CU the age rank is
+  // blockIdx * 4 / gridDim; in other grids the shift is merely harmless.)
   const uint32_t ntiles = (uint32_t)((e_tiles - e_begin) / TILE);
-  const uint32_t q1 = PRIO_Q1, q2 = PRIO_Q2, q3 = PRIO_Q3;
+  const uint32_t age = (blockIdx.x * 4u) / gridDim.x;
+  const uint32_t q1 = ntiles / 4 + age, q2 = ntiles / 2 + age, q3 = ntiles - ntiles / 4 + age;
   __builtin_amdgcn_s_setprio(3);
   int64_t t0 = e_begin;
   int64_t ov_t0 = 0;
@@ -589,75 +590,111 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     if (pass) wb[wcnt + lane_rank(m)] = K;
     wcnt += (uint32_t)__popcll(m);
   }
-  // Lane log-sum-exp state relative to the lane maximum, then the workgroup's.
+  // End of the segment, in four barriers.
+  // (1) Each wave's log-sum-exp (relative to the wave's maximum) and its
+  //     threshold go to LDS.
   LSE r{lm, 0.0};
   if constexpr (WANT_LSE) {
     if (lm != lm || lm == __builtin_inff()) r.s = __builtin_nan("");
     else if (lm != -__builtin_inff()) r.s = LS * exp2_split(((double)om - (double)lm) * (double)c);
   }
-  if (lane == 0) atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)T);
-  r = block_lse(r, c, sh.wm, sh.ws);  // (its barriers also publish s_T)
-  // Keep only the records that reach the final shared threshold (at least k
-  // in all: it is some wave's k-th largest, or the first tile's bound).
+  {
+    const float Mw = wave_max_nan(r.m);
+    double t = 0.0;
+    if (Mw != Mw || Mw == __builtin_inff()) t = __builtin_nan("");
+    else if (r.m != -__builtin_inff()) t = r.s * exp2_split(((double)r.m - (double)Mw) * (double)c);
+    t = wave_sum_f64(t);
+    if (lane == 0) {
+      sh.wm[wave] = Mw;
+      sh.ws[wave] = t;
+      atomicMax(reinterpret_cast<unsigned long long*>(&s_T), (unsigned long long)T);
+    }
+  }
+  __syncthreads();
+  // (2) The workgroup's log-sum-exp (every thread), and each wave's records
+  //     that reach the final shared threshold (at least k in all: it is some
+  //     wave's k-th largest, a valid histogram bound, or the first tile's
+  //     bound), taken into registers with their place among the wave's kept.
+  {
+    float M = sh.wm[0];
+#pragma unroll
+    for (int q = 1; q < NWAVE; ++q) M = fmax_nan(M, sh.wm[q]);
+    double S = 0.0;
+    if (M != M || M == __builtin_inff()) {
+      S = __builtin_nan("");
+    } else {
+#pragma unroll
+      for (int q = 0; q < NWAVE; ++q)
+        if (sh.wm[q] != -__builtin_inff()) S += sh.ws[q] * exp2_split(((double)sh.wm[q] - (double)M) * (double)c);
+    }
+    r = LSE{M, S};
+  }
+  constexpr uint32_t kPer = kWCap / 64;
+  uint64_t held[kPer];
+  uint32_t place[kPer];
   {
     const uint64_t Tb = s_T > T ? s_T : T;
-    uint32_t base = 0;
-    for (uint32_t c0 = 0; c0 < wcnt; c0 += 64) {
-      const uint32_t i = c0 + lane;
-      const uint64_t K = i < wcnt ? wb[i] : 0ull;
-      const bool keep = i < wcnt && K >= Tb;
+    uint32_t kept = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kPer; ++q) {
+      const uint32_t i = q * 64 + lane;
+      held[q] = i < wcnt ? wb[i] : 0ull;
+      const bool keep = i < wcnt && held[q] >= Tb;
       const uint64_t m = __ballot(keep);
-      wave_lds_sync();
-      if (keep) wb[base + lane_rank(m)] = K;
-      base += (uint32_t)__popcll(m);
+      place[q] = keep ? kept + lane_rank(m) : 0xFFFFFFFFu;
+      kept += (uint32_t)__popcll(m);
     }
-    wcnt = base;
+    wcnt = kept;
   }
   if (lane == 0) wcount[wave] = wcnt;
   __syncthreads();
-  // Gather the four lists at the front of s_key: every record goes through
-  // registers first (a destination may overlap another wave's list).
+  // (3) Every wave writes its kept records to their place at the front of
+  //     s_key (the lists are all in registers by now), then zeros after them.
   uint32_t off = 0, n = 0;
 #pragma unroll
   for (int q = 0; q < NWAVE; ++q) {
     if (q < wave) off += wcount[q];
     n += wcount[q];
   }
-  {
-    constexpr uint32_t kPer = kWCap / 64;
-    uint64_t held[kPer];
 #pragma unroll
-    for (uint32_t q = 0; q < kPer; ++q) {
-      const uint32_t i = q * 64 + lane;
-      held[q] = i < wcnt ? wb[i] : 0ull;
-    }
-    __syncthreads();
-#pragma unroll
-    for (uint32_t q = 0; q < kPer; ++q) {
-      const uint32_t i = q * 64 + lane;
-      if (i < wcnt) s_key[off + i] = held[q];
-    }
-  }
+  for (uint32_t q = 0; q < kPer; ++q)
+    if (place[q] != 0xFFFFFFFFu) s_key[off + place[q]] = held[q];
+  if (n <= kRank && tid < 8) s_key[n + tid] = 0ull;  // (else the select below pads)
   __syncthreads();
-  // Winners in (value desc, id asc) order at okey: more than kRank records
-  // are first cut to k by the radix select; then each record's rank among
-  // the rest is its place (ranks >= k drop out).
+  // (4) Winners in (value desc, id asc) order at okey: more than kRank
+  //     records are first cut to k by the radix select; then each record's
+  //     rank among the rest is its place (ranks >= k drop out).
   uint64_t* okey = s_key + kBlockCap / 2;
-  auto rank_order = [&](uint32_t& nn) {
+  auto rank_order = [&](uint32_t& nn, bool padded) {
     if (nn > kRank) {
       select_compact<kBlockCap>(sh, s_key, nullptr, nn, k);
       nn = k;
+      padded = false;
+    }
+    if (!padded) {
+      // zeros after the keys (never above a real key), so the count runs in
+      // whole blocks of 8: two keys per 16-byte read, four reads in flight
+      if (tid < 8) s_key[nn + tid] = 0ull;
+      __syncthreads();
     }
     if ((uint32_t)tid < nn) {
       const uint64_t K = s_key[tid];
       uint32_t r0 = 0;
-      for (uint32_t j = 0; j < nn; ++j) r0 += s_key[j] > K ? 1u : 0u;
+      const uint32_t n8 = (nn + 7u) & ~7u;
+      for (uint32_t j = 0; j < n8; j += 8) {
+        const u64x2 q0 = *reinterpret_cast<const u64x2*>(&s_key[j]);
+        const u64x2 q1 = *reinterpret_cast<const u64x2*>(&s_key[j + 2]);
+        const u64x2 q2 = *reinterpret_cast<const u64x2*>(&s_key[j + 4]);
+        const u64x2 q3 = *reinterpret_cast<const u64x2*>(&s_key[j + 6]);
+        r0 += (uint32_t)(q0.x > K) + (uint32_t)(q0.y > K) + (uint32_t)(q1.x > K) + (uint32_t)(q1.y > K) +
+              (uint32_t)(q2.x > K) + (uint32_t)(q2.y > K) + (uint32_t)(q3.x > K) + (uint32_t)(q3.y > K);
+      }
       if (r0 < k) okey[r0] = K;
     }
     __syncthreads();
     nn = min(nn, k);
   };
-  rank_order(n);
+  rank_order(n, n <= kRank);
 
   if (a.S > 1) {
     const int64_t slot = row * a.S + seg;
@@ -695,7 +732,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       for (uint32_t i = tid; i < cs; i += NT) s_key[o + i] = ld_dev(&a.rec_key[(s0 + sg) * k + i]);
     }
     __syncthreads();
-    rank_order(n);
+    rank_order(n, false);
   }
 
   const bool bad = (r.m != r.m) || (r.m == __builtin_inff());
@@ -712,7 +749,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       a.out_ids[row * k + j] = ok ? ~(uint32_t)K : kFail;
       a.out_vals[row * k + j] = ok ? __uint_as_float(win_bits(K)) : __builtin_nanf("");
     }
-    if (tid == 0) {
+    if (tid == NT - 1) {  // a thread the loop above leaves idle (k <= 128)
       if (a.out_argmax) a.out_argmax[row] = (none || n == 0) ? kFail : ~(uint32_t)okey[0];
       if (a.out_lse)
         a.out_lse[row] = bad ? __builtin_nanf("")
