@@ -23,11 +23,13 @@ def load(path):
     L.oracle_chunk_geometry.argtypes = [i64, i64, C.POINTER(i64), C.POINTER(i64)]
     L.oracle_argmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, C.c_int]
     L.oracle_lse.argtypes = [vp, C.c_int, i64, i64, i64, f64, vp, C.c_int]
+    L.oracle_argmax_excluding.argtypes = [vp, C.c_int, i64, i64, i64, vp, i64, vp, vp, C.c_int]
     L.oracle_topk.argtypes = [vp, C.c_int, i64, i64, i64, i32, vp, vp, vp, vp, C.c_int]
     L.oracle_sample.argtypes = [vp, C.c_int, i64, i64, i64, f32, i32, f32, vp, vp, vp, vp, C.c_int]
     L.oracle_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, vp, C.c_int]
-    for f in (L.oracle_argmax, L.oracle_lse, L.oracle_topk, L.oracle_sample, L.oracle_spec_accept):
+    for f in (L.oracle_argmax, L.oracle_lse, L.oracle_topk, L.oracle_sample, L.oracle_spec_accept,
+              L.oracle_argmax_excluding):
         f.restype = C.c_int
     return L
 
@@ -75,6 +77,19 @@ def argmax(x, vocab=None, nthreads=0):
     val = np.empty(R, np.float32)
     _check(lib().oracle_argmax(_p(x), dt, R, V, ld, _p(idx), _p(val), nthreads))
     return idx, val
+
+
+def argmax_excluding(x, excluded, vocab=None, nthreads=0):
+    """Greedy serving argmax with an excluded-id set: (idx, status) per row."""
+    x, dt = _rows(x)
+    R, ld = x.shape
+    V = ld if vocab is None else vocab
+    ex = np.ascontiguousarray(np.asarray(excluded, dtype=np.uint32).reshape(-1))
+    idx = np.empty(R, np.uint32)
+    status = np.empty(R, np.uint32)
+    _check(lib().oracle_argmax_excluding(_p(x), dt, R, V, ld, _p(ex) if ex.size else None, ex.size, _p(idx),
+                                         _p(status), nthreads))
+    return idx, status
 
 
 def lse(x, temperature=1.0, vocab=None, nthreads=0):

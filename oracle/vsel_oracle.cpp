@@ -174,6 +174,43 @@ int oracle_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, in
   return 0;
 }
 
+// Greedy serving variant ("Chapter 21", section 21.4): the first-maximum
+// argmax with the request's excluded ids (its end-of-generation set) taken
+// as -inf inside the reduction only -- the row itself is not modified.  A
+// NaN or +inf anywhere in the row, excluded or not, fails it closed.  Ids at
+// or past vocab exclude nothing.  out_status: 0 ok, 1 nonfinite, 2 no
+// element above -inf; out_idx is 0xFFFFFFFF whenever the status is not 0.
+int oracle_argmax_excluding(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                            const uint32_t* excluded, int64_t n_excluded, uint32_t* out_idx,
+                            uint32_t* out_status, int nthreads) {
+  if (!logits || !out_idx || !out_status || rows < 0 || vocab < 1 || ld < vocab || n_excluded < 0 ||
+      (n_excluded > 0 && !excluded) || (dtype != 0 && dtype != 1))
+    return 1;
+  std::vector<char> is_excluded(static_cast<size_t>(vocab), 0);
+  for (int64_t j = 0; j < n_excluded; ++j)
+    if (excluded[j] < static_cast<uint64_t>(vocab)) is_excluded[excluded[j]] = 1;
+  Rows R{logits, dtype, ld};
+  const float neg_inf = -std::numeric_limits<float>::infinity();
+  for_rows(rows, nthreads, [&](int64_t r) {
+    float best = neg_inf;
+    uint32_t idx = 0;
+    bool bad = false;
+    for (int64_t i = 0; i < vocab; ++i) {
+      const float x = R.at(r, i);
+      if (is_bad(x)) bad = true;
+      const float v = is_excluded[i] ? neg_inf : x;
+      if (v > best) {
+        best = v;
+        idx = static_cast<uint32_t>(i);
+      }
+    }
+    const uint32_t status = bad ? 1u : (best == neg_inf ? 2u : 0u);
+    out_status[r] = status;
+    out_idx[r] = status ? kFailClosed : idx;
+  });
+  return 0;
+}
+
 // c3: per-row log-sum-exp at temperature T > 0, float64.
 int oracle_lse(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                double temperature, double* out_lse, int nthreads) {

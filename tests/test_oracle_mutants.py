@@ -31,6 +31,12 @@ MUTANTS = [
      [P.test_spec_invariants_config4_like]),
     ("bonus draw from the wrong target row", "w[x] = p_of(G, x);", "w[x] = p_of(G - 1, x);",
      [P.test_bonus_draw_comes_from_the_last_target_row]),
+    ("excluded ids masked before the finite check",
+     "const float x = R.at(r, i);\n      if (is_bad(x)) bad = true;\n      const float v = is_excluded[i] ? neg_inf : x;",
+     "const float v = is_excluded[i] ? neg_inf : R.at(r, i);\n      if (is_bad(v)) bad = true;",
+     [P.test_argmax_excluding_special_cases]),
+    ("excluded set ignored", "const float v = is_excluded[i] ? neg_inf : x;", "const float v = x;",
+     [P.test_argmax_excluding_matches_numpy_on_masked_rows, P.test_argmax_excluding_brute_force_subsets]),
     ("draw from the last crossing instead of the first", "if (target < c) {", "if (target < c && j + 1 == w.size()) {",
      [P.test_sample_u_grid_frequencies_and_support]),
 ]

@@ -73,6 +73,63 @@ def test_argmax_fail_closed_and_masks(oracle):
     assert list(idx) == [SENT, SENT, SENT, 1, 0, 0]
 
 
+# ---- greedy serving variant ("Chapter 21", section 21.4): excluded ids are
+# -inf inside the reduction only; any NaN / +inf in the row fails it closed.
+def test_argmax_excluding_matches_numpy_on_masked_rows(oracle):
+    rng = np.random.default_rng(11)
+    for V in (1, 5, 64, 1025, 4097):
+        x = (np.round(rng.normal(0, 1, (6, V)) * 4) / 4).astype(np.float32)  # coarse grid: many ties
+        for n_ex in sorted({0, 1, min(V, 3), min(V, 40)}):
+            ex = rng.choice(V, size=n_ex, replace=False).astype(np.uint32)
+            idx, st = oracle.argmax_excluding(x, ex)
+            masked = x.copy()
+            masked[:, ex] = -np.inf
+            for r in range(x.shape[0]):
+                if np.all(np.isneginf(masked[r])):
+                    assert st[r] == 2 and idx[r] == SENT
+                else:
+                    assert st[r] == 0 and idx[r] == np.argmax(masked[r])  # numpy: first occurrence
+    # excluding every position that holds the maximum moves the answer to the next value
+    x = np.array([[3, 9, 1, 9, 9, 7, 7]], np.float32)
+    idx, st = oracle.argmax_excluding(x, [1, 3, 4])
+    assert (idx[0], st[0]) == (5, 0)
+
+
+def test_argmax_excluding_special_cases(oracle):
+    inf = np.inf
+    x = np.array([[1, 5, 3, 5, 2],
+                  [1, np.nan, 3, 2, 0],     # NaN at an excluded id still fails closed
+                  [1, inf, 3, 2, 0],        # so does +inf
+                  [-inf, 4, -inf, -inf, -inf],
+                  [2, 2, 2, 2, 2]], np.float32)
+    idx, st = oracle.argmax_excluding(x, [1])
+    assert list(st) == [0, 1, 1, 2, 0]
+    assert list(idx) == [3, SENT, SENT, SENT, 0]
+    # every id excluded: no candidate; ids past the vocabulary exclude nothing; duplicates are fine
+    idx, st = oracle.argmax_excluding(x[:1], [0, 1, 2, 3, 4])
+    assert (idx[0], st[0]) == (SENT, 2)
+    idx, st = oracle.argmax_excluding(x[:1], [5, 99, 1 << 31, 1, 1])
+    assert (idx[0], st[0]) == (3, 0)
+    # an empty set is the plain argmax (the plain argmax is pinned above)
+    y = np.random.default_rng(3).normal(0, 1, (4, 333)).astype(np.float32)
+    assert np.array_equal(oracle.argmax_excluding(y, [])[0], oracle.argmax(y)[0])
+
+
+def test_argmax_excluding_brute_force_subsets(oracle):
+    # every subset of the ids of small rows with ties, against a direct reading
+    rows = np.array([[0, 1, 1, 0, 1], [2, 2, 2, 2, 2], [-1, 3, -2, 3, 0]], np.float32)
+    for r in rows:
+        for mask in range(32):
+            ex = [i for i in range(5) if mask >> i & 1]
+            idx, st = oracle.argmax_excluding(r[None, :], ex)
+            kept = [i for i in range(5) if i not in ex]
+            if not kept:
+                assert (idx[0], st[0]) == (SENT, 2)
+            else:
+                m = max(r[i] for i in kept)
+                assert (idx[0], st[0]) == (min(i for i in kept if r[i] == m), 0)
+
+
 def test_bf16_rows_widen_exactly(oracle):
     rng = np.random.default_rng(3)
     f = rng.normal(0, 4, (4, 777)).astype(np.float32)
