@@ -182,6 +182,10 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
     ex["topk_k64_us"] = time_calls(lambda i: vsel.vsel_topk(bufs[i % 3], 64, vocab=V, out=out64), 50, 5, stream)
     ex["topk_k64_gbs"] = algorithmic_bytes(ROWS, V, 2, 64) / (ex["topk_k64_us"] * 1e-6) / 1e9
     ex["argmax_only_bf16_1024rows_us"] = time_calls(lambda i: vsel.vsel_argmax(bufs[i % 3], vocab=V), 50, 5, stream)
+    # greedy serving variant: a 16-id end-of-generation set, status word per row
+    exd = torch.from_numpy(W.excluded_ids(V, 16, seed=7).view(np.int32)).to(dev)
+    ex["argmax_excluding16_bf16_1024rows_us"] = time_calls(
+        lambda i: vsel.vsel_argmax_excluding(bufs[i % 3], exd, vocab=V), 50, 5, stream)
 
     def cold_copies(x, total=1 << 30):
         n = max(1, -(-total // (x.numel() * x.element_size())))

@@ -5,6 +5,9 @@
  * sampler needs leave the device:
  *
  *   vsel_argmax       first-maximum argmax per row
+ *   vsel_argmax_excluding
+ *                     the greedy serving argmax: excluded ids masked inside
+ *                     the reduction, a status word per row
  *   vsel_topk         exact top-k (value, token id) per row, fused with the
  *                     row's argmax and log-sum-exp in one pass over the row
  *   vsel_sample       temperature sampling with top-k then top-p, one caller
@@ -100,6 +103,28 @@ size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int3
 vsel_status vsel_argmax(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                         uint32_t* out_idx, float* out_val, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Largest excluded-id set accepted by vsel_argmax_excluding. */
+#define VSEL_EXCLUDED_MAX 256
+
+/* Greedy serving argmax with an excluded-id set and a status word per row.
+ * The production greedy kernel of "Chapter 21", section 21.4: the request's
+ * end-of-generation ids are masked inside the reduction (taken as -inf; the
+ * logits are not modified) and the fail-closed latch is reported per row.
+ *   excluded   [n_excluded] uint32 device ids, any order; duplicates and ids
+ *              >= vocab are allowed and exclude nothing more.  One set for
+ *              every row of the call.  NULL when n_excluded == 0.
+ *   n_excluded 0 <= n_excluded <= VSEL_EXCLUDED_MAX
+ *   out_idx    [rows] uint32: the first maximum of the non-excluded elements,
+ *              VSEL_NONFINITE whenever out_status is not 0
+ *   out_status [rows] uint32: 0 ok; 1 the row holds a NaN or +inf, at an
+ *              excluded id or not; 2 no non-excluded element above -inf
+ *   workspace  as for VSEL_OP_ARGMAX with the same rows and vocab
+ */
+vsel_status vsel_argmax_excluding(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                                  const uint32_t* excluded, int32_t n_excluded, uint32_t* out_idx,
+                                  uint32_t* out_status, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Exact top-k of each row, fused with its argmax and log-sum-exp.
  * After decode, the k largest logits of each row are selected on the device

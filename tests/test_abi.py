@@ -23,9 +23,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(vsel_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_four_operations():
+def test_header_declares_the_operations():
     names = declared_functions()
-    for op in ("vsel_argmax", "vsel_topk", "vsel_sample", "vsel_spec_accept", "vsel_workspace_bytes"):
+    for op in ("vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_spec_accept",
+               "vsel_workspace_bytes"):
         assert op in names
 
 
@@ -68,6 +69,15 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
     assert L.vsel_argmax(C.c_void_p(4097), 1, 4, 100, 100, fake, None, ws, 1 << 20, None) == EINVAL
     assert L.vsel_argmax(fake, 0, 4, 100, 100, fake, None, ws, 16, None) == EWS                # too small
     assert L.vsel_argmax(fake, 0, 4, 100, 100, fake, None, C.c_void_p((1 << 20) + 8), 1 << 20, None) == EWS
+    def excl(n, ids=fake, status=fake, **kw):
+        return L.vsel_argmax_excluding(fake, 0, kw.get("rows", 4), 100, 100, ids, n, fake, status, ws,
+                                       kw.get("ws_bytes", 1 << 20), None)
+    assert excl(-1) == EINVAL
+    assert excl(257) == EINVAL                                  # above the set limit
+    assert excl(3, ids=None) == EINVAL                          # ids missing
+    assert excl(3, status=None) == EINVAL                       # status output missing
+    assert excl(0, rows=0) == EINVAL
+    assert excl(256, ws_bytes=16) == EWS
     assert L.vsel_topk(fake, 0, 4, 100, 100, 0, fake, fake, None, None, ws, 1 << 20, None) == EINVAL
     assert L.vsel_topk(fake, 0, 4, 100, 100, 101, fake, fake, None, None, ws, 1 << 20, None) == EINVAL
     assert L.vsel_topk(fake, 0, 4, 5000, 5000, 1025, fake, fake, None, None, ws, 1 << 20, None) == EINVAL

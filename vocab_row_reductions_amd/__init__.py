@@ -15,14 +15,15 @@ import os
 
 import torch  # loads the HIP runtime that libvsel.so then shares
 
-__all__ = ["vsel_argmax", "vsel_topk", "vsel_sample", "vsel_spec_accept", "workspace_bytes",
-           "VselError", "NONFINITE", "K_MAX", "library_path"]
+__all__ = ["vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_spec_accept", "workspace_bytes",
+           "VselError", "NONFINITE", "K_MAX", "EXCLUDED_MAX", "library_path"]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(HERE, "libvsel.so")
 
 NONFINITE = 0xFFFFFFFF
 K_MAX = 1024
+EXCLUDED_MAX = 256
 F32, BF16 = 0, 1
 OP_ARGMAX, OP_TOPK, OP_SAMPLE, OP_SPEC = 0, 1, 2, 3
 
@@ -42,11 +43,12 @@ def _load():
     L.vsel_workspace_bytes.restype = sz
     L.vsel_workspace_bytes.argtypes = [C.c_int, C.c_int, i64, i64, i32]
     L.vsel_argmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, sz, vp]
+    L.vsel_argmax_excluding.argtypes = [vp, C.c_int, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.vsel_topk.argtypes = [vp, C.c_int, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]
     L.vsel_sample.argtypes = [vp, C.c_int, i64, i64, i64, f32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.vsel_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp, sz, vp]
-    for f in (L.vsel_argmax, L.vsel_topk, L.vsel_sample, L.vsel_spec_accept):
+    for f in (L.vsel_argmax, L.vsel_argmax_excluding, L.vsel_topk, L.vsel_sample, L.vsel_spec_accept):
         f.restype = C.c_int
     return L
 
@@ -120,6 +122,31 @@ def vsel_argmax(logits: torch.Tensor, vocab=None, out_idx=None, out_val=None, wa
     _check(lib.vsel_argmax(_ptr(logits), dt, rows, V, ld, _ptr(out_idx), _ptr(out_val), _ptr(ws),
                            ws.numel(), _stream(dev)), "vsel_argmax")
     return out_idx, out_val
+
+
+def vsel_argmax_excluding(logits: torch.Tensor, excluded: torch.Tensor, vocab=None, out_idx=None,
+                          out_status=None):
+    """Greedy serving argmax with excluded ids -> (idx int32[rows], status int32[rows]).
+
+    `excluded` is a 1-D int32/uint32-bit device tensor of at most EXCLUDED_MAX ids
+    shared by every row; status 0 ok, 1 non-finite row, 2 no candidate."""
+    rows, V, ld = _rows(logits, vocab)
+    dt = _dtype(logits)
+    dev = logits.device
+    if excluded.dim() != 1 or excluded.dtype not in (torch.int32, torch.uint32) or not excluded.is_cuda:
+        raise ValueError("excluded must be a 1-D int32 device tensor")
+    if not excluded.is_contiguous():
+        raise ValueError("excluded must be contiguous")
+    n = excluded.numel()
+    if out_idx is None:
+        out_idx = torch.empty(rows, dtype=torch.int32, device=dev)
+    if out_status is None:
+        out_status = torch.empty(rows, dtype=torch.int32, device=dev)
+    ws = workspace(OP_ARGMAX, dt, rows, V, 0, dev)
+    _check(lib.vsel_argmax_excluding(_ptr(logits), dt, rows, V, ld, _ptr(excluded) if n else None, n,
+                                     _ptr(out_idx), _ptr(out_status), _ptr(ws), ws.numel(), _stream(dev)),
+           "vsel_argmax_excluding")
+    return out_idx, out_status
 
 
 def vsel_topk(logits: torch.Tensor, k: int, vocab=None, want_argmax=True, want_lse=True, out=None):

@@ -356,6 +356,29 @@ vsel_status vsel_argmax(const void* logits, int dtype, int64_t rows, int64_t voc
   return launched(launch_scan(dtype, false, a, (hipStream_t)stream));
 }
 
+vsel_status vsel_argmax_excluding(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                                  const uint32_t* excluded, int32_t n_excluded, uint32_t* out_idx,
+                                  uint32_t* out_status, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !out_idx || !out_status || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
+      !aligned_elem(logits, elem_size(dtype)) || n_excluded < 0 || n_excluded > kMaxExcluded ||
+      (n_excluded > 0 && !excluded))
+    return VSEL_EINVAL;
+  Layout L;
+  const ScanWs w = scan_layout(L, rows, plan_scan_bound(rows, vocab));
+  if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+  const Plan p = plan_scan(dtype, false, rows, vocab);
+  ScanArgs a = scan_args(logits, dtype, rows, vocab, ld, p, 1.0);
+  a.out_idx = out_idx;
+  a.out_status = out_status;
+  a.excl = excluded;
+  a.n_excl = n_excluded;
+  a.tickets = at<uint32_t>(ws, w.tickets);
+  a.p_key = at<uint64_t>(ws, w.p_key);
+  a.p_m = at<float>(ws, w.p_m);
+  a.p_s = at<double>(ws, w.p_s);
+  return launched(launch_scan(dtype, false, a, (hipStream_t)stream));
+}
+
 static vsel_status topk_common(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                                int32_t k, bool want_lse, TopkArgs& a, void* ws, size_t ws_bytes,
                                void* stream) {

@@ -46,7 +46,13 @@ struct ScanArgs {
   uint64_t* p_key;
   float* p_m;
   double* p_s;
+  // greedy serving variant: ids taken as -inf inside the reduction, and a
+  // per-row status (0 ok, 1 nonfinite, 2 no element above -inf)
+  const uint32_t* excl;
+  int32_t n_excl;      // 0 .. kMaxExcluded
+  uint32_t* out_status;
 };
+constexpr int kMaxExcluded = 256;
 
 // ---------------------------------------------------------------- top-k
 struct TopkArgs {

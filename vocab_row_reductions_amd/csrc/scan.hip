@@ -21,7 +21,7 @@ namespace vsel {
 constexpr int SG = 8;            // 16-byte groups per lane per tile
 constexpr float kLazyScan = 64.0f; // the exp2 offset moves when a maximum passes it by this
 
-template <typename DT, bool WANT_LSE, bool VEC>
+template <typename DT, bool WANT_LSE, bool VEC, bool EXCL = false>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
   constexpr int E = Elem<DT>::E;
   constexpr int64_t TILE = (int64_t)NT * SG * E;
@@ -66,6 +66,61 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
     trig = m + kLazyScan / c;
     corr = exp2_split((double)oc - (double)m * (double)c);
     huge = !(__builtin_fabsf(m) <= 0x1p25f);
+  };
+
+  // Greedy serving variant ("Chapter 21", section 21.4): the request's
+  // excluded ids are -inf inside the reduction only.  Each wave holds the
+  // (at most 256) ids in four registers per lane; a tile tests them with one
+  // range compare and a ballot each, and the lane holding an excluded
+  // element replaces it in its registers before anything reads it.  A NaN
+  // or +inf there keeps its value, so the row still fails closed.
+  const int n_excl = EXCL ? a.n_excl : 0;
+  uint32_t exid[kMaxExcluded / 64];
+#pragma unroll
+  for (int q = 0; q < kMaxExcluded / 64; ++q) {
+    const int i = q * 64 + lane;
+    exid[q] = (EXCL && i < n_excl) ? a.excl[i] : 0xFFFFFFFFu;
+  }
+  auto mask_bits = [&](uint32_t b) -> uint32_t {
+    // the element's bits as float32 (bfloat16 widened); keep NaN and +inf
+    const float x = __uint_as_float(E == 8 ? (b << 16) : b);
+    const bool keep = (x != x) || x == __builtin_inff();
+    return keep ? b : (E == 8 ? 0xFF80u : kNegInfBits);
+  };
+  auto exclude = [&](auto& g, uint32_t t0, uint32_t span) {
+    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+#pragma unroll
+    for (int q = 0; q < kMaxExcluded / 64; ++q) {
+      if (q * 64 >= n_excl) break;
+      const uint32_t rel = exid[q] - t0;  // ids below t0 wrap past span
+      uint64_t hits = __ballot(rel < span);
+      while (hits) {
+        const int bl = __builtin_ctzll(hits);
+        hits &= hits - 1;
+        const uint32_t er = (uint32_t)__builtin_amdgcn_readlane((int)rel, bl);
+        const uint32_t gi = er / (uint32_t)E, el = er % (uint32_t)E;
+        const uint32_t jj = gi / NT, owner = gi % NT;
+        if ((uint32_t)tid == owner) {
+#pragma unroll
+          for (int j = 0; j < NGP; ++j) {
+            if ((uint32_t)j != jj) continue;
+            if constexpr (E == 8) {
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                if ((uint32_t)w != (el >> 1)) continue;
+                const uint32_t word = g[j].w[w];
+                if (el & 1u) g[j].w[w] = (word & 0xFFFFu) | (mask_bits(word >> 16) << 16);
+                else g[j].w[w] = (word & 0xFFFF0000u) | mask_bits(word & 0xFFFFu);
+              }
+            } else {
+#pragma unroll
+              for (int w = 0; w < 4; ++w)
+                if ((uint32_t)w == el) g[j].w[w] = mask_bits(g[j].w[w]);
+            }
+          }
+        }
+      }
+    }
   };
 
   auto group = [&](const Group& g, uint32_t pos) {
@@ -157,6 +212,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
     Group g[SG];
     if constexpr (VEC) load_tile_buf<DT, SG>(g, xr + t0);
     else load_tile_full<DT, SG, false>(g, xr + t0);
+    if constexpr (EXCL) exclude(g, (uint32_t)t0, (uint32_t)TILE);
     if (first) {
       seed(g);
       first = false;
@@ -172,6 +228,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
   for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
     Group g1[1];
     load_tile<DT, 1, VEC>(g1, xr, t0, e_full);
+    if constexpr (EXCL) exclude(g1, (uint32_t)t0, (uint32_t)(NT * E));
     if (first) {
       seed(g1);
       first = false;
@@ -180,10 +237,28 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
     lse_check(g1, m1);
     fold();
   }
-  // the row's last few elements (fewer than one group): one lane
+  // the row's last few elements (fewer than one group): one lane, after
+  // wave 0 marks which of them are excluded
+  uint32_t tail_ex = 0;
+  if (EXCL && e_full < e_end && wave == 0 && n_excl > 0) {
+#pragma unroll
+    for (int q = 0; q < kMaxExcluded / 64; ++q) {
+      const uint32_t rel = exid[q] - (uint32_t)e_full;
+      const uint64_t hits = __ballot(rel < (uint32_t)(e_end - e_full));
+      uint64_t h = hits;
+      while (h) {
+        const int bl = __builtin_ctzll(h);
+        h &= h - 1;
+        tail_ex |= 1u << (uint32_t)__builtin_amdgcn_readlane((int)rel, bl);
+      }
+    }
+  }
   if (e_full < e_end && tid == 0) {
     for (int64_t i = e_full; i < e_end; ++i) {
-      const float x = __uint_as_float(gbits_at<DT>(xr, i));
+      const uint32_t braw = gbits_at<DT>(xr, i);
+      const bool ex = (tail_ex >> (uint32_t)(i - e_full)) & 1u;
+      const float xo = __uint_as_float(braw);
+      const float x = (ex && !(xo != xo || xo == __builtin_inff())) ? -__builtin_inff() : xo;
       if (x > best) {
         best = x;
         tail_idx = (uint32_t)i;
@@ -236,6 +311,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
   const bool none = bad || P == 0;
   const uint32_t idx = none ? kFail : ~(uint32_t)P;
   if (a.out_idx) a.out_idx[row] = idx;
+  if (a.out_status) a.out_status[row] = bad ? 1u : (P == 0 ? 2u : 0u);
   if (a.out_val)
     a.out_val[row] = bad ? __builtin_nanf("") : (P == 0 ? -__builtin_inff() : __uint_as_float(gbits_at<DT>(xr, idx)));
   if (a.out_logp0) a.out_logp0[row] = none ? __builtin_nanf("") : 0.0f;
@@ -250,7 +326,17 @@ template <typename DT, bool L>
 static hipError_t go(const ScanArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.rows1 + a.rows2) * a.S));
   // both row sets must take the vector path for the VEC kernel
-  if (a.vec1 && (a.rows2 == 0 || a.vec2))
+  const bool vec = a.vec1 && (a.rows2 == 0 || a.vec2);
+  if constexpr (!L) {
+    if (a.n_excl > 0) {
+      if (vec)
+        hipLaunchKernelGGL((scan_kernel<DT, false, true, true>), grid, dim3(NT), 0, s, a);
+      else
+        hipLaunchKernelGGL((scan_kernel<DT, false, false, true>), grid, dim3(NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (vec)
     hipLaunchKernelGGL((scan_kernel<DT, L, true>), grid, dim3(NT), 0, s, a);
   else
     hipLaunchKernelGGL((scan_kernel<DT, L, false>), grid, dim3(NT), 0, s, a);

@@ -173,3 +173,20 @@ def decode_batch_bf16(rows: int = 1024, vocab: int = V_DECODE, ld: int = LD_PADD
 def uniforms(n: int, seed: int) -> np.ndarray:
     """n float32 uniforms in [0, 1) from the uniform stream of `seed`."""
     return np.random.default_rng(seed + 1000).random(n, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- greedy serving
+def excluded_ids(vocab: int, n: int, seed: int, out_of_range: int = 0, duplicates: int = 0) -> np.ndarray:
+    """An end-of-generation id set as a serving request would hold it: n distinct
+    ids drawn uniformly from [0, vocab), then `out_of_range` ids at or past
+    vocab and `duplicates` repeats of ids already in the set, shuffled.
+    Returns uint32[n + out_of_range + duplicates]."""
+    rng = np.random.default_rng(seed)
+    n = min(n, vocab)
+    ids = rng.choice(vocab, size=n, replace=False).astype(np.uint32)
+    extra = [vocab + rng.integers(0, 1000, size=out_of_range)] if out_of_range else []
+    if duplicates and n:
+        extra.append(ids[rng.integers(0, n, size=duplicates)])
+    allids = np.concatenate([ids] + [np.asarray(e, dtype=np.uint32) for e in extra])
+    rng.shuffle(allids)
+    return allids.astype(np.uint32)
