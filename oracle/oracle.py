@@ -28,8 +28,9 @@ def load(path):
     L.oracle_sample.argtypes = [vp, C.c_int, i64, i64, i64, f32, i32, f32, vp, vp, vp, vp, C.c_int]
     L.oracle_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, vp, C.c_int]
+    L.oracle_spec_match.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, C.c_int]
     for f in (L.oracle_argmax, L.oracle_lse, L.oracle_topk, L.oracle_sample, L.oracle_spec_accept,
-              L.oracle_argmax_excluding):
+              L.oracle_argmax_excluding, L.oracle_spec_match):
         f.restype = C.c_int
     return L
 
@@ -147,4 +148,25 @@ def spec_accept(target, draft, tokens, u_acc, u_res, u_bon, batch, gamma, temper
         _p(tokens), _p(u_acc), _p(u_res), _p(u_bon), _p(out["len_mrs"]), _p(out["tok_mrs"]),
         _p(out["len_aa"]), _p(out["tok_aa"]), _p(out["summin"]), _p(out["acc_margin"]),
         _p(out["draw_margin"]), nthreads))
+    return out
+
+
+def spec_match(target, draft, tokens, u_match, batch, gamma, temperature, vocab=None, nthreads=0):
+    """Sampler-match acceptance (fresh draw from p at each position, accept on
+    equality, emit the draw) and the per-position sum_x p(x) q(x).
+    u_match: float32 [batch, gamma+1].  Returns len_sm, tok_sm, sumprod and
+    match_margin (the draw margin at each tested position, +inf elsewhere)."""
+    target = np.ascontiguousarray(target, dtype=np.float32)
+    draft = np.ascontiguousarray(draft, dtype=np.float32)
+    assert target.shape[0] == batch * (gamma + 1) and draft.shape[0] == batch * gamma
+    V = target.shape[1] if vocab is None else vocab
+    tokens = np.ascontiguousarray(tokens, dtype=np.uint32).reshape(batch * gamma)
+    u_match = np.ascontiguousarray(u_match, dtype=np.float32).reshape(batch * (gamma + 1))
+    out = dict(len_sm=np.empty(batch, np.int32), tok_sm=np.empty((batch, gamma + 1), np.uint32),
+               sumprod=np.empty((batch, gamma), np.float64),
+               match_margin=np.empty((batch, gamma + 1), np.float64))
+    _check(lib().oracle_spec_match(
+        _p(target), target.shape[1], _p(draft), draft.shape[1], batch, gamma, V, float(temperature),
+        _p(tokens), _p(u_match), _p(out["len_sm"]), _p(out["tok_sm"]), _p(out["sumprod"]),
+        _p(out["match_margin"]), nthreads))
     return out

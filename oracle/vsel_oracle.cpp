@@ -445,4 +445,89 @@ int oracle_spec_accept(const float* target, int64_t ld_t, const float* draft, in
   return 0;
 }
 
+// f1: sampler-match ("speculative-acceptance.md", "The rules": the default
+// rule at T > 0).  At each verify position i = 0, 1, ... a fresh draw x_i
+// from p_i (id order, as draw()) with u_match[b*(gamma+1) + i]; the drafted
+// t_i is accepted iff x_i == t_i, and the chain ends at the first mismatch L
+// (or at gamma, where x_gamma is drawn from the bonus row p_gamma), emitting
+// t_0 .. t_{L-1}, x_L: the draw is emitted on both branches, so every
+// emitted token is a draw from the target.
+//   sumprod[b*gamma+i] = sum_x p_i(x) q_i(x) for every position: the rule's
+//   acceptance probability for a proposal drawn from q ("The acceptance
+//   ceiling", the sampler-match row), the diagnostic beside sum min(p, q).
+//   T == 0 is greedy: the sampler is argmax, so the rule is
+//   argmax-against-argmax, and sumprod is 1 where the two argmaxes agree.
+// Outputs as oracle_spec_accept (len -1 and sentinel tokens for a
+// fail-closed sequence).  match_margin[b*(gamma+1)+i]: the draw margin at
+// every position the chain tested (+inf elsewhere).
+int oracle_spec_match(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
+                      int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
+                      const float* u_match, int32_t* len_sm, uint32_t* tok_sm, double* sumprod,
+                      double* match_margin, int nthreads) {
+  if (!target || !draft || !draft_tokens || !u_match || !len_sm || !tok_sm) return 1;
+  if (batch < 0 || gamma < 1 || vocab < 1 || ld_t < vocab || ld_d < vocab || !(temperature >= 0.0f)) return 1;
+  Rows Zr{target, 0, ld_t}, Dr{draft, 0, ld_d};
+  const int64_t G = gamma, V = vocab;
+  const double T = temperature;
+  for_rows(batch, nthreads, [&](int64_t b) {
+    const int64_t zrow0 = b * (G + 1), drow0 = b * G;
+    uint32_t* tk = tok_sm + b * (G + 1);
+    for (int64_t i = 0; i <= G; ++i) {
+      tk[i] = kFailClosed;
+      if (match_margin) match_margin[b * (G + 1) + i] = kInf;
+    }
+    for (int64_t i = 0; i < G; ++i)
+      if (sumprod) sumprod[b * G + i] = kNaN;
+    std::vector<uint32_t> amz(G + 1), amd(G);
+    for (int64_t i = 0; i <= G; ++i)
+      if ((amz[i] = argmax_row(Zr, zrow0 + i, V, nullptr)) == kFailClosed) {
+        len_sm[b] = -1;
+        return;
+      }
+    for (int64_t i = 0; i < G; ++i)
+      if ((amd[i] = argmax_row(Dr, drow0 + i, V, nullptr)) == kFailClosed || draft_tokens[b * G + i] >= V) {
+        len_sm[b] = -1;
+        return;
+      }
+    if (temperature == 0.0f) {  // the sampler is argmax
+      int64_t L = G;
+      for (int64_t i = 0; i < G; ++i)
+        if (draft_tokens[b * G + i] != amz[i]) {
+          L = i;
+          break;
+        }
+      len_sm[b] = static_cast<int32_t>(L);
+      for (int64_t i = 0; i < L; ++i) tk[i] = draft_tokens[b * G + i];
+      tk[L] = amz[L];
+      if (sumprod)
+        for (int64_t i = 0; i < G; ++i) sumprod[b * G + i] = (amz[i] == amd[i]) ? 1.0 : 0.0;
+      return;
+    }
+    std::vector<double> lp(G + 1), lq(G);
+    for (int64_t i = 0; i <= G; ++i) lp[i] = lse_row(Zr, zrow0 + i, V, T);
+    for (int64_t i = 0; i < G; ++i) lq[i] = lse_row(Dr, drow0 + i, V, T);
+    auto p_of = [&](int64_t i, int64_t x) { return std::exp(static_cast<double>(Zr.at(zrow0 + i, x)) / T - lp[i]); };
+    auto q_of = [&](int64_t i, int64_t x) { return std::exp(static_cast<double>(Dr.at(drow0 + i, x)) / T - lq[i]); };
+    if (sumprod)
+      for (int64_t i = 0; i < G; ++i) {
+        double s = 0.0;
+        for (int64_t x = 0; x < V; ++x) s += p_of(i, x) * q_of(i, x);
+        sumprod[b * G + i] = s;
+      }
+    std::vector<double> w(static_cast<size_t>(V));
+    for (int64_t i = 0; i <= G; ++i) {
+      for (int64_t x = 0; x < V; ++x) w[x] = p_of(i, x);
+      double m;
+      const uint32_t x = static_cast<uint32_t>(draw(w, u_match[b * (G + 1) + i], &m));
+      if (match_margin) match_margin[b * (G + 1) + i] = m;
+      tk[i] = x;
+      if (i == G || x != draft_tokens[b * G + i]) {
+        len_sm[b] = static_cast<int32_t>(i);
+        return;
+      }
+    }
+  });
+  return 0;
+}
+
 }  // extern "C"

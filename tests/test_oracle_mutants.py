@@ -6,6 +6,7 @@ import subprocess
 import pytest
 
 import tests.test_oracle_pins as P
+import tests.test_oracle_pins_match as M
 from oracle import build as B
 from oracle import oracle as O
 
@@ -39,6 +40,20 @@ MUTANTS = [
      [P.test_argmax_excluding_matches_numpy_on_masked_rows, P.test_argmax_excluding_brute_force_subsets]),
     ("draw from the last crossing instead of the first", "if (target < c) {", "if (target < c && j + 1 == w.size()) {",
      [P.test_sample_u_grid_frequencies_and_support]),
+    ("sampler-match accepts on a mismatch", "if (i == G || x != draft_tokens[b * G + i]) {",
+     "if (i == G || x == draft_tokens[b * G + i]) {",
+     [M.test_sampler_match_accepts_at_sum_pq_and_is_lossless, M.test_sampler_match_draws_follow_the_cumulative_sum]),
+    ("sampler-match draws from the draft distribution", "for (int64_t x = 0; x < V; ++x) w[x] = p_of(i, x);",
+     "for (int64_t x = 0; x < V; ++x) w[x] = i < G ? q_of(i, x) : p_of(i, x);",
+     [M.test_sampler_match_accepts_at_sum_pq_and_is_lossless]),
+    ("sampler-match emits the drafted token at the mismatch", "      tk[i] = x;\n",
+     "      tk[i] = i < G ? draft_tokens[b * G + i] : x;\n",
+     [M.test_sampler_match_chi_square_and_power, M.test_sampler_match_draws_follow_the_cumulative_sum]),
+    ("sampler-match bonus from the last verify row", "for (int64_t x = 0; x < V; ++x) w[x] = p_of(i, x);",
+     "for (int64_t x = 0; x < V; ++x) w[x] = p_of(std::min<int64_t>(i, G - 1), x);",
+     [M.test_sampler_match_bonus_comes_from_the_last_target_row]),
+    ("sum p q with min", "s += p_of(i, x) * q_of(i, x);", "s += std::min(p_of(i, x), q_of(i, x));",
+     [M.test_sumprod_closed_forms]),
 ]
 
 
