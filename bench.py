@@ -237,6 +237,15 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
     tested = int(np.minimum(L + 1, 8).sum())
     ex["spec_accept_32x8_per_position_acceptance"] = float(L.sum() / tested)
     ex["spec_accept_32x8_mean_summin"] = float(so["summin"].float().mean().item())
+    # the same batch under sampler-match (one uniform per position and the bonus)
+    um = g(W.uniforms(32 * 9, seed=2026))
+    margs = (args[0], um, 32, 8, 1.0)
+    mo = vsel.vsel_spec_match(tg, dr, *margs)
+    ex["spec_match_32x8_eager_us"] = time_calls(lambda i: vsel.vsel_spec_match(tg, dr, *margs, out=mo), 50, 5, stream)
+    ex["spec_match_32x8_device_us"] = time_graph(lambda i: vsel.vsel_spec_match(tg, dr, *margs, out=mo), 10, stream)
+    Lm = mo["len_sm"].cpu().numpy()
+    ex["spec_match_32x8_per_position_acceptance"] = float(Lm.sum() / int(np.minimum(Lm + 1, 8).sum()))
+    ex["spec_match_32x8_mean_sumprod"] = float(mo["sumprod"].float().mean().item())
     del tg, dr
     # fp32 variant of the headline batch (one buffer pair, 827 MB each)
     x32 = bufs[0][:, :V].float().contiguous()
@@ -255,7 +264,9 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
     cu = time_calls(lambda i: dst.copy_(bufs[i % 3]), 30, 3, stream)
     ex["torch_copy_bf16_batch_us"] = cu
     ex["torch_copy_bf16_batch_gbs"] = 2 * src.numel() * 2 / (cu * 1e-6) / 1e9
-    return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in ex.items()}
+    # three decimals for times and rates; four significant digits for probabilities below 0.01
+    return {k: (float(f"{v:.4g}") if isinstance(v, float) and abs(v) < 0.01 else round(v, 3) if isinstance(v, float) else v)
+            for k, v in ex.items()}
 
 
 if __name__ == "__main__":

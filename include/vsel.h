@@ -12,6 +12,8 @@
  *                     row's argmax and log-sum-exp in one pass over the row
  *   vsel_sample       temperature sampling with top-k then top-p, one caller
  *                     uniform per row
+ *   vsel_spec_match   speculative-decoding acceptance by sampler-match and
+ *                     the per-position sum p*q
  *   vsel_spec_accept  speculative-decoding acceptance: modified rejection
  *                     sampling and argmax-against-argmax, with the per-position
  *                     coupling sum of min(p, q)
@@ -211,6 +213,33 @@ vsel_status vsel_spec_accept(const float* target_logits, int64_t ld_t, const flo
                              uint32_t* out_tok_mrs, int32_t* out_len_aa, uint32_t* out_tok_aa,
                              float* out_summin, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* Speculative-decoding acceptance by sampler-match ("speculative-acceptance.md",
+ * "The rules": sampler-match, the default rule at temperature > 0): at verify
+ * position i a fresh token x_i is drawn from p_i with u_match[i] (id order,
+ * the first x with u*W < w_0 + ... + w_x over W = sum of p_i), and draft t_i
+ * is accepted iff x_i == t_i.  The chain stops at the first mismatch L (or at
+ * gamma, where x_gamma is drawn from the bonus row) and emits t_0 .. t_{L-1},
+ * x_L: the draw is emitted on both branches, so the stream is a target-only
+ * sample.  sumprod_i = sum_x p_i(x) q_i(x), the rule's acceptance probability
+ * for a proposal drawn from q ("The acceptance ceiling"; the diagnostic of
+ * "Verifying the gain before trusting a throughput number"), for every
+ * position.  temperature == 0 is greedy: the sampler is argmax, so the rule is
+ * argmax-against-argmax and sumprod_i is 1 where the two argmaxes agree.
+ *   Shapes, limits and fail-closed sequences as vsel_spec_accept; workspace as
+ *   VSEL_OP_SPEC_ACCEPT with the same batch, vocab and gamma.
+ *   u_match     [batch*(gamma+1)] float32 in [0, 1): position i of sequence b
+ *               at b*(gamma+1) + i, the bonus draw at b*(gamma+1) + gamma
+ *   out_len     [batch] int32: accepted drafts L in [0, gamma], or -1
+ *   out_tok     [batch*(gamma+1)] uint32: t_0..t_{L-1} then x_L; the rest
+ *               VSEL_NONFINITE
+ *   out_sumprod [batch*gamma] float32 or NULL
+ */
+vsel_status vsel_spec_match(const float* target_logits, int64_t ld_t, const float* draft_logits,
+                            int64_t ld_d, int64_t batch, int32_t gamma, int64_t vocab,
+                            float temperature, const uint32_t* draft_tokens, const float* u_match,
+                            int32_t* out_len, uint32_t* out_tok, float* out_sumprod,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

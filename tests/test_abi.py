@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_operations():
     names = declared_functions()
     for op in ("vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_spec_accept",
-               "vsel_workspace_bytes"):
+               "vsel_spec_match", "vsel_workspace_bytes"):
         assert op in names
 
 
@@ -98,3 +98,13 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
     assert spec(T=-1.0) == EINVAL
     assert spec(ld_t=99) == EINVAL
     assert spec(ld_d=50) == EINVAL
+    def match(u=fake, ln=fake, tk=fake, **kw):
+        a = {**args, **kw}
+        return L.vsel_spec_match(fake, a.get("ld_t", 100), fake, a.get("ld_d", 100), a["batch"], a["gamma"],
+                                 a["vocab"], a["T"], fake, u, ln, tk, None, ws, 1 << 20, None)
+    assert match(u=None) == EINVAL                 # uniforms missing
+    assert match(ln=None) == EINVAL                # length output missing
+    assert match(tk=None) == EINVAL                # token output missing
+    assert match(gamma=0) == EINVAL
+    assert match(T=float("nan")) == EINVAL
+    assert match(ld_t=99) == EINVAL

@@ -67,3 +67,15 @@ def test_spec_accept_graph(g):
     keys = list(ref)
     replay_check(lambda: g.vsel.vsel_spec_accept(*args, 4, 3, 1.0, out=out), lambda: [out[k] for k in keys],
                  [ref[k] for k in keys], lambda: g.vsel.vsel_argmax(args[0]))
+
+
+def test_spec_match_graph(g):
+    d = W.speculative_batch(batch=4, gamma=3, vocab=30000, seed=75)
+    um = g.dev(W.uniforms(4 * 4, seed=75))
+    args = [g.dev(d[k]) for k in ("target", "draft", "tokens")]
+    ref = g.vsel.vsel_spec_match(*args, um, 4, 3, 1.0)
+    ref = {k: v.clone() for k, v in ref.items()}
+    out = {k: torch.empty_like(v) for k, v in ref.items()}
+    keys = list(ref)
+    replay_check(lambda: g.vsel.vsel_spec_match(*args, um, 4, 3, 1.0, out=out), lambda: [out[k] for k in keys],
+                 [ref[k] for k in keys], lambda: g.vsel.vsel_argmax(args[0]))

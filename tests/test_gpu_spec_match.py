@@ -1,0 +1,156 @@
+"""GPU parity of vsel_spec_match (sampler-match acceptance and sum p*q) with
+the oracle.
+
+Bit-exact accepted lengths and emitted tokens, except at a draw whose oracle
+float64 margin to a CDF boundary is below 1e-9 of the total mass: the
+sequence's later outputs are then not compared.  sum p*q within 1e-6 absolute
+plus 1e-5 relative.  Uniforms placed a few millionths from a boundary (inside
+the band that float32 terms cannot decide, outside the exempt band) drive the
+kernel's float64 re-decision.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DRAW_MARGIN = 1e-9
+
+
+@pytest.fixture(scope="module")
+def g():
+    import tests.gpu_helpers as G
+    import vocab_row_reductions_amd as vsel
+    G.vsel = vsel
+    return G
+
+
+def match_uniforms(B, G, seed):
+    return W.uniforms(B * (G + 1), seed=seed + 500).reshape(B, G + 1)
+
+
+def run(g, target, draft, tokens, um, B, G, T):
+    out = g.vsel.vsel_spec_match(g.dev(target), g.dev(draft), g.dev(tokens), g.dev(um.reshape(-1)), B, G, T)
+    return {k: (g.u32(v) if k.startswith("tok") else v.cpu().numpy()) for k, v in out.items()}
+
+
+def compare(g, oracle, target, draft, tokens, um, B, G, T):
+    got = run(g, target, draft, tokens, um, B, G, T)
+    ref = oracle.spec_match(target, draft, tokens, um, B, G, T)
+    ok = np.isfinite(ref["sumprod"])
+    assert np.all(np.abs(got["sumprod"][ok] - ref["sumprod"][ok]) <= 1e-6 + 1e-5 * np.abs(ref["sumprod"][ok]))
+    assert np.array_equal(np.isnan(got["sumprod"]), ~ok)
+    exempt = 0
+    for b in range(B):
+        close = np.nonzero(ref["match_margin"][b] < DRAW_MARGIN)[0]
+        if len(close):                      # compare only what precedes the first near-tie
+            i = close[0]
+            exempt += 1
+            assert np.array_equal(got["tok_sm"][b, :i], ref["tok_sm"][b, :i])
+            continue
+        assert got["len_sm"][b] == ref["len_sm"][b], f"sequence {b}: accepted length"
+        assert np.array_equal(got["tok_sm"][b], ref["tok_sm"][b]), f"sequence {b}: tokens"
+    return got, ref, exempt
+
+
+def test_config4_speculative_batch(g, oracle):
+    d = W.speculative_batch()
+    B, G = d["batch"], d["gamma"]
+    um = match_uniforms(B, G, 4)
+    got, ref, exempt = compare(g, oracle, d["target"], d["draft"], d["tokens"], um, B, G, d["temperature"])
+    assert exempt <= 1
+    # sum p q sits below sum min(p, q) at every position
+    mrs = oracle.spec_accept(d["target"], d["draft"], d["tokens"], d["u_acc"], d["u_res"], d["u_bon"], B, G,
+                             d["temperature"])
+    assert np.all(got["sumprod"] <= mrs["summin"] + 1e-6)
+
+
+@pytest.mark.parametrize("V", [2, 7, 1000, 70001])
+@pytest.mark.parametrize("T", [1.0, 0.6])
+def test_shapes(g, oracle, V, T):
+    d = W.speculative_batch(batch=5, gamma=3, vocab=V, seed=V)
+    um = match_uniforms(5, 3, V)
+    compare(g, oracle, d["target"], d["draft"], d["tokens"], um, 5, 3, T)
+
+
+def test_long_chains(g, oracle):
+    """Drafts set to the target's own draws (from the oracle, one position at
+    a time), so every chain runs to the bonus row."""
+    B, G, V = 6, 5, 40000
+    d = W.speculative_batch(batch=B, gamma=G, vocab=V, seed=41)
+    um = match_uniforms(B, G, 41)
+    tok = np.zeros((B, G), np.uint32)
+    for b in range(B):
+        for i in range(G):
+            r0 = b * (G + 1) + i
+            r = oracle.spec_match(d["target"][r0:r0 + 2], d["draft"][b * G + i:b * G + i + 1], np.zeros(1, np.uint32),
+                                  um[b, i:i + 2].copy(), 1, 1, 1.0)
+            tok[b, i] = r["tok_sm"][0, 0]   # the draw at this position (accepted or not)
+    got, ref, _ = compare(g, oracle, d["target"], d["draft"], tok.reshape(-1), um, B, G, 1.0)
+    assert np.all(ref["len_sm"] == G)
+
+
+def test_boundary_uniforms_take_the_exact_path(g, oracle):
+    """u placed 3e-6 above and below the lower edge of the drafted token's
+    interval: the float32 masses cannot decide, the float64 re-decision must."""
+    B, G, V = 8, 1, 50000
+    d = W.speculative_batch(batch=B, gamma=G, vocab=V, seed=42)
+    tg = d["target"].astype(np.float64)
+    tok = np.zeros(B, np.uint32)
+    um = np.zeros((B, G + 1), np.float32)
+    um[:, 1] = 0.5
+    for b in range(B):
+        z = tg[b * 2]
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        c = np.cumsum(p)
+        # one of the row's most likely tokens, with some mass below it
+        top = [int(x) for x in np.argsort(-p)[:32] if x > 0 and c[x - 1] > 1e-3]
+        t = top[b % len(top)]
+        assert p[t] > 1e-4
+        tok[b] = t
+        um[b, 0] = np.float32(c[t - 1] + (3e-6 if b % 2 == 0 else -3e-6))
+    got, ref, exempt = compare(g, oracle, d["target"], d["draft"], tok, um, B, G, 1.0)
+    assert exempt == 0
+    assert list(ref["len_sm"]) == [1 if b % 2 == 0 else 0 for b in range(B)]
+
+
+def test_temperature_zero_is_argmax_rule(g, oracle):
+    d = W.speculative_batch(batch=6, gamma=4, vocab=3000, seed=43)
+    um = match_uniforms(6, 4, 43)
+    got = run(g, d["target"], d["draft"], d["tokens"], um, 6, 4, 0.0)
+    aa = oracle.spec_accept(d["target"], d["draft"], d["tokens"], d["u_acc"], d["u_res"], d["u_bon"], 6, 4, 0.0)
+    assert np.array_equal(got["len_sm"], aa["len_aa"])
+    assert np.array_equal(got["tok_sm"], aa["tok_aa"])
+    assert np.array_equal(got["sumprod"], aa["summin"].astype(np.float32))
+
+
+def test_fail_closed(g, oracle):
+    d = W.speculative_batch(batch=3, gamma=2, vocab=900, seed=44)
+    tgt = d["target"].copy()
+    tgt[1 * 3 + 2, 5] = np.nan               # bonus row of sequence 1
+    tok = d["tokens"].copy()
+    tok[2 * 2] = 900                         # out-of-range draft in sequence 2
+    um = match_uniforms(3, 2, 44)
+    got, ref, _ = compare(g, oracle, tgt, d["draft"], tok, um, 3, 2, 1.0)
+    assert list(got["len_sm"][1:]) == [-1, -1] and np.all(got["tok_sm"][1:] == g.SENT)
+
+
+def test_chi_square_of_the_gpu_stream(g):
+    """The first emitted token of 12,000 one-position rounds is a draw from p."""
+    p = np.array([0.4, 0.3, 0.1, 0.1, 0.05, 0.05])
+    q = p[::-1].copy()
+    n = 12000
+    rng = np.random.default_rng(W.BASE_SEED + 79)
+    zt, zd = np.log(p).astype(np.float32), np.log(q).astype(np.float32)
+    t = rng.choice(6, size=n, p=q / q.sum()).astype(np.uint32)
+    um = rng.random((n, 2), dtype=np.float32)
+    got = run(g, np.repeat(zt[None], 2 * n, 0), np.repeat(zd[None], n, 0), t, um, n, 1, 1.0)
+    pf = np.exp(zt.astype(np.float64))
+    pf /= pf.sum()
+    counts = np.bincount(got["tok_sm"][:, 0], minlength=6)
+    stat = float(((counts - pf * n) ** 2 / (pf * n)).sum())
+    assert stat < 25.7448
+    acc = (got["len_sm"] == 1).mean()
+    assert abs(acc - float((pf * (q / q.sum())).sum())) < 4 * np.sqrt(acc * (1 - acc) / n)

@@ -229,6 +229,7 @@ struct SpecWs {
   StatsWs st;
   size_t tk_pos, tk_seq, tk_row, tk_draw;
   size_t p_summin, acc, draw_L, p_lse, lse64, p_w, p_c;
+  size_t p_low, p_wt;  // sampler-match
 };
 SpecWs spec_layout(Layout& L, int64_t B, int64_t G, int64_t V, const Plan& ps, const Plan& pp) {
   SpecWs w{};
@@ -250,6 +251,8 @@ SpecWs spec_layout(Layout& L, int64_t B, int64_t G, int64_t V, const Plan& ps, c
   w.lse64 = L.take((size_t)(2 * B) * 8);
   w.p_w = L.take((size_t)(B * kMaxSegments) * 8);
   w.p_c = L.take((size_t)(B * cdiv(V, kChunk)) * 8);
+  w.p_low = L.take((size_t)(B * G * pp.S) * 8);
+  w.p_wt = L.take((size_t)(B * G * pp.S) * 8);
   return w;
 }
 
@@ -499,13 +502,12 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
   return topk_common(logits, dtype, rows, vocab, ld, k, false, a, ws, ws_bytes, stream);
 }
 
-vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
-                             int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
-                             const float* u_accept, const float* u_resid, const float* u_bonus,
-                             int32_t* out_len_mrs, uint32_t* out_tok_mrs, int32_t* out_len_aa,
-                             uint32_t* out_tok_aa, float* out_summin, void* ws, size_t ws_bytes, void* stream) {
-  if (!target || !draft || !draft_tokens || !u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs)
-    return VSEL_EINVAL;
+// Argument checks, pass 1 (row statistics of every target and draft row)
+// and the common kernel arguments of both speculative entry points.
+static vsel_status spec_prepare(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
+                                int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
+                                void* ws, size_t ws_bytes, hipStream_t s, SpecArgs& p) {
+  if (!target || !draft || !draft_tokens) return VSEL_EINVAL;
   if (batch < 1 || gamma < 1 || gamma > kMaxSegments || vocab < 1 || vocab >= (int64_t(1) << 31) || ld_t < vocab ||
       ld_d < vocab)
     return VSEL_EINVAL;
@@ -518,7 +520,6 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
   const Plan ps = plan_scan(VSEL_F32, temperature > 0.0f, B * (2 * G + 1), vocab);
   const Plan pp = plan_scan(VSEL_F32, true, B * G, vocab);
-  hipStream_t s = (hipStream_t)stream;
 
   ScanArgs a = scan_args(target, VSEL_F32, B * (G + 1), vocab, ld_t, ps, temperature);
   a.x2 = draft;
@@ -533,10 +534,9 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   a.st_max = at<float>(ws, w.st.mx);
   a.st_lse = at<double>(ws, w.st.lse);
   a.st_bad = at<uint32_t>(ws, w.st.bad);
-  hipError_t e = launch_scan(VSEL_F32, temperature > 0.0f, a, s);
-  if (e != hipSuccess) return VSEL_EDEVICE;
+  if (launch_scan(VSEL_F32, temperature > 0.0f, a, s) != hipSuccess) return VSEL_EDEVICE;
 
-  SpecArgs p{};
+  p = SpecArgs{};
   p.tgt = target;
   p.dft = draft;
   p.ld_t = ld_t;
@@ -548,14 +548,6 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   p.inv_T = temperature > 0 ? 1.0f / temperature : 0.0f;
   p.lse_c = a.lse_c;
   p.tokens = draft_tokens;
-  p.u_acc = u_accept;
-  p.u_res = u_resid;
-  p.u_bon = u_bonus;
-  p.len_mrs = out_len_mrs;
-  p.tok_mrs = out_tok_mrs;
-  p.len_aa = out_len_aa;
-  p.tok_aa = out_tok_aa;
-  p.summin = out_summin;
   p.seg_len = pp.seg_len;
   p.S = pp.S;
   p.vec_t = a.vec1;
@@ -579,7 +571,49 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   p.nchunk = cdiv(vocab, kChunk);
   p.p_w = at<double>(ws, w.p_w);
   p.p_c = at<double>(ws, w.p_c);
+  p.p_low = at<double>(ws, w.p_low);
+  p.p_wt = at<double>(ws, w.p_wt);
+  return VSEL_OK;
+}
+
+vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
+                             int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
+                             const float* u_accept, const float* u_resid, const float* u_bonus,
+                             int32_t* out_len_mrs, uint32_t* out_tok_mrs, int32_t* out_len_aa,
+                             uint32_t* out_tok_aa, float* out_summin, void* ws, size_t ws_bytes, void* stream) {
+  if (!u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs) return VSEL_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  SpecArgs p;
+  const vsel_status st =
+      spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws, ws_bytes, s, p);
+  if (st != VSEL_OK) return st;
+  p.u_acc = u_accept;
+  p.u_res = u_resid;
+  p.u_bon = u_bonus;
+  p.len_mrs = out_len_mrs;
+  p.tok_mrs = out_tok_mrs;
+  p.len_aa = out_len_aa;
+  p.tok_aa = out_tok_aa;
+  p.summin = out_summin;
   return launched(launch_spec(p, s));
+}
+
+vsel_status vsel_spec_match(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
+                            int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
+                            const float* u_match, int32_t* out_len, uint32_t* out_tok, float* out_sumprod,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!u_match || !out_len || !out_tok) return VSEL_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  SpecArgs p;
+  const vsel_status st =
+      spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws, ws_bytes, s, p);
+  if (st != VSEL_OK) return st;
+  p.match = 1;
+  p.u_match = u_match;
+  p.len_sm = out_len;
+  p.tok_sm = out_tok;
+  p.sumprod = out_sumprod;
+  return launched(launch_spec_match(p, s));
 }
 
 }  // extern "C"

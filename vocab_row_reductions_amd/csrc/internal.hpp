@@ -128,6 +128,14 @@ struct SpecArgs {
   int64_t nchunk;       // chunks per row, ceil(V / kChunk)
   double* p_w;          // [B*dS] segment masses
   double* p_c;          // [B*nchunk] chunk masses
+  // sampler-match (vsel_spec_match): a fresh draw from p at each position
+  int32_t match;
+  const float* u_match;  // [B*(gamma+1)]
+  int32_t* len_sm;
+  uint32_t* tok_sm;
+  float* sumprod;        // [B*gamma] or null
+  double* p_low;         // [B*gamma*S] mass of p below the drafted token, per segment
+  double* p_wt;          // [B*gamma*S] mass of p, per segment
 };
 
 // Plain full-row draw for vsel_sample with top_k == 0.
@@ -162,6 +170,7 @@ int topk_wave_blocks_per_cu(int dtype, bool want_lse);
 int scan_blocks_per_cu(int dtype, bool want_lse);
 int topk_blocks_per_cu(int dtype, bool want_lse, int cap);
 hipError_t launch_spec(const SpecArgs& a, hipStream_t s);
+hipError_t launch_spec_match(const SpecArgs& a, hipStream_t s);
 hipError_t launch_draw_rows(int dtype, const DrawArgs& a, hipStream_t s);
 
 }  // namespace vsel

@@ -21,6 +21,16 @@
 //      max(p - q, 0), or p for the bonus token), then the last workgroup
 //      picks the segment whose prefix crosses u * W and rescans it in id
 //      order.
+//
+// Sampler-match ("speculative-acceptance.md", "The rules", the default rule
+// at T > 0) replaces passes 2-4 by:
+//   2. match pass, one workgroup per (position, segment): the masses of p
+//      below the drafted token t and in all, and sum p*q (the rule's
+//      acceptance probability, "Verifying the gain").  The fresh draw from p
+//      lands on t iff mass(< t) <= u*W < mass(< t) + p(t); the masses come from
+//      float32 terms, so a decision closer to a boundary than they resolve is
+//      taken again with float64 terms over the row;
+//   4. the draw at the first mismatch (or the bonus row), as above from p.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -181,6 +191,162 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     }
   a.len_mrs[b] = (int32_t)L;
   for (int64_t q = 0; q < L; ++q) tm[q] = a.tokens[b * G + q];
+  a.draw_L[b] = (int32_t)L;
+}
+
+// ---------------------------------------------------------------- sampler-match pass
+// Float32 terms are within about 1e-6 of the total mass of their float64
+// values on any row, so a decision farther than this from both boundaries of
+// the drafted token's interval stands; a nearer one is taken again exactly.
+constexpr double kMatchTol = 1e-5;
+
+template <bool VEC>
+__global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
+  constexpr int E = 4, TILE = NT * PG * E;
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t pos = it.row;
+  const int seg = (int)it.seg;
+  const int64_t G = a.gamma;
+  if (pos >= a.B * G) return;
+  const int64_t b = pos / G, i = pos % G;
+  const int64_t trow = b * (G + 1) + i, drow = b * G + i;
+  const int64_t nT = a.B * (G + 1);
+  const float* __restrict__ zr = a.tgt + trow * a.ld_t;
+  const float* __restrict__ dr = a.dft + drow * a.ld_d;
+  const uint32_t t = a.tokens[pos];
+  const bool bad = a.st_bad[trow] || a.st_bad[nT + drow] || t >= (uint64_t)a.V;
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+
+  double sp = 0.0, lo = 0.0, ws = 0.0;  // sum p q, mass of p below t, mass of p
+  if (a.T > 0.0f && !bad) {
+    const float c = a.lse_c;
+    const double Lp = a.st_lse[trow] * (double)kLog2e, Lq = a.st_lse[nT + drow] * (double)kLog2e;
+    const float Lp_hi = (float)Lp, Lq_hi = (float)Lq;
+    const float fp = (float)exp2(-(Lp - (double)Lp_hi)), fq = (float)exp2(-(Lq - (double)Lq_hi));
+    // group j of this lane starts at element t0 + (j*NT + tid)*E
+    auto pair = [&](const auto& gz, const auto& gd, int64_t t0) {
+      constexpr int NGP = (int)(sizeof(gz) / sizeof(Group));
+      float a_sp = 0.0f, a_lo = 0.0f, a_ws = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NGP; ++j)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t x = (uint32_t)t0 + (uint32_t)((j * NT + tid) * E + e);
+          const float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
+          const float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          a_sp = fmaf(p, q, a_sp);
+          a_ws += p;
+          a_lo += x < t ? p : 0.0f;
+        }
+      sp += (double)a_sp;
+      lo += (double)a_lo;
+      ws += (double)a_ws;
+    };
+    const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
+    const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
+    for (int64_t t0 = e_begin; t0 < e_tiles; t0 += TILE) {
+      Group gz[PG], gd[PG];
+      load_tile_full<float, PG, VEC>(gz, zr + t0);
+      load_tile_full<float, PG, VEC>(gd, dr + t0);
+      pair(gz, gd, t0);
+    }
+    for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
+      Group gz[1], gd[1];
+      load_tile<float, 1, VEC>(gz, zr, t0, e_full);  // past e_full: -inf, so p = q = 0
+      load_tile<float, 1, VEC>(gd, dr, t0, e_full);
+      pair(gz, gd, t0);
+    }
+    if (tid == 0)
+      for (int64_t x = e_full; x < e_end; ++x) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
+        const float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        sp += (double)(p * q);
+        ws += (double)p;
+        if ((uint64_t)x < t) lo += (double)p;
+      }
+  }
+  sp = block_sum_f64(sh, sp);
+  lo = block_sum_f64(sh, lo);
+  ws = block_sum_f64(sh, ws);
+  if (a.S > 1) {
+    if (tid == 0) {
+      st_dev(&a.p_summin[pos * a.S + seg], sp);
+      st_dev(&a.p_low[pos * a.S + seg], lo);
+      st_dev(&a.p_wt[pos * a.S + seg], ws);
+    }
+    if (!last_done(sh, a.tk_pos + pos, (uint32_t)a.S)) return;
+    sp = merge_sum(sh, a.p_summin + pos * a.S, a.S);
+    lo = merge_sum(sh, a.p_low + pos * a.S, a.S);
+    ws = merge_sum(sh, a.p_wt + pos * a.S, a.S);
+  }
+  // Position decision (every thread holds the same sums, so the branches
+  // below are uniform): 1 the fresh draw is t, 0 it is not, 2 fail closed.
+  uint32_t flag;
+  if (bad) {
+    flag = 2u;
+  } else if (a.T == 0.0f) {
+    flag = (t == a.st_amax[trow]) ? 1u : 0u;
+    sp = (a.st_amax[trow] == a.st_amax[nT + drow]) ? 1.0 : 0.0;
+  } else {
+    const double Td = a.T, lse = a.st_lse[trow];
+    const double pt = exp((double)zr[t] / Td - lse);
+    const double u = (double)a.u_match[b * (G + 1) + i];
+    const double target = u * ws, tol = kMatchTol * ws;
+    if (target >= lo + tol && target < lo + pt - tol) {
+      flag = 1u;
+    } else if (target < lo - tol || target >= lo + pt + tol) {
+      flag = 0u;
+    } else {
+      // too close to call: the masses again, from float64 terms
+      double l2 = 0.0, w2 = 0.0;
+      for (int64_t x = tid; x < a.V; x += NT) {
+        const double px = exp((double)zr[x] / Td - lse);
+        w2 += px;
+        if ((uint64_t)x < t) l2 += px;
+      }
+      l2 = block_sum_f64(sh, l2);
+      w2 = block_sum_f64(sh, w2);
+      const double tg = u * w2;
+      flag = (l2 <= tg && tg < l2 + pt) ? 1u : 0u;
+    }
+  }
+  if (tid == 0) {
+    st_dev(&a.acc[pos], flag);
+    if (a.sumprod) st_dev(&a.sumprod[pos], bad ? __builtin_nanf("") : (float)sp);
+  }
+  if (!last_done(sh, a.tk_seq + b, (uint32_t)G)) return;
+  if (tid < G) sh.hist[tid] = ld_dev(&a.acc[b * G + tid]);
+  __syncthreads();
+  if (tid != 0) return;
+
+  // Sequence decision: the chain runs to the first position whose draw is
+  // not the drafted token (gamma: the bonus row); the draw there is emitted.
+  uint32_t* tk = a.tok_sm + b * (G + 1);
+  bool fail = a.st_bad[b * (G + 1) + G] != 0;
+  for (int64_t q = 0; q < G; ++q) fail |= sh.hist[q] == 2u;
+  for (int64_t q = 0; q <= G; ++q) tk[q] = kFail;
+  if (fail) {
+    a.len_sm[b] = -1;
+    if (a.sumprod)
+      for (int64_t q = 0; q < G; ++q) st_dev(&a.sumprod[b * G + q], __builtin_nanf(""));
+    a.draw_L[b] = -1;
+    return;
+  }
+  int64_t L = G;
+  for (int64_t q = 0; q < G; ++q)
+    if (sh.hist[q] == 0u) {
+      L = q;
+      break;
+    }
+  a.len_sm[b] = (int32_t)L;
+  for (int64_t q = 0; q < L; ++q) tk[q] = a.tokens[b * G + q];
+  if (a.T == 0.0f) {  // the sampler is argmax: its draw is the argmax
+    tk[L] = a.st_amax[b * (G + 1) + L];
+    a.draw_L[b] = -1;
+    return;
+  }
   a.draw_L[b] = (int32_t)L;
 }
 
@@ -400,7 +566,13 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   r.T = a.T;
   r.V = a.V;
   double u;
-  if (L < G) {
+  if (a.match) {  // sampler-match: a fresh draw from p at row L
+    r.z = a.tgt + (b * (G + 1) + L) * a.ld_t;
+    r.d = nullptr;
+    r.lp = r.lq = 0.0;
+    r.m = a.st_max[b * (G + 1) + L];
+    u = a.u_match[b * (G + 1) + L];
+  } else if (L < G) {
     r.z = a.tgt + (b * (G + 1) + L) * a.ld_t;
     r.d = a.dft + (b * G + L) * a.ld_d;
     r.lp = a.lse64[b * 2];
@@ -442,7 +614,7 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   }
   double W;
   const uint32_t tok = draw_pick(sh, r, pw, pc, a.dS, a.dseg, u, &W);
-  if (tid == 0) a.tok_mrs[b * (G + 1) + L] = tok;
+  if (tid == 0) (a.match ? a.tok_sm : a.tok_mrs)[b * (G + 1) + L] = tok;
 }
 
 template <typename DT>
@@ -498,6 +670,18 @@ hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
   else
     hipLaunchKernelGGL(draw_lse_kernel<false>, dim3((unsigned)(a.B * 2 * a.S)), dim3(NT), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_spec_match(const SpecArgs& a, hipStream_t s) {
+  const unsigned npos = (unsigned)(a.B * a.gamma * a.S);
+  if (a.vec_t && a.vec_d)
+    hipLaunchKernelGGL(match_kernel<true>, dim3(npos), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(match_kernel<false>, dim3(npos), dim3(NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.T == 0.0f) return e;
   hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
