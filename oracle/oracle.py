@@ -28,9 +28,11 @@ def load(path):
     L.oracle_sample.argtypes = [vp, C.c_int, i64, i64, i64, f32, i32, f32, vp, vp, vp, vp, C.c_int]
     L.oracle_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp, vp, C.c_int]
+    L.oracle_sample_chain.argtypes = [vp, C.c_int, i64, i64, i64, f32, f32, i32, f32, f32, f32, vp, vp, vp, vp,
+                                      C.c_int]
     L.oracle_spec_match.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, C.c_int]
     for f in (L.oracle_argmax, L.oracle_lse, L.oracle_topk, L.oracle_sample, L.oracle_spec_accept,
-              L.oracle_argmax_excluding, L.oracle_spec_match):
+              L.oracle_argmax_excluding, L.oracle_spec_match, L.oracle_sample_chain):
         f.restype = C.c_int
     return L
 
@@ -125,6 +127,24 @@ def sample(x, temperature, top_k, top_p, u, vocab=None, nthreads=0):
     margins = np.empty((R, 2), np.float64)
     _check(lib().oracle_sample(_p(x), dt, R, V, ld, float(temperature), int(top_k), float(top_p),
                                _p(u), _p(tok), _p(logp), _p(margins), nthreads))
+    return tok, logp, margins
+
+
+def sample_chain(x, temperature, u, top_n_sigma=0.0, top_k=0, typical_p=1.0, top_p=1.0, min_p=0.0, vocab=None,
+                 nthreads=0):
+    """The ordered sampler chain (top-n-sigma, top-k, typical-p, top-p, min-p,
+    temperature) -> (tokens uint32[R], logp float64[R], margins float64[R, 3])."""
+    x, dt = _rows(x)
+    R, ld = x.shape
+    V = ld if vocab is None else vocab
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    assert u.shape == (R,)
+    tok = np.empty(R, np.uint32)
+    logp = np.empty(R, np.float64)
+    margins = np.empty((R, 3), np.float64)
+    _check(lib().oracle_sample_chain(_p(x), dt, R, V, ld, float(temperature), float(top_n_sigma), int(top_k),
+                                     float(typical_p), float(top_p), float(min_p), _p(u), _p(tok), _p(logp),
+                                     _p(margins), nthreads))
     return tok, logp, margins
 
 

@@ -320,6 +320,145 @@ int oracle_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, in
   return 0;
 }
 
+// f3: the ordered sampler chain ("Chapter 21", section 21.7: in source order
+// top_n_sigma masking against the maximum, top_k truncation, typical_p, then
+// the top_p nucleus cutoff, each over the full candidate list; min_p among the
+// filters on the untempered distribution, and the temperature last:
+// "speculative-acceptance.md", "The rules").  Candidates start as the whole
+// row in id order; every filter keeps at least one.
+//   1. top_n_sigma > 0: keep z >= z_max - n * sigma, sigma the population
+//      standard deviation of the row's values above -inf (order unchanged);
+//   2. top_k > 0: the top_k largest (value desc, id asc), in that order;
+//   3. typical_p < 1: p = softmax of the candidates (untempered), H = -sum p
+//      log p; reorder by |-log p - H| ascending (ties keep the current order),
+//      keep the shortest prefix with sum p >= typical_p;
+//   4. top_p < 1: reorder by (value desc, id asc), keep the shortest prefix
+//      with sum p >= top_p, p the softmax of the current candidates;
+//   5. min_p > 0: keep p >= min_p * max p over the candidates, i.e.
+//      z >= z_max + log(min_p) (order unchanged);
+//   6. w = exp((z - z_max) / T) over the kept candidates, the inverse-CDF draw
+//      with u in their current order, logp = log(w_j / sum w).
+// T == 0 or top_k == 1: the argmax, logp 0 (nothing drawn).
+// margins (3 per row, +inf when not applicable): the draw margin over W, and
+// the distance of typical_p / top_p to the nearer cumulative sum at its cut.
+int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                        float temperature, float top_n_sigma, int32_t top_k, float typical_p, float top_p,
+                        float min_p, const float* u, uint32_t* out_token, double* out_logp, double* margins,
+                        int nthreads) {
+  if (!logits || !u || !out_token || rows < 0 || vocab < 1 || ld < vocab) return 1;
+  if (!(temperature >= 0.0f) || top_k < 0 || !(top_p > 0.0f && top_p <= 1.0f) ||
+      !(typical_p > 0.0f && typical_p <= 1.0f) || !(min_p >= 0.0f && min_p <= 1.0f) || !(top_n_sigma >= 0.0f))
+    return 1;
+  Rows R{logits, dtype, ld};
+  const double T = temperature;
+  for_rows(rows, nthreads, [&](int64_t r) {
+    double mg[3] = {kInf, kInf, kInf};
+    auto finish = [&](uint32_t tok, double logp) {
+      out_token[r] = tok;
+      if (out_logp) out_logp[r] = logp;
+      if (margins)
+        for (int q = 0; q < 3; ++q) margins[3 * r + q] = mg[q];
+    };
+    const uint32_t am = argmax_row(R, r, vocab, nullptr);
+    if (am == kFailClosed) return finish(kFailClosed, kNaN);
+    if (temperature == 0.0f || top_k == 1) return finish(am, 0.0);
+    auto z = [&](uint32_t x) { return static_cast<double>(R.at(r, x)); };
+    const double zmax = z(am);
+    std::vector<uint32_t> cand(static_cast<size_t>(vocab));
+    std::iota(cand.begin(), cand.end(), 0u);
+    // 1. top-n-sigma
+    if (top_n_sigma > 0.0f) {
+      double n = 0.0, mean = 0.0;
+      for (uint32_t x : cand)
+        if (z(x) > -kInf) {
+          n += 1.0;
+          mean += z(x);
+        }
+      mean /= n;
+      double var = 0.0;
+      for (uint32_t x : cand)
+        if (z(x) > -kInf) var += (z(x) - mean) * (z(x) - mean);
+      const double thr = zmax - static_cast<double>(top_n_sigma) * std::sqrt(var / n);
+      std::vector<uint32_t> kept;
+      for (uint32_t x : cand)
+        if (z(x) >= thr) kept.push_back(x);
+      cand.swap(kept);
+    }
+    auto by_value = [&](uint32_t a, uint32_t b) { return z(a) > z(b) || (z(a) == z(b) && a < b); };
+    // 2. top-k
+    if (top_k > 0) {
+      const size_t k = std::min<size_t>(static_cast<size_t>(top_k), cand.size());
+      std::partial_sort(cand.begin(), cand.begin() + k, cand.end(), by_value);
+      cand.resize(k);
+    }
+    // untempered softmax of the current candidates (relative to zmax: cancels)
+    auto probs = [&](std::vector<double>& p) {
+      p.resize(cand.size());
+      double Z = 0.0;
+      for (size_t j = 0; j < cand.size(); ++j) Z += (p[j] = std::exp(z(cand[j]) - zmax));
+      for (double& v : p) v /= Z;
+    };
+    // shortest prefix of the current order with cumulative p >= P (at least 1)
+    auto cut = [&](const std::vector<double>& p, double P, double* margin) {
+      double cum = 0.0;
+      for (size_t j = 0; j < p.size(); ++j) {
+        const double prev = cum;
+        cum += p[j];
+        if (cum >= P) {
+          *margin = std::min(cum - P, j > 0 ? P - prev : kInf);
+          cand.resize(j + 1);
+          return;
+        }
+      }
+    };
+    // 3. typical-p
+    if (typical_p < 1.0f) {
+      std::vector<double> p;
+      probs(p);
+      double H = 0.0;
+      for (double v : p)
+        if (v > 0.0) H -= v * std::log(v);
+      std::vector<size_t> idx(cand.size());
+      std::iota(idx.begin(), idx.end(), size_t(0));
+      auto score = [&](size_t j) { return p[j] > 0.0 ? std::fabs(-std::log(p[j]) - H) : kInf; };
+      std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return score(a) < score(b); });
+      std::vector<uint32_t> c2(cand.size());
+      std::vector<double> p2(cand.size());
+      for (size_t j = 0; j < idx.size(); ++j) {
+        c2[j] = cand[idx[j]];
+        p2[j] = p[idx[j]];
+      }
+      cand.swap(c2);
+      cut(p2, typical_p, &mg[1]);
+    }
+    // 4. top-p
+    if (top_p < 1.0f) {
+      std::sort(cand.begin(), cand.end(), by_value);
+      std::vector<double> p;
+      probs(p);
+      cut(p, top_p, &mg[2]);
+    }
+    // 5. min-p
+    if (min_p > 0.0f) {
+      double cmax = -kInf;
+      for (uint32_t x : cand) cmax = std::max(cmax, z(x));
+      const double thr = cmax + std::log(static_cast<double>(min_p));
+      std::vector<uint32_t> kept;
+      for (uint32_t x : cand)
+        if (z(x) >= thr) kept.push_back(x);
+      cand.swap(kept);
+    }
+    // 6. temperature, then the draw in the current order
+    std::vector<double> w(cand.size());
+    for (size_t j = 0; j < cand.size(); ++j) w[j] = std::exp((z(cand[j]) - zmax) / T);
+    const size_t j = draw(w, static_cast<double>(u[r]), &mg[0]);
+    double S = 0.0;
+    for (double v : w) S += v;
+    finish(cand[j], (z(cand[j]) - zmax) / T - std::log(S));
+  });
+  return 0;
+}
+
 // c5: speculative acceptance for `batch` sequences of `gamma` drafted tokens.
 // target: batch*(gamma+1) rows (row b*(gamma+1)+i is verify position i of
 // sequence b; the last one is the bonus row); draft: batch*gamma rows.

@@ -7,6 +7,7 @@ import pytest
 
 import tests.test_oracle_pins as P
 import tests.test_oracle_pins_match as M
+import tests.test_oracle_pins_chain as C
 from oracle import build as B
 from oracle import oracle as O
 
@@ -54,6 +55,15 @@ MUTANTS = [
      [M.test_sampler_match_bonus_comes_from_the_last_target_row]),
     ("sum p q with min", "s += p_of(i, x) * q_of(i, x);", "s += std::min(p_of(i, x), q_of(i, x));",
      [M.test_sumprod_closed_forms]),
+    ("typical order reversed", "return score(a) < score(b);", "return score(a) > score(b);",
+     [C.test_worked_example]),
+    ("top-n-sigma with the sample standard deviation", "std::sqrt(var / n)", "std::sqrt(var / (n - 1.0))",
+     [C.test_top_n_sigma_matches_numpy_std]),
+    ("top-p kept in typical order", "      std::sort(cand.begin(), cand.end(), by_value);\n", "",
+     [C.test_worked_example, C.test_typical_and_top_p_cuts_satisfy_their_definitions]),
+    ("min-p in tempered units", "const double thr = cmax + std::log(static_cast<double>(min_p));",
+     "const double thr = cmax + T * std::log(static_cast<double>(min_p));",
+     [C.test_worked_example, C.test_min_p_matches_a_numpy_mask]),
 ]
 
 
