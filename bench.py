@@ -224,6 +224,16 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
     ol = torch.empty(64, dtype=torch.float32, device=dev)
     lat("sample_64x202048", lambda i: vsel.vsel_sample(xs[0], 0.7, 20, 0.95, ud, out_token=ot, out_logprob=ol),
         lambda i: vsel.vsel_sample(xs[i % len(xs)], 0.7, 20, 0.95, ud, out_token=ot, out_logprob=ol))
+    # the ordered chain on the same rows: the moments pass, then top-k with
+    # top-n-sigma, typical-p, top-p and min-p on the candidates; and the
+    # whole-row draw with the two threshold filters
+    chain = dict(top_n_sigma=1.0, top_k=50, typical_p=0.9, top_p=0.95, min_p=0.05)
+    lat("sample_chain_64x202048", lambda i: vsel.vsel_sample_chain(xs[0], 0.7, ud, out_token=ot, out_logprob=ol,
+                                                                   **chain),
+        lambda i: vsel.vsel_sample_chain(xs[i % len(xs)], 0.7, ud, out_token=ot, out_logprob=ol, **chain))
+    ex["sample_chain_rowdraw_64x202048_device_cold_us"] = time_graph(
+        lambda i: vsel.vsel_sample_chain(xs[i % len(xs)], 0.7, ud, top_n_sigma=1.0, min_p=0.05, out_token=ot,
+                                         out_logprob=ol), 20, stream)
     del xs
     # config 4: speculative acceptance (target + draft rows: 440 MB, already past the Infinity Cache)
     d = W.speculative_batch()

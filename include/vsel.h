@@ -12,6 +12,8 @@
  *                     row's argmax and log-sum-exp in one pass over the row
  *   vsel_sample       temperature sampling with top-k then top-p, one caller
  *                     uniform per row
+ *   vsel_sample_chain the ordered sampler chain: top-n-sigma, top-k,
+ *                     typical-p, top-p, min-p, then the temperature
  *   vsel_spec_match   speculative-decoding acceptance by sampler-match and
  *                     the per-position sum p*q
  *   vsel_spec_accept  speculative-decoding acceptance: modified rejection
@@ -68,7 +70,8 @@ typedef enum {
   VSEL_OP_ARGMAX = 0,
   VSEL_OP_TOPK = 1,
   VSEL_OP_SAMPLE = 2,
-  VSEL_OP_SPEC_ACCEPT = 3
+  VSEL_OP_SPEC_ACCEPT = 3,
+  VSEL_OP_SAMPLE_CHAIN = 4
 } vsel_op;
 
 /* Index/token written for a fail-closed row: the high-bit latch of the greedy
@@ -90,6 +93,7 @@ const char* vsel_status_string(int status);
  *   VSEL_OP_TOPK:        rows, vocab, k.
  *   VSEL_OP_SAMPLE:      rows, vocab, k = top_k.
  *   VSEL_OP_SPEC_ACCEPT: rows = batch, vocab, k = gamma.
+ *   VSEL_OP_SAMPLE_CHAIN: rows, vocab, k = top_k.
  * Returns 0 for arguments the operation would reject. */
 size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int32_t k);
 
@@ -177,6 +181,41 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
                         float temperature, int32_t top_k, float top_p, const float* u,
                         uint32_t* out_token, float* out_logprob, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* The ordered sampler chain with one caller uniform per row ("Chapter 21",
+ * section 21.7: top_n_sigma masking against the maximum, top_k, typical_p,
+ * then the top_p nucleus; min_p a filter on the untempered distribution too,
+ * and the temperature applied last, "speculative-acceptance.md", "The rules").
+ * Per row, starting from the whole row in id order; each filter keeps at
+ * least one candidate:
+ *   1. top_n_sigma > 0: keep z >= z_max - top_n_sigma * sigma, sigma the
+ *      population standard deviation of the row's elements above -inf
+ *      (order unchanged);
+ *   2. top_k > 0: the top min(top_k, candidates) in (value desc, id asc) order;
+ *   3. typical_p < 1: p = softmax of the candidates, H = -sum p log p; reorder
+ *      by |-log p - H| ascending (ties keep value order) and keep the
+ *      shortest prefix with sum p >= typical_p;
+ *   4. top_p < 1: back to (value desc, id asc) order, keep the shortest prefix
+ *      with sum p >= top_p (p the softmax of the candidates left);
+ *   5. min_p > 0: keep z >= max z + log(min_p), i.e. p >= min_p * max p
+ *      (order unchanged);
+ *   6. w = exp((z - z_max) / temperature) over the kept candidates, the
+ *      inverse-CDF draw with u in their current order (float64), and
+ *      out_logprob = log(w_j / W).
+ * temperature == 0 or top_k == 1: the argmax token, logprob 0.  With all
+ * filters off except top_k / top_p this is vsel_sample.
+ *   temperature >= 0 and finite; top_n_sigma >= 0 and finite;
+ *   0 <= top_k <= VSEL_K_MAX; 0 < typical_p <= 1; 0 < top_p <= 1;
+ *   0 <= min_p <= 1.  top_k == 0 (the whole row) allows only the threshold
+ *   filters (top_n_sigma, min_p): typical_p and top_p need top_k >= 1, and
+ *   typical_p < 1 needs top_k <= 128.  With top_k == 0, vocab <= 67,108,864.
+ *   u, out_token, out_logprob as vsel_sample; workspace VSEL_OP_SAMPLE_CHAIN
+ *   with k = top_k.
+ */
+vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                              float temperature, float top_n_sigma, int32_t top_k, float typical_p,
+                              float top_p, float min_p, const float* u, uint32_t* out_token,
+                              float* out_logprob, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Speculative-decoding acceptance for `batch` sequences of `gamma` drafts.
  * p_i = softmax(target row i / T), q_i = softmax(draft row i / T).

@@ -339,8 +339,10 @@ int oracle_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, in
 //   6. w = exp((z - z_max) / T) over the kept candidates, the inverse-CDF draw
 //      with u in their current order, logp = log(w_j / sum w).
 // T == 0 or top_k == 1: the argmax, logp 0 (nothing drawn).
-// margins (3 per row, +inf when not applicable): the draw margin over W, and
-// the distance of typical_p / top_p to the nearer cumulative sum at its cut.
+// margins (5 per row, +inf when not applicable): the draw margin over W; the
+// distance of typical_p / top_p to the nearer cumulative sum at its cut; the
+// distance of the top-n-sigma and min-p thresholds to the nearest candidate
+// value (logit units).
 int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                         float temperature, float top_n_sigma, int32_t top_k, float typical_p, float top_p,
                         float min_p, const float* u, uint32_t* out_token, double* out_logp, double* margins,
@@ -352,12 +354,12 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
   Rows R{logits, dtype, ld};
   const double T = temperature;
   for_rows(rows, nthreads, [&](int64_t r) {
-    double mg[3] = {kInf, kInf, kInf};
+    double mg[5] = {kInf, kInf, kInf, kInf, kInf};
     auto finish = [&](uint32_t tok, double logp) {
       out_token[r] = tok;
       if (out_logp) out_logp[r] = logp;
       if (margins)
-        for (int q = 0; q < 3; ++q) margins[3 * r + q] = mg[q];
+        for (int q = 0; q < 5; ++q) margins[5 * r + q] = mg[q];
     };
     const uint32_t am = argmax_row(R, r, vocab, nullptr);
     if (am == kFailClosed) return finish(kFailClosed, kNaN);
@@ -380,8 +382,10 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
         if (z(x) > -kInf) var += (z(x) - mean) * (z(x) - mean);
       const double thr = zmax - static_cast<double>(top_n_sigma) * std::sqrt(var / n);
       std::vector<uint32_t> kept;
-      for (uint32_t x : cand)
+      for (uint32_t x : cand) {
         if (z(x) >= thr) kept.push_back(x);
+        mg[3] = std::min(mg[3], std::fabs(z(x) - thr));
+      }
       cand.swap(kept);
     }
     auto by_value = [&](uint32_t a, uint32_t b) { return z(a) > z(b) || (z(a) == z(b) && a < b); };
@@ -444,8 +448,10 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
       for (uint32_t x : cand) cmax = std::max(cmax, z(x));
       const double thr = cmax + std::log(static_cast<double>(min_p));
       std::vector<uint32_t> kept;
-      for (uint32_t x : cand)
+      for (uint32_t x : cand) {
         if (z(x) >= thr) kept.push_back(x);
+        mg[4] = std::min(mg[4], std::fabs(z(x) - thr));
+      }
       cand.swap(kept);
     }
     // 6. temperature, then the draw in the current order

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_operations():
     names = declared_functions()
-    for op in ("vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_spec_accept",
-               "vsel_spec_match", "vsel_workspace_bytes"):
+    for op in ("vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_sample_chain",
+               "vsel_spec_accept", "vsel_spec_match", "vsel_workspace_bytes"):
         assert op in names
 
 
@@ -45,9 +45,13 @@ def test_version_and_status_strings(vsel):
 def test_workspace_sizes(vsel):
     wb = vsel.workspace_bytes
     for op, k in ((vsel.OP_ARGMAX, 0), (vsel.OP_TOPK, 84), (vsel.OP_SAMPLE, 20), (vsel.OP_SAMPLE, 0),
-                  (vsel.OP_SPEC, 8)):
+                  (vsel.OP_SPEC, 8), (vsel.OP_SAMPLE_CHAIN, 0), (vsel.OP_SAMPLE_CHAIN, 128)):
         n = wb(op, vsel.F32, 32, 202048, k)
         assert n > 0 and n % 256 == 0
+    # the chain holds the sampler's workspace and the row moments after it
+    for k in (0, 1, 50, 1024):
+        assert wb(vsel.OP_SAMPLE_CHAIN, vsel.BF16, 64, 202048, k) > wb(vsel.OP_SAMPLE, vsel.BF16, 64, 202048, k)
+    assert wb(vsel.OP_SAMPLE_CHAIN, vsel.F32, 4, 100, 1025) == 0
     assert wb(vsel.OP_TOPK, vsel.BF16, 1024, 202048, 84) > 0
     # rejected shapes size to 0
     assert wb(vsel.OP_TOPK, vsel.F32, 4, 100, 101) == 0          # k > vocab
@@ -86,6 +90,15 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
                   (0.7, 1025, 0.9), (float("nan"), 20, 0.9), (float("inf"), 20, 0.9)]
     for T, k, p in bad_sample:
         assert L.vsel_sample(fake, 0, 4, 100, 100, T, k, p, fake, fake, None, ws, 1 << 20, None) == EINVAL
+    def chain(T=0.7, sig=0.0, k=20, typ=1.0, p=1.0, mp=0.0, u=fake, ws_bytes=1 << 20):
+        return L.vsel_sample_chain(fake, 0, 4, 100, 100, T, sig, k, typ, p, mp, u, fake, None, ws, ws_bytes, None)
+    bad_chain = [dict(sig=-1.0), dict(sig=float("inf")), dict(sig=float("nan")), dict(typ=0.0), dict(typ=1.5),
+                 dict(mp=-0.1), dict(mp=1.01), dict(mp=float("nan")), dict(k=0, typ=0.9), dict(k=0, p=0.9),
+                 dict(k=129, typ=0.9), dict(k=-1), dict(k=1025), dict(p=0.0), dict(T=float("inf")),
+                 dict(T=-0.1), dict(u=None)]
+    for kw in bad_chain:
+        assert chain(**kw) == EINVAL, kw
+    assert chain(sig=1.0, ws_bytes=4096) == EWS
     args = dict(batch=2, gamma=3, vocab=100, T=1.0)
     def spec(**kw):
         a = {**args, **kw}

@@ -58,6 +58,17 @@ def test_sample_graph(g):
                      lambda: [ot, ol], ref, lambda: g.vsel.vsel_topk(x, 5))
 
 
+def test_sample_chain_graph(g):
+    xs, u = W.sampling_rows(rows=9, vocab=50000, seed=76)
+    x, ud = g.dev_rows(xs), g.dev(u)
+    for kw in (dict(top_n_sigma=1.0, top_k=40, typical_p=0.8, top_p=0.9, min_p=0.02), dict(top_n_sigma=0.7, min_p=0.01)):
+        tok, lp = g.vsel.vsel_sample_chain(x, 0.8, ud, **kw)
+        ref = [tok.clone(), lp.clone()]
+        ot, ol = torch.empty_like(tok), torch.empty_like(lp)
+        replay_check(lambda: g.vsel.vsel_sample_chain(x, 0.8, ud, out_token=ot, out_logprob=ol, **kw),
+                     lambda: [ot, ol], ref, lambda: g.vsel.vsel_topk(x, 5))
+
+
 def test_spec_accept_graph(g):
     d = W.speculative_batch(batch=4, gamma=3, vocab=30000, seed=74)
     args = [g.dev(d[k]) for k in ("target", "draft", "tokens", "u_acc", "u_res", "u_bon")]

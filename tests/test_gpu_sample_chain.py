@@ -1,0 +1,148 @@
+"""GPU parity of vsel_sample_chain (the ordered sampler chain: top-n-sigma,
+top-k, typical-p, top-p, min-p, then the temperature) with the oracle.
+
+Tokens bit-exact except on rows where one of the oracle's float64 margins is
+below 1e-9: the draw boundary, the typical-p or top-p cut, or the distance of
+the top-n-sigma or min-p threshold to the nearest candidate value.  There the
+last bits of two float64 evaluations (a different summation order for sigma,
+another libm for exp and log) may legitimately decide differently; such rows
+are counted and must be rare.  Log-probabilities within 1e-5 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+MARGIN = 1e-9
+
+
+@pytest.fixture(scope="module")
+def g():
+    import tests.gpu_helpers as G
+    import vocab_row_reductions_amd as vsel
+    G.vsel = vsel
+    return G
+
+
+def compare(g, oracle, x, T, u, ld=None, max_exempt_frac=0.02, exact_thresholds=False, **kw):
+    """exact_thresholds: the rows' thresholds are exact on both sides (sigma 0,
+    min_p 1), so an element lying on one is no reason to exempt the row."""
+    xd = g.dev_rows(x, ld)
+    tok, lp = g.vsel.vsel_sample_chain(xd, T, g.dev(u), vocab=x.shape[1], **kw)
+    otok, olp, om = oracle.sample_chain(x, T, u, **kw)
+    exempt = np.any((om[:, :3] if exact_thresholds else om) < MARGIN, axis=1)
+    assert exempt.mean() <= max_exempt_frac, f"{exempt.sum()} rows within {MARGIN} of a decision"
+    gt = g.u32(tok)
+    bad = np.nonzero((gt != otok) & ~exempt)[0]
+    assert len(bad) == 0, f"rows {bad[:8]}: gpu {gt[bad[:8]]} oracle {otok[bad[:8]]} ({kw})"
+    same = (~exempt) & (otok != g.SENT)
+    lpn = lp.cpu().numpy()
+    assert np.all(np.abs(lpn[same] - olp[same]) <= 1e-5)
+    assert np.array_equal(np.isnan(lpn), np.isnan(olp))
+    return gt, otok
+
+
+CHAINS = [
+    dict(top_n_sigma=1.0, top_k=50, typical_p=0.9, top_p=0.95, min_p=0.05),
+    dict(top_n_sigma=1.5),                                   # whole row, one threshold
+    dict(min_p=0.1),
+    dict(top_n_sigma=0.5, min_p=0.02),
+    dict(top_k=100, typical_p=0.7),
+    dict(top_k=128, typical_p=0.5, top_p=0.8, min_p=0.05, top_n_sigma=2.0),
+    dict(top_k=500, top_n_sigma=1.0, min_p=0.01, top_p=0.9),  # k above the per-wave kernel's range
+    dict(top_k=1024, min_p=0.2),
+    dict(top_k=20, top_p=0.95),                              # the plain sampler's chain
+]
+
+
+def test_config3_rows_full_chain(g, oracle):
+    x, u = W.sampling_rows()
+    compare(g, oracle, x, 0.7, u, max_exempt_frac=0.0, **CHAINS[0])
+
+
+@pytest.mark.parametrize("ci", range(len(CHAINS)))
+@pytest.mark.parametrize("V", [7, 1000, 70001, 202048])
+def test_chains_over_shapes_f32(g, oracle, ci, V):
+    kw = dict(CHAINS[ci])
+    if kw.get("top_k", 0) > V:
+        kw["top_k"] = V
+    x, u = W.sampling_rows(rows=8, vocab=V, seed=300 + V + ci, masked_frac=0.01 if V > 100 else 0.0)
+    compare(g, oracle, x, 0.9, u, ld=V + 8, **kw)
+
+
+@pytest.mark.parametrize("ci", [0, 1, 3, 5, 6])
+@pytest.mark.parametrize("ld_pad", [0, 3])
+def test_chains_bf16(g, oracle, ci, ld_pad):
+    """bf16 rows; an odd stride sends every top-k to the workgroup kernel."""
+    V = 50021
+    x, u = W.sampling_rows(rows=8, vocab=V, seed=400 + ci + ld_pad)
+    xb = W.f32_to_bf16_bits(x)
+    compare(g, oracle, xb, 1.2, u, ld=V + ld_pad, **CHAINS[ci])
+
+
+def test_reduces_to_vsel_sample(g):
+    x, u = W.sampling_rows(rows=16, vocab=30000, seed=401)
+    xd, ud = g.dev_rows(x), g.dev(u)
+    for top_k, top_p in ((20, 0.95), (0, 1.0), (300, 0.5), (128, 1.0)):
+        a = g.vsel.vsel_sample(xd, 0.8, top_k, top_p, ud)
+        b = g.vsel.vsel_sample_chain(xd, 0.8, ud, top_k=top_k, top_p=top_p)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_greedy_limits(g):
+    x, u = W.sampling_rows(rows=16, vocab=9000, seed=402)
+    xd, ud = g.dev_rows(x), g.dev(u)
+    idx, _ = g.vsel.vsel_argmax(xd)
+    for T, kw in ((0.0, dict(top_n_sigma=1.0, min_p=0.1)), (0.7, dict(top_k=1, typical_p=0.5)),
+                  (0.0, dict(top_k=40, typical_p=0.3, top_p=0.2))):
+        tok, lp = g.vsel.vsel_sample_chain(xd, T, ud, **kw)
+        assert torch.equal(tok, idx) and torch.all(lp == 0)
+
+
+def test_threshold_edge_rows(g, oracle):
+    """Rows with one finite element (sigma 0), a large common offset (sigma
+    from shifted sums), many ties at the maximum, and min_p = 1 (only the
+    maximum's ties survive)."""
+    V = 5000
+    rng = np.random.default_rng(W.BASE_SEED + 403)
+    x = rng.normal(0.0, 1.0, (6, V)).astype(np.float32)
+    x[0, :] = -np.inf
+    x[0, 1234] = 2.5                                   # sigma 0: only the maximum
+    x[1] += np.float32(3000.0)                         # large offset
+    x[2, ::7] = np.float32(6.0)                        # ties at the maximum
+    x[3, :] = np.round(x[3] * 4) / 4                   # coarse grid: many equal values
+    u = rng.random(6, dtype=np.float32)
+    compare(g, oracle, x, 1.0, u, max_exempt_frac=0.0, exact_thresholds=True, top_n_sigma=1.0)
+    compare(g, oracle, x, 1.0, u, max_exempt_frac=0.0, exact_thresholds=True, min_p=1.0)
+    compare(g, oracle, x, 0.5, u, max_exempt_frac=0.0, exact_thresholds=True, top_k=64, top_n_sigma=0.3, min_p=0.5)
+    tok, _ = g.vsel.vsel_sample_chain(g.dev_rows(x), 1.0, g.dev(u), min_p=1.0)
+    assert g.u32(tok)[0] == 1234 and g.u32(tok)[2] % 7 == 0
+
+
+def test_fail_closed(g, oracle):
+    x, u = W.sampling_rows(rows=4, vocab=3000, seed=404)
+    x = x.copy()
+    x[1, 17] = np.nan
+    x[2, 5] = np.inf
+    for kw in (dict(top_n_sigma=1.0, min_p=0.1), dict(top_k=30, typical_p=0.8, top_n_sigma=1.0)):
+        gt, _ = compare(g, oracle, x, 0.8, u, **kw)
+        assert gt[1] == g.SENT and gt[2] == g.SENT and gt[0] != g.SENT
+
+
+def test_support_of_each_filter(g):
+    """Over a grid of uniforms, every drawn token lies in the filter's kept set
+    (computed here with numpy), and every kept token is drawn."""
+    z = np.array([2.0, 1.5, 1.4, 0.2, -0.5, -1.0, -3.0, -6.0], np.float32)
+    n = 8192
+    u = ((np.arange(n) + 0.5) / n).astype(np.float32)
+    xd = g.dev_rows(np.repeat(z[None], n, 0))
+    zz = z.astype(np.float64)
+    cases = [(dict(min_p=0.3), np.nonzero(np.exp(zz - zz.max()) >= 0.3)[0]),
+             (dict(top_n_sigma=1.0), np.nonzero(zz >= zz.max() - np.std(zz))[0]),
+             (dict(top_k=6, top_n_sigma=0.8, min_p=0.1),
+              np.nonzero((zz >= zz.max() - 0.8 * np.std(zz)) & (np.exp(zz - zz.max()) >= 0.1))[0])]
+    for kw, kept in cases:
+        tok, _ = g.vsel.vsel_sample_chain(xd, 1.0, g.dev(u), **kw)
+        assert set(np.unique(g.u32(tok)).tolist()) == set(kept.tolist()), kw

@@ -15,7 +15,8 @@ import os
 
 import torch  # loads the HIP runtime that libvsel.so then shares
 
-__all__ = ["vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_spec_accept", "vsel_spec_match",
+__all__ = ["vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_sample_chain", "vsel_spec_accept",
+           "vsel_spec_match",
            "workspace_bytes",
            "VselError", "NONFINITE", "K_MAX", "EXCLUDED_MAX", "library_path"]
 
@@ -26,7 +27,7 @@ NONFINITE = 0xFFFFFFFF
 K_MAX = 1024
 EXCLUDED_MAX = 256
 F32, BF16 = 0, 1
-OP_ARGMAX, OP_TOPK, OP_SAMPLE, OP_SPEC = 0, 1, 2, 3
+OP_ARGMAX, OP_TOPK, OP_SAMPLE, OP_SPEC, OP_SAMPLE_CHAIN = 0, 1, 2, 3, 4
 
 
 class VselError(RuntimeError):
@@ -47,6 +48,8 @@ def _load():
     L.vsel_argmax_excluding.argtypes = [vp, C.c_int, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.vsel_topk.argtypes = [vp, C.c_int, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]
     L.vsel_sample.argtypes = [vp, C.c_int, i64, i64, i64, f32, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.vsel_sample_chain.argtypes = [vp, C.c_int, i64, i64, i64, f32, f32, i32, f32, f32, f32, vp, vp, vp, vp, sz,
+                                    vp]
     L.vsel_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp, sz, vp]
     L.vsel_spec_match.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -185,6 +188,26 @@ def vsel_sample(logits: torch.Tensor, temperature: float, top_k: int, top_p: flo
     _check(lib.vsel_sample(_ptr(logits), dt, rows, V, ld, float(temperature), int(top_k), float(top_p),
                            _ptr(u.contiguous()), _ptr(out_token), _ptr(out_logprob), _ptr(ws), ws.numel(),
                            _stream(dev)), "vsel_sample")
+    return out_token, out_logprob
+
+
+def vsel_sample_chain(logits: torch.Tensor, temperature: float, u: torch.Tensor, top_n_sigma=0.0, top_k=0,
+                      typical_p=1.0, top_p=1.0, min_p=0.0, vocab=None, out_token=None, out_logprob=None):
+    """The ordered sampler chain (top-n-sigma, top-k, typical-p, top-p, min-p,
+    then the temperature) with one uniform per row -> (token i32, logprob f32)."""
+    rows, V, ld = _rows(logits, vocab)
+    dt = _dtype(logits)
+    dev = logits.device
+    if u.dtype != torch.float32 or u.numel() != rows or not u.is_cuda:
+        raise ValueError("u must be a float32 device tensor with one uniform per row")
+    if out_token is None:
+        out_token = torch.empty(rows, dtype=torch.int32, device=dev)
+    if out_logprob is None:
+        out_logprob = torch.empty(rows, dtype=torch.float32, device=dev)
+    ws = workspace(OP_SAMPLE_CHAIN, dt, rows, V, int(top_k), dev)
+    _check(lib.vsel_sample_chain(_ptr(logits), dt, rows, V, ld, float(temperature), float(top_n_sigma), int(top_k),
+                                 float(typical_p), float(top_p), float(min_p), _ptr(u.contiguous()), _ptr(out_token),
+                                 _ptr(out_logprob), _ptr(ws), ws.numel(), _stream(dev)), "vsel_sample_chain")
     return out_token, out_logprob
 
 

@@ -256,6 +256,42 @@ SpecWs spec_layout(Layout& L, int64_t B, int64_t G, int64_t V, const Plan& ps, c
   return w;
 }
 
+// Workspace of the sampler for this shape (0: invalid shape).
+size_t sample_ws_bytes(int64_t rows, int64_t vocab, int64_t k) {
+  if (!rows_ok(rows, vocab, vocab) || k < 0 || k > VSEL_K_MAX) return 0;
+  Layout a;
+  scan_layout(a, rows, plan_scan_bound(rows, vocab));
+  size_t need = a.off;
+  if (k == 0) {
+    Layout b;
+    if (vocab > kMaxDrawVocab) return 0;
+    rowdraw_layout(b, rows, vocab, plan_scan_bound(rows, vocab));
+    need = std::max(need, b.off);
+  } else if (k > 1) {
+    const int64_t kk = std::min<int64_t>(k, vocab);
+    Layout b;
+    topk_layout(b, rows, kk, plan_topk_bound(rows, vocab, kk));
+    need = std::max(need, b.off);
+  }
+  return need;
+}
+
+// Row moments for the chain's top-n-sigma filter, placed after the
+// sampler's own workspace.
+struct MomWs {
+  size_t tickets, sigma, p_n, p_mean, p_m2;
+};
+MomWs moments_layout(Layout& L, int64_t rows, const Plan& p) {
+  MomWs w{};
+  w.tickets = L.take((size_t)rows * 4);
+  w.sigma = L.take((size_t)rows * 8);
+  const size_t n = (size_t)(rows * p.S);
+  w.p_n = L.take(n * 8);
+  w.p_mean = L.take(n * 8);
+  w.p_m2 = L.take(n * 8);
+  return w;
+}
+
 bool ws_ok(void* ws, size_t have, size_t need) {
   return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) % kWsAlign == 0) && have >= need;
 }
@@ -310,23 +346,14 @@ size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int3
       topk_layout(L, rows, k, plan_topk_bound(rows, vocab, k));
       return L.off;
     }
-    case VSEL_OP_SAMPLE: {
-      if (!rows_ok(rows, vocab, vocab) || k < 0 || k > VSEL_K_MAX) return 0;
-      Layout a;
-      scan_layout(a, rows, plan_scan_bound(rows, vocab));
-      size_t need = a.off;
-      if (k == 0) {
-        Layout b;
-        if (vocab > kMaxDrawVocab) return 0;
-        rowdraw_layout(b, rows, vocab, plan_scan_bound(rows, vocab));
-        need = std::max(need, b.off);
-      } else if (k > 1) {
-        const int64_t kk = std::min<int64_t>(k, vocab);
-        Layout b;
-        topk_layout(b, rows, kk, plan_topk_bound(rows, vocab, kk));
-        need = std::max(need, b.off);
-      }
-      return need;
+    case VSEL_OP_SAMPLE:
+      return sample_ws_bytes(rows, vocab, k);
+    case VSEL_OP_SAMPLE_CHAIN: {
+      const size_t base = sample_ws_bytes(rows, vocab, k);
+      if (base == 0) return 0;
+      L.off = align_up(base);
+      moments_layout(L, rows, plan_scan_bound(rows, vocab));
+      return L.off;
     }
     case VSEL_OP_SPEC_ACCEPT: {
       const int64_t B = rows, G = k;
@@ -425,19 +452,47 @@ vsel_status vsel_topk(const void* logits, int dtype, int64_t rows, int64_t vocab
   return topk_common(logits, dtype, rows, vocab, ld, k, out_lse != nullptr, a, ws, ws_bytes, stream);
 }
 
-vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
-                        float temperature, int32_t top_k, float top_p, const float* u, uint32_t* out_token,
-                        float* out_logprob, void* ws, size_t ws_bytes, void* stream) {
+// The sampler (vsel_sample) and the ordered chain (vsel_sample_chain): the
+// greedy short-circuit, the whole-row draw (top_k == 0; threshold filters
+// only) or the top-k kernel with the chain on its candidates.  mom: where the
+// row moments go (the chain, whose caller has checked the whole workspace);
+// with top_n_sigma > 0 their pass runs first.
+static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                               float temperature, int32_t top_k, float top_p, float top_n_sigma, float typical_p,
+                               float min_p, const MomWs* mom, const float* u, uint32_t* out_token,
+                               float* out_logprob, void* ws, size_t ws_bytes, void* stream) {
   if (!logits || !u || !out_token || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
       !aligned_elem(logits, elem_size(dtype)))
     return VSEL_EINVAL;
   if (!(temperature >= 0.0f) || std::isinf(temperature) || top_k < 0 || top_k > VSEL_K_MAX ||
       !(top_p > 0.0f && top_p <= 1.0f))
     return VSEL_EINVAL;
-  if (top_k == 0 && top_p < 1.0f) return VSEL_EINVAL;
+  if (top_k == 0 && (top_p < 1.0f || typical_p < 1.0f)) return VSEL_EINVAL;
+  if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
+  if (top_n_sigma > 0.0f && !mom) return VSEL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
+  const bool greedy = temperature == 0.0f || top_k == 1;
 
-  if (temperature == 0.0f || top_k == 1) {
+  const double* sigma = nullptr;
+  if (top_n_sigma > 0.0f && !greedy) {
+    const Plan p = plan_scan(dtype, false, rows, vocab);
+    MomArgs m{};
+    m.x = logits;
+    m.ld = ld;
+    m.rows = rows;
+    m.V = vocab;
+    m.seg_len = p.seg_len;
+    m.S = p.S;
+    m.tickets = at<uint32_t>(ws, mom->tickets);
+    m.p_n = at<double>(ws, mom->p_n);
+    m.p_mean = at<double>(ws, mom->p_mean);
+    m.p_m2 = at<double>(ws, mom->p_m2);
+    m.sigma = at<double>(ws, mom->sigma);
+    if (launch_moments(dtype, m, s) != hipSuccess) return VSEL_EDEVICE;
+    sigma = m.sigma;
+  }
+
+  if (greedy) {
     // Greedy: the argmax, nothing drawn; log-probability 0.
     Layout L;
     const ScanWs w = scan_layout(L, rows, plan_scan_bound(rows, vocab));
@@ -488,6 +543,9 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
     d.nchunk = cdiv(vocab, kChunk);
     d.p_w = at<double>(ws, w.p_w);
     d.p_c = at<double>(ws, w.p_c);
+    d.top_n_sigma = top_n_sigma;
+    d.min_p = min_p;
+    d.sigma = sigma;
     return launched(launch_draw_rows(dtype, d, s));
   }
 
@@ -496,10 +554,45 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
   a.mode = 1;
   a.temperature = temperature;
   a.top_p = top_p;
+  a.top_n_sigma = top_n_sigma;
+  a.typical_p = typical_p;
+  a.min_p = min_p;
+  a.sigma = sigma;
   a.u = u;
   a.out_token = out_token;
   a.out_logp = out_logprob;
   return topk_common(logits, dtype, rows, vocab, ld, k, false, a, ws, ws_bytes, stream);
+}
+
+vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                        float temperature, int32_t top_k, float top_p, const float* u, uint32_t* out_token,
+                        float* out_logprob, void* ws, size_t ws_bytes, void* stream) {
+  return sample_impl(logits, dtype, rows, vocab, ld, temperature, top_k, top_p, 0.0f, 1.0f, 0.0f, nullptr, u,
+                     out_token, out_logprob, ws, ws_bytes, stream);
+}
+
+vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
+                              float temperature, float top_n_sigma, int32_t top_k, float typical_p, float top_p,
+                              float min_p, const float* u, uint32_t* out_token, float* out_logprob, void* ws,
+                              size_t ws_bytes, void* stream) {
+  // everything sample_impl checks, before the moments pass can launch
+  if (!logits || !u || !out_token || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
+      !aligned_elem(logits, elem_size(dtype)))
+    return VSEL_EINVAL;
+  if (!(temperature >= 0.0f) || std::isinf(temperature) || !(top_k >= 0 && top_k <= VSEL_K_MAX) ||
+      !(top_p > 0.0f && top_p <= 1.0f) || !(top_n_sigma >= 0.0f) || std::isinf(top_n_sigma) ||
+      !(typical_p > 0.0f && typical_p <= 1.0f) || !(min_p >= 0.0f && min_p <= 1.0f))
+    return VSEL_EINVAL;
+  if (top_k == 0 && (top_p < 1.0f || typical_p < 1.0f)) return VSEL_EINVAL;
+  if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
+  const size_t base = sample_ws_bytes(rows, vocab, top_k);
+  if (base == 0) return VSEL_EINVAL;
+  Layout L;
+  L.off = align_up(base);
+  const MomWs m = moments_layout(L, rows, plan_scan_bound(rows, vocab));
+  if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+  return sample_impl(logits, dtype, rows, vocab, ld, temperature, top_k, top_p, top_n_sigma, typical_p, min_p, &m,
+                     u, out_token, out_logprob, ws, ws_bytes, stream);
 }
 
 // Argument checks, pass 1 (row statistics of every target and draft row)

@@ -1,0 +1,100 @@
+// chain.hip -- row moments for the top-n-sigma filter of the sampler chain
+// ("Chapter 21", section 21.7: top_n_sigma masks the candidates against the
+// maximum; the width is n standard deviations of the row's values).
+//
+// One pass over each row, one workgroup per (row, segment).  Each lane sums
+// its values above -inf shifted by its own first such value (float64), so a
+// row with a large common offset keeps its variance; lanes, waves and then
+// segments merge their (count, mean, squared deviations) in a fixed order
+// (the pairwise update of Chan, Golub and LeVeque), so the result is the
+// same on every call.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace vsel {
+
+struct Mom {
+  double n, mean, m2;
+};
+
+__device__ __forceinline__ Mom mom_merge(Mom a, Mom b) {
+  if (b.n == 0.0) return a;
+  if (a.n == 0.0) return b;
+  const double n = a.n + b.n, d = b.mean - a.mean;
+  return Mom{n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
+}
+
+// Lanes folded into lane 0 in a fixed order (lane l takes lane l + 2^s).
+__device__ __forceinline__ Mom wave_mom(Mom v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const Mom o{__shfl_down(v.n, d), __shfl_down(v.mean, d), __shfl_down(v.m2, d)};
+    if (((int)(threadIdx.x & 63) & (2 * d - 1)) == 0) v = mom_merge(v, o);
+  }
+  return v;  // lane 0
+}
+
+template <typename DT>
+__global__ __launch_bounds__(NT) void moments_kernel(MomArgs a) {
+  __shared__ SelShared sh;
+  __shared__ double wn[NWAVE], wmean[NWAVE], wm2[NWAVE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows) return;
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  // this thread's values: e_begin + tid, + NT, ... (in index order)
+  double n = 0.0, s1 = 0.0, s2 = 0.0, r = 0.0;
+  for (int64_t x = e_begin + tid; x < e_end; x += NT) {
+    const float z = __uint_as_float(gbits_at<DT>(xr, x));
+    if (!(z > -__builtin_inff())) continue;  // -inf (a mask) takes no part; NaN rows fail closed elsewhere
+    if (n == 0.0) r = z;
+    const double d = (double)z - r;
+    n += 1.0;
+    s1 += d;
+    s2 += d * d;
+  }
+  Mom v{n, 0.0, 0.0};
+  if (n > 0.0) v = Mom{n, r + s1 / n, s2 - s1 * s1 / n};
+  v = wave_mom(v);
+  if (lane == 0) {
+    wn[wave] = v.n;
+    wmean[wave] = v.mean;
+    wm2[wave] = v.m2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    Mom w{0.0, 0.0, 0.0};
+    for (int q = 0; q < NWAVE; ++q) w = mom_merge(w, Mom{wn[q], wmean[q], wm2[q]});
+    v = w;
+  }
+  if (a.S > 1) {
+    if (tid == 0) {
+      st_dev(&a.p_n[row * a.S + seg], v.n);
+      st_dev(&a.p_mean[row * a.S + seg], v.mean);
+      st_dev(&a.p_m2[row * a.S + seg], v.m2);
+    }
+    if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
+    if (tid == 0) {
+      Mom w{0.0, 0.0, 0.0};
+      for (int sg = 0; sg < a.S; ++sg)
+        w = mom_merge(w, Mom{ld_dev(&a.p_n[row * a.S + sg]), ld_dev(&a.p_mean[row * a.S + sg]),
+                             ld_dev(&a.p_m2[row * a.S + sg])});
+      v = w;
+    }
+  }
+  if (tid == 0) a.sigma[row] = v.n > 0.0 ? sqrt(fmax(v.m2, 0.0) / v.n) : 0.0;
+}
+
+hipError_t launch_moments(int dtype, const MomArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.rows * a.S));
+  if (dtype == 0)
+    hipLaunchKernelGGL(moments_kernel<float>, grid, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL(moments_kernel<uint16_t>, grid, dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace vsel

@@ -417,49 +417,160 @@ __device__ void sort_desc(uint64_t* key, uint32_t* bits, uint32_t n) {
   __syncthreads();
 }
 
-// Temperature sampling with top-p on sorted candidates (one thread, float64):
-// untempered nucleus cut, then the tempered inverse-CDF draw with u.
-__device__ inline void sample_tail(const uint64_t* key, const uint32_t* bits, uint32_t n, float temperature,
-                            float top_p, float u, uint32_t* tok, float* logp) {
-  const double T = temperature;
-  const double z0 = __uint_as_float(bits[0]);
-  uint32_t keep = n;
-  if (top_p < 1.0f) {
-    double Z0 = 0.0;
-    for (uint32_t j = 0; j < n; ++j) Z0 += exp((double)__uint_as_float(bits[j]) - z0);
-    double cum = 0.0;
-    keep = 0;
-    for (uint32_t j = 0; j < n; ++j) {
-      cum += exp((double)__uint_as_float(bits[j]) - z0) / Z0;
-      if (cum >= (double)top_p) {
-        keep = j + 1;
+// The ordered sampler chain on the top-k candidates ("Chapter 21", section
+// 21.7: top_n_sigma against the maximum, top_k, typical_p, then the top_p
+// nucleus, each over the candidate list; min_p among the filters on the
+// untempered distribution and the temperature last, "speculative-acceptance.md",
+// "The rules").  key/bits: the n candidates in (value desc, id asc) order, so
+// candidate 0 holds the row maximum.
+//   top_n_sigma > 0: keep z >= z_0 - n * sigma (a prefix: the list is sorted);
+//   typical_p < 1: p over the candidates, H = -sum p log p; reorder by
+//     |-log p - H| ascending (ties keep value order), keep the shortest prefix
+//     with sum p >= typical_p;
+//   top_p < 1: back to value order, keep the shortest prefix with sum p >= top_p
+//     (p the softmax of the candidates left);
+//   min_p > 0: keep z >= max z + log(min_p) (order unchanged);
+//   then w = exp((z - z_0) / T) and the inverse-CDF draw with u in the current
+//   order.  logp = log(w_j / sum w).
+// All threads call; thread 0 gets tok and logp.  Every sum runs in list order
+// on thread 0 (float64), the exponentials, logarithms and typicality ranks run
+// in parallel.  Scratch: E and S n doubles, ORD and LIST n words (S and ORD
+// only with typical_p < 1).
+struct ChainParams {
+  float temperature, top_p, top_n_sigma, typical_p, min_p;
+};
+__device__ inline void chain_tail(const uint64_t* key, const uint32_t* bits, uint32_t n, const ChainParams& cp,
+                                  double sigma, float u, double* E, double* S, uint32_t* ORD, uint32_t* LIST,
+                                  uint32_t* tok, float* logp) {
+  const int tid = threadIdx.x;
+  __shared__ uint32_t c_cnt;
+  __shared__ double c_Z, c_H;
+  auto zv = [&](uint32_t j) { return (double)__uint_as_float(bits[j]); };
+  const double z0 = zv(0);
+  for (uint32_t j = tid; j < n; j += NT) {
+    E[j] = exp(zv(j) - z0);
+    LIST[j] = j;
+  }
+  if (tid == 0) {
+    uint32_t n1 = n;
+    if (cp.top_n_sigma > 0.0f) {
+      const double thr = z0 - (double)cp.top_n_sigma * sigma;
+      n1 = 1;
+      while (n1 < n && zv(n1) >= thr) ++n1;
+    }
+    c_cnt = n1;
+  }
+  __syncthreads();
+  uint32_t cnt = c_cnt;
+  bool value_order = true;
+  if (cp.typical_p < 1.0f) {
+    if (tid == 0) {
+      double Z = 0.0;
+      for (uint32_t j = 0; j < cnt; ++j) Z += E[j];
+      c_Z = Z;
+    }
+    __syncthreads();
+    const double Z = c_Z;
+    for (uint32_t j = tid; j < cnt; j += NT) S[j] = E[j] > 0.0 ? log(E[j] / Z) : -__builtin_inf();
+    __syncthreads();
+    if (tid == 0) {
+      double H = 0.0;
+      for (uint32_t j = 0; j < cnt; ++j)
+        if (E[j] > 0.0) H -= (E[j] / Z) * S[j];
+      c_H = H;
+    }
+    __syncthreads();
+    const double H = c_H;
+    for (uint32_t j = tid; j < cnt; j += NT) S[j] = E[j] > 0.0 ? fabs(-S[j] - H) : __builtin_inf();
+    __syncthreads();
+    for (uint32_t j = tid; j < cnt; j += NT) {
+      const double sj = S[j];
+      uint32_t r = 0;
+      for (uint32_t i = 0; i < cnt; ++i) r += (S[i] < sj || (S[i] == sj && i < j)) ? 1u : 0u;
+      ORD[r] = j;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double cum = 0.0;
+      uint32_t m = cnt;
+      for (uint32_t r = 0; r < cnt; ++r) {
+        cum += E[ORD[r]] / Z;
+        if (cum >= (double)cp.typical_p) {
+          m = r + 1;
+          break;
+        }
+      }
+      for (uint32_t r = 0; r < m; ++r) LIST[r] = ORD[r];
+      c_cnt = m;
+    }
+    __syncthreads();
+    cnt = c_cnt;
+    value_order = false;
+  }
+  if (tid == 0) {
+    if (cp.top_p < 1.0f) {
+      if (!value_order)  // back to value order: candidate indices ascending
+        for (uint32_t i = 1; i < cnt; ++i) {
+          const uint32_t v = LIST[i];
+          uint32_t j = i;
+          for (; j > 0 && LIST[j - 1] > v; --j) LIST[j] = LIST[j - 1];
+          LIST[j] = v;
+        }
+      value_order = true;
+      double Z = 0.0;
+      for (uint32_t i = 0; i < cnt; ++i) Z += E[LIST[i]];
+      double cum = 0.0;
+      for (uint32_t i = 0; i < cnt; ++i) {
+        cum += E[LIST[i]] / Z;
+        if (cum >= (double)cp.top_p) {
+          cnt = i + 1;
+          break;
+        }
+      }
+    }
+    if (cp.min_p > 0.0f) {
+      double cmax = zv(LIST[0]);
+      if (!value_order)
+        for (uint32_t i = 1; i < cnt; ++i) cmax = fmax(cmax, zv(LIST[i]));
+      const double thr = cmax + log((double)cp.min_p);
+      uint32_t m = 0;
+      for (uint32_t i = 0; i < cnt; ++i)
+        if (zv(LIST[i]) >= thr) LIST[m++] = LIST[i];
+      cnt = m;
+    }
+    c_cnt = cnt;
+  }
+  __syncthreads();
+  cnt = c_cnt;
+  // the tempered weights (E is free now), then the draw in list order
+  const double T = cp.temperature;
+  for (uint32_t i = tid; i < cnt; i += NT) E[i] = exp((zv(LIST[i]) - z0) / T);
+  __syncthreads();
+  if (tid == 0) {
+    double W = 0.0;
+    for (uint32_t i = 0; i < cnt; ++i) W += E[i];
+    const double target = (double)u * W;
+    double c = 0.0;
+    int pick = -1;
+    for (uint32_t i = 0; i < cnt; ++i) {
+      c += E[i];
+      if (target < c) {
+        pick = (int)i;
         break;
       }
     }
-    if (keep == 0) keep = n;
-  }
-  double W = 0.0;
-  for (uint32_t j = 0; j < keep; ++j) W += exp(((double)__uint_as_float(bits[j]) - z0) / T);
-  const double target = (double)u * W;
-  double c = 0.0;
-  int pick = -1;
-  for (uint32_t j = 0; j < keep; ++j) {
-    c += exp(((double)__uint_as_float(bits[j]) - z0) / T);
-    if (target < c) {
-      pick = (int)j;
-      break;
+    if (pick < 0) {
+      for (int i = (int)cnt - 1; i >= 0; --i)
+        if (E[i] > 0.0) {
+          pick = i;
+          break;
+        }
+      if (pick < 0) pick = 0;
     }
+    const uint32_t j = LIST[pick];
+    *tok = ~(uint32_t)key[j];
+    *logp = (float)((zv(j) - z0) / T - log(W));
   }
-  if (pick < 0) {
-    for (int j = (int)keep - 1; j >= 0; --j)
-      if (exp(((double)__uint_as_float(bits[j]) - z0) / T) > 0.0) {
-        pick = j;
-        break;
-      }
-    if (pick < 0) pick = 0;
-  }
-  *tok = ~(uint32_t)key[pick];
-  *logp = (float)(((double)__uint_as_float(bits[pick]) - z0) / T - log(W));
 }
 
 // A value every lane of the wave holds, kept in scalar registers.

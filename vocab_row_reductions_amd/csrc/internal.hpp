@@ -69,9 +69,13 @@ struct TopkArgs {
   uint32_t* out_ids;
   uint32_t* out_argmax;
   float* out_lse;
-  // sampling
+  // sampling: the ordered chain (ChainParams in device.hpp)
   float temperature;
   float top_p;
+  float top_n_sigma;    // 0: off
+  float typical_p;      // 1: off (needs k <= kWaveTopkMax)
+  float min_p;          // 0: off
+  const double* sigma;  // [rows] standard deviation of each row (top_n_sigma > 0)
   const float* u;
   uint32_t* out_token;
   float* out_logp;
@@ -157,6 +161,27 @@ struct DrawArgs {
   int64_t nchunk;       // chunks per row, ceil(V / kChunk); seg_len is a multiple of kChunk
   double* p_w;          // [rows*S] segment masses
   double* p_c;          // [rows*nchunk] chunk masses
+  // the chain's threshold filters over the whole row: elements below
+  // st_max - top_n_sigma * sigma or st_max + log(min_p) weigh nothing
+  float top_n_sigma;    // 0: off
+  float min_p;          // 0: off
+  const double* sigma;  // [rows]
+};
+
+// Mean and standard deviation of each row's values above -inf (float64,
+// shifted sums merged in a fixed order), for the top-n-sigma filter.
+struct MomArgs {
+  const void* x;
+  int64_t ld;
+  int64_t rows;
+  int64_t V;
+  int64_t seg_len;
+  int32_t S;
+  uint32_t* tickets;
+  double* p_n;          // [rows*S] segment partials: count, mean, sum of squared deviations
+  double* p_mean;
+  double* p_m2;
+  double* sigma;        // [rows] output
 };
 
 hipError_t launch_scan(int dtype, bool want_lse, const ScanArgs& a, hipStream_t s);
@@ -172,5 +197,6 @@ int topk_blocks_per_cu(int dtype, bool want_lse, int cap);
 hipError_t launch_spec(const SpecArgs& a, hipStream_t s);
 hipError_t launch_spec_match(const SpecArgs& a, hipStream_t s);
 hipError_t launch_draw_rows(int dtype, const DrawArgs& a, hipStream_t s);
+hipError_t launch_moments(int dtype, const MomArgs& a, hipStream_t s);
 
 }  // namespace vsel

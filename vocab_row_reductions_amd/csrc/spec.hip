@@ -400,19 +400,22 @@ __global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
 // Source of a draw: weight w(x) >= 0 of row element x.
 //   residual: max(p - q, 0), p = exp(z/T - lp), q = exp(d/T - lq)
 //   plain:    exp((z - m) / T), proportional to p (u*W does not see the scale)
+//   (plain only) elements below thr weigh nothing: the sampler chain's
+//   threshold filters over a whole row
 template <typename DT>
 struct DrawSrc {
   const DT* z;
   const float* d;  // null: plain
   double lp, lq, m, T;
   int64_t V;
+  double thr = -__builtin_inf();
   __device__ __forceinline__ float zv(int64_t x) const { return __uint_as_float(gbits_at<DT>(z, x)); }
   __device__ __forceinline__ double w(float zx, float dx) const {
     if (d) {
       const double p = exp((double)zx / T - lp), q = exp((double)dx / T - lq);
       return p > q ? p - q : 0.0;
     }
-    return exp(((double)zx - m) / T);
+    return (double)zx >= thr ? exp(((double)zx - m) / T) : 0.0;
   }
 };
 
@@ -640,6 +643,8 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
   r.m = a.st_max[row];
   r.T = a.T;
   r.V = a.V;
+  if (a.top_n_sigma > 0.0f) r.thr = r.m - (double)a.top_n_sigma * a.sigma[row];
+  if (a.min_p > 0.0f) r.thr = fmax(r.thr, r.m + log((double)a.min_p));
   double* pc = a.p_c + row * a.nchunk;
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
   const double ms = chunk_masses(r, e_begin, e_end, cmw, pc + e_begin / kChunk);

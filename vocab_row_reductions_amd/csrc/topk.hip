@@ -55,7 +55,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   constexpr int E = Elem<DT>::E;
   __shared__ uint64_t s_key[CAP];
   __shared__ uint32_t s_bits[CAP];
-  __shared__ WaveStage stg[NWAVE];
+  __shared__ __attribute__((aligned(16))) WaveStage stg[NWAVE];
   __shared__ SelShared sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -368,12 +368,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         a.out_lse[row] = bad ? __builtin_nanf("")
                              : (r.m == -__builtin_inff() ? -__builtin_inff() : (float)((double)r.m + log(r.s)));
     }
-  } else if (tid == 0) {
+  } else {
+    // the sampler chain; scratch in the halves of the buffers the winners
+    // left free and in the staging area
     uint32_t tok = kFail;
     float lp = __builtin_nanf("");
-    if (!none) sample_tail(okey, obits, n, a.temperature, a.top_p, a.u[row], &tok, &lp);
-    a.out_token[row] = tok;
-    if (a.out_logp) a.out_logp[row] = lp;
+    if (!none && n > 0) {
+      double* E = reinterpret_cast<double*>(okey == s_key ? s_key + CAP / 2 : s_key);
+      uint32_t* LIST = obits == s_bits ? s_bits + CAP / 2 : s_bits;
+      double* Sc = reinterpret_cast<double*>(&stg[0]);
+      uint32_t* ORD = &stg[1].w[0][0];
+      const ChainParams cp{a.temperature, a.top_p, a.top_n_sigma, a.typical_p, a.min_p};
+      chain_tail(okey, obits, n, cp, a.sigma ? a.sigma[row] : 0.0, a.u[row], E, Sc, ORD, LIST, &tok, &lp);
+    }
+    if (tid == 0) {
+      a.out_token[row] = tok;
+      if (a.out_logp) a.out_logp[row] = lp;
+    }
   }
 }
 

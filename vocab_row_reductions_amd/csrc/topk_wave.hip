@@ -760,10 +760,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     if (!none)
       for (uint32_t j = tid; j < n; j += NT) obits[j] = win_bits(okey[j]);
     __syncthreads();
+    // the sampler chain; scratch in the lists' part of s_key and in a
+    // staging area (free now)
+    uint32_t tok = kFail;
+    float lp = __builtin_nanf("");
+    if (!none && n > 0) {
+      double* E = reinterpret_cast<double*>(s_key);
+      double* Sc = E + kWStage;
+      uint32_t* ORD = &area_all[1].w[0][0];
+      uint32_t* LIST = ORD + kWStage;
+      const ChainParams cp{a.temperature, a.top_p, a.top_n_sigma, a.typical_p, a.min_p};
+      chain_tail(okey, obits, n, cp, a.sigma ? a.sigma[row] : 0.0, a.u[row], E, Sc, ORD, LIST, &tok, &lp);
+    }
     if (tid == 0) {
-      uint32_t tok = kFail;
-      float lp = __builtin_nanf("");
-      if (!none && n > 0) sample_tail(okey, obits, n, a.temperature, a.top_p, a.u[row], &tok, &lp);
       a.out_token[row] = tok;
       if (a.out_logp) a.out_logp[row] = lp;
     }
