@@ -146,3 +146,71 @@ def test_support_of_each_filter(g):
     for kw, kept in cases:
         tok, _ = g.vsel.vsel_sample_chain(xd, 1.0, g.dev(u), **kw)
         assert set(np.unique(g.u32(tok)).tolist()) == set(kept.tolist()), kw
+
+
+# ---- top-p over whole rows (top_k = 0): the weighted selections in value order
+ROW_NUCLEUS = [dict(top_p=0.9), dict(top_p=0.95, min_p=0.05), dict(top_p=0.5, top_n_sigma=1.0),
+               dict(top_p=0.99, top_n_sigma=2.0, min_p=0.001), dict(top_p=0.3)]
+
+
+def test_whole_row_top_p_sampling_rows(g, oracle):
+    x, u = W.sampling_rows()
+    compare(g, oracle, x, 0.7, u, max_exempt_frac=0.0, top_p=0.95)
+    compare(g, oracle, x, 1.3, u, max_exempt_frac=0.0, top_p=0.9, top_n_sigma=1.5, min_p=0.01)
+
+
+@pytest.mark.parametrize("ci", range(len(ROW_NUCLEUS)))
+@pytest.mark.parametrize("V", [1, 7, 1000, 70001, 202048])
+def test_whole_row_top_p_shapes(g, oracle, ci, V):
+    x, u = W.sampling_rows(rows=8, vocab=V, seed=500 + V + ci, masked_frac=0.01 if V > 100 else 0.0)
+    # one element: sigma is 0 on both sides, the threshold sits on the maximum exactly
+    compare(g, oracle, x, 0.8, u, ld=V + 5, exact_thresholds=(V == 1), **ROW_NUCLEUS[ci])
+
+
+@pytest.mark.parametrize("sd,top_p", [(0.3, 0.9), (1.0, 0.5), (0.05, 0.999), (3.0, 0.97)])
+def test_whole_row_top_p_large_nuclei(g, oracle, sd, top_p):
+    """Flat rows: the nucleus and the draw window hold far more candidates than
+    one workgroup sorts, so the window is narrowed by key passes."""
+    rng = np.random.default_rng(W.BASE_SEED + int(sd * 100) + int(top_p * 1000))
+    x = rng.normal(0.0, sd, (6, W.V_DECODE)).astype(np.float32)
+    u = rng.random(6, dtype=np.float32)
+    compare(g, oracle, x, 1.0, u, top_p=top_p)
+    compare(g, oracle, x, 0.5, u, top_p=top_p, min_p=0.5)
+
+
+def test_whole_row_top_p_ties(g, oracle):
+    """Equal values: the cut and the draw fall inside runs of ties, which only
+    the ids order (key passes over the id bits)."""
+    V = 7777
+    rng = np.random.default_rng(W.BASE_SEED + 510)
+    x = np.zeros((5, V), np.float32)
+    x[1] = np.round(rng.normal(0, 1, V) * 2) / 2        # a few distinct values
+    x[2, ::3] = 1.0                                     # two values
+    x[3] = rng.normal(0, 1, V).astype(np.float32)
+    x[3, 100:4200] = x[3].max()                         # 4,100 tied maxima
+    x[4, :] = -np.inf
+    x[4, 17] = 0.5                                      # one candidate
+    u = rng.random(5, dtype=np.float32)
+    for T, top_p in ((1.0, 0.9), (0.6, 0.37), (2.0, 0.999)):
+        compare(g, oracle, x, T, u, max_exempt_frac=0.0, top_p=top_p)
+    # the largest tie: the whole 202,048-element row equal
+    xe = np.full((2, W.V_DECODE), 0.25, np.float32)
+    compare(g, oracle, xe, 1.0, np.array([0.3, 0.8], np.float32), max_exempt_frac=0.0, top_p=0.9)
+
+
+@pytest.mark.parametrize("ld_pad", [0, 3])
+def test_whole_row_top_p_bf16(g, oracle, ld_pad):
+    V = 50021
+    x, u = W.sampling_rows(rows=8, vocab=V, seed=520 + ld_pad)
+    compare(g, oracle, W.f32_to_bf16_bits(x), 1.1, u, ld=V + ld_pad, top_p=0.9, min_p=0.02)
+    flat = np.random.default_rng(W.BASE_SEED + 521).normal(0, 0.5, (4, V)).astype(np.float32)
+    compare(g, oracle, W.f32_to_bf16_bits(flat), 1.0, u[:4], ld=V + ld_pad, top_p=0.8)
+
+
+def test_whole_row_top_p_fail_closed(g, oracle):
+    x, u = W.sampling_rows(rows=4, vocab=3000, seed=530)
+    x = x.copy()
+    x[1, 17] = np.nan
+    x[2, :] = -np.inf
+    gt, _ = compare(g, oracle, x, 0.8, u, top_p=0.9, top_n_sigma=1.0)
+    assert gt[1] == g.SENT and gt[2] == g.SENT and gt[0] != g.SENT

@@ -281,6 +281,29 @@ size_t sample_ws_bytes(int64_t rows, int64_t vocab, int64_t k) {
 struct MomWs {
   size_t tickets, sigma, p_n, p_mean, p_m2;
 };
+// The whole-row nucleus passes (top_k = 0, top_p < 1).
+struct NucWs {
+  size_t tickets, h0w, h0c, hTw, hTc, lkey, lbits, lcnt, p_z0, p_a, p_at, p_a2, plan;
+};
+NucWs nucleus_layout(Layout& L, int64_t rows, const Plan& p) {
+  NucWs w{};
+  const size_t R = (size_t)rows, n = (size_t)(rows * p.S);
+  w.tickets = L.take(R * 3 * 4);
+  w.h0w = L.take(R * kNucBins * 8);
+  w.h0c = L.take(R * kNucBins * 4);
+  w.hTw = L.take(R * kNucBins * 8);
+  w.hTc = L.take(R * kNucBins * 4);
+  w.lkey = L.take(R * kNucCap * 8);
+  w.lbits = L.take(R * kNucCap * 4);
+  w.lcnt = L.take(R * 4);
+  w.p_z0 = L.take(n * 8);
+  w.p_a = L.take(n * 8);
+  w.p_at = L.take(n * 8);
+  w.p_a2 = L.take(n * 8);
+  w.plan = L.take(R * sizeof(NucPlan));
+  return w;
+}
+
 MomWs moments_layout(Layout& L, int64_t rows, const Plan& p) {
   MomWs w{};
   w.tickets = L.take((size_t)rows * 4);
@@ -289,6 +312,21 @@ MomWs moments_layout(Layout& L, int64_t rows, const Plan& p) {
   w.p_n = L.take(n * 8);
   w.p_mean = L.take(n * 8);
   w.p_m2 = L.take(n * 8);
+  return w;
+}
+
+// The chain's regions after the sampler's own workspace: the row moments,
+// and for top_k = 0 the nucleus passes.
+struct ChainWs {
+  MomWs mom;
+  NucWs nuc;
+  bool has_nuc;
+};
+ChainWs chain_layout(Layout& L, int64_t rows, int64_t vocab, int32_t top_k) {
+  ChainWs w{};
+  w.mom = moments_layout(L, rows, plan_scan_bound(rows, vocab));
+  w.has_nuc = top_k == 0;
+  if (w.has_nuc) w.nuc = nucleus_layout(L, rows, plan_scan_bound(rows, vocab));
   return w;
 }
 
@@ -352,7 +390,7 @@ size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int3
       const size_t base = sample_ws_bytes(rows, vocab, k);
       if (base == 0) return 0;
       L.off = align_up(base);
-      moments_layout(L, rows, plan_scan_bound(rows, vocab));
+      chain_layout(L, rows, vocab, k);
       return L.off;
     }
     case VSEL_OP_SPEC_ACCEPT: {
@@ -459,7 +497,7 @@ vsel_status vsel_topk(const void* logits, int dtype, int64_t rows, int64_t vocab
 // with top_n_sigma > 0 their pass runs first.
 static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                                float temperature, int32_t top_k, float top_p, float top_n_sigma, float typical_p,
-                               float min_p, const MomWs* mom, const float* u, uint32_t* out_token,
+                               float min_p, const ChainWs* cw, const float* u, uint32_t* out_token,
                                float* out_logprob, void* ws, size_t ws_bytes, void* stream) {
   if (!logits || !u || !out_token || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
       !aligned_elem(logits, elem_size(dtype)))
@@ -467,9 +505,9 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
   if (!(temperature >= 0.0f) || std::isinf(temperature) || top_k < 0 || top_k > VSEL_K_MAX ||
       !(top_p > 0.0f && top_p <= 1.0f))
     return VSEL_EINVAL;
-  if (top_k == 0 && (top_p < 1.0f || typical_p < 1.0f)) return VSEL_EINVAL;
+  if (top_k == 0 && (typical_p < 1.0f || (top_p < 1.0f && !(cw && cw->has_nuc)))) return VSEL_EINVAL;
   if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
-  if (top_n_sigma > 0.0f && !mom) return VSEL_EINVAL;
+  if (top_n_sigma > 0.0f && !cw) return VSEL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   const bool greedy = temperature == 0.0f || top_k == 1;
 
@@ -478,16 +516,17 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
     const Plan p = plan_scan(dtype, false, rows, vocab);
     MomArgs m{};
     m.x = logits;
+    m.vec = aligned16(logits, ld, elem_size(dtype)) ? 1 : 0;
     m.ld = ld;
     m.rows = rows;
     m.V = vocab;
     m.seg_len = p.seg_len;
     m.S = p.S;
-    m.tickets = at<uint32_t>(ws, mom->tickets);
-    m.p_n = at<double>(ws, mom->p_n);
-    m.p_mean = at<double>(ws, mom->p_mean);
-    m.p_m2 = at<double>(ws, mom->p_m2);
-    m.sigma = at<double>(ws, mom->sigma);
+    m.tickets = at<uint32_t>(ws, cw->mom.tickets);
+    m.p_n = at<double>(ws, cw->mom.p_n);
+    m.p_mean = at<double>(ws, cw->mom.p_mean);
+    m.p_m2 = at<double>(ws, cw->mom.p_m2);
+    m.sigma = at<double>(ws, cw->mom.sigma);
     if (launch_moments(dtype, m, s) != hipSuccess) return VSEL_EDEVICE;
     sigma = m.sigma;
   }
@@ -525,6 +564,44 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
     a.st_bad = at<uint32_t>(ws, w.st.bad);
     hipError_t e = launch_scan(dtype, false, a, s);
     if (e != hipSuccess) return VSEL_EDEVICE;
+    if (top_p < 1.0f) {
+      // the nucleus over the whole row, then the draw in value order
+      NucArgs n{};
+      n.x = logits;
+      n.ld = ld;
+      n.rows = rows;
+      n.V = vocab;
+      n.st_max = a.st_max;
+      n.st_bad = a.st_bad;
+      n.sigma = sigma;
+      n.top_n_sigma = top_n_sigma;
+      n.top_p = top_p;
+      n.min_p = min_p;
+      n.T = temperature;
+      n.u = u;
+      n.out_token = out_token;
+      n.out_logp = out_logprob;
+      // the nucleus passes keep two workgroups per CU resident (LDS bound)
+      const Plan pn = plan_segments(rows, vocab, 0, 2 * (int64_t)device_cus(), kCapLarge);
+      n.seg_len = pn.seg_len;
+      n.S = pn.S;
+      n.vec = a.vec1;
+      const NucWs& nw = cw->nuc;
+      n.tickets = at<uint32_t>(ws, nw.tickets);
+      n.h0w = at<double>(ws, nw.h0w);
+      n.h0c = at<uint32_t>(ws, nw.h0c);
+      n.hTw = at<double>(ws, nw.hTw);
+      n.hTc = at<uint32_t>(ws, nw.hTc);
+      n.lkey = at<uint64_t>(ws, nw.lkey);
+      n.lbits = at<uint32_t>(ws, nw.lbits);
+      n.lcnt = at<uint32_t>(ws, nw.lcnt);
+      n.p_z0 = at<double>(ws, nw.p_z0);
+      n.p_a = at<double>(ws, nw.p_a);
+      n.p_at = at<double>(ws, nw.p_at);
+      n.p_a2 = at<double>(ws, nw.p_a2);
+      n.plan = at<NucPlan>(ws, nw.plan);
+      return launched(launch_row_nucleus(dtype, n, s));
+    }
     DrawArgs d{};
     d.x = logits;
     d.ld = ld;
@@ -583,15 +660,15 @@ vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64
       !(top_p > 0.0f && top_p <= 1.0f) || !(top_n_sigma >= 0.0f) || std::isinf(top_n_sigma) ||
       !(typical_p > 0.0f && typical_p <= 1.0f) || !(min_p >= 0.0f && min_p <= 1.0f))
     return VSEL_EINVAL;
-  if (top_k == 0 && (top_p < 1.0f || typical_p < 1.0f)) return VSEL_EINVAL;
+  if (top_k == 0 && typical_p < 1.0f) return VSEL_EINVAL;
   if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
   const size_t base = sample_ws_bytes(rows, vocab, top_k);
   if (base == 0) return VSEL_EINVAL;
   Layout L;
   L.off = align_up(base);
-  const MomWs m = moments_layout(L, rows, plan_scan_bound(rows, vocab));
+  const ChainWs cw = chain_layout(L, rows, vocab, top_k);
   if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
-  return sample_impl(logits, dtype, rows, vocab, ld, temperature, top_k, top_p, top_n_sigma, typical_p, min_p, &m,
+  return sample_impl(logits, dtype, rows, vocab, ld, temperature, top_k, top_p, top_n_sigma, typical_p, min_p, &cw,
                      u, out_token, out_logprob, ws, ws_bytes, stream);
 }
 

@@ -34,7 +34,7 @@ __device__ __forceinline__ Mom wave_mom(Mom v) {
   return v;  // lane 0
 }
 
-template <typename DT>
+template <typename DT, bool VEC>
 __global__ __launch_bounds__(NT) void moments_kernel(MomArgs a) {
   __shared__ SelShared sh;
   __shared__ double wn[NWAVE], wmean[NWAVE], wm2[NWAVE];
@@ -45,17 +45,17 @@ __global__ __launch_bounds__(NT) void moments_kernel(MomArgs a) {
   if (row >= a.rows) return;
   const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
-  // this thread's values: e_begin + tid, + NT, ... (in index order)
+  // this thread's values, in the order the tiles give them
   double n = 0.0, s1 = 0.0, s2 = 0.0, r = 0.0;
-  for (int64_t x = e_begin + tid; x < e_end; x += NT) {
-    const float z = __uint_as_float(gbits_at<DT>(xr, x));
-    if (!(z > -__builtin_inff())) continue;  // -inf (a mask) takes no part; NaN rows fail closed elsewhere
+  for_each_elem<DT, 4, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t) {
+    const float z = __uint_as_float(bits);
+    if (!(z > -__builtin_inff())) return;  // -inf (a mask) takes no part; NaN rows fail closed elsewhere
     if (n == 0.0) r = z;
     const double d = (double)z - r;
     n += 1.0;
     s1 += d;
     s2 += d * d;
-  }
+  });
   Mom v{n, 0.0, 0.0};
   if (n > 0.0) v = Mom{n, r + s1 / n, s2 - s1 * s1 / n};
   v = wave_mom(v);
@@ -90,10 +90,17 @@ __global__ __launch_bounds__(NT) void moments_kernel(MomArgs a) {
 
 hipError_t launch_moments(int dtype, const MomArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.rows * a.S));
-  if (dtype == 0)
-    hipLaunchKernelGGL(moments_kernel<float>, grid, dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL(moments_kernel<uint16_t>, grid, dim3(NT), 0, s, a);
+  if (dtype == 0) {
+    if (a.vec)
+      hipLaunchKernelGGL((moments_kernel<float, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((moments_kernel<float, false>), grid, dim3(NT), 0, s, a);
+  } else {
+    if (a.vec)
+      hipLaunchKernelGGL((moments_kernel<uint16_t, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((moments_kernel<uint16_t, false>), grid, dim3(NT), 0, s, a);
+  }
   return hipGetLastError();
 }
 

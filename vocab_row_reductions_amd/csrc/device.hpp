@@ -142,6 +142,25 @@ __device__ __forceinline__ void walk_groups(const DT* __restrict__ xr, int64_t e
   }
 }
 
+// Every element of [e_begin, e_end) of a row: whole 16-byte groups through
+// walk_groups (NG per lane per tile), then the last few elements one per
+// lane.  fn(bits, i) gets the element's float32 bits and index; in a tile
+// that ends early, padding elements (-inf, at indices past e_end) are passed
+// too.  All threads call it the same number of times per tile.
+template <typename DT, int NG, bool VEC, class Fn>
+__device__ __forceinline__ void for_each_elem(const DT* __restrict__ xr, int64_t e_begin, int64_t e_end, Fn&& fn) {
+  constexpr int E = Elem<DT>::E;
+  const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
+  walk_groups<DT, NG, VEC>(xr, e_begin, e_full, [&](const auto& g, int64_t t0) {
+    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+#pragma unroll
+    for (int j = 0; j < NGP; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) fn(gbits<DT>(g[j], e), t0 + (int64_t)((j * NT + (int)threadIdx.x) * E + e));
+  });
+  for (int64_t i = e_full + threadIdx.x; i < e_end; i += NT) fn(gbits_at<DT>(xr, i), i);
+}
+
 // Order-preserving unsigned image of a float's bits: larger float -> larger
 // key; -0.0 is folded onto +0.0 first so the two tie as floats do.
 __device__ __forceinline__ uint32_t fkey(uint32_t u) {

@@ -172,6 +172,7 @@ struct DrawArgs {
 // shifted sums merged in a fixed order), for the top-n-sigma filter.
 struct MomArgs {
   const void* x;
+  int32_t vec;          // rows start and stride 16-byte aligned (segments are multiples of 8 elements)
   int64_t ld;
   int64_t rows;
   int64_t V;
@@ -182,6 +183,50 @@ struct MomArgs {
   double* p_mean;
   double* p_m2;
   double* sigma;        // [rows] output
+};
+
+// The sampler chain over whole rows with a top-p cut: three passes over
+// (row, segment) workgroups (a guide histogram, the cut window, the draw
+// window).  Histograms, window counters and tickets are zero between calls.
+constexpr int kNucBins = 4096;     // guide bins per row
+constexpr int kNucCap = 4096;      // window candidates per row
+struct NucPlan {                   // per row, written by the last workgroup of a pass
+  uint32_t state;                  // 0 cut placed, 1 draw pass needed, 2 done, 3/4 row/draw left to one workgroup
+  uint32_t b_lo, b_hi;             // cut window (untempered guide bins)
+  uint32_t c_lo, c_hi;             // draw window (tempered guide bins, above the cut window)
+  uint32_t pad;
+  double z0;                       // exact candidate mass, untempered
+  double wt;                       // exact kept mass, tempered
+  uint64_t kfin;                   // smallest kept composite key
+};
+struct NucArgs {
+  const void* x;
+  int64_t ld;
+  int64_t rows;
+  int64_t V;
+  int64_t seg_len;         // a multiple of 8 elements
+  int32_t S;
+  int32_t vec;             // rows start and stride 16-byte aligned
+  const float* st_max;     // [rows] row maxima (scan)
+  const uint32_t* st_bad;  // [rows] fail-closed rows (scan)
+  const double* sigma;     // [rows] standard deviations (top_n_sigma > 0)
+  float top_n_sigma, top_p, min_p, T;
+  const float* u;
+  uint32_t* out_token;
+  float* out_logp;
+  uint32_t* tickets;       // [rows*3]
+  double* h0w;             // [rows*kNucBins] untempered guide masses
+  uint32_t* h0c;           // [rows*kNucBins] counts
+  double* hTw;             // [rows*kNucBins] tempered guide masses (above the cut window)
+  uint32_t* hTc;
+  uint64_t* lkey;          // [rows*kNucCap] window candidates
+  uint32_t* lbits;
+  uint32_t* lcnt;          // [rows]
+  double* p_z0;            // [rows*S] segment partials
+  double* p_a;
+  double* p_at;
+  double* p_a2;
+  NucPlan* plan;           // [rows]
 };
 
 hipError_t launch_scan(int dtype, bool want_lse, const ScanArgs& a, hipStream_t s);
@@ -198,5 +243,6 @@ hipError_t launch_spec(const SpecArgs& a, hipStream_t s);
 hipError_t launch_spec_match(const SpecArgs& a, hipStream_t s);
 hipError_t launch_draw_rows(int dtype, const DrawArgs& a, hipStream_t s);
 hipError_t launch_moments(int dtype, const MomArgs& a, hipStream_t s);
+hipError_t launch_row_nucleus(int dtype, const NucArgs& a, hipStream_t s);
 
 }  // namespace vsel

@@ -1,0 +1,870 @@
+// nucleus.hip -- the sampler chain over whole rows with a top-p cut
+// ("Chapter 21", section 21.7: top_n_sigma, then the top_p nucleus over the
+// candidate list; min_p among the untempered filters and the temperature last,
+// "speculative-acceptance.md", "The rules"), for top_k = 0: the candidates are
+// the whole row, ordered by (value desc, id asc).
+//
+// Both decisions of a row are weighted selections in that order:
+//   1. the nucleus cut: the first candidate at which the cumulative untempered
+//      mass exp(z - max) reaches top_p times the candidates' total;
+//   2. the draw: among the kept candidates (the nucleus, narrowed by min_p),
+//      the first at which the cumulative tempered mass exp((z - max) / T)
+//      passes u times the kept total.
+// The row is never sorted.  A guide histogram of the masses (float32
+// exponentials summed in float64, bins of equal steps of (max - z) / T) places
+// a window of candidates around the crossing, wider than the guide's error.
+// An exact pass then sums the float64 masses above the window and the totals
+// in a fixed order and gathers the window's candidates; they are sorted in LDS
+// and walked in order.
+//
+// Three launches, each over (row, segment) workgroups, the last workgroup of
+// a row finishing it:
+//   nuc_hist:    guide histogram of the untempered masses and their exact
+//                total; the last workgroup places the cut window (from the
+//                top of the row when everything above the crossing fits LDS).
+//   nuc_collect: the exact mass above the window and the window's candidates,
+//                and the guide histogram and exact mass of the tempered
+//                weights above it; the last workgroup cuts, applies min_p,
+//                totals the kept mass and draws when the draw falls in the
+//                window, else places the draw window.
+//   nuc_draw:    for the remaining rows, the same over the draw window.
+// A window with more candidates than LDS holds is left to the row's last
+// workgroup alone, which narrows it by guide passes over equal steps of the
+// composite key (value, then id); these also separate tied values.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace vsel {
+
+constexpr int kNB = kNucBins;          // guide bins of the parallel passes
+constexpr int kFbNB = 2048;            // guide bins of the one-workgroup refinement
+constexpr double kSpan = 40.0;         // (max - z) / T in [0, 40) in equal steps; lower values share the last bin
+constexpr uint32_t kCapW = kNucCap;    // window candidates sorted in LDS
+constexpr double kGuard = 1e-5;        // window half-width around a target, relative to the total mass
+constexpr int kMaxLevels = 12;         // key passes (each narrows the key range by at least 2^11 / 3)
+constexpr uint32_t kRun = kCapW / NT;  // sorted window candidates walked per thread
+constexpr int kNG = 4;                 // 16-byte groups per lane per tile
+
+// e^x in float64 for x <= 0 (0 below -745).  x = k ln2/64 + r, the reduction
+// with ln2/64 split in two (the high part has 25 significant bits, so k * hi
+// is exact for the k that occur); e^r by its Taylor series to r^6 (|r| <=
+// ln2/128, so the truncation is below 1e-19); then 2^(k/64) as a table entry
+// 2^((k mod 64)/64) and an exponent shift.  A few units in the last place,
+// like a library exp.
+constexpr double kL64Hi = 0x1.62e42f0000000p-7;   // ln2/64, high part
+constexpr double kL64Lo = 0x1.df473de6af279p-32;  // ln2/64 - kL64Hi
+constexpr double kInvL64 = 0x1.71547652b82fep+6;  // 64/ln2
+__device__ __forceinline__ double exp_le0(double x, const double* e2) {
+  const double xc = fmax(x, -745.0);
+  const double k = rint(xc * kInvL64);
+  const double r = fma(-k, kL64Lo, fma(-k, kL64Hi, xc));
+  double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ki = (int)k;
+  const double v = ldexp(e2[ki & 63] * p, ki >> 6);
+  return x < -745.0 ? 0.0 : v;
+}
+
+// The table 2^(j/64), j = 0..63, in LDS (all threads call).
+__device__ __forceinline__ void init_e2(double* e2) {
+  if (threadIdx.x < 64) e2[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+  __syncthreads();
+}
+
+// The candidates of one selection and their weights.
+struct NucSet {
+  double m;           // the row maximum
+  double thr;         // candidates have z >= thr (and z > -inf)
+  uint64_t kfloor;    // ... and composite key >= kfloor
+  double T;           // weight exp((z - m) / T)
+  const double* e2;   // the exp table
+  __device__ __forceinline__ bool in(float z, uint64_t K) const {
+    return z > -__builtin_inff() && (double)z >= thr && K >= kfloor;
+  }
+  __device__ __forceinline__ double x(float z) const { return T == 1.0 ? (double)z - m : ((double)z - m) / T; }
+  __device__ __forceinline__ double w(float z) const { return exp_le0(x(z), e2); }
+  __device__ __forceinline__ float gw(float z) const {
+    return __builtin_amdgcn_exp2f((float)(x(z) * 1.4426950408889634));
+  }
+  // first-level bin: equal steps of (m - z) / T over [0, kSpan)
+  template <int NB>
+  __device__ __forceinline__ uint32_t bin(float z) const {
+    const double d = -x(z);
+    return d >= kSpan ? (uint32_t)(NB - 1) : (uint32_t)(d * (NB / kSpan));
+  }
+};
+
+// ---------------------------------------------------------------- block helpers
+struct NucRed {
+  double rd[NWAVE * 2];
+  uint64_t rk[NWAVE * 2];
+  uint32_t ru[NWAVE];
+  uint32_t b_lo, b_hi, cnt, cnt_top;  // pick_bins results
+  uint32_t n;
+  uint64_t ksel;
+  uint32_t bsel;
+};
+
+// Fixed-order sum over the workgroup (every thread gets it).
+__device__ __forceinline__ double nuc_sum(NucRed& r, double v, int slot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_f64(v);
+  __syncthreads();
+  if (lane == 0) r.rd[slot * NWAVE + wave] = v;
+  __syncthreads();
+  double t = r.rd[slot * NWAVE];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) t += r.rd[slot * NWAVE + q];
+  return t;
+}
+
+// Exclusive prefix of one value per thread, in thread order (fixed order).
+__device__ __forceinline__ double block_excl_scan_f64(NucRed& r, double v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double incl = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) r.rd[wave] = incl;
+  __syncthreads();
+  double off = 0.0;
+  for (int q = 0; q < wave; ++q) off += r.rd[q];
+  return off + incl - v;
+}
+
+__device__ __forceinline__ uint32_t block_min_u32(NucRed& r, uint32_t v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int d = 1; d < 64; d <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d));
+  __syncthreads();
+  if (lane == 0) r.ru[wave] = v;
+  __syncthreads();
+  uint32_t o = r.ru[0];
+  for (int q = 1; q < NWAVE; ++q) o = min(o, r.ru[q]);
+  return o;
+}
+
+__device__ __forceinline__ int block_max_i32(NucRed& r, int v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int d = 1; d < 64; d <<= 1) v = max(v, __shfl_xor(v, d));
+  __syncthreads();
+  if (lane == 0) r.ru[wave] = (uint32_t)v;
+  __syncthreads();
+  int o = (int)r.ru[0];
+  for (int q = 1; q < NWAVE; ++q) o = max(o, (int)r.ru[q]);
+  return o;
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(NucRed& r, uint32_t v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int d = 1; d < 64; d <<= 1) v += (uint32_t)__shfl_xor((int)v, d);
+  __syncthreads();
+  if (lane == 0) r.ru[wave] = v;
+  __syncthreads();
+  uint32_t o = 0;
+  for (int q = 0; q < NWAVE; ++q) o += r.ru[q];
+  return o;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) { return ~wave_max_u64(~v); }
+
+// Wave 0 chooses the bins [b_lo, b_hi] of nb (<= NB) whose cumulative guide
+// mass (after `base`, the mass above bin 0) first reaches t0 and t1; it counts
+// their candidates (cnt) and those of bins [0, b_hi] (cnt_top).  A target
+// past the last bin takes the last non-empty bin.  All threads call.
+template <int NB>
+__device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int nb, double base, double t0,
+                          double t1) {
+  const int lane = threadIdx.x & 63;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    constexpr int PER = NB / 64;
+    double ls = 0.0;
+    int lastnz = -1;
+#pragma unroll 8
+    for (int q = 0; q < PER; ++q) {
+      const int b = lane * PER + q;
+      if (b < nb) {
+        ls += hw[b];
+        if (hc[b]) lastnz = b;
+      }
+    }
+    double incl = ls;
+    for (int d = 1; d < 64; d <<= 1) {
+      const double o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    const double excl = incl - ls;
+    int last = lastnz;
+    for (int d = 1; d < 64; d <<= 1) last = max(last, __shfl_xor(last, d));
+    int b_sel[2];
+    const double tt[2] = {t0, t1};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint64_t hit = __ballot(base + incl >= tt[q]);
+      int b = last < 0 ? 0 : last;
+      if (hit) {
+        const int L = __builtin_ctzll(hit);
+        int cand = 0x7FFFFFFF;
+        if (lane == L) {
+          double c = base + excl;
+#pragma unroll 4
+          for (int j = 0; j < PER; ++j) {
+            const int bb = L * PER + j;
+            if (bb >= nb) break;
+            c += hw[bb];
+            if (c >= tt[q]) {
+              cand = bb;
+              break;
+            }
+          }
+          if (cand == 0x7FFFFFFF) cand = min(L * PER + PER - 1, nb - 1);
+        }
+        b = __shfl(cand, L);
+      }
+      b_sel[q] = b;
+    }
+    const int lo = b_sel[0], hi = max(b_sel[0], b_sel[1]);
+    uint32_t c = 0, ct = 0;
+#pragma unroll 8
+    for (int q = 0; q < PER; ++q) {
+      const int b = lane * PER + q;
+      if (b <= hi && b < nb) {
+        ct += hc[b];
+        if (b >= lo) c += hc[b];
+      }
+    }
+    for (int d = 1; d < 64; d <<= 1) {
+      c += __shfl_xor(c, d);
+      ct += __shfl_xor(ct, d);
+    }
+    if (lane == 0) {
+      r.b_lo = (uint32_t)lo;
+      r.b_hi = (uint32_t)hi;
+      r.cnt = c;
+      r.cnt_top = ct;
+    }
+  }
+  __syncthreads();
+}
+
+// Walk n sorted candidates (bits) with weights S.w from a cumulative mass A:
+// the first index whose cumulative c satisfies c >= t (strict = false) or
+// t < c (strict = true); none: the last with a positive weight (or the last).
+// Each thread sums a run of kRun candidates in order, the runs are prefixed
+// in a fixed order, and every thread walks its own run.  All threads call.
+__device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const NucSet& S, double A, double t,
+                                bool strict) {
+  const uint32_t j0 = threadIdx.x * kRun;
+  double wl[kRun];
+  double run = 0.0;
+#pragma unroll
+  for (uint32_t q = 0; q < kRun; ++q) {
+    wl[q] = (j0 + q < n) ? S.w(__uint_as_float(bits[j0 + q])) : 0.0;
+    run += wl[q];
+  }
+  double c = A + block_excl_scan_f64(r, run);
+  uint32_t first = 0xFFFFFFFFu;
+  int lastpos = -1;
+#pragma unroll
+  for (uint32_t q = 0; q < kRun; ++q) {
+    if (j0 + q < n) {
+      c += wl[q];
+      if (wl[q] > 0.0) lastpos = (int)(j0 + q);
+      if (first == 0xFFFFFFFFu && (strict ? (t < c) : (c >= t))) first = j0 + q;
+    }
+  }
+  first = block_min_u32(r, first);
+  lastpos = block_max_i32(r, lastpos);
+  if (first != 0xFFFFFFFFu) return first;
+  if (lastpos >= 0) return (uint32_t)lastpos;
+  return n > 0 ? n - 1 : 0;
+}
+
+// Fixed-order sum of S.w over the first n sorted candidates.
+__device__ double sum_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const NucSet& S) {
+  const uint32_t j0 = threadIdx.x * kRun;
+  double run = 0.0;
+  for (uint32_t q = 0; q < kRun; ++q)
+    if (j0 + q < n) run += S.w(__uint_as_float(bits[j0 + q]));
+  return nuc_sum(r, run, 0);
+}
+
+// Key range [klo, khi] split into at most kFbNB bins of 2^shift keys from the top.
+__device__ __forceinline__ int key_shift(uint64_t klo, uint64_t khi) {
+  const uint64_t w = khi - klo;
+  const int bits = w == 0 ? 0 : 64 - __builtin_clzll(w);
+  return bits > 11 ? bits - 11 : 0;
+}
+
+// ---------------------------------------------------------------- one-workgroup selection
+struct FbShared {
+  double hw[kFbNB];      // guide mass per bin; while sorting, the window's element bits (uint32)
+  uint32_t hc[kFbNB];
+  uint64_t list[kCapW];
+};
+
+struct SelOut {
+  uint64_t key;   // the selected candidate
+  uint32_t bits;  // its element bits
+  double tot;     // the candidates' total mass (float64, fixed order)
+};
+
+// The weighted selection over the candidates of `S` by one workgroup alone:
+// the first candidate in (value desc, id asc) order whose cumulative weight c
+// satisfies c >= frac * W (strict = false) or frac * W < c (strict = true), W
+// the candidates' total mass.  Guide passes narrow a window until its
+// candidates fit LDS (first by steps of (m - z) / T, then by key ranges), then
+// one exact pass sums the mass above it.  All threads call; all get the result.
+template <typename DT, bool VEC>
+__device__ SelOut wg_select(FbShared& s, NucRed& r, const DT* __restrict__ xr, int64_t V, const NucSet& S,
+                            double frac, bool strict) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  for (int b = tid; b < kFbNB; b += NT) {
+    s.hw[b] = 0.0;
+    s.hc[b] = 0u;
+  }
+  __syncthreads();
+  double g = 0.0;
+  for_each_elem<DT, kNG, VEC>(xr, 0, V, [&](uint32_t bits, int64_t i) {
+    const float z = __uint_as_float(bits);
+    if (S.in(z, comp_key(bits, (uint32_t)i))) {
+      const float gw = S.gw(z);
+      const uint32_t b = S.bin<kFbNB>(z);
+      __hip_atomic_fetch_add(&s.hw[b], (double)gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(&s.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      g += gw;
+    }
+  });
+  __syncthreads();
+  const double gtot = nuc_sum(r, g, 0);
+  pick_bins<kFbNB>(r, s.hw, s.hc, kFbNB, 0.0, frac * gtot - kGuard * gtot, frac * gtot + kGuard * gtot);
+  bool by_key = false;  // window by first-level bins [b_lo, b_hi], else by keys [klo, khi]
+  const uint32_t b_lo = r.b_lo, b_hi = r.b_hi;
+  uint64_t klo = 0, khi = 0;
+  double tot = 0.0, A = 0.0;
+  uint32_t* lbits = reinterpret_cast<uint32_t*>(s.hw);
+  for (int level = 0;; ++level) {
+    // exact pass: the total and the mass above the window in float64 (fixed
+    // order), the window's candidates into LDS, the window's key range
+    __syncthreads();
+    if (tid == 0) r.n = 0u;
+    __syncthreads();
+    double t_l = 0.0, a_l = 0.0;
+    uint64_t kmin = ~0ull, kmax = 0ull;
+    for_each_elem<DT, kNG, VEC>(xr, 0, V, [&](uint32_t bits, int64_t i) {
+      const float z = __uint_as_float(bits);
+      const uint64_t K = comp_key(bits, (uint32_t)i);
+      if (!S.in(z, K)) return;
+      const double w = S.w(z);
+      t_l += w;
+      bool above, inw;
+      if (by_key) {
+        above = K > khi;
+        inw = !above && K >= klo;
+      } else {
+        const uint32_t b = S.bin<kFbNB>(z);
+        above = b < b_lo;
+        inw = !above && b <= b_hi;
+      }
+      if (above) a_l += w;
+      if (inw) {
+        kmin = min(kmin, K);
+        kmax = max(kmax, K);
+        const uint32_t p = atomicAdd(&r.n, 1u);
+        if (p < kCapW) {
+          s.list[p] = K;
+          lbits[p] = bits;
+        }
+      }
+    });
+    tot = nuc_sum(r, t_l, 0);
+    A = nuc_sum(r, a_l, 1);
+    {
+      const int lane = tid & 63, wave = tid >> 6;
+      kmin = wave_min_u64(kmin);
+      kmax = wave_max_u64(kmax);
+      if (lane == 0) {
+        r.rk[wave] = kmin;
+        r.rk[NWAVE + wave] = kmax;
+      }
+      __syncthreads();
+      kmin = r.rk[0];
+      kmax = r.rk[NWAVE];
+#pragma unroll
+      for (int q = 1; q < NWAVE; ++q) {
+        kmin = min(kmin, r.rk[q]);
+        kmax = max(kmax, r.rk[NWAVE + q]);
+      }
+    }
+    if (r.n <= kCapW || level == kMaxLevels) break;
+    // too many: narrow the window by a guide pass over its key range
+    klo = kmin;
+    khi = kmax;
+    by_key = true;
+    const int sh = key_shift(klo, khi);
+    __syncthreads();
+    for (int b = tid; b < kFbNB; b += NT) {
+      s.hw[b] = 0.0;
+      s.hc[b] = 0u;
+    }
+    __syncthreads();
+    for_each_elem<DT, kNG, VEC>(xr, 0, V, [&](uint32_t bits, int64_t i) {
+      const float z = __uint_as_float(bits);
+      const uint64_t K = comp_key(bits, (uint32_t)i);
+      if (!S.in(z, K) || K > khi || K < klo) return;
+      const uint32_t b = (uint32_t)((khi - K) >> sh);
+      __hip_atomic_fetch_add(&s.hw[b], (double)S.gw(z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(&s.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    });
+    __syncthreads();
+    const int nb = (int)((khi - klo) >> sh) + 1;
+    pick_bins<kFbNB>(r, s.hw, s.hc, nb, A, frac * tot - kGuard * tot, frac * tot + kGuard * tot);
+    // the chosen bins as a key range
+    const uint64_t c_lo = r.b_lo, c_hi = r.b_hi;
+    const uint64_t top = c_lo << sh;                         // offset of the window's top below khi
+    const uint64_t bot = (c_hi << sh) + ((1ull << sh) - 1);  // offset of its lowest key (may pass klo)
+    const uint64_t khi2 = khi - top;
+    klo = (bot >= khi - klo) ? klo : khi - bot;
+    khi = khi2;
+  }
+  const uint32_t n = min(r.n, kCapW);
+  sort_desc<kCapW>(s.list, lbits, n);
+  const uint32_t j = walk_sorted(r, lbits, n, S, A, frac * tot, strict);
+  if (tid == 0) {
+    r.ksel = s.list[j];
+    r.bsel = lbits[j];
+  }
+  __syncthreads();
+  const SelOut o{r.ksel, r.bsel, tot};
+  __syncthreads();
+  return o;
+}
+
+// Smallest composite key of an element with value >= thr.  (Keys of
+// consecutive floats differ by one, so the next float up is key + 1.)
+__device__ __forceinline__ uint64_t key_floor(double thr) {
+  const float v = (float)thr;
+  uint32_t k = fkey(__float_as_uint(v));
+  if ((double)v < thr) k += 1u;
+  return (uint64_t)k << 32;
+}
+
+// ---------------------------------------------------------------- the parallel passes
+struct NucCommon {
+  int64_t e_begin, e_end;
+  double m, thr;
+  uint64_t kmp;  // smallest key min_p keeps (0: min_p off)
+};
+
+__device__ __forceinline__ NucCommon nuc_common(const NucArgs& a, int64_t row, int seg) {
+  NucCommon c;
+  c.e_begin = (int64_t)seg * a.seg_len;
+  c.e_end = min(a.V, c.e_begin + a.seg_len);
+  c.m = a.st_max[row];
+  c.thr = a.top_n_sigma > 0.0f ? c.m - (double)a.top_n_sigma * a.sigma[row] : -__builtin_inf();
+  c.kmp = a.min_p > 0.0f ? key_floor(c.m + log((double)a.min_p)) : 0ull;
+  return c;
+}
+
+// The whole row by one workgroup: the cut, min_p, the draw.
+template <typename DT, bool VEC>
+__device__ void row_alone(FbShared& s, NucRed& r, const NucArgs& a, int64_t row, const NucCommon& c,
+                          const DT* __restrict__ xr, const double* e2) {
+  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
+  const SelOut cut = wg_select<DT, VEC>(s, r, xr, a.V, S1, (double)a.top_p, false);
+  const uint64_t kfin = max(cut.key, c.kmp);
+  const NucSet S2{c.m, c.thr, kfin, (double)a.T, e2};
+  const SelOut d = wg_select<DT, VEC>(s, r, xr, a.V, S2, (double)a.u[row], true);
+  if (threadIdx.x == 0) {
+    a.out_token[row] = ~(uint32_t)d.key;
+    if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - c.m) / (double)a.T - log(d.tot));
+  }
+}
+
+// LDS histogram -> the row's global histogram (device-scope atomics that
+// return, so they are complete when the workgroup arrives at its ticket).
+__device__ __forceinline__ void flush_hist(const double* hw, const uint32_t* hc, double* gw, uint32_t* gc) {
+  for (int b = threadIdx.x; b < kNB; b += NT) {
+    const uint32_t c = hc[b];
+    if (c) {
+      (void)__hip_atomic_fetch_add(&gw[b], hw[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      (void)__hip_atomic_fetch_add(&gc[b], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// The row's global histogram -> LDS, leaving zeros behind.  Each thread
+// issues all of its loads before it waits for any.
+__device__ __forceinline__ void take_hist(double* hw, uint32_t* hc, double* gw, uint32_t* gc) {
+  constexpr int Q = kNB / NT;
+  __syncthreads();
+  double v[Q];
+  uint32_t c[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    v[q] = ld_dev(&gw[q * NT + threadIdx.x]);
+    c[q] = ld_dev(&gc[q * NT + threadIdx.x]);
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int b = q * NT + threadIdx.x;
+    hw[b] = v[q];
+    hc[b] = c[q];
+    st_dev(&gw[b], 0.0);
+    st_dev(&gc[b], 0u);
+  }
+  __syncthreads();
+}
+
+// The row's n (<= kCapW) window candidates -> LDS, all loads issued first.
+__device__ __forceinline__ void take_list(uint64_t* key, uint32_t* bits, const uint64_t* lkey, const uint32_t* lbits,
+                                          uint32_t n) {
+  constexpr int Q = kCapW / NT;
+  uint64_t k[Q];
+  uint32_t b[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint32_t j = q * NT + threadIdx.x;
+    if (j < n) {
+      k[q] = ld_dev(&lkey[j]);
+      b[q] = ld_dev(&lbits[j]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint32_t j = q * NT + threadIdx.x;
+    if (j < n) {
+      key[j] = k[q];
+      bits[j] = b[q];
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void zero_hist(double* gw, uint32_t* gc) {
+  for (int b = threadIdx.x; b < kNB; b += NT) {
+    st_dev(&gw[b], 0.0);
+    st_dev(&gc[b], 0u);
+  }
+}
+
+// Window candidates of one workgroup: staged in LDS as indices within the
+// segment while streaming, then given positions in the row's list with one
+// counter atomic and written out (their values re-read from the cache).
+// Past the list's end they are only counted.
+struct Stage {
+  uint32_t idx[kCapW];
+  uint32_t n;
+  uint32_t base;
+};
+
+__device__ __forceinline__ void stage_window(Stage& st, int64_t i, int64_t e_begin) {
+  const uint32_t p = atomicAdd(&st.n, 1u);
+  if (p < kCapW) st.idx[p] = (uint32_t)(i - e_begin);
+}
+
+template <typename DT>
+__device__ __forceinline__ void flush_window(Stage& st, const DT* __restrict__ xr, int64_t e_begin, uint32_t* cnt,
+                                             uint64_t* lkey, uint32_t* lbits) {
+  __syncthreads();
+  const uint32_t n = st.n;
+  if (n == 0) return;
+  if (threadIdx.x == 0) st.base = __hip_atomic_fetch_add(cnt, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t base = st.base;
+  for (uint32_t j = threadIdx.x; j < min(n, kCapW); j += NT) {
+    const uint32_t pos = base + j;
+    if (pos < kCapW) {
+      const int64_t i = e_begin + st.idx[j];
+      const uint32_t bits = gbits_at<DT>(xr, i);
+      st_dev(&lkey[pos], comp_key(bits, (uint32_t)i));
+      st_dev(&lbits[pos], bits);
+    }
+  }
+}
+
+union NucLds {
+  struct {
+    double hw[kNB];
+    uint32_t hc[kNB];
+  } h;
+  struct {
+    uint64_t key[kCapW];
+    uint32_t bits[kCapW];
+  } w;
+};
+
+// Pass 1: guide histogram of exp(z - m) over the candidates and their exact
+// total; the last workgroup places the cut window.
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
+  __shared__ SelShared sh;
+  __shared__ NucRed r;
+  __shared__ NucLds L;
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows) return;
+  if (a.st_bad[row]) {
+    if (seg == 0 && tid == 0) {
+      a.out_token[row] = kFail;
+      if (a.out_logp) a.out_logp[row] = __builtin_nanf("");
+    }
+    return;
+  }
+  init_e2(e2);
+  const NucCommon c = nuc_common(a, row, seg);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
+  for (int b = tid; b < kNB; b += NT) {
+    L.h.hw[b] = 0.0;
+    L.h.hc[b] = 0u;
+  }
+  __syncthreads();
+  double z0 = 0.0;
+  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
+    const float z = __uint_as_float(bits);
+    if (z > -__builtin_inff() && (double)z >= c.thr) {
+      const uint32_t b = S1.bin<kNB>(z);
+      __hip_atomic_fetch_add(&L.h.hw[b], (double)S1.gw(z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      z0 += S1.w(z);
+    }
+  });
+  __syncthreads();
+  double* gw = a.h0w + row * kNB;
+  uint32_t* gc = a.h0c + row * kNB;
+  flush_hist(L.h.hw, L.h.hc, gw, gc);
+  z0 = nuc_sum(r, z0, 0);
+  if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], z0);
+  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  const double Z0 = merge_sum(sh, a.p_z0 + row * a.S, a.S);
+  take_hist(L.h.hw, L.h.hc, gw, gc);
+  const double t = (double)a.top_p * Z0, g = kGuard * Z0;
+  pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, t - g, t + g);
+  if (tid == 0) {
+    NucPlan& p = a.plan[row];
+    p.b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the top of the row when it fits
+    p.b_hi = r.b_hi;
+    p.z0 = Z0;
+    p.state = 0u;
+  }
+}
+
+// Pass 2: the exact mass above the cut window and the window's candidates; the
+// tempered guide histogram and exact mass of the kept candidates above it.
+// The last workgroup cuts, applies min_p and draws, or places the draw window.
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
+  __shared__ SelShared sh;
+  __shared__ NucRed r;
+  __shared__ NucLds L;
+  __shared__ Stage st;
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows || a.st_bad[row]) return;
+  if (tid == 0) st.n = 0u;
+  init_e2(e2);
+  const NucCommon c = nuc_common(a, row, seg);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const uint32_t b_lo = a.plan[row].b_lo, b_hi = a.plan[row].b_hi;
+  const double z0 = a.plan[row].z0;
+  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
+  const NucSet ST{c.m, c.thr, c.kmp, (double)a.T, e2};
+  for (int b = tid; b < kNB; b += NT) {
+    L.h.hw[b] = 0.0;
+    L.h.hc[b] = 0u;
+  }
+  __syncthreads();
+  uint64_t* lkey = a.lkey + row * kCapW;
+  uint32_t* lbits = a.lbits + row * kCapW;
+  double A = 0.0, AT = 0.0;
+  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
+    const float z = __uint_as_float(bits);
+    const uint64_t K = comp_key(bits, (uint32_t)i);
+    const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
+    const uint32_t b = cand ? S1.bin<kNB>(z) : (uint32_t)kNB;
+    if (b < b_lo) {
+      A += S1.w(z);
+      if (K >= c.kmp) {
+        AT += ST.w(z);
+        const uint32_t bt = ST.bin<kNB>(z);
+        __hip_atomic_fetch_add(&L.h.hw[bt], (double)ST.gw(z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&L.h.hc[bt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    if (b >= b_lo && b <= b_hi) stage_window(st, i, c.e_begin);
+  });
+  flush_window<DT>(st, xr, c.e_begin, &a.lcnt[row], lkey, lbits);
+  __syncthreads();
+  double* gw = a.hTw + row * kNB;
+  uint32_t* gc = a.hTc + row * kNB;
+  flush_hist(L.h.hw, L.h.hc, gw, gc);
+  A = nuc_sum(r, A, 0);
+  AT = nuc_sum(r, AT, 1);
+  if (tid == 0) {
+    st_dev(&a.p_a[row * a.S + seg], A);
+    st_dev(&a.p_at[row * a.S + seg], AT);
+  }
+  if (!last_done(sh, a.tickets + row * 3 + 1, (uint32_t)a.S)) return;
+  // ---- the row's last workgroup
+  const double Atot = merge_sum(sh, a.p_a + row * a.S, a.S);
+  const double ATtot = merge_sum(sh, a.p_at + row * a.S, a.S);
+  const uint32_t n = ld_dev(&a.lcnt[row]);
+  __syncthreads();
+  if (tid == 0) st_dev(&a.lcnt[row], 0u);
+  if (n > kCapW) {
+    // the window is too crowded for LDS: the row is left to nuc_alone
+    zero_hist(gw, gc);
+    if (tid == 0) a.plan[row].state = 3u;
+    return;
+  }
+  take_list(L.w.key, L.w.bits, lkey, lbits, n);
+  sort_desc<kCapW>(L.w.key, L.w.bits, n);
+  // the cut, then min_p: the kept candidates of the window are its first nk
+  const uint32_t jc = walk_sorted(r, L.w.bits, n, S1, Atot, (double)a.top_p * z0, false);
+  const uint64_t kfin = max(L.w.key[jc], c.kmp);
+  uint32_t nk = 0;
+  for (uint32_t j = tid; j < n; j += NT) nk += L.w.key[j] >= kfin ? 1u : 0u;
+  nk = block_sum_u32(r, nk);
+  const NucSet S2{c.m, c.thr, kfin, (double)a.T, e2};
+  const double WT = ATtot + sum_sorted(r, L.w.bits, nk, S2);
+  const double t2 = (double)a.u[row] * WT;
+  if (t2 < ATtot) {
+    // the draw falls above the window: place the draw window
+    take_hist(L.h.hw, L.h.hc, gw, gc);
+    pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, t2 - kGuard * WT, t2 + kGuard * WT);
+    if (tid == 0) {
+      NucPlan& q = a.plan[row];
+      q.c_lo = r.b_lo;
+      q.c_hi = r.b_hi;
+      q.wt = WT;
+      q.kfin = kfin;
+      q.state = 1u;
+    }
+    return;
+  }
+  zero_hist(gw, gc);
+  const uint32_t jd = walk_sorted(r, L.w.bits, nk, S2, ATtot, t2, true);
+  if (tid == 0) {
+    a.out_token[row] = ~(uint32_t)L.w.key[jd];
+    if (a.out_logp)
+      a.out_logp[row] = (float)(((double)__uint_as_float(L.w.bits[jd]) - c.m) / (double)a.T - log(WT));
+    a.plan[row].state = 2u;
+  }
+}
+
+// Pass 3 (rows whose draw falls above the cut window): the exact tempered mass
+// above the draw window and its candidates; the last workgroup draws.
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
+  __shared__ SelShared sh;
+  __shared__ NucRed r;
+  __shared__ NucLds L;
+  __shared__ Stage st;
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows || a.st_bad[row]) return;
+  if (a.plan[row].state != 1u) return;
+  const NucPlan p = a.plan[row];
+  if (tid == 0) st.n = 0u;
+  init_e2(e2);
+  const NucCommon c = nuc_common(a, row, seg);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
+  const NucSet S2{c.m, c.thr, p.kfin, (double)a.T, e2};
+  uint64_t* lkey = a.lkey + row * kCapW;
+  uint32_t* lbits = a.lbits + row * kCapW;
+  double A2 = 0.0;
+  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
+    const float z = __uint_as_float(bits);
+    const uint64_t K = comp_key(bits, (uint32_t)i);
+    // kept candidates above the cut window
+    const bool kept = z > -__builtin_inff() && (double)z >= c.thr && S1.bin<kNB>(z) < p.b_lo && K >= p.kfin;
+    const uint32_t bt = kept ? S2.bin<kNB>(z) : (uint32_t)kNB;
+    if (bt < p.c_lo) A2 += S2.w(z);
+    if (bt >= p.c_lo && bt <= p.c_hi) stage_window(st, i, c.e_begin);
+  });
+  flush_window<DT>(st, xr, c.e_begin, &a.lcnt[row], lkey, lbits);
+  A2 = nuc_sum(r, A2, 0);
+  if (tid == 0) st_dev(&a.p_a2[row * a.S + seg], A2);
+  if (!last_done(sh, a.tickets + row * 3 + 2, (uint32_t)a.S)) return;
+  const double A2tot = merge_sum(sh, a.p_a2 + row * a.S, a.S);
+  const uint32_t n = ld_dev(&a.lcnt[row]);
+  __syncthreads();
+  if (tid == 0) st_dev(&a.lcnt[row], 0u);
+  if (n > kCapW) {
+    // the draw window is too crowded for LDS: the draw is left to nuc_alone
+    if (tid == 0) a.plan[row].state = 4u;
+    return;
+  }
+  take_list(L.w.key, L.w.bits, lkey, lbits, n);
+  sort_desc<kCapW>(L.w.key, L.w.bits, n);
+  const uint32_t jd = walk_sorted(r, L.w.bits, n, S2, A2tot, (double)a.u[row] * p.wt, true);
+  if (tid == 0) {
+    a.out_token[row] = ~(uint32_t)L.w.key[jd];
+    if (a.out_logp)
+      a.out_logp[row] = (float)(((double)__uint_as_float(L.w.bits[jd]) - c.m) / (double)a.T - log(p.wt));
+  }
+}
+
+// Rows whose window was too crowded for LDS (one workgroup per row): the
+// whole row (state 3) or its draw (state 4) by the workgroup alone.
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
+  __shared__ NucRed r;
+  __shared__ FbShared fb;
+  __shared__ double e2[64];
+  const int64_t row = blockIdx.x;
+  if (row >= a.rows || a.st_bad[row]) return;
+  const uint32_t state = a.plan[row].state;
+  if (state != 3u && state != 4u) return;
+  init_e2(e2);
+  const NucCommon c = nuc_common(a, row, 0);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  if (state == 3u) {
+    row_alone<DT, VEC>(fb, r, a, row, c, xr, e2);
+    return;
+  }
+  const NucPlan p = a.plan[row];
+  const NucSet S2{c.m, c.thr, p.kfin, (double)a.T, e2};
+  const SelOut d = wg_select<DT, VEC>(fb, r, xr, a.V, S2, (double)a.u[row], true);
+  if (threadIdx.x == 0) {
+    a.out_token[row] = ~(uint32_t)d.key;
+    if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - c.m) / (double)a.T - log(d.tot));
+  }
+}
+
+template <typename DT, bool VEC>
+static void go_nucleus(const NucArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.rows * a.S));
+  hipLaunchKernelGGL((nuc_hist_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((nuc_collect_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((nuc_draw_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((nuc_alone_kernel<DT, VEC>), dim3((unsigned)a.rows), dim3(NT), 0, s, a);
+}
+
+hipError_t launch_row_nucleus(int dtype, const NucArgs& a, hipStream_t s) {
+  if (dtype == 0)
+    a.vec ? go_nucleus<float, true>(a, s) : go_nucleus<float, false>(a, s);
+  else
+    a.vec ? go_nucleus<uint16_t, true>(a, s) : go_nucleus<uint16_t, false>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace vsel
