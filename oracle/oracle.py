@@ -26,11 +26,12 @@ def load(path):
     L.oracle_argmax_excluding.argtypes = [vp, C.c_int, i64, i64, i64, vp, i64, vp, vp, C.c_int]
     L.oracle_topk.argtypes = [vp, C.c_int, i64, i64, i64, i32, vp, vp, vp, vp, C.c_int]
     L.oracle_sample.argtypes = [vp, C.c_int, i64, i64, i64, f32, i32, f32, vp, vp, vp, vp, C.c_int]
-    L.oracle_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp,
-                                     vp, vp, vp, vp, vp, vp, vp, C.c_int]
+    L.oracle_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, i32, f32, f32, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, C.c_int]
     L.oracle_sample_chain.argtypes = [vp, C.c_int, i64, i64, i64, f32, f32, i32, f32, f32, f32, vp, vp, vp, vp,
                                       C.c_int]
-    L.oracle_spec_match.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, C.c_int]
+    L.oracle_spec_match.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, i32, f32, f32, vp, vp, vp, vp, vp, vp, vp,
+                                    C.c_int]
     for f in (L.oracle_argmax, L.oracle_lse, L.oracle_topk, L.oracle_sample, L.oracle_spec_accept,
               L.oracle_argmax_excluding, L.oracle_spec_match, L.oracle_sample_chain):
         f.restype = C.c_int
@@ -149,7 +150,7 @@ def sample_chain(x, temperature, u, top_n_sigma=0.0, top_k=0, typical_p=1.0, top
 
 
 def spec_accept(target, draft, tokens, u_acc, u_res, u_bon, batch, gamma, temperature,
-                vocab=None, nthreads=0):
+                vocab=None, nthreads=0, top_k=0, top_p=1.0, min_p=0.0):
     target = np.ascontiguousarray(target, dtype=np.float32)
     draft = np.ascontiguousarray(draft, dtype=np.float32)
     assert target.shape[0] == batch * (gamma + 1) and draft.shape[0] == batch * gamma
@@ -162,16 +163,18 @@ def spec_accept(target, draft, tokens, u_acc, u_res, u_bon, batch, gamma, temper
         len_mrs=np.empty(batch, np.int32), tok_mrs=np.empty((batch, gamma + 1), np.uint32),
         len_aa=np.empty(batch, np.int32), tok_aa=np.empty((batch, gamma + 1), np.uint32),
         summin=np.empty((batch, gamma), np.float64), acc_margin=np.empty((batch, gamma), np.float64),
-        draw_margin=np.empty(batch, np.float64))
+        draw_margin=np.empty(batch, np.float64), filter_margin=np.empty(batch, np.float64))
     _check(lib().oracle_spec_accept(
         _p(target), target.shape[1], _p(draft), draft.shape[1], batch, gamma, V, float(temperature),
+        int(top_k), float(top_p), float(min_p),
         _p(tokens), _p(u_acc), _p(u_res), _p(u_bon), _p(out["len_mrs"]), _p(out["tok_mrs"]),
         _p(out["len_aa"]), _p(out["tok_aa"]), _p(out["summin"]), _p(out["acc_margin"]),
-        _p(out["draw_margin"]), nthreads))
+        _p(out["draw_margin"]), _p(out["filter_margin"]), nthreads))
     return out
 
 
-def spec_match(target, draft, tokens, u_match, batch, gamma, temperature, vocab=None, nthreads=0):
+def spec_match(target, draft, tokens, u_match, batch, gamma, temperature, vocab=None, nthreads=0,
+               top_k=0, top_p=1.0, min_p=0.0):
     """Sampler-match acceptance (fresh draw from p at each position, accept on
     equality, emit the draw) and the per-position sum_x p(x) q(x).
     u_match: float32 [batch, gamma+1].  Returns len_sm, tok_sm, sumprod and
@@ -184,9 +187,10 @@ def spec_match(target, draft, tokens, u_match, batch, gamma, temperature, vocab=
     u_match = np.ascontiguousarray(u_match, dtype=np.float32).reshape(batch * (gamma + 1))
     out = dict(len_sm=np.empty(batch, np.int32), tok_sm=np.empty((batch, gamma + 1), np.uint32),
                sumprod=np.empty((batch, gamma), np.float64),
-               match_margin=np.empty((batch, gamma + 1), np.float64))
+               match_margin=np.empty((batch, gamma + 1), np.float64), filter_margin=np.empty(batch, np.float64))
     _check(lib().oracle_spec_match(
         _p(target), target.shape[1], _p(draft), draft.shape[1], batch, gamma, V, float(temperature),
+        int(top_k), float(top_p), float(min_p),
         _p(tokens), _p(u_match), _p(out["len_sm"]), _p(out["tok_sm"]), _p(out["sumprod"]),
-        _p(out["match_margin"]), nthreads))
+        _p(out["match_margin"]), _p(out["filter_margin"]), nthreads))
     return out

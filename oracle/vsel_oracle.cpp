@@ -111,6 +111,95 @@ double lse_row(const Rows& R, int64_t r, int64_t V, double T) {
   return M + std::log(s);
 }
 
+// A verify row's effective distribution ("speculative-acceptance.md", "The
+// rules": top-k / top-p / min-p filtering on the untempered distribution, then
+// the final temperature scaling): p(x) = exp(z_x / T - lse) on the kept ids,
+// 0 elsewhere.  Filters, in this order, each keeping at least one id:
+//   top_k > 0: the top_k largest under (value desc, id asc);
+//   top_p < 1: in that order, the shortest prefix whose cumulative untempered
+//     probability (softmax of the candidates) reaches top_p;
+//   min_p > 0: z >= max z + log(min_p) over the candidates.
+// No filter: every id kept, lse the whole row's.  `margin` (may be null) gets
+// the smaller of the top-p cut's distance to the nearer cumulative sum and the
+// min-p threshold's distance to the nearest candidate value (+inf if none).
+struct RowDist {
+  std::vector<char> keep;  // empty: every id kept
+  double lse = 0.0;
+  bool kept(int64_t x) const { return keep.empty() || keep[static_cast<size_t>(x)]; }
+};
+RowDist row_dist(const Rows& R, int64_t r, int64_t V, double T, int32_t top_k, float top_p, float min_p,
+                 double* margin) {
+  RowDist d;
+  if (margin) *margin = kInf;
+  if (top_k <= 0 && top_p >= 1.0f && min_p <= 0.0f) {
+    d.lse = lse_row(R, r, V, T);
+    return d;
+  }
+  auto z = [&](uint32_t x) { return static_cast<double>(R.at(r, x)); };
+  std::vector<uint32_t> cand(static_cast<size_t>(V));
+  std::iota(cand.begin(), cand.end(), 0u);
+  if (top_k > 0 || top_p < 1.0f) {
+    auto by_value = [&](uint32_t a, uint32_t b) { return z(a) > z(b) || (z(a) == z(b) && a < b); };
+    const size_t k = top_k > 0 ? std::min<size_t>(static_cast<size_t>(top_k), cand.size()) : cand.size();
+    std::partial_sort(cand.begin(), cand.begin() + k, cand.end(), by_value);
+    cand.resize(k);
+  }
+  double zmax = -kInf;
+  for (uint32_t x : cand) zmax = std::max(zmax, z(x));
+  if (top_p < 1.0f) {
+    double Z = 0.0;
+    for (uint32_t x : cand) Z += std::exp(z(x) - zmax);
+    double cum = 0.0;
+    for (size_t j = 0; j < cand.size(); ++j) {
+      const double prev = cum;
+      cum += std::exp(z(cand[j]) - zmax) / Z;
+      if (cum >= static_cast<double>(top_p)) {
+        if (margin) *margin = std::min(*margin, std::min(cum - top_p, j > 0 ? top_p - prev : kInf));
+        cand.resize(j + 1);
+        break;
+      }
+    }
+  }
+  if (min_p > 0.0f) {
+    const double thr = zmax + std::log(static_cast<double>(min_p));
+    std::vector<uint32_t> kept;
+    for (uint32_t x : cand) {
+      if (z(x) >= thr) kept.push_back(x);
+      if (margin) *margin = std::min(*margin, std::fabs(z(x) - thr));
+    }
+    cand.swap(kept);
+  }
+  d.keep.assign(static_cast<size_t>(V), 0);
+  double M = -kInf;
+  for (uint32_t x : cand) {
+    d.keep[x] = 1;
+    M = std::max(M, z(x) / T);
+  }
+  double s = 0.0;
+  for (uint32_t x : cand) s += std::exp(z(x) / T - M);
+  d.lse = M + std::log(s);
+  return d;
+}
+
+// The effective distributions of one sequence: target rows zrow0 .. +G (the
+// last is the bonus row) and draft rows drow0 .. +G-1, all under the same
+// sampler settings.  Returns the smallest filter margin.
+double seq_dists(const Rows& Zr, int64_t zrow0, const Rows& Dr, int64_t drow0, int64_t G, int64_t V, double T,
+                 int32_t top_k, float top_p, float min_p, std::vector<RowDist>& dp, std::vector<RowDist>& dq) {
+  dp.resize(static_cast<size_t>(G + 1));
+  dq.resize(static_cast<size_t>(G));
+  double fm = kInf, m;
+  for (int64_t i = 0; i <= G; ++i) {
+    dp[i] = row_dist(Zr, zrow0 + i, V, T, top_k, top_p, min_p, &m);
+    fm = std::min(fm, m);
+  }
+  for (int64_t i = 0; i < G; ++i) {
+    dq[i] = row_dist(Dr, drow0 + i, V, T, top_k, top_p, min_p, &m);
+    fm = std::min(fm, m);
+  }
+  return fm;
+}
+
 // The k first elements of the row under the total order
 //   a before b  <=>  x_a > x_b, or x_a == x_b and a < b.
 std::vector<uint32_t> topk_row(const Rows& R, int64_t r, int64_t V, int64_t k) {
@@ -468,7 +557,9 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
 // c5: speculative acceptance for `batch` sequences of `gamma` drafted tokens.
 // target: batch*(gamma+1) rows (row b*(gamma+1)+i is verify position i of
 // sequence b; the last one is the bonus row); draft: batch*gamma rows.
-//   p_i = softmax(Z_i / T), q_i = softmax(D_i / T), float64 via log-sum-exp.
+//   p_i = softmax(Z_i / T), q_i = softmax(D_i / T), float64 via log-sum-exp;
+//   with filters (top_k, top_p, min_p: row_dist) both are the filtered,
+//   renormalised distributions, the same sampler settings on target and draft.
 //   Modified rejection sampling ("speculative-acceptance.md", "Modified
 //   rejection sampling"; the exact CPU acceptance of "Chapter 21", section
 //   21.9): accept t_i iff u_acc * q_i(t_i) <= p_i(t_i) (q = 0 accepts); at the
@@ -484,15 +575,17 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
 // sequence (any nonfinite row used by it, or a drafted id >= vocab);
 // tokens[b*(gamma+1) + 0..L] emitted, the rest 0xFFFFFFFF.
 // Margins (optional): acc_margin[b*gamma+i] = |u_acc*q_i(t_i) - p_i(t_i)| for
-// tested positions (+inf elsewhere); draw_margin[b] as in draw().
+// tested positions (+inf elsewhere); draw_margin[b] as in draw();
+// filter_margin[b] the smallest row_dist margin over the sequence's rows.
 int oracle_spec_accept(const float* target, int64_t ld_t, const float* draft, int64_t ld_d,
-                       int64_t batch, int32_t gamma, int64_t vocab, float temperature,
-                       const uint32_t* draft_tokens, const float* u_acc, const float* u_res,
-                       const float* u_bon, int32_t* len_mrs, uint32_t* tok_mrs, int32_t* len_aa,
-                       uint32_t* tok_aa, double* summin, double* acc_margin, double* draw_margin,
-                       int nthreads) {
+                       int64_t batch, int32_t gamma, int64_t vocab, float temperature, int32_t top_k,
+                       float top_p, float min_p, const uint32_t* draft_tokens, const float* u_acc,
+                       const float* u_res, const float* u_bon, int32_t* len_mrs, uint32_t* tok_mrs,
+                       int32_t* len_aa, uint32_t* tok_aa, double* summin, double* acc_margin,
+                       double* draw_margin, double* filter_margin, int nthreads) {
   if (!target || !draft || !draft_tokens || !u_acc || !u_res || !u_bon || !len_mrs || !tok_mrs) return 1;
   if (batch < 0 || gamma < 1 || vocab < 1 || ld_t < vocab || ld_d < vocab || !(temperature >= 0.0f)) return 1;
+  if (top_k < 0 || !(top_p > 0.0f && top_p <= 1.0f) || !(min_p >= 0.0f && min_p <= 1.0f)) return 1;
   Rows Zr{target, 0, ld_t}, Dr{draft, 0, ld_d};
   const int64_t G = gamma, V = vocab;
   const double T = temperature;
@@ -509,6 +602,7 @@ int oracle_spec_accept(const float* target, int64_t ld_t, const float* draft, in
       if (summin) summin[b * G + i] = kNaN;
     }
     if (draw_margin) draw_margin[b] = kInf;
+    if (filter_margin) filter_margin[b] = kInf;
     auto fail = [&] {
       len_mrs[b] = -1;
       if (len_aa) len_aa[b] = -1;
@@ -544,11 +638,15 @@ int oracle_spec_accept(const float* target, int64_t ld_t, const float* draft, in
       return;
     }
 
-    std::vector<double> lp(G + 1), lq(G);
-    for (int64_t i = 0; i <= G; ++i) lp[i] = lse_row(Zr, zrow0 + i, V, T);
-    for (int64_t i = 0; i < G; ++i) lq[i] = lse_row(Dr, drow0 + i, V, T);
-    auto p_of = [&](int64_t i, int64_t x) { return std::exp(static_cast<double>(Zr.at(zrow0 + i, x)) / T - lp[i]); };
-    auto q_of = [&](int64_t i, int64_t x) { return std::exp(static_cast<double>(Dr.at(drow0 + i, x)) / T - lq[i]); };
+    std::vector<RowDist> dp, dq;
+    const double fm = seq_dists(Zr, zrow0, Dr, drow0, G, V, T, top_k, top_p, min_p, dp, dq);
+    if (filter_margin) filter_margin[b] = fm;
+    auto p_of = [&](int64_t i, int64_t x) {
+      return dp[i].kept(x) ? std::exp(static_cast<double>(Zr.at(zrow0 + i, x)) / T - dp[i].lse) : 0.0;
+    };
+    auto q_of = [&](int64_t i, int64_t x) {
+      return dq[i].kept(x) ? std::exp(static_cast<double>(Dr.at(drow0 + i, x)) / T - dq[i].lse) : 0.0;
+    };
 
     if (summin)
       for (int64_t i = 0; i < G; ++i) {
@@ -602,15 +700,17 @@ int oracle_spec_accept(const float* target, int64_t ld_t, const float* draft, in
 //   ceiling", the sampler-match row), the diagnostic beside sum min(p, q).
 //   T == 0 is greedy: the sampler is argmax, so the rule is
 //   argmax-against-argmax, and sumprod is 1 where the two argmaxes agree.
-// Outputs as oracle_spec_accept (len -1 and sentinel tokens for a
-// fail-closed sequence).  match_margin[b*(gamma+1)+i]: the draw margin at
-// every position the chain tested (+inf elsewhere).
+// p and q filtered as in oracle_spec_accept.  Outputs as oracle_spec_accept
+// (len -1 and sentinel tokens for a fail-closed sequence).
+// match_margin[b*(gamma+1)+i]: the draw margin at every position the chain
+// tested (+inf elsewhere); filter_margin as in oracle_spec_accept.
 int oracle_spec_match(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
-                      int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
-                      const float* u_match, int32_t* len_sm, uint32_t* tok_sm, double* sumprod,
-                      double* match_margin, int nthreads) {
+                      int32_t gamma, int64_t vocab, float temperature, int32_t top_k, float top_p, float min_p,
+                      const uint32_t* draft_tokens, const float* u_match, int32_t* len_sm, uint32_t* tok_sm,
+                      double* sumprod, double* match_margin, double* filter_margin, int nthreads) {
   if (!target || !draft || !draft_tokens || !u_match || !len_sm || !tok_sm) return 1;
   if (batch < 0 || gamma < 1 || vocab < 1 || ld_t < vocab || ld_d < vocab || !(temperature >= 0.0f)) return 1;
+  if (top_k < 0 || !(top_p > 0.0f && top_p <= 1.0f) || !(min_p >= 0.0f && min_p <= 1.0f)) return 1;
   Rows Zr{target, 0, ld_t}, Dr{draft, 0, ld_d};
   const int64_t G = gamma, V = vocab;
   const double T = temperature;
@@ -623,6 +723,7 @@ int oracle_spec_match(const float* target, int64_t ld_t, const float* draft, int
     }
     for (int64_t i = 0; i < G; ++i)
       if (sumprod) sumprod[b * G + i] = kNaN;
+    if (filter_margin) filter_margin[b] = kInf;
     std::vector<uint32_t> amz(G + 1), amd(G);
     for (int64_t i = 0; i <= G; ++i)
       if ((amz[i] = argmax_row(Zr, zrow0 + i, V, nullptr)) == kFailClosed) {
@@ -648,11 +749,15 @@ int oracle_spec_match(const float* target, int64_t ld_t, const float* draft, int
         for (int64_t i = 0; i < G; ++i) sumprod[b * G + i] = (amz[i] == amd[i]) ? 1.0 : 0.0;
       return;
     }
-    std::vector<double> lp(G + 1), lq(G);
-    for (int64_t i = 0; i <= G; ++i) lp[i] = lse_row(Zr, zrow0 + i, V, T);
-    for (int64_t i = 0; i < G; ++i) lq[i] = lse_row(Dr, drow0 + i, V, T);
-    auto p_of = [&](int64_t i, int64_t x) { return std::exp(static_cast<double>(Zr.at(zrow0 + i, x)) / T - lp[i]); };
-    auto q_of = [&](int64_t i, int64_t x) { return std::exp(static_cast<double>(Dr.at(drow0 + i, x)) / T - lq[i]); };
+    std::vector<RowDist> dp, dq;
+    const double fm = seq_dists(Zr, zrow0, Dr, drow0, G, V, T, top_k, top_p, min_p, dp, dq);
+    if (filter_margin) filter_margin[b] = fm;
+    auto p_of = [&](int64_t i, int64_t x) {
+      return dp[i].kept(x) ? std::exp(static_cast<double>(Zr.at(zrow0 + i, x)) / T - dp[i].lse) : 0.0;
+    };
+    auto q_of = [&](int64_t i, int64_t x) {
+      return dq[i].kept(x) ? std::exp(static_cast<double>(Dr.at(drow0 + i, x)) / T - dq[i].lse) : 0.0;
+    };
     if (sumprod)
       for (int64_t i = 0; i < G; ++i) {
         double s = 0.0;

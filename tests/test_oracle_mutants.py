@@ -8,6 +8,7 @@ import pytest
 import tests.test_oracle_pins as P
 import tests.test_oracle_pins_match as M
 import tests.test_oracle_pins_chain as C
+import tests.test_oracle_pins_filtered as F
 from oracle import build as B
 from oracle import oracle as O
 
@@ -64,6 +65,12 @@ MUTANTS = [
     ("min-p in tempered units", "const double thr = cmax + std::log(static_cast<double>(min_p));",
      "const double thr = cmax + T * std::log(static_cast<double>(min_p));",
      [C.test_worked_example, C.test_min_p_matches_a_numpy_mask]),
+    ("filtered p not renormalised over the kept ids", "d.lse = M + std::log(s);", "d.lse = lse_row(R, r, V, T);",
+     [F.test_filtered_coupling_sums_match_numpy]),
+    ("draft rows left unfiltered", "dq[i] = row_dist(Dr, drow0 + i, V, T, top_k, top_p, min_p, &m);",
+     "dq[i] = row_dist(Dr, drow0 + i, V, T, 0, 1.0f, 0.0f, &m);", [F.test_filtered_coupling_sums_match_numpy]),
+    ("filtered nucleus cut on the tempered distribution", "cum += std::exp(z(cand[j]) - zmax) / Z;",
+     "cum += std::exp((z(cand[j]) - zmax) / T) / Z;", [F.test_filtered_coupling_sums_match_numpy]),
 ]
 
 
