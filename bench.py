@@ -259,6 +259,14 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
     Lm = mo["len_sm"].cpu().numpy()
     ex["spec_match_32x8_per_position_acceptance"] = float(Lm.sum() / int(np.minimum(Lm + 1, 8).sum()))
     ex["spec_match_32x8_mean_sumprod"] = float(mo["sumprod"].float().mean().item())
+    # both rules with filtered p and q (top-k 50 then top-p 0.95; top-p 0.9 over whole rows)
+    for name, kw in (("k50_p095", dict(top_k=50, top_p=0.95)), ("wholerow_p09", dict(top_p=0.9))):
+        fo = vsel.vsel_spec_accept_filtered(tg, dr, *args, **kw)
+        ex[f"spec_accept_filtered_{name}_32x8_device_us"] = time_graph(
+            lambda i: vsel.vsel_spec_accept_filtered(tg, dr, *args, out=fo, **kw), 10, stream)
+        fm = vsel.vsel_spec_match_filtered(tg, dr, *margs, **kw)
+        ex[f"spec_match_filtered_{name}_32x8_device_us"] = time_graph(
+            lambda i: vsel.vsel_spec_match_filtered(tg, dr, *margs, out=fm, **kw), 10, stream)
     del tg, dr
     # fp32 variant of the headline batch (one buffer pair, 827 MB each)
     x32 = bufs[0][:, :V].float().contiguous()

@@ -19,6 +19,9 @@
  *   vsel_spec_accept  speculative-decoding acceptance: modified rejection
  *                     sampling and argmax-against-argmax, with the per-position
  *                     coupling sum of min(p, q)
+ *   vsel_spec_accept_filtered, vsel_spec_match_filtered
+ *                     the same rules with p and q filtered by top-k, top-p
+ *                     and min-p before the temperature
  *
  * Common conventions
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
@@ -41,8 +44,10 @@
  *   - Workspace: device scratch of at least vsel_workspace_bytes(...) bytes,
  *     zero-filled ONCE by the caller after allocation.  Calls leave the
  *     counters they use at zero again, so a workspace can be reused by later
- *     calls on the same stream (calls that share a workspace must be ordered
- *     on one stream).  After a call that failed on the device, zero it again.
+ *     calls of the same operation with the same rows, vocab and k (the
+ *     arguments it was sized for) on the same stream (calls that share a
+ *     workspace must be ordered on one stream).  Before using it for other
+ *     arguments, or after a call that failed on the device, zero it again.
  *   - Errors are returned synchronously, before anything is launched:
  *     VSEL_EINVAL for a bad argument, VSEL_EWORKSPACE for a workspace that is
  *     too small or misaligned (256 bytes), VSEL_EDEVICE when a launch fails.
@@ -71,7 +76,8 @@ typedef enum {
   VSEL_OP_TOPK = 1,
   VSEL_OP_SAMPLE = 2,
   VSEL_OP_SPEC_ACCEPT = 3,
-  VSEL_OP_SAMPLE_CHAIN = 4
+  VSEL_OP_SAMPLE_CHAIN = 4,
+  VSEL_OP_SPEC_FILTERED = 5
 } vsel_op;
 
 /* Index/token written for a fail-closed row: the high-bit latch of the greedy
@@ -94,6 +100,7 @@ const char* vsel_status_string(int status);
  *   VSEL_OP_SAMPLE:      rows, vocab, k = top_k.
  *   VSEL_OP_SPEC_ACCEPT: rows = batch, vocab, k = gamma.
  *   VSEL_OP_SAMPLE_CHAIN: rows, vocab, k = top_k.
+ *   VSEL_OP_SPEC_FILTERED: rows = batch, vocab, k = gamma (any filters).
  * Returns 0 for arguments the operation would reject. */
 size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int32_t k);
 
@@ -280,6 +287,40 @@ vsel_status vsel_spec_match(const float* target_logits, int64_t ld_t, const floa
                             float temperature, const uint32_t* draft_tokens, const float* u_match,
                             int32_t* out_len, uint32_t* out_tok, float* out_sumprod,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Speculative-decoding acceptance with filtered distributions
+ * ("speculative-acceptance.md", "The rules": p is the target's distribution
+ * after top-k / top-p / min-p filtering on the untempered distribution and the
+ * final temperature scaling; q the distribution the drafter drew from, here
+ * under the same sampler settings).  For every target and draft row:
+ *   1. top_k > 0: the top min(top_k, vocab) elements, (value desc, id asc);
+ *      top_k == 0: the whole row, in that order when top_p < 1;
+ *   2. top_p < 1: the shortest prefix whose cumulative untempered probability
+ *      (softmax of the candidates) reaches top_p;
+ *   3. min_p > 0: z >= max z + log(min_p) over the candidates;
+ *   p(x) = exp(z_x/T) / sum over the kept ids, 0 for the others.
+ * The rules, draws, outputs, limits and fail-closed sequences are those of
+ * vsel_spec_accept and vsel_spec_match with these p and q (a drafted token
+ * outside the draft's kept set has q = 0 and is accepted by the modified
+ * rejection test).  temperature == 0 is greedy and ignores the filters.
+ *   0 <= top_k <= VSEL_K_MAX, 0 < top_p <= 1, 0 <= min_p <= 1
+ *   workspace: VSEL_OP_SPEC_FILTERED with rows = batch, k = gamma
+ */
+vsel_status vsel_spec_accept_filtered(const float* target_logits, int64_t ld_t, const float* draft_logits,
+                                      int64_t ld_d, int64_t batch, int32_t gamma, int64_t vocab,
+                                      float temperature, int32_t top_k, float top_p, float min_p,
+                                      const uint32_t* draft_tokens, const float* u_accept,
+                                      const float* u_resid, const float* u_bonus, int32_t* out_len_mrs,
+                                      uint32_t* out_tok_mrs, int32_t* out_len_aa, uint32_t* out_tok_aa,
+                                      float* out_summin, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+vsel_status vsel_spec_match_filtered(const float* target_logits, int64_t ld_t, const float* draft_logits,
+                                     int64_t ld_d, int64_t batch, int32_t gamma, int64_t vocab,
+                                     float temperature, int32_t top_k, float top_p, float min_p,
+                                     const uint32_t* draft_tokens, const float* u_match, int32_t* out_len,
+                                     uint32_t* out_tok, float* out_sumprod, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_operations():
     names = declared_functions()
     for op in ("vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_sample_chain",
-               "vsel_spec_accept", "vsel_spec_match", "vsel_workspace_bytes"):
+               "vsel_spec_accept", "vsel_spec_match", "vsel_spec_accept_filtered", "vsel_spec_match_filtered",
+               "vsel_workspace_bytes"):
         assert op in names
 
 
@@ -52,6 +53,9 @@ def test_workspace_sizes(vsel):
     for k in (0, 1, 50, 1024):
         assert wb(vsel.OP_SAMPLE_CHAIN, vsel.BF16, 64, 202048, k) > wb(vsel.OP_SAMPLE, vsel.BF16, 64, 202048, k)
     assert wb(vsel.OP_SAMPLE_CHAIN, vsel.F32, 4, 100, 1025) == 0
+    # the filtered rules hold the speculative workspace and the filter pass's after it
+    assert wb(vsel.OP_SPEC_FILTERED, vsel.F32, 32, 202048, 8) > wb(vsel.OP_SPEC, vsel.F32, 32, 202048, 8) > 0
+    assert wb(vsel.OP_SPEC_FILTERED, vsel.F32, 2, 100, 257) == 0
     assert wb(vsel.OP_TOPK, vsel.BF16, 1024, 202048, 84) > 0
     # rejected shapes size to 0
     assert wb(vsel.OP_TOPK, vsel.F32, 4, 100, 101) == 0          # k > vocab
@@ -121,3 +125,14 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
     assert match(gamma=0) == EINVAL
     assert match(T=float("nan")) == EINVAL
     assert match(ld_t=99) == EINVAL
+    def filt(fn, k=5, p=0.9, mp=0.0, ws_bytes=1 << 20):
+        if fn == "accept":
+            return L.vsel_spec_accept_filtered(fake, 100, fake, 100, 2, 3, 100, 1.0, k, p, mp, fake, fake, fake,
+                                               fake, fake, fake, None, None, None, ws, ws_bytes, None)
+        return L.vsel_spec_match_filtered(fake, 100, fake, 100, 2, 3, 100, 1.0, k, p, mp, fake, fake, fake, fake,
+                                          None, ws, ws_bytes, None)
+    for fn in ("accept", "match"):
+        for kw in (dict(k=-1), dict(k=1025), dict(p=0.0), dict(p=1.5), dict(mp=-0.5), dict(mp=2.0),
+                   dict(p=float("nan"))):
+            assert filt(fn, **kw) == EINVAL, (fn, kw)
+        assert filt(fn, ws_bytes=4096) == EWS

@@ -91,3 +91,21 @@ def test_spec_match_graph(g):
     keys = list(ref)
     replay_check(lambda: g.vsel.vsel_spec_match(*args, um, 4, 3, 1.0, out=out), lambda: [out[k] for k in keys],
                  [ref[k] for k in keys], lambda: g.vsel.vsel_argmax(args[0]))
+
+
+def test_filtered_spec_graphs(g):
+    d = W.speculative_batch(batch=4, gamma=3, vocab=30000, seed=77)
+    args = [g.dev(d[k]) for k in ("target", "draft", "tokens", "u_acc", "u_res", "u_bon")]
+    um = g.dev(W.uniforms(4 * 4, seed=77))
+    for kw in (dict(top_k=40, top_p=0.9), dict(top_p=0.9, min_p=0.01), dict(min_p=0.05)):
+        ref = {k: v.clone() for k, v in g.vsel.vsel_spec_accept_filtered(*args, 4, 3, 1.0, **kw).items()}
+        out = {k: torch.empty_like(v) for k, v in ref.items()}
+        keys = list(ref)
+        replay_check(lambda: g.vsel.vsel_spec_accept_filtered(*args, 4, 3, 1.0, out=out, **kw),
+                     lambda: [out[k] for k in keys], [ref[k] for k in keys], lambda: g.vsel.vsel_argmax(args[0]))
+        ref = {k: v.clone() for k, v in g.vsel.vsel_spec_match_filtered(args[0], args[1], args[2], um, 4, 3, 1.0,
+                                                                         **kw).items()}
+        out = {k: torch.empty_like(v) for k, v in ref.items()}
+        keys = list(ref)
+        replay_check(lambda: g.vsel.vsel_spec_match_filtered(args[0], args[1], args[2], um, 4, 3, 1.0, out=out, **kw),
+                     lambda: [out[k] for k in keys], [ref[k] for k in keys], lambda: g.vsel.vsel_argmax(args[0]))

@@ -16,7 +16,7 @@ import os
 import torch  # loads the HIP runtime that libvsel.so then shares
 
 __all__ = ["vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_sample_chain", "vsel_spec_accept",
-           "vsel_spec_match",
+           "vsel_spec_match", "vsel_spec_accept_filtered", "vsel_spec_match_filtered",
            "workspace_bytes",
            "VselError", "NONFINITE", "K_MAX", "EXCLUDED_MAX", "library_path"]
 
@@ -27,7 +27,7 @@ NONFINITE = 0xFFFFFFFF
 K_MAX = 1024
 EXCLUDED_MAX = 256
 F32, BF16 = 0, 1
-OP_ARGMAX, OP_TOPK, OP_SAMPLE, OP_SPEC, OP_SAMPLE_CHAIN = 0, 1, 2, 3, 4
+OP_ARGMAX, OP_TOPK, OP_SAMPLE, OP_SPEC, OP_SAMPLE_CHAIN, OP_SPEC_FILTERED = 0, 1, 2, 3, 4, 5
 
 
 class VselError(RuntimeError):
@@ -53,8 +53,12 @@ def _load():
     L.vsel_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp, sz, vp]
     L.vsel_spec_match.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in (L.vsel_argmax, L.vsel_argmax_excluding, L.vsel_topk, L.vsel_sample, L.vsel_spec_accept,
-              L.vsel_spec_match):
+    L.vsel_spec_accept_filtered.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, i32, f32, f32, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, sz, vp]
+    L.vsel_spec_match_filtered.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, i32, f32, f32, vp, vp, vp, vp,
+                                           vp, vp, sz, vp]
+    for f in (L.vsel_argmax, L.vsel_argmax_excluding, L.vsel_topk, L.vsel_sample, L.vsel_sample_chain,
+              L.vsel_spec_accept, L.vsel_spec_match, L.vsel_spec_accept_filtered, L.vsel_spec_match_filtered):
         f.restype = C.c_int
     return L
 
@@ -269,4 +273,65 @@ def vsel_spec_match(target: torch.Tensor, draft: torch.Tensor, draft_tokens: tor
     _check(lib.vsel_spec_match(_ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature),
                                _ptr(draft_tokens), _ptr(u_match), _ptr(out["len_sm"]), _ptr(out["tok_sm"]),
                                _ptr(out.get("sumprod")), _ptr(ws), ws.numel(), _stream(dev)), "vsel_spec_match")
+    return out
+
+
+def vsel_spec_accept_filtered(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                              u_accept: torch.Tensor, u_resid: torch.Tensor, u_bonus: torch.Tensor, batch: int,
+                              gamma: int, temperature: float, top_k=0, top_p=1.0, min_p=0.0, vocab=None, out=None):
+    """vsel_spec_accept with p and q filtered by top-k, top-p and min-p before the temperature."""
+    if target.dtype != torch.float32 or draft.dtype != torch.float32:
+        raise TypeError("speculative acceptance takes float32 rows")
+    rt, Vt, ld_t = _rows(target, vocab)
+    rd, Vd, ld_d = _rows(draft, vocab)
+    if rt != batch * (gamma + 1) or rd != batch * gamma or Vt != Vd:
+        raise ValueError("target must hold batch*(gamma+1) rows and draft batch*gamma rows")
+    dev = target.device
+    for t in (draft_tokens, u_accept, u_resid, u_bonus):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("token and uniform tensors must be contiguous device tensors")
+    if draft_tokens.dtype not in (torch.int32,) or draft_tokens.numel() != batch * gamma:
+        raise ValueError("draft_tokens must be int32[batch*gamma] (uint32 bits)")
+    if out is None:
+        out = dict(len_mrs=torch.empty(batch, dtype=torch.int32, device=dev),
+                   tok_mrs=torch.empty((batch, gamma + 1), dtype=torch.int32, device=dev),
+                   len_aa=torch.empty(batch, dtype=torch.int32, device=dev),
+                   tok_aa=torch.empty((batch, gamma + 1), dtype=torch.int32, device=dev),
+                   summin=torch.empty((batch, gamma), dtype=torch.float32, device=dev))
+    ws = workspace(OP_SPEC_FILTERED, F32, batch, Vt, gamma, dev)
+    _check(lib.vsel_spec_accept_filtered(
+        _ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature), int(top_k), float(top_p),
+        float(min_p), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resid), _ptr(u_bonus), _ptr(out["len_mrs"]),
+        _ptr(out["tok_mrs"]), _ptr(out.get("len_aa")), _ptr(out.get("tok_aa")), _ptr(out.get("summin")), _ptr(ws),
+        ws.numel(), _stream(dev)), "vsel_spec_accept_filtered")
+    return out
+
+
+def vsel_spec_match_filtered(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                             u_match: torch.Tensor, batch: int, gamma: int, temperature: float, top_k=0, top_p=1.0,
+                             min_p=0.0, vocab=None, out=None):
+    """vsel_spec_match with p and q filtered by top-k, top-p and min-p before the temperature."""
+    if target.dtype != torch.float32 or draft.dtype != torch.float32:
+        raise TypeError("speculative acceptance takes float32 rows")
+    rt, Vt, ld_t = _rows(target, vocab)
+    rd, Vd, ld_d = _rows(draft, vocab)
+    if rt != batch * (gamma + 1) or rd != batch * gamma or Vt != Vd:
+        raise ValueError("target must hold batch*(gamma+1) rows and draft batch*gamma rows")
+    dev = target.device
+    for t in (draft_tokens, u_match):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("token and uniform tensors must be contiguous device tensors")
+    if draft_tokens.dtype not in (torch.int32,) or draft_tokens.numel() != batch * gamma:
+        raise ValueError("draft_tokens must be int32[batch*gamma] (uint32 bits)")
+    if u_match.dtype != torch.float32 or u_match.numel() != batch * (gamma + 1):
+        raise ValueError("u_match must be float32[batch*(gamma+1)]")
+    if out is None:
+        out = dict(len_sm=torch.empty(batch, dtype=torch.int32, device=dev),
+                   tok_sm=torch.empty((batch, gamma + 1), dtype=torch.int32, device=dev),
+                   sumprod=torch.empty((batch, gamma), dtype=torch.float32, device=dev))
+    ws = workspace(OP_SPEC_FILTERED, F32, batch, Vt, gamma, dev)
+    _check(lib.vsel_spec_match_filtered(
+        _ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature), int(top_k), float(top_p),
+        float(min_p), _ptr(draft_tokens), _ptr(u_match), _ptr(out["len_sm"]), _ptr(out["tok_sm"]),
+        _ptr(out.get("sumprod")), _ptr(ws), ws.numel(), _stream(dev)), "vsel_spec_match_filtered")
     return out

@@ -330,6 +330,42 @@ ChainWs chain_layout(Layout& L, int64_t rows, int64_t vocab, int32_t top_k) {
   return w;
 }
 
+// Filtered speculative acceptance: after the speculative workspace, per row
+// the smallest kept key and the kept set's lse (target rows, then draft
+// rows), then the filter pass's scratch: a top-k workspace and, apart from
+// it, a nucleus workspace (also used by the min-p threshold pass), each at
+// its own 256-byte aligned base and used by the target rows and then the
+// draft rows.  The two are disjoint, so calls with any filters can share one
+// workspace: each keeps its own counters at zero.
+struct SpecFiltWs {
+  size_t kfl, lse, sub_topk, topk_bytes, sub_nuc, nuc_bytes, end;
+};
+SpecFiltWs spec_filter_layout(size_t spec_end, int64_t B, int64_t G, int64_t V) {
+  SpecFiltWs w{};
+  const int64_t nT = B * (G + 1), nrows = B * (2 * G + 1);
+  Layout L;
+  L.off = align_up(spec_end);
+  w.kfl = L.take((size_t)nrows * 8);
+  w.lse = L.take((size_t)nrows * 8);
+  size_t tk = 0, nu = 0;
+  for (const int64_t rows : {nT, B * G}) {
+    for (int64_t k = 1; k <= std::min<int64_t>(VSEL_K_MAX, V); ++k) {
+      Layout b;
+      topk_layout(b, rows, k, plan_topk_bound(rows, V, k));
+      tk = std::max(tk, b.off);
+    }
+    Layout b;
+    nucleus_layout(b, rows, plan_scan_bound(rows, V));
+    nu = std::max(nu, b.off);
+  }
+  w.sub_topk = L.take(tk);
+  w.topk_bytes = tk;
+  w.sub_nuc = L.take(nu);
+  w.nuc_bytes = nu;
+  w.end = L.off;
+  return w;
+}
+
 bool ws_ok(void* ws, size_t have, size_t need) {
   return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) % kWsAlign == 0) && have >= need;
 }
@@ -393,12 +429,14 @@ size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int3
       chain_layout(L, rows, vocab, k);
       return L.off;
     }
-    case VSEL_OP_SPEC_ACCEPT: {
+    case VSEL_OP_SPEC_ACCEPT:
+    case VSEL_OP_SPEC_FILTERED: {
       const int64_t B = rows, G = k;
       if (B < 1 || G < 1 || G > kMaxSegments || vocab > kMaxDrawVocab || !rows_ok(B * (2 * G + 1), vocab, vocab))
         return 0;
       spec_layout(L, B, G, vocab, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
-      return L.off;
+      if (op == VSEL_OP_SPEC_ACCEPT) return L.off;
+      return spec_filter_layout(L.off, B, G, vocab).end;
     }
     default:
       return 0;
@@ -766,6 +804,151 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   p.tok_aa = out_tok_aa;
   p.summin = out_summin;
   return launched(launch_spec(p, s));
+}
+
+// The filter pass of filtered speculative acceptance: for the target rows and
+// then the draft rows, the smallest kept key and the kept set's lse at T.
+// top_k >= 1: the top-k kernel's candidates (top-p and min-p on them);
+// top_k == 0: the whole-row nucleus (top_p < 1) or the min-p threshold.
+// Temperature 0 or no filter: nothing to do (the unfiltered rules).
+static vsel_status spec_filter(SpecArgs& p, int32_t top_k, float top_p, float min_p, void* ws, const SpecFiltWs& fw,
+                               hipStream_t s) {
+  if (p.T == 0.0f || (top_k == 0 && top_p >= 1.0f && min_p <= 0.0f)) return VSEL_OK;
+  const int64_t G = p.gamma, nT = p.B * (G + 1), nD = p.B * G;
+  uint64_t* kfl = at<uint64_t>(ws, fw.kfl);
+  double* lse = at<double>(ws, fw.lse);
+  void* sub = at<char>(ws, fw.sub_nuc);
+  for (int part = 0; part < 2; ++part) {
+    const float* x = part == 0 ? p.tgt : p.dft;
+    const int64_t ld = part == 0 ? p.ld_t : p.ld_d;
+    const int64_t rows = part == 0 ? nT : nD, off = part == 0 ? 0 : nT;
+    if (top_k >= 1) {
+      TopkArgs a{};
+      a.mode = 2;
+      a.temperature = p.T;
+      a.top_p = top_p;
+      a.top_n_sigma = 0.0f;
+      a.typical_p = 1.0f;
+      a.min_p = min_p;
+      a.out_kfl = kfl + off;
+      a.out_lse_f = lse + off;
+      const int32_t k = (int32_t)std::min<int64_t>(top_k, p.V);
+      const vsel_status st =
+          topk_common(x, VSEL_F32, rows, p.V, ld, k, false, a, at<char>(ws, fw.sub_topk), fw.topk_bytes, s);
+      if (st != VSEL_OK) return st;
+      continue;
+    }
+    Layout L;
+    const NucWs nw = nucleus_layout(L, rows, plan_scan_bound(rows, p.V));
+    NucArgs n{};
+    n.x = x;
+    n.ld = ld;
+    n.rows = rows;
+    n.V = p.V;
+    n.vec = aligned16(x, ld, 4) ? 1 : 0;
+    n.st_max = p.st_max + off;
+    n.st_bad = p.st_bad + off;
+    n.sigma = nullptr;
+    n.top_n_sigma = 0.0f;
+    n.top_p = top_p;
+    n.min_p = min_p;
+    n.T = p.T;
+    n.tickets = at<uint32_t>(sub, nw.tickets);
+    n.h0w = at<double>(sub, nw.h0w);
+    n.h0c = at<uint32_t>(sub, nw.h0c);
+    n.hTw = at<double>(sub, nw.hTw);
+    n.hTc = at<uint32_t>(sub, nw.hTc);
+    n.lkey = at<uint64_t>(sub, nw.lkey);
+    n.lbits = at<uint32_t>(sub, nw.lbits);
+    n.lcnt = at<uint32_t>(sub, nw.lcnt);
+    n.p_z0 = at<double>(sub, nw.p_z0);
+    n.p_a = at<double>(sub, nw.p_a);
+    n.p_at = at<double>(sub, nw.p_at);
+    n.p_a2 = at<double>(sub, nw.p_a2);
+    n.plan = at<NucPlan>(sub, nw.plan);
+    n.out_kfl = kfl + off;
+    n.out_lse_f = lse + off;
+    if (top_p < 1.0f) {
+      const Plan pn = plan_segments(rows, p.V, 0, 2 * (int64_t)device_cus(), kCapLarge);
+      n.seg_len = pn.seg_len;
+      n.S = pn.S;
+      if (launch_row_nucleus(VSEL_F32, n, s) != hipSuccess) return VSEL_EDEVICE;
+    } else {
+      const Plan ps = plan_scan(VSEL_F32, false, rows, p.V);
+      n.seg_len = ps.seg_len;
+      n.S = ps.S;
+      if (launch_kept_lse(VSEL_F32, n, s) != hipSuccess) return VSEL_EDEVICE;
+    }
+  }
+  p.kfl = kfl;
+  p.st_lse = lse;
+  return VSEL_OK;
+}
+
+static bool filters_ok(int32_t top_k, float top_p, float min_p) {
+  return top_k >= 0 && top_k <= VSEL_K_MAX && top_p > 0.0f && top_p <= 1.0f && min_p >= 0.0f && min_p <= 1.0f;
+}
+
+// The whole workspace of a filtered call, checked before anything launches.
+static bool spec_filtered_ws(int64_t batch, int32_t gamma, int64_t vocab, void* ws, size_t ws_bytes, SpecFiltWs& fw) {
+  if (batch < 1 || gamma < 1 || gamma > kMaxSegments || vocab < 1 || vocab > kMaxDrawVocab ||
+      !rows_ok(batch * (2 * (int64_t)gamma + 1), vocab, vocab))
+    return true;  // spec_prepare reports the bad argument
+  Layout L;
+  spec_layout(L, batch, gamma, vocab, plan_scan_bound(batch * (2 * (int64_t)gamma + 1), vocab),
+              plan_scan_bound(batch * (int64_t)gamma, vocab));
+  fw = spec_filter_layout(L.off, batch, gamma, vocab);
+  return ws_ok(ws, ws_bytes, fw.end);
+}
+
+vsel_status vsel_spec_accept_filtered(const float* target, int64_t ld_t, const float* draft, int64_t ld_d,
+                                      int64_t batch, int32_t gamma, int64_t vocab, float temperature, int32_t top_k,
+                                      float top_p, float min_p, const uint32_t* draft_tokens, const float* u_accept,
+                                      const float* u_resid, const float* u_bonus, int32_t* out_len_mrs,
+                                      uint32_t* out_tok_mrs, int32_t* out_len_aa, uint32_t* out_tok_aa,
+                                      float* out_summin, void* ws, size_t ws_bytes, void* stream) {
+  if (!u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs) return VSEL_EINVAL;
+  if (!filters_ok(top_k, top_p, min_p)) return VSEL_EINVAL;
+  SpecFiltWs fw{};
+  if (!spec_filtered_ws(batch, gamma, vocab, ws, ws_bytes, fw)) return VSEL_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  SpecArgs p;
+  vsel_status st =
+      spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws, ws_bytes, s, p);
+  if (st != VSEL_OK) return st;
+  if ((st = spec_filter(p, top_k, top_p, min_p, ws, fw, s)) != VSEL_OK) return st;
+  p.u_acc = u_accept;
+  p.u_res = u_resid;
+  p.u_bon = u_bonus;
+  p.len_mrs = out_len_mrs;
+  p.tok_mrs = out_tok_mrs;
+  p.len_aa = out_len_aa;
+  p.tok_aa = out_tok_aa;
+  p.summin = out_summin;
+  return launched(launch_spec(p, s));
+}
+
+vsel_status vsel_spec_match_filtered(const float* target, int64_t ld_t, const float* draft, int64_t ld_d,
+                                     int64_t batch, int32_t gamma, int64_t vocab, float temperature, int32_t top_k,
+                                     float top_p, float min_p, const uint32_t* draft_tokens, const float* u_match,
+                                     int32_t* out_len, uint32_t* out_tok, float* out_sumprod, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (!u_match || !out_len || !out_tok) return VSEL_EINVAL;
+  if (!filters_ok(top_k, top_p, min_p)) return VSEL_EINVAL;
+  SpecFiltWs fw{};
+  if (!spec_filtered_ws(batch, gamma, vocab, ws, ws_bytes, fw)) return VSEL_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  SpecArgs p;
+  vsel_status st =
+      spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws, ws_bytes, s, p);
+  if (st != VSEL_OK) return st;
+  if ((st = spec_filter(p, top_k, top_p, min_p, ws, fw, s)) != VSEL_OK) return st;
+  p.match = 1;
+  p.u_match = u_match;
+  p.len_sm = out_len;
+  p.tok_sm = out_tok;
+  p.sumprod = out_sumprod;
+  return launched(launch_spec_match(p, s));
 }
 
 vsel_status vsel_spec_match(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,

@@ -457,6 +457,11 @@ __device__ void sort_desc(uint64_t* key, uint32_t* bits, uint32_t n) {
 // only with typical_p < 1).
 struct ChainParams {
   float temperature, top_p, top_n_sigma, typical_p, min_p;
+  // instead of drawing, the kept set's smallest composite key and log sum of
+  // exp(z/T) over it (filtered speculative acceptance; typical_p == 1, so the
+  // kept set is a prefix in value order)
+  uint64_t* kfl_out;
+  double* lse_out;
 };
 __device__ inline void chain_tail(const uint64_t* key, const uint32_t* bits, uint32_t n, const ChainParams& cp,
                                   double sigma, float u, double* E, double* S, uint32_t* ORD, uint32_t* LIST,
@@ -565,7 +570,12 @@ __device__ inline void chain_tail(const uint64_t* key, const uint32_t* bits, uin
   const double T = cp.temperature;
   for (uint32_t i = tid; i < cnt; i += NT) E[i] = exp((zv(LIST[i]) - z0) / T);
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0 && cp.kfl_out) {
+    double W = 0.0;
+    for (uint32_t i = 0; i < cnt; ++i) W += E[i];
+    *cp.kfl_out = key[LIST[cnt - 1]];
+    *cp.lse_out = z0 / T + log(W);
+  } else if (tid == 0) {
     double W = 0.0;
     for (uint32_t i = 0; i < cnt; ++i) W += E[i];
     const double target = (double)u * W;

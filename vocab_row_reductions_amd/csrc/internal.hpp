@@ -64,7 +64,7 @@ struct TopkArgs {
   int32_t S;
   int32_t k;
   int32_t vec;
-  int32_t mode;   // 0: top-k outputs, 1: sampling tail
+  int32_t mode;   // 0: top-k outputs, 1: sampling tail, 2: kept-set floor and lse
   float* out_vals;
   uint32_t* out_ids;
   uint32_t* out_argmax;
@@ -76,6 +76,10 @@ struct TopkArgs {
   float typical_p;      // 1: off (needs k <= kWaveTopkMax)
   float min_p;          // 0: off
   const double* sigma;  // [rows] standard deviation of each row (top_n_sigma > 0)
+  // mode 2 (filtered speculative acceptance): per row, the smallest kept
+  // composite key and the kept set's log sum of exp(z/T); nothing is drawn
+  uint64_t* out_kfl;
+  double* out_lse_f;
   const float* u;
   uint32_t* out_token;
   float* out_logp;
@@ -140,6 +144,10 @@ struct SpecArgs {
   float* sumprod;        // [B*gamma] or null
   double* p_low;         // [B*gamma*S] mass of p below the drafted token, per segment
   double* p_wt;          // [B*gamma*S] mass of p, per segment
+  // filtered p and q (top-k / top-p / min-p): element x of a row is kept iff
+  // its composite key is >= kfl[row] (target rows then draft rows); st_lse
+  // then holds log sum over the kept elements of exp(z/T), exact in float64.
+  const uint64_t* kfl;   // null: unfiltered
 };
 
 // Plain full-row draw for vsel_sample with top_k == 0.
@@ -227,6 +235,10 @@ struct NucArgs {
   double* p_at;
   double* p_a2;
   NucPlan* plan;           // [rows]
+  // floor mode (filtered speculative acceptance): instead of drawing, the
+  // kept set's smallest composite key and log sum of exp(z/T) over it
+  uint64_t* out_kfl;       // null: sampling
+  double* out_lse_f;
 };
 
 hipError_t launch_scan(int dtype, bool want_lse, const ScanArgs& a, hipStream_t s);
@@ -244,5 +256,9 @@ hipError_t launch_spec_match(const SpecArgs& a, hipStream_t s);
 hipError_t launch_draw_rows(int dtype, const DrawArgs& a, hipStream_t s);
 hipError_t launch_moments(int dtype, const MomArgs& a, hipStream_t s);
 hipError_t launch_row_nucleus(int dtype, const NucArgs& a, hipStream_t s);
+// Floor mode with min_p only (top_p == 1): kept = z >= max + log(min_p).
+// Uses x, ld, rows, V, seg_len, S, vec, st_max, st_bad, min_p, T, tickets,
+// p_z0 and the outputs.
+hipError_t launch_kept_lse(int dtype, const NucArgs& a, hipStream_t s);
 
 }  // namespace vsel

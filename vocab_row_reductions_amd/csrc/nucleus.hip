@@ -481,8 +481,14 @@ __device__ void row_alone(FbShared& s, NucRed& r, const NucArgs& a, int64_t row,
   const SelOut cut = wg_select<DT, VEC>(s, r, xr, a.V, S1, (double)a.top_p, false);
   const uint64_t kfin = max(cut.key, c.kmp);
   const NucSet S2{c.m, c.thr, kfin, (double)a.T, e2};
-  const SelOut d = wg_select<DT, VEC>(s, r, xr, a.V, S2, (double)a.u[row], true);
+  // floor mode: only the kept set's total (a selection at 0 returns it)
+  const SelOut d = wg_select<DT, VEC>(s, r, xr, a.V, S2, a.out_kfl ? 0.0 : (double)a.u[row], true);
   if (threadIdx.x == 0) {
+    if (a.out_kfl) {
+      a.out_kfl[row] = kfin;
+      a.out_lse_f[row] = c.m / (double)a.T + log(d.tot);
+      return;
+    }
     a.out_token[row] = ~(uint32_t)d.key;
     if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - c.m) / (double)a.T - log(d.tot));
   }
@@ -616,8 +622,13 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   if (row >= a.rows) return;
   if (a.st_bad[row]) {
     if (seg == 0 && tid == 0) {
-      a.out_token[row] = kFail;
-      if (a.out_logp) a.out_logp[row] = __builtin_nanf("");
+      if (a.out_kfl) {  // (the caller fails such rows closed)
+        a.out_kfl[row] = 0ull;
+        a.out_lse_f[row] = __builtin_nan("");
+      } else {
+        a.out_token[row] = kFail;
+        if (a.out_logp) a.out_logp[row] = __builtin_nanf("");
+      }
     }
     return;
   }
@@ -741,6 +752,15 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   nk = block_sum_u32(r, nk);
   const NucSet S2{c.m, c.thr, kfin, (double)a.T, e2};
   const double WT = ATtot + sum_sorted(r, L.w.bits, nk, S2);
+  if (a.out_kfl) {  // floor mode: the kept set, nothing drawn
+    zero_hist(gw, gc);
+    if (tid == 0) {
+      a.out_kfl[row] = kfin;
+      a.out_lse_f[row] = c.m / (double)a.T + log(WT);
+      a.plan[row].state = 2u;
+    }
+    return;
+  }
   const double t2 = (double)a.u[row] * WT;
   if (t2 < ATtot) {
     // the draw falls above the window: place the draw window
@@ -848,6 +868,63 @@ __global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
     a.out_token[row] = ~(uint32_t)d.key;
     if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - c.m) / (double)a.T - log(d.tot));
   }
+}
+
+// Floor mode with min_p only: the kept set is z >= max + log(min_p); its
+// log sum of exp(z/T) in float64 (fixed order), per (row, segment).
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void kept_lse_kernel(NucArgs a) {
+  __shared__ SelShared sh;
+  __shared__ NucRed r;
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows) return;
+  if (a.st_bad[row]) {
+    if (seg == 0 && tid == 0) {
+      a.out_kfl[row] = 0ull;
+      a.out_lse_f[row] = __builtin_nan("");
+    }
+    return;
+  }
+  init_e2(e2);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const double m = a.st_max[row], T = a.T;
+  const double thr = m + log((double)a.min_p);
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  double w = 0.0;
+  for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t) {
+    const float z = __uint_as_float(bits);
+    if ((double)z >= thr) w += exp_le0(((double)z - m) / T, e2);
+  });
+  w = nuc_sum(r, w, 0);
+  if (a.S > 1) {
+    if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], w);
+    if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
+    w = merge_sum(sh, a.p_z0 + row * a.S, a.S);
+  }
+  if (tid == 0) {
+    a.out_kfl[row] = key_floor(thr);
+    a.out_lse_f[row] = m / T + log(w);
+  }
+}
+
+hipError_t launch_kept_lse(int dtype, const NucArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.rows * a.S));
+  if (dtype == 0) {
+    if (a.vec)
+      hipLaunchKernelGGL((kept_lse_kernel<float, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((kept_lse_kernel<float, false>), grid, dim3(NT), 0, s, a);
+  } else {
+    if (a.vec)
+      hipLaunchKernelGGL((kept_lse_kernel<uint16_t, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((kept_lse_kernel<uint16_t, false>), grid, dim3(NT), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 template <typename DT, bool VEC>

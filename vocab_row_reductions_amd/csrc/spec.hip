@@ -61,7 +61,7 @@ __device__ __forceinline__ double block_excl_scan_f64(SelShared& sh, double v, d
 }
 
 // ---------------------------------------------------------------- pass 2
-template <bool VEC>
+template <bool VEC, bool FILT>
 __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
   constexpr int E = 4, TILE = NT * PG * E;
   __shared__ SelShared sh;
@@ -79,21 +79,29 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
   const bool bad = a.st_bad[trow] || a.st_bad[nT + drow];
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
 
+  // filtered rows: an element below its row's key floor has p (q) = 0
+  const uint64_t kz = FILT ? a.kfl[trow] : 0ull, kd = FILT ? a.kfl[nT + drow] : 0ull;
   double tot = 0.0;
   if (a.T > 0.0f && !bad) {
     const float c = a.lse_c;
     const double Lp = a.st_lse[trow] * (double)kLog2e, Lq = a.st_lse[nT + drow] * (double)kLog2e;
     const float Lp_hi = (float)Lp, Lq_hi = (float)Lq;
     const float fp = (float)exp2(-(Lp - (double)Lp_hi)), fq = (float)exp2(-(Lq - (double)Lq_hi));
-    auto pair = [&](const auto& gz, const auto& gd) {
+    // group j of this lane starts at element t0 + (j*NT + tid)*E
+    auto pair = [&](const auto& gz, const auto& gd, int64_t t0) {
       constexpr int NGP = (int)(sizeof(gz) / sizeof(Group));
       float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < NGP; ++j)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
-          const float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
+          float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          if constexpr (FILT) {
+            const uint32_t x = (uint32_t)t0 + (uint32_t)((j * NT + tid) * E + e);
+            if (comp_key(gz[j].w[e], x) < kz) p = 0.0f;
+            if (comp_key(gd[j].w[e], x) < kd) q = 0.0f;
+          }
           acc += fminf(p, q);
         }
       tot += (double)acc;
@@ -104,18 +112,20 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
       Group gz[PG], gd[PG];
       load_tile_full<float, PG, VEC>(gz, zr + t0);
       load_tile_full<float, PG, VEC>(gd, dr + t0);
-      pair(gz, gd);
+      pair(gz, gd, t0);
     }
     for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
       Group gz[1], gd[1];
       load_tile<float, 1, VEC>(gz, zr, t0, e_full);
       load_tile<float, 1, VEC>(gd, dr, t0, e_full);
-      pair(gz, gd);
+      pair(gz, gd, t0);
     }
     if (tid == 0)
       for (int64_t x = e_full; x < e_end; ++x) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
-        const float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
+        float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        if (FILT && comp_key(__float_as_uint(zr[x]), (uint32_t)x) < kz) p = 0.0f;
+        if (FILT && comp_key(__float_as_uint(dr[x]), (uint32_t)x) < kd) q = 0.0f;
         tot += (double)fminf(p, q);
       }
   }
@@ -136,8 +146,10 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
       tot = (a.st_amax[trow] == a.st_amax[nT + drow]) ? 1.0 : 0.0;
     } else {
       const double Td = a.T;
-      const double pt = exp((double)zr[t] / Td - a.st_lse[trow]);
-      const double qt = exp((double)dr[t] / Td - a.st_lse[nT + drow]);
+      double pt = exp((double)zr[t] / Td - a.st_lse[trow]);
+      double qt = exp((double)dr[t] / Td - a.st_lse[nT + drow]);
+      if (FILT && comp_key(__float_as_uint(zr[t]), t) < kz) pt = 0.0;
+      if (FILT && comp_key(__float_as_uint(dr[t]), t) < kd) qt = 0.0;
       flag = ((double)a.u_acc[pos] * qt <= pt) ? 1u : 0u;
     }
     st_dev(&a.acc[pos], flag);
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
 // the drafted token's interval stands; a nearer one is taken again exactly.
 constexpr double kMatchTol = 1e-5;
 
-template <bool VEC>
+template <bool VEC, bool FILT>
 __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
   constexpr int E = 4, TILE = NT * PG * E;
   __shared__ SelShared sh;
@@ -219,6 +231,7 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
   const bool bad = a.st_bad[trow] || a.st_bad[nT + drow] || t >= (uint64_t)a.V;
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
 
+  const uint64_t kz = FILT ? a.kfl[trow] : 0ull, kd = FILT ? a.kfl[nT + drow] : 0ull;
   double sp = 0.0, lo = 0.0, ws = 0.0;  // sum p q, mass of p below t, mass of p
   if (a.T > 0.0f && !bad) {
     const float c = a.lse_c;
@@ -234,8 +247,12 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const uint32_t x = (uint32_t)t0 + (uint32_t)((j * NT + tid) * E + e);
-          const float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
-          const float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
+          float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          if constexpr (FILT) {
+            if (comp_key(gz[j].w[e], x) < kz) p = 0.0f;
+            if (comp_key(gd[j].w[e], x) < kd) q = 0.0f;
+          }
           a_sp = fmaf(p, q, a_sp);
           a_ws += p;
           a_lo += x < t ? p : 0.0f;
@@ -260,8 +277,10 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
     }
     if (tid == 0)
       for (int64_t x = e_full; x < e_end; ++x) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
-        const float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
+        float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        if (FILT && comp_key(__float_as_uint(zr[x]), (uint32_t)x) < kz) p = 0.0f;
+        if (FILT && comp_key(__float_as_uint(dr[x]), (uint32_t)x) < kd) q = 0.0f;
         sp += (double)(p * q);
         ws += (double)p;
         if ((uint64_t)x < t) lo += (double)p;
@@ -291,7 +310,7 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
     sp = (a.st_amax[trow] == a.st_amax[nT + drow]) ? 1.0 : 0.0;
   } else {
     const double Td = a.T, lse = a.st_lse[trow];
-    const double pt = exp((double)zr[t] / Td - lse);
+    const double pt = (FILT && comp_key(__float_as_uint(zr[t]), t) < kz) ? 0.0 : exp((double)zr[t] / Td - lse);
     const double u = (double)a.u_match[b * (G + 1) + i];
     const double target = u * ws, tol = kMatchTol * ws;
     if (target >= lo + tol && target < lo + pt - tol) {
@@ -302,7 +321,8 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
       // too close to call: the masses again, from float64 terms
       double l2 = 0.0, w2 = 0.0;
       for (int64_t x = tid; x < a.V; x += NT) {
-        const double px = exp((double)zr[x] / Td - lse);
+        const double px =
+            (FILT && comp_key(__float_as_uint(zr[x]), (uint32_t)x) < kz) ? 0.0 : exp((double)zr[x] / Td - lse);
         w2 += px;
         if ((uint64_t)x < t) l2 += px;
       }
@@ -402,6 +422,8 @@ __global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
 //   plain:    exp((z - m) / T), proportional to p (u*W does not see the scale)
 //   (plain only) elements below thr weigh nothing: the sampler chain's
 //   threshold filters over a whole row
+//   filtered p and q: an element whose composite key is below kz (of the
+//   target row) or kd (of the draft row) has p = 0 or q = 0
 template <typename DT>
 struct DrawSrc {
   const DT* z;
@@ -409,13 +431,16 @@ struct DrawSrc {
   double lp, lq, m, T;
   int64_t V;
   double thr = -__builtin_inf();
+  uint64_t kz = 0, kd = 0;
   __device__ __forceinline__ float zv(int64_t x) const { return __uint_as_float(gbits_at<DT>(z, x)); }
-  __device__ __forceinline__ double w(float zx, float dx) const {
+  __device__ __forceinline__ double w(float zx, float dx, int64_t x) const {
+    const bool pk = kz == 0 || comp_key(__float_as_uint(zx), (uint32_t)x) >= kz;
     if (d) {
-      const double p = exp((double)zx / T - lp), q = exp((double)dx / T - lq);
+      const bool qk = kd == 0 || comp_key(__float_as_uint(dx), (uint32_t)x) >= kd;
+      const double p = pk ? exp((double)zx / T - lp) : 0.0, q = qk ? exp((double)dx / T - lq) : 0.0;
       return p > q ? p - q : 0.0;
     }
-    return (double)zx >= thr ? exp(((double)zx - m) / T) : 0.0;
+    return pk && (double)zx >= thr ? exp(((double)zx - m) / T) : 0.0;
   }
 };
 
@@ -450,7 +475,7 @@ __device__ double chunk_masses(const DrawSrc<DT>& r, int64_t e_begin, int64_t e_
       const int q = q0 + wave * CW + j;
       double s = 0.0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s += r.w(zz[j][e], dd[j][e]);
+      for (int e = 0; e < 4; ++e) s += r.w(zz[j][e], dd[j][e], e_begin + (int64_t)q * kChunk + lane * 4 + e);
       s = wave_sum_f64(s);
       if (lane == 0 && q < nch) {
         cm[q] = s;
@@ -536,7 +561,7 @@ __device__ uint32_t draw_pick(SelShared& sh, const DrawSrc<DT>& r, const double*
   __syncthreads();
   const int64_t c0 = e_begin + (int64_t)s_ch * kChunk;
   const int64_t x = c0 + tid;
-  const double wx = x < e_end ? r.w(r.zv(x), r.d ? r.d[x] : 0.0f) : 0.0;
+  const double wx = x < e_end ? r.w(r.zv(x), r.d ? r.d[x] : 0.0f, x) : 0.0;
   double total;
   const double excl = block_excl_scan_f64(sh, wx, &total);
   const double t2 = s_in;
@@ -544,7 +569,7 @@ __device__ uint32_t draw_pick(SelShared& sh, const DrawSrc<DT>& r, const double*
   __syncthreads();
   if (tid == 0 && s_tok == kFail) {  // rounding: the chunk's last element with weight
     for (int64_t y = min(e_end, c0 + kChunk) - 1; y >= c0; --y)
-      if (r.w(r.zv(y), r.d ? r.d[y] : 0.0f) > 0.0) {
+      if (r.w(r.zv(y), r.d ? r.d[y] : 0.0f, y) > 0.0) {
         s_tok = (uint32_t)y;
         break;
       }
@@ -569,6 +594,7 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   r.T = a.T;
   r.V = a.V;
   double u;
+  const int64_t nT = a.B * (G + 1);
   if (a.match) {  // sampler-match: a fresh draw from p at row L
     r.z = a.tgt + (b * (G + 1) + L) * a.ld_t;
     r.d = nullptr;
@@ -578,8 +604,9 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   } else if (L < G) {
     r.z = a.tgt + (b * (G + 1) + L) * a.ld_t;
     r.d = a.dft + (b * G + L) * a.ld_d;
-    r.lp = a.lse64[b * 2];
-    r.lq = a.lse64[b * 2 + 1];
+    // filtered: the exact kept-set lse of the filter pass
+    r.lp = a.kfl ? a.st_lse[b * (G + 1) + L] : a.lse64[b * 2];
+    r.lq = a.kfl ? a.st_lse[nT + b * G + L] : a.lse64[b * 2 + 1];
     r.m = 0.0;
     u = a.u_res[b * G + L];
   } else {
@@ -588,6 +615,10 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
     r.lp = r.lq = 0.0;
     r.m = a.st_max[b * (G + 1) + G];
     u = a.u_bon[b];
+  }
+  if (a.kfl) {
+    r.kz = a.kfl[b * (G + 1) + (a.match ? L : min((int64_t)L, G))];
+    r.kd = L < G ? a.kfl[nT + b * G + L] : 0ull;
   }
   double* pc = a.p_c + b * a.nchunk;
   const int64_t e_begin = (int64_t)seg * a.dseg, e_end = min(a.V, e_begin + a.dseg);
@@ -664,12 +695,23 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
 hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
   const bool vec = a.vec_t && a.vec_d;
   const unsigned npos = (unsigned)(a.B * a.gamma * a.S);
-  if (vec)
-    hipLaunchKernelGGL(coupling_kernel<true>, dim3(npos), dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL(coupling_kernel<false>, dim3(npos), dim3(NT), 0, s, a);
+  if (a.kfl) {
+    if (vec)
+      hipLaunchKernelGGL((coupling_kernel<true, true>), dim3(npos), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((coupling_kernel<false, true>), dim3(npos), dim3(NT), 0, s, a);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((coupling_kernel<true, false>), dim3(npos), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((coupling_kernel<false, false>), dim3(npos), dim3(NT), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0.0f) return e;
+  if (a.kfl) {  // the filter pass already holds the exact lse of every row
+    hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
+    return hipGetLastError();
+  }
   if (vec)
     hipLaunchKernelGGL(draw_lse_kernel<true>, dim3((unsigned)(a.B * 2 * a.S)), dim3(NT), 0, s, a);
   else
@@ -681,10 +723,18 @@ hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
 
 hipError_t launch_spec_match(const SpecArgs& a, hipStream_t s) {
   const unsigned npos = (unsigned)(a.B * a.gamma * a.S);
-  if (a.vec_t && a.vec_d)
-    hipLaunchKernelGGL(match_kernel<true>, dim3(npos), dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL(match_kernel<false>, dim3(npos), dim3(NT), 0, s, a);
+  const bool vec = a.vec_t && a.vec_d;
+  if (a.kfl) {
+    if (vec)
+      hipLaunchKernelGGL((match_kernel<true, true>), dim3(npos), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((match_kernel<false, true>), dim3(npos), dim3(NT), 0, s, a);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((match_kernel<true, false>), dim3(npos), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((match_kernel<false, false>), dim3(npos), dim3(NT), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0.0f) return e;
   hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);

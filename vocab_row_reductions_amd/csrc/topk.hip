@@ -378,12 +378,19 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
       uint32_t* LIST = obits == s_bits ? s_bits + CAP / 2 : s_bits;
       double* Sc = reinterpret_cast<double*>(&stg[0]);
       uint32_t* ORD = &stg[1].w[0][0];
-      const ChainParams cp{a.temperature, a.top_p, a.top_n_sigma, a.typical_p, a.min_p};
-      chain_tail(okey, obits, n, cp, a.sigma ? a.sigma[row] : 0.0, a.u[row], E, Sc, ORD, LIST, &tok, &lp);
+      const ChainParams cp{a.temperature, a.top_p,  a.top_n_sigma, a.typical_p, a.min_p,
+                           a.mode == 2 ? a.out_kfl + row : nullptr, a.mode == 2 ? a.out_lse_f + row : nullptr};
+      chain_tail(okey, obits, n, cp, a.sigma ? a.sigma[row] : 0.0, a.u ? a.u[row] : 0.0f, E, Sc, ORD, LIST, &tok,
+                 &lp);
     }
     if (tid == 0) {
-      a.out_token[row] = tok;
-      if (a.out_logp) a.out_logp[row] = lp;
+      if (a.mode == 1) {
+        a.out_token[row] = tok;
+        if (a.out_logp) a.out_logp[row] = lp;
+      } else if (none || n == 0) {  // (the caller fails such rows closed)
+        a.out_kfl[row] = 0ull;
+        a.out_lse_f[row] = __builtin_nan("");
+      }
     }
   }
 }
