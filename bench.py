@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_936_948
+TRAFFIC_BYTES = 414_938_439
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "28db74d6df6983ad7ad3b480779ef226d20a0265c7ca1ab59e985efc219c46e2"
+TRAFFIC_SHA256 = "8ae3fd44850de3a98c797ef04f69957ebca6d5838c7ab986cbb8081b372b932e"
 
 
 def measured_traffic():
