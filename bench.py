@@ -264,6 +264,9 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
     ex["sample_chain_rowdraw_64x202048_device_cold_us"] = time_graph(
         lambda i: vsel.vsel_sample_chain(xs[i % len(xs)], 0.7, ud, top_n_sigma=1.0, min_p=0.05, out_token=ot,
                                          out_logprob=ol), 20, stream)
+    ex["sample_chain_typical09_wholerow_64x202048_device_cold_us"] = time_graph(
+        lambda i: vsel.vsel_sample_chain(xs[i % len(xs)], 0.7, ud, typical_p=0.9, out_token=ot, out_logprob=ol), 10,
+        stream)
     ex["sample_chain_topp095_wholerow_64x202048_device_cold_us"] = time_graph(
         lambda i: vsel.vsel_sample_chain(xs[i % len(xs)], 0.7, ud, top_p=0.95, out_token=ot, out_logprob=ol), 20,
         stream)

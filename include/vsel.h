@@ -213,10 +213,12 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
  * filters off except top_k / top_p this is vsel_sample.
  *   temperature >= 0 and finite; top_n_sigma >= 0 and finite;
  *   0 <= top_k <= VSEL_K_MAX; 0 < typical_p <= 1; 0 < top_p <= 1;
- *   0 <= min_p <= 1.  typical_p < 1 needs 1 <= top_k <= 128.  With
- *   top_k == 0, vocab <= 67,108,864; top_p < 1 then cuts the nucleus of the
- *   whole row, and the draw runs in (value desc, id asc) order (with
- *   top_p == 1 it runs in id order, as in vsel_sample).
+ *   0 <= min_p <= 1.  typical_p < 1 needs top_k <= 128.  With top_k == 0,
+ *   vocab <= 67,108,864, and the filters act on the whole row: typical_p < 1
+ *   orders it by |z - c| (c = the p-weighted mean of z, since -log p - H =
+ *   c - z), then id; top_p < 1 orders it (or the typical set) by value, and
+ *   the draw follows the last order (with neither, id order, as in
+ *   vsel_sample).  The typical order compares the distances in float32.
  *   u, out_token, out_logprob as vsel_sample; workspace VSEL_OP_SAMPLE_CHAIN
  *   with k = top_k.
  */

@@ -134,7 +134,7 @@ def sample(x, temperature, top_k, top_p, u, vocab=None, nthreads=0):
 def sample_chain(x, temperature, u, top_n_sigma=0.0, top_k=0, typical_p=1.0, top_p=1.0, min_p=0.0, vocab=None,
                  nthreads=0):
     """The ordered sampler chain (top-n-sigma, top-k, typical-p, top-p, min-p,
-    temperature) -> (tokens uint32[R], logp float64[R], margins float64[R, 5])."""
+    temperature) -> (tokens uint32[R], logp float64[R], margins float64[R, 6])."""
     x, dt = _rows(x)
     R, ld = x.shape
     V = ld if vocab is None else vocab
@@ -142,7 +142,7 @@ def sample_chain(x, temperature, u, top_n_sigma=0.0, top_k=0, typical_p=1.0, top
     assert u.shape == (R,)
     tok = np.empty(R, np.uint32)
     logp = np.empty(R, np.float64)
-    margins = np.empty((R, 5), np.float64)
+    margins = np.empty((R, 6), np.float64)
     _check(lib().oracle_sample_chain(_p(x), dt, R, V, ld, float(temperature), float(top_n_sigma), int(top_k),
                                      float(typical_p), float(top_p), float(min_p), _p(u), _p(tok), _p(logp),
                                      _p(margins), nthreads))

@@ -428,10 +428,12 @@ int oracle_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, in
 //   6. w = exp((z - z_max) / T) over the kept candidates, the inverse-CDF draw
 //      with u in their current order, logp = log(w_j / sum w).
 // T == 0 or top_k == 1: the argmax, logp 0 (nothing drawn).
-// margins (5 per row, +inf when not applicable): the draw margin over W; the
+// margins (6 per row, +inf when not applicable): the draw margin over W; the
 // distance of typical_p / top_p to the nearer cumulative sum at its cut; the
 // distance of the top-n-sigma and min-p thresholds to the nearest candidate
-// value (logit units).
+// value (logit units); the smallest relative gap between the typicality
+// scores of the typical cut's element, or of the element drawn in typical
+// order, and its neighbours in that order (elements of equal value excluded).
 int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                         float temperature, float top_n_sigma, int32_t top_k, float typical_p, float top_p,
                         float min_p, const float* u, uint32_t* out_token, double* out_logp, double* margins,
@@ -443,12 +445,12 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
   Rows R{logits, dtype, ld};
   const double T = temperature;
   for_rows(rows, nthreads, [&](int64_t r) {
-    double mg[5] = {kInf, kInf, kInf, kInf, kInf};
+    double mg[6] = {kInf, kInf, kInf, kInf, kInf, kInf};
     auto finish = [&](uint32_t tok, double logp) {
       out_token[r] = tok;
       if (out_logp) out_logp[r] = logp;
       if (margins)
-        for (int q = 0; q < 5; ++q) margins[5 * r + q] = mg[q];
+        for (int q = 0; q < 6; ++q) margins[6 * r + q] = mg[q];
     };
     const uint32_t am = argmax_row(R, r, vocab, nullptr);
     if (am == kFailClosed) return finish(kFailClosed, kNaN);
@@ -505,6 +507,13 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
       }
     };
     // 3. typical-p
+    // tscore: each candidate's typicality score, kept for the near-tie margin
+    std::vector<double> tscore;
+    auto tgap = [&](uint32_t a, uint32_t b) {  // relative score gap of two ids (+inf for equal values)
+      if (z(a) == z(b)) return kInf;
+      const double sa = tscore[a], sb = tscore[b];
+      return std::fabs(sa - sb) / std::max(std::max(sa, sb), 1e-300);
+    };
     if (typical_p < 1.0f) {
       std::vector<double> p;
       probs(p);
@@ -517,12 +526,20 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
       std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return score(a) < score(b); });
       std::vector<uint32_t> c2(cand.size());
       std::vector<double> p2(cand.size());
+      tscore.assign(static_cast<size_t>(vocab), kInf);
       for (size_t j = 0; j < idx.size(); ++j) {
         c2[j] = cand[idx[j]];
         p2[j] = p[idx[j]];
+        tscore[c2[j]] = score(idx[j]);
       }
       cand.swap(c2);
+      const std::vector<uint32_t> full = cand;
       cut(p2, typical_p, &mg[1]);
+      // near-ties of the typical order beside the cut (an order taken in
+      // float32 scores may swap them)
+      const size_t jc = cand.size() - 1;
+      if (jc + 1 < full.size()) mg[5] = std::min(mg[5], tgap(full[jc], full[jc + 1]));
+      if (jc > 0) mg[5] = std::min(mg[5], tgap(full[jc], full[jc - 1]));
     }
     // 4. top-p
     if (top_p < 1.0f) {
@@ -547,6 +564,10 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
     std::vector<double> w(cand.size());
     for (size_t j = 0; j < cand.size(); ++j) w[j] = std::exp((z(cand[j]) - zmax) / T);
     const size_t j = draw(w, static_cast<double>(u[r]), &mg[0]);
+    if (typical_p < 1.0f && top_p >= 1.0f) {  // the draw ran in typical order: near-ties beside it
+      if (j + 1 < cand.size()) mg[5] = std::min(mg[5], tgap(cand[j], cand[j + 1]));
+      if (j > 0) mg[5] = std::min(mg[5], tgap(cand[j], cand[j - 1]));
+    }
     double S = 0.0;
     for (double v : w) S += v;
     finish(cand[j], (z(cand[j]) - zmax) / T - std::log(S));

@@ -97,7 +97,7 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
     def chain(T=0.7, sig=0.0, k=20, typ=1.0, p=1.0, mp=0.0, u=fake, ws_bytes=1 << 20):
         return L.vsel_sample_chain(fake, 0, 4, 100, 100, T, sig, k, typ, p, mp, u, fake, None, ws, ws_bytes, None)
     bad_chain = [dict(sig=-1.0), dict(sig=float("inf")), dict(sig=float("nan")), dict(typ=0.0), dict(typ=1.5),
-                 dict(mp=-0.1), dict(mp=1.01), dict(mp=float("nan")), dict(k=0, typ=0.9),
+                 dict(mp=-0.1), dict(mp=1.01), dict(mp=float("nan")),
                  dict(k=129, typ=0.9), dict(k=-1), dict(k=1025), dict(p=0.0), dict(T=float("inf")),
                  dict(T=-0.1), dict(u=None)]
     for kw in bad_chain:

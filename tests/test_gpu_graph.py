@@ -62,7 +62,7 @@ def test_sample_chain_graph(g):
     xs, u = W.sampling_rows(rows=9, vocab=50000, seed=76)
     x, ud = g.dev_rows(xs), g.dev(u)
     for kw in (dict(top_n_sigma=1.0, top_k=40, typical_p=0.8, top_p=0.9, min_p=0.02), dict(top_n_sigma=0.7, min_p=0.01),
-               dict(top_p=0.9, min_p=0.01)):
+               dict(top_p=0.9, min_p=0.01), dict(typical_p=0.8, top_p=0.95)):
         tok, lp = g.vsel.vsel_sample_chain(x, 0.8, ud, **kw)
         ref = [tok.clone(), lp.clone()]
         ot, ol = torch.empty_like(tok), torch.empty_like(lp)

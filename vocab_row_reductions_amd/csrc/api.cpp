@@ -543,7 +543,7 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
   if (!(temperature >= 0.0f) || std::isinf(temperature) || top_k < 0 || top_k > VSEL_K_MAX ||
       !(top_p > 0.0f && top_p <= 1.0f))
     return VSEL_EINVAL;
-  if (top_k == 0 && (typical_p < 1.0f || (top_p < 1.0f && !(cw && cw->has_nuc)))) return VSEL_EINVAL;
+  if (top_k == 0 && (typical_p < 1.0f || top_p < 1.0f) && !(cw && cw->has_nuc)) return VSEL_EINVAL;
   if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
   if (top_n_sigma > 0.0f && !cw) return VSEL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
@@ -602,6 +602,28 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
     a.st_bad = at<uint32_t>(ws, w.st.bad);
     hipError_t e = launch_scan(dtype, false, a, s);
     if (e != hipSuccess) return VSEL_EDEVICE;
+    if (typical_p < 1.0f) {
+      // typical-p over the whole row (then top-p, min-p, the draw), one
+      // workgroup per row
+      NucArgs n{};
+      n.x = logits;
+      n.ld = ld;
+      n.rows = rows;
+      n.V = vocab;
+      n.vec = a.vec1;
+      n.st_max = a.st_max;
+      n.st_bad = a.st_bad;
+      n.sigma = sigma;
+      n.top_n_sigma = top_n_sigma;
+      n.top_p = top_p;
+      n.min_p = min_p;
+      n.typical_p = typical_p;
+      n.T = temperature;
+      n.u = u;
+      n.out_token = out_token;
+      n.out_logp = out_logprob;
+      return launched(launch_row_typical(dtype, n, s));
+    }
     if (top_p < 1.0f) {
       // the nucleus over the whole row, then the draw in value order
       NucArgs n{};
@@ -698,7 +720,6 @@ vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64
       !(top_p > 0.0f && top_p <= 1.0f) || !(top_n_sigma >= 0.0f) || std::isinf(top_n_sigma) ||
       !(typical_p > 0.0f && typical_p <= 1.0f) || !(min_p >= 0.0f && min_p <= 1.0f))
     return VSEL_EINVAL;
-  if (top_k == 0 && typical_p < 1.0f) return VSEL_EINVAL;
   if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
   const size_t base = sample_ws_bytes(rows, vocab, top_k);
   if (base == 0) return VSEL_EINVAL;

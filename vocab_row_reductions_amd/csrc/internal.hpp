@@ -219,6 +219,7 @@ struct NucArgs {
   const uint32_t* st_bad;  // [rows] fail-closed rows (scan)
   const double* sigma;     // [rows] standard deviations (top_n_sigma > 0)
   float top_n_sigma, top_p, min_p, T;
+  float typical_p;         // (the typical-p kernel)
   const float* u;
   uint32_t* out_token;
   float* out_logp;
@@ -260,5 +261,8 @@ hipError_t launch_row_nucleus(int dtype, const NucArgs& a, hipStream_t s);
 // Uses x, ld, rows, V, seg_len, S, vec, st_max, st_bad, min_p, T, tickets,
 // p_z0 and the outputs.
 hipError_t launch_kept_lse(int dtype, const NucArgs& a, hipStream_t s);
+// Typical-p over whole rows, one workgroup per row (x, ld, rows, V, vec,
+// st_max, st_bad, sigma, the filters, T, u and the outputs).
+hipError_t launch_row_typical(int dtype, const NucArgs& a, hipStream_t s);
 
 }  // namespace vsel

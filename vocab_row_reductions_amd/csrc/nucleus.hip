@@ -75,25 +75,44 @@ __device__ __forceinline__ void init_e2(double* e2) {
   __syncthreads();
 }
 
-// The candidates of one selection and their weights.
+// The candidates of one selection, their order and their weights.
+//   order 0: (value desc, id asc), key comp_key;
+//   order 1: typicality, (|z - c| asc, id asc), key score_key: the distance
+//     to the typical centre c in float32 above the complemented id.
+//   A typical set (kT != 0) keeps the elements whose score key is >= kT.
 struct NucSet {
   double m;           // the row maximum
   double thr;         // candidates have z >= thr (and z > -inf)
-  uint64_t kfloor;    // ... and composite key >= kfloor
+  uint64_t kfloor;    // ... and order key >= kfloor
   double T;           // weight exp((z - m) / T)
   const double* e2;   // the exp table
+  int order;          // 0 value, 1 typicality
+  double c;           // typical centre (order 1, typical sets)
+  double span;        // order 1: first-level bins are equal steps of the score over [0, span)
+  uint64_t kT;        // typical set: score key >= kT (0: none)
+  __device__ __forceinline__ uint64_t score_key(uint32_t bits, uint32_t i) const {
+    const float sc = (float)fabs((double)__uint_as_float(bits) - c);
+    return ((uint64_t)(~__float_as_uint(sc)) << 32) | (uint64_t)(~i);
+  }
+  __device__ __forceinline__ uint64_t key(uint32_t bits, uint32_t i) const {
+    return order == 0 ? comp_key(bits, i) : score_key(bits, i);
+  }
   __device__ __forceinline__ bool in(float z, uint64_t K) const {
     return z > -__builtin_inff() && (double)z >= thr && K >= kfloor;
+  }
+  __device__ __forceinline__ bool in(uint32_t bits, uint32_t i, uint64_t K) const {
+    return in(__uint_as_float(bits), K) && (kT == 0 || score_key(bits, i) >= kT);
   }
   __device__ __forceinline__ double x(float z) const { return T == 1.0 ? (double)z - m : ((double)z - m) / T; }
   __device__ __forceinline__ double w(float z) const { return exp_le0(x(z), e2); }
   __device__ __forceinline__ float gw(float z) const {
     return __builtin_amdgcn_exp2f((float)(x(z) * 1.4426950408889634));
   }
-  // first-level bin: equal steps of (m - z) / T over [0, kSpan)
+  // first-level bin: equal steps of (m - z) / T over [0, kSpan) (order 0),
+  // or of the score over [0, span) (order 1)
   template <int NB>
   __device__ __forceinline__ uint32_t bin(float z) const {
-    const double d = -x(z);
+    const double d = order == 0 ? -x(z) : fabs((double)z - c) * (kSpan / span);
     return d >= kSpan ? (uint32_t)(NB - 1) : (uint32_t)(d * (NB / kSpan));
   }
 };
@@ -334,7 +353,7 @@ __device__ SelOut wg_select(FbShared& s, NucRed& r, const DT* __restrict__ xr, i
   double g = 0.0;
   for_each_elem<DT, kNG, VEC>(xr, 0, V, [&](uint32_t bits, int64_t i) {
     const float z = __uint_as_float(bits);
-    if (S.in(z, comp_key(bits, (uint32_t)i))) {
+    if (S.in(bits, (uint32_t)i, S.key(bits, (uint32_t)i))) {
       const float gw = S.gw(z);
       const uint32_t b = S.bin<kFbNB>(z);
       __hip_atomic_fetch_add(&s.hw[b], (double)gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -360,8 +379,8 @@ __device__ SelOut wg_select(FbShared& s, NucRed& r, const DT* __restrict__ xr, i
     uint64_t kmin = ~0ull, kmax = 0ull;
     for_each_elem<DT, kNG, VEC>(xr, 0, V, [&](uint32_t bits, int64_t i) {
       const float z = __uint_as_float(bits);
-      const uint64_t K = comp_key(bits, (uint32_t)i);
-      if (!S.in(z, K)) return;
+      const uint64_t K = S.key(bits, (uint32_t)i);
+      if (!S.in(bits, (uint32_t)i, K)) return;
       const double w = S.w(z);
       t_l += w;
       bool above, inw;
@@ -417,8 +436,8 @@ __device__ SelOut wg_select(FbShared& s, NucRed& r, const DT* __restrict__ xr, i
     __syncthreads();
     for_each_elem<DT, kNG, VEC>(xr, 0, V, [&](uint32_t bits, int64_t i) {
       const float z = __uint_as_float(bits);
-      const uint64_t K = comp_key(bits, (uint32_t)i);
-      if (!S.in(z, K) || K > khi || K < klo) return;
+      const uint64_t K = S.key(bits, (uint32_t)i);
+      if (!S.in(bits, (uint32_t)i, K) || K > khi || K < klo) return;
       const uint32_t b = (uint32_t)((khi - K) >> sh);
       __hip_atomic_fetch_add(&s.hw[b], (double)S.gw(z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_add(&s.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -868,6 +887,112 @@ __global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
     a.out_token[row] = ~(uint32_t)d.key;
     if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - c.m) / (double)a.T - log(d.tot));
   }
+}
+
+// Typical-p over whole rows (top_k = 0), one workgroup per row ("Chapter 21",
+// section 21.7: typical_p after top_n_sigma and before top_p; ties keep the
+// candidates' id order).  With p the softmax of the candidates, -log p - H =
+// E_p[z] - z, so the typical order is the distance of z to the centre
+// c = E_p[z] (then id); the typical set is the shortest prefix of that order
+// whose mass reaches typical_p.  Then top-p in value order within it (when
+// top_p < 1), min-p against its maximum, and the draw in value order (top_p
+// < 1) or typical order (top_p == 1).
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void row_typical_kernel(NucArgs a) {
+  __shared__ NucRed r;
+  __shared__ FbShared fb;
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  if (row >= a.rows) return;
+  if (a.st_bad[row]) {
+    if (tid == 0) {
+      a.out_token[row] = kFail;
+      if (a.out_logp) a.out_logp[row] = __builtin_nanf("");
+    }
+    return;
+  }
+  init_e2(e2);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const double m = a.st_max[row];
+  const double thr = a.top_n_sigma > 0.0f ? m - (double)a.top_n_sigma * a.sigma[row] : -__builtin_inf();
+  // 1. the candidates' mass and mass-weighted value (float64, fixed order):
+  //    the centre c, and the score range for the first-level bins
+  double z0 = 0.0, y = 0.0, zlo = m;
+  for_each_elem<DT, kNG, VEC>(xr, 0, a.V, [&](uint32_t bits, int64_t) {
+    const float z = __uint_as_float(bits);
+    if (z > -__builtin_inff() && (double)z >= thr) {
+      const double w = exp_le0((double)z - m, e2);
+      z0 += w;
+      y += w * (double)z;
+      zlo = fmin(zlo, (double)z);
+    }
+  });
+  const double Z0 = nuc_sum(r, z0, 0), Y = nuc_sum(r, y, 1);
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int d = 1; d < 64; d <<= 1) zlo = fmin(zlo, __shfl_xor(zlo, d));
+    __syncthreads();
+    if (lane == 0) r.rd[wave] = zlo;
+    __syncthreads();
+    for (int q = 0; q < NWAVE; ++q) zlo = fmin(zlo, r.rd[q]);
+    __syncthreads();
+  }
+  const double cen = Y / Z0;
+  const double span = fmax(fmax(m - cen, cen - zlo), 1e-30) * (1.0 + 1e-6);
+  // 2. the typical cut
+  const NucSet ST{m, thr, 0ull, 1.0, e2, 1, cen, span, 0ull};
+  const uint64_t kT = wg_select<DT, VEC>(fb, r, xr, a.V, ST, (double)a.typical_p, false).key;
+  // the typical set's maximum (the min-p reference)
+  double mT = -__builtin_inf();
+  if (a.min_p > 0.0f) {
+    const NucSet SM{m, thr, 0ull, 1.0, e2, 0, cen, span, kT};
+    for_each_elem<DT, kNG, VEC>(xr, 0, a.V, [&](uint32_t bits, int64_t i) {
+      if (SM.in(bits, (uint32_t)i, 0ull)) mT = fmax(mT, (double)__uint_as_float(bits));
+    });
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int d = 1; d < 64; d <<= 1) mT = fmax(mT, __shfl_xor(mT, d));
+    __syncthreads();
+    if (lane == 0) r.rd[wave] = mT;
+    __syncthreads();
+    for (int q = 0; q < NWAVE; ++q) mT = fmax(mT, r.rd[q]);
+    __syncthreads();
+  }
+  SelOut d;
+  if (a.top_p < 1.0f) {
+    // 3. top-p in value order within the typical set, then min-p (a value
+    //    prefix too), then the draw in value order
+    const NucSet SV{m, thr, 0ull, 1.0, e2, 0, cen, span, kT};
+    uint64_t kfin = wg_select<DT, VEC>(fb, r, xr, a.V, SV, (double)a.top_p, false).key;
+    if (a.min_p > 0.0f) kfin = max(kfin, key_floor(mT + log((double)a.min_p)));
+    const NucSet SD{m, thr, kfin, (double)a.T, e2, 0, cen, span, kT};
+    d = wg_select<DT, VEC>(fb, r, xr, a.V, SD, (double)a.u[row], true);
+  } else {
+    // 3. min-p (a value threshold), then the draw in typical order
+    const double thr2 = a.min_p > 0.0f ? fmax(thr, mT + log((double)a.min_p)) : thr;
+    const NucSet SD{m, thr2, 0ull, (double)a.T, e2, 1, cen, span, kT};
+    d = wg_select<DT, VEC>(fb, r, xr, a.V, SD, (double)a.u[row], true);
+  }
+  if (tid == 0) {
+    a.out_token[row] = ~(uint32_t)d.key;
+    if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - m) / (double)a.T - log(d.tot));
+  }
+}
+
+hipError_t launch_row_typical(int dtype, const NucArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.rows);
+  if (dtype == 0) {
+    if (a.vec)
+      hipLaunchKernelGGL((row_typical_kernel<float, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((row_typical_kernel<float, false>), grid, dim3(NT), 0, s, a);
+  } else {
+    if (a.vec)
+      hipLaunchKernelGGL((row_typical_kernel<uint16_t, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((row_typical_kernel<uint16_t, false>), grid, dim3(NT), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 // Floor mode with min_p only: the kept set is z >= max + log(min_p); its
