@@ -638,7 +638,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 #pragma unroll
     for (uint32_t q = 0; q < kPer; ++q) {
       const uint32_t i = q * 64 + lane;
-      held[q] = i < wcnt ? wb[i] : 0ull;
+      held[q] = wb[i];  // i < kWCap: inside the wave's list; entries past wcnt are masked
       const bool keep = i < wcnt && held[q] >= Tb;
       const uint64_t m = __ballot(keep);
       place[q] = keep ? kept + lane_rank(m) : 0xFFFFFFFFu;
