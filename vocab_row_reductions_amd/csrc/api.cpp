@@ -338,7 +338,7 @@ ChainWs chain_layout(Layout& L, int64_t rows, int64_t vocab, int32_t top_k) {
 // draft rows.  The two are disjoint, so calls with any filters can share one
 // workspace: each keeps its own counters at zero.
 struct SpecFiltWs {
-  size_t kfl, lse, sub_topk, topk_bytes, sub_nuc, nuc_bytes, end;
+  size_t kfl, lse, sub_topk, topk_bytes, sub_nuc[2], end;
 };
 SpecFiltWs spec_filter_layout(size_t spec_end, int64_t B, int64_t G, int64_t V) {
   SpecFiltWs w{};
@@ -347,8 +347,15 @@ SpecFiltWs spec_filter_layout(size_t spec_end, int64_t B, int64_t G, int64_t V) 
   L.off = align_up(spec_end);
   w.kfl = L.take((size_t)nrows * 8);
   w.lse = L.take((size_t)nrows * 8);
-  size_t tk = 0, nu = 0;
-  for (const int64_t rows : {nT, B * G}) {
+  // The top-k passes of the two parts (target rows, draft rows) share one
+  // region: its only zero-required words, the tickets, lead every top-k
+  // layout, so each part's tickets lie in the other's.  The nucleus passes
+  // need their window counters zero as well, which sit behind row-sized
+  // regions: each part gets a region of its own.
+  size_t tk = 0, nu[2] = {0, 0};
+  const int64_t part_rows[2] = {nT, B * G};
+  for (int part = 0; part < 2; ++part) {
+    const int64_t rows = part_rows[part];
     for (int64_t k = 1; k <= std::min<int64_t>(VSEL_K_MAX, V); ++k) {
       Layout b;
       topk_layout(b, rows, k, plan_topk_bound(rows, V, k));
@@ -356,12 +363,12 @@ SpecFiltWs spec_filter_layout(size_t spec_end, int64_t B, int64_t G, int64_t V) 
     }
     Layout b;
     nucleus_layout(b, rows, plan_scan_bound(rows, V));
-    nu = std::max(nu, b.off);
+    nu[part] = b.off;
   }
   w.sub_topk = L.take(tk);
   w.topk_bytes = tk;
-  w.sub_nuc = L.take(nu);
-  w.nuc_bytes = nu;
+  w.sub_nuc[0] = L.take(nu[0]);
+  w.sub_nuc[1] = L.take(nu[1]);
   w.end = L.off;
   return w;
 }
@@ -838,8 +845,8 @@ static vsel_status spec_filter(SpecArgs& p, int32_t top_k, float top_p, float mi
   const int64_t G = p.gamma, nT = p.B * (G + 1), nD = p.B * G;
   uint64_t* kfl = at<uint64_t>(ws, fw.kfl);
   double* lse = at<double>(ws, fw.lse);
-  void* sub = at<char>(ws, fw.sub_nuc);
   for (int part = 0; part < 2; ++part) {
+    void* sub = at<char>(ws, fw.sub_nuc[part]);
     const float* x = part == 0 ? p.tgt : p.dft;
     const int64_t ld = part == 0 ? p.ld_t : p.ld_d;
     const int64_t rows = part == 0 ? nT : nD, off = part == 0 ? 0 : nT;

@@ -10,9 +10,11 @@
 //   2. the draw: among the kept candidates (the nucleus, narrowed by min_p),
 //      the first at which the cumulative tempered mass exp((z - max) / T)
 //      passes u times the kept total.
-// The row is never sorted.  A guide histogram of the masses (float32
-// exponentials summed in float64, bins of equal steps of (max - z) / T) places
-// a window of candidates around the crossing, wider than the guide's error.
+// The row is never sorted.  A guide histogram of the masses (summed in
+// float64 in the order the LDS atomics land, bins of equal steps of
+// (max - z) / T; the parallel passes add the exact weights, the one-workgroup
+// refinement float32 exponentials) places a window of candidates around the
+// crossing, wider than the guide's error.
 // An exact pass then sums the float64 masses above the window and the totals
 // in a fixed order and gathers the window's candidates; they are sorted in LDS
 // and walked in order.
@@ -664,10 +666,12 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
     const float z = __uint_as_float(bits);
     if (z > -__builtin_inff() && (double)z >= c.thr) {
+      // the exact weight serves the guide too (the total needs it anyway)
       const uint32_t b = S1.bin<kNB>(z);
-      __hip_atomic_fetch_add(&L.h.hw[b], (double)S1.gw(z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const double w = S1.w(z);
+      __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      z0 += S1.w(z);
+      z0 += w;
     }
   });
   __syncthreads();
@@ -721,18 +725,25 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   uint64_t* lkey = a.lkey + row * kCapW;
   uint32_t* lbits = a.lbits + row * kCapW;
   double A = 0.0, AT = 0.0;
+  // At T = 1 the tempered weights are the untempered ones; floor mode draws
+  // nothing and needs no tempered guide.
+  const bool same_t = a.T == 1.0f, want_guide = a.out_kfl == nullptr;
   for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
     const float z = __uint_as_float(bits);
     const uint64_t K = comp_key(bits, (uint32_t)i);
     const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
     const uint32_t b = cand ? S1.bin<kNB>(z) : (uint32_t)kNB;
     if (b < b_lo) {
-      A += S1.w(z);
+      const double w1 = S1.w(z);
+      A += w1;
       if (K >= c.kmp) {
-        AT += ST.w(z);
-        const uint32_t bt = ST.bin<kNB>(z);
-        __hip_atomic_fetch_add(&L.h.hw[bt], (double)ST.gw(z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(&L.h.hc[bt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const double wt = same_t ? w1 : ST.w(z);
+        AT += wt;
+        if (want_guide) {
+          const uint32_t bt = same_t ? b : ST.bin<kNB>(z);
+          __hip_atomic_fetch_add(&L.h.hw[bt], wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&L.h.hc[bt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
       }
     }
     if (b >= b_lo && b <= b_hi) stage_window(st, i, c.e_begin);
