@@ -238,6 +238,29 @@ def test_whole_row_typical_sampling_rows(g, oracle):
     compare(g, oracle, x, 1.0, u, typ_gap=TYP_GAP, max_exempt_frac=0.05, typical_p=0.7, top_p=0.95, min_p=0.01)
 
 
+def test_whole_row_typical_ties(g, oracle):
+    """Equal values share a typicality score, so the cut and the draw fall inside
+    runs of ties that only the ids order: windows far larger than LDS holds,
+    narrowed by one workgroup's key passes."""
+    V = 7777
+    rng = np.random.default_rng(W.BASE_SEED + 720)
+    x = np.zeros((5, V), np.float32)
+    x[1] = np.round(rng.normal(0, 1, V) * 2) / 2        # a few distinct values
+    x[2, ::3] = 1.0                                     # two values
+    x[3] = rng.normal(0, 1, V).astype(np.float32)
+    x[3, 100:4200] = x[3].max()                         # 4,100 tied maxima
+    x[4, :] = -np.inf
+    x[4, 17] = 0.5                                      # one candidate
+    u = rng.random(5, dtype=np.float32)
+    for T, kw in ((1.0, dict(typical_p=0.9)), (0.6, dict(typical_p=0.37, top_p=0.8)),
+                  (2.0, dict(typical_p=0.999, min_p=0.1))):
+        compare(g, oracle, x, T, u, typ_gap=TYP_GAP, max_exempt_frac=0.0, **kw)
+    # the largest tie: the whole 202,048-element row equal
+    xe = np.full((2, W.V_DECODE), 0.25, np.float32)
+    compare(g, oracle, xe, 1.0, np.array([0.3, 0.8], np.float32), typ_gap=TYP_GAP, max_exempt_frac=0.0,
+            typical_p=0.9)
+
+
 @pytest.mark.parametrize("ld_pad", [0, 3])
 def test_whole_row_typical_bf16_and_flat(g, oracle, ld_pad):
     """bf16 rows (runs of equal values: equal scores, ordered by id) and flat

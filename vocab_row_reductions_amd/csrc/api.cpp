@@ -283,7 +283,7 @@ struct MomWs {
 };
 // The whole-row nucleus passes (top_k = 0, top_p < 1).
 struct NucWs {
-  size_t tickets, h0w, h0c, hTw, hTc, lkey, lbits, lcnt, p_z0, p_a, p_at, p_a2, plan;
+  size_t tickets, h0w, h0c, hTw, hTc, lkey, lbits, lcnt, p_z0, p_a, p_at, p_a2, plan, jobs;
 };
 NucWs nucleus_layout(Layout& L, int64_t rows, const Plan& p) {
   NucWs w{};
@@ -301,6 +301,7 @@ NucWs nucleus_layout(Layout& L, int64_t rows, const Plan& p) {
   w.p_at = L.take(n * 8);
   w.p_a2 = L.take(n * 8);
   w.plan = L.take(R * sizeof(NucPlan));
+  w.jobs = L.take(R * sizeof(SelJob));
   return w;
 }
 
@@ -332,11 +333,11 @@ ChainWs chain_layout(Layout& L, int64_t rows, int64_t vocab, int32_t top_k) {
 
 // Filtered speculative acceptance: after the speculative workspace, per row
 // the smallest kept key and the kept set's lse (target rows, then draft
-// rows), then the filter pass's scratch: a top-k workspace and, apart from
-// it, a nucleus workspace (also used by the min-p threshold pass), each at
-// its own 256-byte aligned base and used by the target rows and then the
-// draft rows.  The two are disjoint, so calls with any filters can share one
-// workspace: each keeps its own counters at zero.
+// rows), then the filter pass's scratch: a top-k workspace, used by the
+// target rows and then the draft rows, and two nucleus workspaces (also used
+// by the min-p threshold pass), one per part, each at its own 256-byte
+// aligned base.  All are disjoint where it matters, so calls with any
+// filters can share one workspace: each keeps its own counters at zero.
 struct SpecFiltWs {
   size_t kfl, lse, sub_topk, topk_bytes, sub_nuc[2], end;
 };
@@ -609,15 +610,14 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
     a.st_bad = at<uint32_t>(ws, w.st.bad);
     hipError_t e = launch_scan(dtype, false, a, s);
     if (e != hipSuccess) return VSEL_EDEVICE;
-    if (typical_p < 1.0f) {
-      // typical-p over the whole row (then top-p, min-p, the draw), one
-      // workgroup per row
+    if (typical_p < 1.0f || top_p < 1.0f) {
+      // typical-p over the whole row (then top-p, min-p, the draw), or the
+      // nucleus over the whole row (then min-p, the draw in value order)
       NucArgs n{};
       n.x = logits;
       n.ld = ld;
       n.rows = rows;
       n.V = vocab;
-      n.vec = a.vec1;
       n.st_max = a.st_max;
       n.st_bad = a.st_bad;
       n.sigma = sigma;
@@ -629,26 +629,7 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
       n.u = u;
       n.out_token = out_token;
       n.out_logp = out_logprob;
-      return launched(launch_row_typical(dtype, n, s));
-    }
-    if (top_p < 1.0f) {
-      // the nucleus over the whole row, then the draw in value order
-      NucArgs n{};
-      n.x = logits;
-      n.ld = ld;
-      n.rows = rows;
-      n.V = vocab;
-      n.st_max = a.st_max;
-      n.st_bad = a.st_bad;
-      n.sigma = sigma;
-      n.top_n_sigma = top_n_sigma;
-      n.top_p = top_p;
-      n.min_p = min_p;
-      n.T = temperature;
-      n.u = u;
-      n.out_token = out_token;
-      n.out_logp = out_logprob;
-      // the nucleus passes keep two workgroups per CU resident (LDS bound)
+      // the passes keep two workgroups per CU resident (LDS bound)
       const Plan pn = plan_segments(rows, vocab, 0, 2 * (int64_t)device_cus(), kCapLarge);
       n.seg_len = pn.seg_len;
       n.S = pn.S;
@@ -667,7 +648,8 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
       n.p_at = at<double>(ws, nw.p_at);
       n.p_a2 = at<double>(ws, nw.p_a2);
       n.plan = at<NucPlan>(ws, nw.plan);
-      return launched(launch_row_nucleus(dtype, n, s));
+      n.jobs = at<SelJob>(ws, nw.jobs);
+      return launched(typical_p < 1.0f ? launch_row_typical(dtype, n, s) : launch_row_nucleus(dtype, n, s));
     }
     DrawArgs d{};
     d.x = logits;

@@ -207,6 +207,24 @@ struct NucPlan {                   // per row, written by the last workgroup of 
   double wt;                       // exact kept mass, tempered
   uint64_t kfin;                   // smallest kept composite key
 };
+// One row's weighted selection, carried from pass to pass of typical-p over
+// whole rows (the typical cut, then top-p within the typical set, then the
+// draw): the candidate set and order, the target, and the results.
+struct SelJob {
+  double m, thr, T;      // candidates z > -inf, z >= thr; weights exp((z - m) / T)
+  double c, span;        // typical order: the centre and the score span of the bins
+  double frac;           // target: the first candidate whose cumulative weight reaches frac x total
+  uint64_t kfloor, kT;   // order-key floor; typical-set floor on the score key (0: none)
+  int32_t order, strict; // 0 value, 1 typicality; strict: cumulative weight must pass the target
+  int32_t state;         // 0 none, 1 guide pass due, 2 window pass due, 3 left to one workgroup, 4 selected
+  int32_t step;          // 1 typical cut, 2 top-p within the set, 3 the draw
+  uint32_t b_lo, b_hi;   // window (guide bins)
+  uint32_t bits, pad;    // selected candidate's element bits
+  uint64_t key;          // selected candidate's order key
+  double tot;            // exact total weight of the candidates
+  double zmax;           // largest value among the candidates up to the selected one
+  double aux;            // the typical set's largest value (the min_p reference)
+};
 struct NucArgs {
   const void* x;
   int64_t ld;
@@ -236,6 +254,7 @@ struct NucArgs {
   double* p_at;
   double* p_a2;
   NucPlan* plan;           // [rows]
+  SelJob* jobs;            // [rows] (typical-p)
   // floor mode (filtered speculative acceptance): instead of drawing, the
   // kept set's smallest composite key and log sum of exp(z/T) over it
   uint64_t* out_kfl;       // null: sampling
@@ -261,8 +280,8 @@ hipError_t launch_row_nucleus(int dtype, const NucArgs& a, hipStream_t s);
 // Uses x, ld, rows, V, seg_len, S, vec, st_max, st_bad, min_p, T, tickets,
 // p_z0 and the outputs.
 hipError_t launch_kept_lse(int dtype, const NucArgs& a, hipStream_t s);
-// Typical-p over whole rows, one workgroup per row (x, ld, rows, V, vec,
-// st_max, st_bad, sigma, the filters, T, u and the outputs).
+// Typical-p over whole rows, then top-p, min-p and the draw, in passes over
+// (row, segment) workgroups (the nucleus arguments, typical_p and jobs).
 hipError_t launch_row_typical(int dtype, const NucArgs& a, hipStream_t s);
 
 }  // namespace vsel

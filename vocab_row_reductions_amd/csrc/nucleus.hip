@@ -194,6 +194,23 @@ __device__ __forceinline__ uint32_t block_sum_u32(NucRed& r, uint32_t v) {
 
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) { return ~wave_max_u64(~v); }
 
+// Minimum / maximum of one float64 per thread over the workgroup (every
+// thread gets it).
+template <bool MAX>
+__device__ __forceinline__ double block_ext_f64(NucRed& r, double v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_xor(v, d);
+    v = MAX ? fmax(v, o) : fmin(v, o);
+  }
+  __syncthreads();
+  if (lane == 0) r.rd[wave] = v;
+  __syncthreads();
+  double o = r.rd[0];
+  for (int q = 1; q < NWAVE; ++q) o = MAX ? fmax(o, r.rd[q]) : fmin(o, r.rd[q]);
+  return o;
+}
+
 // Wave 0 chooses the bins [b_lo, b_hi] of nb (<= NB) whose cumulative guide
 // mass (after `base`, the mass above bin 0) first reaches t0 and t1; it counts
 // their candidates (cnt) and those of bins [0, b_hi] (cnt_top).  A target
@@ -599,7 +616,7 @@ __device__ __forceinline__ void stage_window(Stage& st, int64_t i, int64_t e_beg
 
 template <typename DT>
 __device__ __forceinline__ void flush_window(Stage& st, const DT* __restrict__ xr, int64_t e_begin, uint32_t* cnt,
-                                             uint64_t* lkey, uint32_t* lbits) {
+                                             uint64_t* lkey, uint32_t* lbits, const NucSet* order = nullptr) {
   __syncthreads();
   const uint32_t n = st.n;
   if (n == 0) return;
@@ -611,7 +628,7 @@ __device__ __forceinline__ void flush_window(Stage& st, const DT* __restrict__ x
     if (pos < kCapW) {
       const int64_t i = e_begin + st.idx[j];
       const uint32_t bits = gbits_at<DT>(xr, i);
-      st_dev(&lkey[pos], comp_key(bits, (uint32_t)i));
+      st_dev(&lkey[pos], order ? order->key(bits, (uint32_t)i) : comp_key(bits, (uint32_t)i));
       st_dev(&lbits[pos], bits);
     }
   }
@@ -900,109 +917,294 @@ __global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
   }
 }
 
-// Typical-p over whole rows (top_k = 0), one workgroup per row ("Chapter 21",
-// section 21.7: typical_p after top_n_sigma and before top_p; ties keep the
-// candidates' id order).  With p the softmax of the candidates, -log p - H =
-// E_p[z] - z, so the typical order is the distance of z to the centre
-// c = E_p[z] (then id); the typical set is the shortest prefix of that order
-// whose mass reaches typical_p.  Then top-p in value order within it (when
-// top_p < 1), min-p against its maximum, and the draw in value order (top_p
-// < 1) or typical order (top_p == 1).
+// Typical-p over whole rows (top_k = 0) ("Chapter 21", section 21.7:
+// typical_p after top_n_sigma and before top_p; ties keep the candidates' id
+// order).  With p the softmax of the candidates, -log p - H = E_p[z] - z, so
+// the typical order is the distance of z to the centre c = E_p[z] (then id);
+// the typical set is the shortest prefix of that order whose mass reaches
+// typical_p.  Then top-p in value order within it (when top_p < 1), min-p
+// against its maximum, and the draw in value order (top_p < 1) or typical
+// order (top_p == 1).
+//
+// Every decision is a weighted selection (SelJob: candidate set, order,
+// weights, target), run by passes over (row, segment) workgroups:
+//   typ_moments: the candidates' mass, mass-weighted value and lowest value;
+//                the last workgroup sets the centre and opens the typical cut;
+//   sel_hist:    guide histogram in the job's order and the exact total; the
+//                last workgroup places a window around the target;
+//   sel_collect: the exact mass before the window and the window's
+//                candidates; the last workgroup sorts them and walks to the
+//                target, or leaves the row to sel_alone when they overflow LDS;
+//   sel_alone:   such rows by one workgroup (guide passes over key ranges).
+// The workgroup that finishes a selection turns it into the row's next job,
+// or writes the token.  The three passes run once per selection: two or three
+// times.
+
+__device__ __forceinline__ NucSet job_set(const SelJob& j, const double* e2) {
+  return NucSet{j.m, j.thr, j.kfloor, j.T, e2, j.order, j.c, j.span, j.kT};
+}
+
 template <typename DT, bool VEC>
-__global__ __launch_bounds__(NT) void row_typical_kernel(NucArgs a) {
+__global__ __launch_bounds__(NT) void typ_moments_kernel(NucArgs a) {
+  __shared__ SelShared sh;
   __shared__ NucRed r;
-  __shared__ FbShared fb;
   __shared__ double e2[64];
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
   if (row >= a.rows) return;
   if (a.st_bad[row]) {
-    if (tid == 0) {
+    if (seg == 0 && tid == 0) {
       a.out_token[row] = kFail;
       if (a.out_logp) a.out_logp[row] = __builtin_nanf("");
+      a.jobs[row].state = 0;
     }
     return;
   }
   init_e2(e2);
+  const NucCommon c = nuc_common(a, row, seg);
   const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
-  const double m = a.st_max[row];
-  const double thr = a.top_n_sigma > 0.0f ? m - (double)a.top_n_sigma * a.sigma[row] : -__builtin_inf();
-  // 1. the candidates' mass and mass-weighted value (float64, fixed order):
-  //    the centre c, and the score range for the first-level bins
-  double z0 = 0.0, y = 0.0, zlo = m;
-  for_each_elem<DT, kNG, VEC>(xr, 0, a.V, [&](uint32_t bits, int64_t) {
+  double z0 = 0.0, y = 0.0, zlo = c.m;
+  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
     const float z = __uint_as_float(bits);
-    if (z > -__builtin_inff() && (double)z >= thr) {
-      const double w = exp_le0((double)z - m, e2);
+    if (z > -__builtin_inff() && (double)z >= c.thr) {
+      const double w = exp_le0((double)z - c.m, e2);
       z0 += w;
       y += w * (double)z;
       zlo = fmin(zlo, (double)z);
     }
   });
-  const double Z0 = nuc_sum(r, z0, 0), Y = nuc_sum(r, y, 1);
-  {
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int d = 1; d < 64; d <<= 1) zlo = fmin(zlo, __shfl_xor(zlo, d));
-    __syncthreads();
-    if (lane == 0) r.rd[wave] = zlo;
-    __syncthreads();
-    for (int q = 0; q < NWAVE; ++q) zlo = fmin(zlo, r.rd[q]);
-    __syncthreads();
-  }
-  const double cen = Y / Z0;
-  const double span = fmax(fmax(m - cen, cen - zlo), 1e-30) * (1.0 + 1e-6);
-  // 2. the typical cut
-  const NucSet ST{m, thr, 0ull, 1.0, e2, 1, cen, span, 0ull};
-  const uint64_t kT = wg_select<DT, VEC>(fb, r, xr, a.V, ST, (double)a.typical_p, false).key;
-  // the typical set's maximum (the min-p reference)
-  double mT = -__builtin_inf();
-  if (a.min_p > 0.0f) {
-    const NucSet SM{m, thr, 0ull, 1.0, e2, 0, cen, span, kT};
-    for_each_elem<DT, kNG, VEC>(xr, 0, a.V, [&](uint32_t bits, int64_t i) {
-      if (SM.in(bits, (uint32_t)i, 0ull)) mT = fmax(mT, (double)__uint_as_float(bits));
-    });
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int d = 1; d < 64; d <<= 1) mT = fmax(mT, __shfl_xor(mT, d));
-    __syncthreads();
-    if (lane == 0) r.rd[wave] = mT;
-    __syncthreads();
-    for (int q = 0; q < NWAVE; ++q) mT = fmax(mT, r.rd[q]);
-    __syncthreads();
-  }
-  SelOut d;
-  if (a.top_p < 1.0f) {
-    // 3. top-p in value order within the typical set, then min-p (a value
-    //    prefix too), then the draw in value order
-    const NucSet SV{m, thr, 0ull, 1.0, e2, 0, cen, span, kT};
-    uint64_t kfin = wg_select<DT, VEC>(fb, r, xr, a.V, SV, (double)a.top_p, false).key;
-    if (a.min_p > 0.0f) kfin = max(kfin, key_floor(mT + log((double)a.min_p)));
-    const NucSet SD{m, thr, kfin, (double)a.T, e2, 0, cen, span, kT};
-    d = wg_select<DT, VEC>(fb, r, xr, a.V, SD, (double)a.u[row], true);
-  } else {
-    // 3. min-p (a value threshold), then the draw in typical order
-    const double thr2 = a.min_p > 0.0f ? fmax(thr, mT + log((double)a.min_p)) : thr;
-    const NucSet SD{m, thr2, 0ull, (double)a.T, e2, 1, cen, span, kT};
-    d = wg_select<DT, VEC>(fb, r, xr, a.V, SD, (double)a.u[row], true);
-  }
+  z0 = nuc_sum(r, z0, 0);
+  y = nuc_sum(r, y, 1);
+  zlo = block_ext_f64<false>(r, zlo);
+  const int64_t p0 = row * a.S;
   if (tid == 0) {
-    a.out_token[row] = ~(uint32_t)d.key;
-    if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - m) / (double)a.T - log(d.tot));
+    st_dev(&a.p_z0[p0 + seg], z0);
+    st_dev(&a.p_a[p0 + seg], y);
+    st_dev(&a.p_at[p0 + seg], zlo);
+  }
+  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  const double Z0 = merge_sum(sh, a.p_z0 + p0, a.S), Y = merge_sum(sh, a.p_a + p0, a.S);
+  const double lo = block_ext_f64<false>(r, tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : c.m);
+  if (tid == 0) {
+    const double cen = Y / Z0;
+    SelJob& j = a.jobs[row];
+    j.m = c.m;
+    j.thr = c.thr;
+    j.T = 1.0;
+    j.c = cen;
+    j.span = fmax(fmax(c.m - cen, cen - lo), 1e-30) * (1.0 + 1e-6);
+    j.frac = (double)a.typical_p;
+    j.kfloor = 0ull;
+    j.kT = 0ull;
+    j.order = 1;
+    j.strict = 0;
+    j.step = 1;
+    j.state = 1;
+  }
+}
+
+// A finished selection (state 4) becomes the row's next job, or its token.
+__device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
+  if (j.step == 1) {
+    // the typical set: score keys >= the cut's; its maximum is the min_p reference
+    j.kT = j.key;
+    j.aux = j.zmax;
+    if (a.top_p < 1.0f) {
+      j.order = 0;  // top-p in value order within the set, untempered
+      j.T = 1.0;
+      j.frac = (double)a.top_p;
+      j.strict = 0;
+      j.step = 2;
+    } else {
+      if (a.min_p > 0.0f) j.thr = fmax(j.thr, j.aux + log((double)a.min_p));
+      j.T = (double)a.T;  // the draw in typical order
+      j.frac = (double)a.u[row];
+      j.strict = 1;
+      j.step = 3;
+    }
+    j.state = 1;
+  } else if (j.step == 2) {
+    uint64_t kfin = j.key;
+    if (a.min_p > 0.0f) kfin = max(kfin, key_floor(j.aux + log((double)a.min_p)));
+    j.kfloor = kfin;  // the draw in value order over the kept set
+    j.T = (double)a.T;
+    j.frac = (double)a.u[row];
+    j.strict = 1;
+    j.step = 3;
+    j.state = 1;
+  } else {
+    a.out_token[row] = ~(uint32_t)j.key;
+    if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(j.bits) - j.m) / j.T - log(j.tot));
+    j.state = 0;
+  }
+}
+
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
+  __shared__ SelShared sh;
+  __shared__ NucRed r;
+  __shared__ NucLds L;
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows || a.jobs[row].state != 1) return;
+  const SelJob jb = a.jobs[row];
+  init_e2(e2);
+  const NucSet S = job_set(jb, e2);
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  for (int b = tid; b < kNB; b += NT) {
+    L.h.hw[b] = 0.0;
+    L.h.hc[b] = 0u;
+  }
+  __syncthreads();
+  double t = 0.0;
+  for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+    if (!S.in(bits, (uint32_t)i, S.key(bits, (uint32_t)i))) return;
+    const float z = __uint_as_float(bits);
+    const double w = S.w(z);
+    const uint32_t b = S.bin<kNB>(z);
+    __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    t += w;
+  });
+  __syncthreads();
+  double* gw = a.h0w + row * kNB;
+  uint32_t* gc = a.h0c + row * kNB;
+  flush_hist(L.h.hw, L.h.hc, gw, gc);
+  t = nuc_sum(r, t, 0);
+  if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], t);
+  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  const double tot = merge_sum(sh, a.p_z0 + row * a.S, a.S);
+  take_hist(L.h.hw, L.h.hc, gw, gc);
+  const double tg = jb.frac * tot, g = kGuard * tot;
+  pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, tg - g, tg + g);
+  if (tid == 0) {
+    SelJob& j = a.jobs[row];
+    j.b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the front of the order when it fits
+    j.b_hi = r.b_hi;
+    j.tot = tot;
+    j.state = 2;
+  }
+}
+
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
+  __shared__ SelShared sh;
+  __shared__ NucRed r;
+  __shared__ NucLds L;
+  __shared__ Stage st;
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows || a.jobs[row].state != 2) return;
+  const SelJob jb = a.jobs[row];
+  if (tid == 0) st.n = 0u;
+  init_e2(e2);
+  const NucSet S = job_set(jb, e2);
+  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  uint64_t* lkey = a.lkey + row * kCapW;
+  uint32_t* lbits = a.lbits + row * kCapW;
+  double A = 0.0, zb = -__builtin_inf();  // mass and largest value before the window
+  for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+    if (!S.in(bits, (uint32_t)i, S.key(bits, (uint32_t)i))) return;
+    const float z = __uint_as_float(bits);
+    const uint32_t b = S.bin<kNB>(z);
+    if (b < jb.b_lo) {
+      A += S.w(z);
+      zb = fmax(zb, (double)z);
+    } else if (b <= jb.b_hi) {
+      stage_window(st, i, e_begin);
+    }
+  });
+  flush_window<DT>(st, xr, e_begin, &a.lcnt[row], lkey, lbits, &S);
+  A = nuc_sum(r, A, 0);
+  zb = block_ext_f64<true>(r, zb);
+  const int64_t p0 = row * a.S;
+  if (tid == 0) {
+    st_dev(&a.p_a[p0 + seg], A);
+    st_dev(&a.p_at[p0 + seg], zb);
+  }
+  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  // ---- the row's last workgroup
+  const double Atot = merge_sum(sh, a.p_a + p0, a.S);
+  const double zbt = block_ext_f64<true>(r, tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : -__builtin_inf());
+  const uint32_t n = ld_dev(&a.lcnt[row]);
+  __syncthreads();
+  if (tid == 0) st_dev(&a.lcnt[row], 0u);
+  if (n > kCapW) {
+    if (tid == 0) a.jobs[row].state = 3;  // too crowded for LDS: left to sel_alone
+    return;
+  }
+  take_list(L.w.key, L.w.bits, lkey, lbits, n);
+  sort_desc<kCapW>(L.w.key, L.w.bits, n);
+  const uint32_t j = walk_sorted(r, L.w.bits, n, S, Atot, jb.frac * jb.tot, jb.strict != 0);
+  double zl = -__builtin_inf();  // the window's candidates up to the selected one
+  for (uint32_t q = tid; q <= j && q < n; q += NT) zl = fmax(zl, (double)__uint_as_float(L.w.bits[q]));
+  zl = block_ext_f64<true>(r, zl);
+  if (tid == 0) {
+    SelJob& o = a.jobs[row];
+    o.key = L.w.key[j];
+    o.bits = L.w.bits[j];
+    o.zmax = fmax(zbt, zl);
+    o.state = 4;
+    typ_advance(a, row, o);
+  }
+}
+
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void sel_alone_kernel(NucArgs a) {
+  __shared__ NucRed r;
+  __shared__ FbShared fb;
+  __shared__ double e2[64];
+  const int64_t row = blockIdx.x;
+  if (row >= a.rows || a.jobs[row].state != 3) return;
+  const SelJob jb = a.jobs[row];
+  init_e2(e2);
+  const NucSet S = job_set(jb, e2);
+  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const SelOut d = wg_select<DT, VEC>(fb, r, xr, a.V, S, jb.frac, jb.strict != 0);
+  double zl = -__builtin_inf();
+  for_each_elem<DT, kNG, VEC>(xr, 0, a.V, [&](uint32_t bits, int64_t i) {
+    const uint64_t K = S.key(bits, (uint32_t)i);
+    if (K >= d.key && S.in(bits, (uint32_t)i, K)) zl = fmax(zl, (double)__uint_as_float(bits));
+  });
+  zl = block_ext_f64<true>(r, zl);
+  if (threadIdx.x == 0) {
+    SelJob& o = a.jobs[row];
+    o.key = d.key;
+    o.bits = d.bits;
+    o.tot = d.tot;
+    o.zmax = zl;
+    o.state = 4;
+    typ_advance(a, row, o);
+  }
+}
+
+template <typename DT, bool VEC>
+static void go_typical(const NucArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.rows * a.S)), one((unsigned)a.rows);
+  hipLaunchKernelGGL((typ_moments_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+  const int nsel = a.top_p < 1.0f ? 3 : 2;
+  for (int q = 0; q < nsel; ++q) {
+    hipLaunchKernelGGL((sel_hist_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((sel_collect_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((sel_alone_kernel<DT, VEC>), one, dim3(NT), 0, s, a);
   }
 }
 
 hipError_t launch_row_typical(int dtype, const NucArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.rows);
-  if (dtype == 0) {
-    if (a.vec)
-      hipLaunchKernelGGL((row_typical_kernel<float, true>), grid, dim3(NT), 0, s, a);
-    else
-      hipLaunchKernelGGL((row_typical_kernel<float, false>), grid, dim3(NT), 0, s, a);
-  } else {
-    if (a.vec)
-      hipLaunchKernelGGL((row_typical_kernel<uint16_t, true>), grid, dim3(NT), 0, s, a);
-    else
-      hipLaunchKernelGGL((row_typical_kernel<uint16_t, false>), grid, dim3(NT), 0, s, a);
-  }
+  if (dtype == 0)
+    a.vec ? go_typical<float, true>(a, s) : go_typical<float, false>(a, s);
+  else
+    a.vec ? go_typical<uint16_t, true>(a, s) : go_typical<uint16_t, false>(a, s);
   return hipGetLastError();
 }
 
