@@ -237,7 +237,7 @@ struct NucArgs {
   const uint32_t* st_bad;  // [rows] fail-closed rows (scan)
   const double* sigma;     // [rows] standard deviations (top_n_sigma > 0)
   float top_n_sigma, top_p, min_p, T;
-  float typical_p;         // (the typical-p kernel)
+  float typical_p;         // (typical-p over whole rows)
   const float* u;
   uint32_t* out_token;
   float* out_logp;

@@ -33,6 +33,10 @@
 // A window with more candidates than LDS holds is left to the row's last
 // workgroup alone, which narrows it by guide passes over equal steps of the
 // composite key (value, then id); these also separate tied values.
+//
+// Typical-p over whole rows (further down) uses the same guide / window /
+// fallback scheme for each of its selections, in the typical order or in
+// value order, with a per-row job record carrying one selection to the next.
 #include "device.hpp"
 #include "internal.hpp"
 
