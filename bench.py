@@ -32,7 +32,7 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 TRAFFIC_BYTES = 414_933_831
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "bf40cff8f6008877a992e60c833d5d19e38a71e817a371a60c27e52bc7b8a7dc"
+TRAFFIC_SHA256 = "413d7401e93698245a76041297509b852f2dfac9f01697508bbab54272612c83"
 
 
 def measured_traffic():
