@@ -125,6 +125,22 @@ def test_adversarial_rows(g, oracle, dtype):
         compare(g, oracle, x, k)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ascending_rows_with_a_ragged_end(g, oracle, dtype):
+    """Ascending rows whose length is not a whole number of 16-byte groups:
+    the candidate lists stay long to the end, and the last few elements (the
+    largest) are added after the last flush."""
+    for V in (50003, 202045, 4099):
+        x = np.tile(np.arange(V, dtype=np.float32), (4, 1))
+        x[1] = np.round(x[1] / 3)                   # runs of three equal values
+        x[2] = x[2] * 1e-3 - 7.0
+        x[3, -3:] = x[3, :3]                        # the smallest at the very end
+        if dtype == "bf16":
+            x = W.f32_to_bf16_bits(x)
+        for k in (1, 20, 84, 128):
+            compare(g, oracle, x, min(k, V), ld=(V + 7) // 8 * 8)   # 16-byte aligned rows: the per-wave kernel
+
+
 def test_back_to_back_calls_reuse_workspace(g, oracle):
     for rep in range(12):
         rng = np.random.default_rng(500 + rep)

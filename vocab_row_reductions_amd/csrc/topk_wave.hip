@@ -583,7 +583,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       LS += huge ? (double)__builtin_amdgcn_exp2f((x - om) * c)
                  : (double)__builtin_amdgcn_exp2f(fmaf(x, c, noff)) * corr;
     }
-    // room: after the last flush the list holds at most select_at <= kWCap - 64
+    // room for the (at most E - 1) keys: a flush may have left the list full,
+    // so cut it first then, to the shared threshold and if need be to the
+    // wave's own k largest (k <= kWCap - 8)
+    if (wcnt > kWCap - 8u) {
+      const uint64_t Ts = uniform_u64(__hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+      if (Ts > T) T = Ts;
+      wcnt = wave_cut(wb, wcnt, T);
+      if (wcnt > kWCap - 8u) {
+        T = wave_kth(wb, wcnt, k, area.hist);
+        wcnt = wave_cut(wb, wcnt, T);
+      }
+    }
     const uint64_t K = comp_key(b, (uint32_t)i);
     const bool pass = has && K >= T;
     const uint64_t m = __ballot(pass);
