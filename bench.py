@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_933_831
+TRAFFIC_BYTES = 414_917_345
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "b0df26c7cd6b8090d3e332c6b7e777f0927d9db139974f0e6aa906622580fc9d"
+TRAFFIC_SHA256 = "1c5b1d71bd5709f8b5eecf9292c7b64519ec479c856c426d3bbedc3bdb06c30c"
 
 
 def sources_digest():
