@@ -247,7 +247,7 @@ SpecWs spec_layout(Layout& L, int64_t B, int64_t G, int64_t V, const Plan& ps, c
   w.p_summin = L.take((size_t)(B * G * pp.S) * 8);
   w.acc = L.take((size_t)(B * G) * 4);
   w.draw_L = L.take((size_t)B * 4);
-  w.p_lse = L.take((size_t)(2 * B * pp.S) * 8);
+  w.p_lse = L.take((size_t)(2 * B * kMaxSegments) * 8);  // per draw segment
   w.lse64 = L.take((size_t)(2 * B) * 8);
   w.p_w = L.take((size_t)(B * kMaxSegments) * 8);
   w.p_c = L.take((size_t)(B * cdiv(V, kChunk)) * 8);

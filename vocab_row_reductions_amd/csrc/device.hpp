@@ -639,6 +639,36 @@ __device__ __forceinline__ double exp2_split(double a) {
   return ldexp((double)__builtin_amdgcn_exp2f((float)(a - n)), (int)n);
 }
 
+// e^x in float64 for x <= 0 (0 below -745).  x = k ln2/64 + r, the reduction
+// with ln2/64 split in two (the high part has 25 significant bits, so k * hi
+// is exact for the k that occur); e^r by its Taylor series to r^6 (|r| <=
+// ln2/128, so the truncation is below 1e-19); then 2^(k/64) as a table entry
+// 2^((k mod 64)/64) and an exponent shift.  A few units in the last place,
+// like a library exp.
+constexpr double kL64Hi = 0x1.62e42f0000000p-7;   // ln2/64, high part
+constexpr double kL64Lo = 0x1.df473de6af279p-32;  // ln2/64 - kL64Hi
+constexpr double kInvL64 = 0x1.71547652b82fep+6;  // 64/ln2
+__device__ __forceinline__ double exp_le0(double x, const double* e2) {
+  const double xc = fmax(x, -745.0);
+  const double k = rint(xc * kInvL64);
+  const double r = fma(-k, kL64Lo, fma(-k, kL64Hi, xc));
+  double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ki = (int)k;
+  const double v = ldexp(e2[ki & 63] * p, ki >> 6);
+  return x < -745.0 ? 0.0 : v;
+}
+
+// The table 2^(j/64), j = 0..63, in LDS (all threads call).
+__device__ __forceinline__ void init_e2(double* e2) {
+  if (threadIdx.x < 64) e2[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+  __syncthreads();
+}
+
 // Log-sum-exp states (m, s) of the workgroup's lanes merged: the maximum
 // first (NaN-propagating), then one rescale per lane and float64 sums, so
 // no step pays more than one exp2.  Every thread must call; every thread

@@ -128,7 +128,7 @@ struct SpecArgs {
   double* p_summin;     // [B*gamma*S]
   uint32_t* acc;        // [B*gamma]
   int32_t* draw_L;      // [B]: -1 none, 0..gamma-1 residual at L, gamma bonus
-  double* p_lse;        // [B*2*S] float64 partial sums for the draw rows
+  double* p_lse;        // [B*2*dS] float64 partial sums for the draw rows
   double* lse64;        // [B*2]
   // the draw: segments of dseg elements (a multiple of kChunk), dS per row
   int64_t dseg;

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
   constexpr int E = 4;
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
-  const Item it = work_item(a.S);
+  const Item it = work_item(a.dS);  // the draw segments: few rows, many workgroups
   const int64_t item = it.row;  // b*2 + which
   const int seg = (int)it.seg;
   if (item >= a.B * 2) return;
@@ -389,8 +389,10 @@ __global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
   const int64_t srow = which == 0 ? b * (G + 1) + L : nT + b * G + L;
   const float* __restrict__ xr = which == 0 ? a.tgt + (b * (G + 1) + L) * a.ld_t : a.dft + (b * G + L) * a.ld_d;
   const double m = a.st_max[srow];
-  const double Td = a.T;
-  const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
+  const double Td = a.T, iT = 1.0 / Td;
+  __shared__ double e2[64];
+  init_e2(e2);
+  const int64_t e_begin = (int64_t)seg * a.dseg, e_end = min(a.V, e_begin + a.dseg);
   double s = 0.0;
   const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
   walk_groups<float, PG, VEC>(xr, e_begin, e_full, [&](const auto& g, int64_t) {
@@ -398,15 +400,15 @@ __global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
 #pragma unroll
     for (int j = 0; j < NGP; ++j)
 #pragma unroll
-      for (int e = 0; e < E; ++e) s += exp(((double)__uint_as_float(g[j].w[e]) - m) / Td);
+      for (int e = 0; e < E; ++e) s += exp_le0(((double)__uint_as_float(g[j].w[e]) - m) * iT, e2);
   });
   if (tid == 0)
-    for (int64_t x = e_full; x < e_end; ++x) s += exp(((double)xr[x] - m) / Td);
+    for (int64_t x = e_full; x < e_end; ++x) s += exp_le0(((double)xr[x] - m) * iT, e2);
   s = block_sum_f64(sh, s);
-  if (a.S > 1) {
-    if (tid == 0) st_dev(&a.p_lse[item * a.S + seg], s);
-    if (!last_done(sh, a.tk_row + item, (uint32_t)a.S)) return;
-    s = merge_sum(sh, a.p_lse + item * a.S, a.S);
+  if (a.dS > 1) {
+    if (tid == 0) st_dev(&a.p_lse[item * a.dS + seg], s);
+    if (!last_done(sh, a.tk_row + item, (uint32_t)a.dS)) return;
+    s = merge_sum(sh, a.p_lse + item * a.dS, a.dS);
   }
   if (tid == 0) a.lse64[item] = m / Td + log(s);
 }
@@ -432,15 +434,20 @@ struct DrawSrc {
   int64_t V;
   double thr = -__builtin_inf();
   uint64_t kz = 0, kd = 0;
+  double iT = 1.0;              // 1 / T
+  const double* e2 = nullptr;   // the exp table in LDS (init_e2)
   __device__ __forceinline__ float zv(int64_t x) const { return __uint_as_float(gbits_at<DT>(z, x)); }
+  // (every exponent is at most 0 up to rounding: lp and lq are log-sum-exps
+  // of the rows at T, m their maxima)
   __device__ __forceinline__ double w(float zx, float dx, int64_t x) const {
     const bool pk = kz == 0 || comp_key(__float_as_uint(zx), (uint32_t)x) >= kz;
     if (d) {
       const bool qk = kd == 0 || comp_key(__float_as_uint(dx), (uint32_t)x) >= kd;
-      const double p = pk ? exp((double)zx / T - lp) : 0.0, q = qk ? exp((double)dx / T - lq) : 0.0;
+      const double p = pk ? exp_le0((double)zx * iT - lp, e2) : 0.0;
+      const double q = qk ? exp_le0((double)dx * iT - lq, e2) : 0.0;
       return p > q ? p - q : 0.0;
     }
-    return pk && (double)zx >= thr ? exp(((double)zx - m) / T) : 0.0;
+    return pk && (double)zx >= thr ? exp_le0(((double)zx - m) * iT, e2) : 0.0;
   }
 };
 
@@ -590,8 +597,12 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   const int64_t G = a.gamma;
   const int32_t L = a.draw_L[b];
   if (L < 0) return;
+  __shared__ double e2[64];
+  init_e2(e2);
   DrawSrc<float> r;
   r.T = a.T;
+  r.iT = 1.0 / r.T;
+  r.e2 = e2;
   r.V = a.V;
   double u;
   const int64_t nT = a.B * (G + 1);
@@ -667,12 +678,16 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
     }
     return;
   }
+  __shared__ double e2[64];
+  init_e2(e2);
   DrawSrc<DT> r;
   r.z = reinterpret_cast<const DT*>(a.x) + row * a.ld;
   r.d = nullptr;
   r.lp = r.lq = 0.0;
   r.m = a.st_max[row];
   r.T = a.T;
+  r.iT = 1.0 / r.T;
+  r.e2 = e2;
   r.V = a.V;
   if (a.top_n_sigma > 0.0f) r.thr = r.m - (double)a.top_n_sigma * a.sigma[row];
   if (a.min_p > 0.0f) r.thr = fmax(r.thr, r.m + log((double)a.min_p));
@@ -713,9 +728,9 @@ hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (vec)
-    hipLaunchKernelGGL(draw_lse_kernel<true>, dim3((unsigned)(a.B * 2 * a.S)), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(draw_lse_kernel<true>, dim3((unsigned)(a.B * 2 * a.dS)), dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL(draw_lse_kernel<false>, dim3((unsigned)(a.B * 2 * a.S)), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(draw_lse_kernel<false>, dim3((unsigned)(a.B * 2 * a.dS)), dim3(NT), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
   return hipGetLastError();
