@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_917_345
+TRAFFIC_BYTES = 414_919_009
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "1c5b1d71bd5709f8b5eecf9292c7b64519ec479c856c426d3bbedc3bdb06c30c"
+TRAFFIC_SHA256 = "273c3bc0f19aca0facf691f1774b7639249408d845f8a1e0ff51c8b899ea507b"
 
 
 def sources_digest():
