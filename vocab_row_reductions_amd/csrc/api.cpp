@@ -42,12 +42,15 @@ int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap) {
 // costs (segment length + a fixed per-segment cost) x max(1, n / sat): a
 // short round is bound by the workgroups' own speed, a full one by HBM.
 // With k > 0 a row of S > 1 segments also pays the merge of S x k records.
+// A kernel that streams `streams` rows per workgroup (target and draft)
+// saturates HBM with proportionally fewer workgroups.
 // Segment lengths are multiples of `granule` elements (a multiple of 8).
 constexpr int64_t kSatPerCu = 4;
 int device_cus();
-Plan plan_segments(int64_t rows, int64_t V, int64_t k, int64_t resident, int cap, int64_t granule = 8) {
+Plan plan_segments(int64_t rows, int64_t V, int64_t k, int64_t resident, int cap, int64_t granule = 8,
+                   int streams = 1) {
   const int64_t sb = seg_bound(rows, V, k, cap);
-  const int64_t sat = kSatPerCu * device_cus();
+  const int64_t sat = kSatPerCu * device_cus() / streams;
   Plan best{1, cdiv(V, granule) * granule};
   double best_cost = 1e300;
   for (int64_t S = 1; S <= sb; ++S) {
@@ -91,8 +94,8 @@ int64_t resident_topk(int dtype, bool lse, int cap) {
   return (int64_t)(b > 0 ? b : 2) * device_cus();
 }
 
-Plan plan_scan(int dtype, bool lse, int64_t rows, int64_t V) {
-  return plan_segments(rows, V, 0, resident_scan(dtype, lse), kCapLarge);
+Plan plan_scan(int dtype, bool lse, int64_t rows, int64_t V, int streams = 1) {
+  return plan_segments(rows, V, 0, resident_scan(dtype, lse), kCapLarge, 8, streams);
 }
 Plan plan_scan_bound(int64_t rows, int64_t V) {
   const int64_t sb = seg_bound(rows, V, 0, kCapLarge);
@@ -741,7 +744,7 @@ static vsel_status spec_prepare(const float* target, int64_t ld_t, const float* 
   const SpecWs w = spec_layout(L, B, G, vocab, plan_scan_bound(B * (2 * G + 1), vocab), plan_scan_bound(B * G, vocab));
   if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
   const Plan ps = plan_scan(VSEL_F32, temperature > 0.0f, B * (2 * G + 1), vocab);
-  const Plan pp = plan_scan(VSEL_F32, true, B * G, vocab);
+  const Plan pp = plan_scan(VSEL_F32, true, B * G, vocab, 2);  // the position passes read two rows
 
   ScanArgs a = scan_args(target, VSEL_F32, B * (G + 1), vocab, ld_t, ps, temperature);
   a.x2 = draft;
