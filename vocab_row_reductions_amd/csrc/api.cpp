@@ -14,6 +14,11 @@ using namespace vsel;
 namespace {
 
 constexpr int64_t kMinSegment = 2048;      // elements per workgroup, at least
+// A top-k segment pays a threshold start, an epilogue and its share of the
+// row's merge, so shorter ones lose: on 64 x 202,048 and 3 or 49 x 248,320
+// f32 rows the best plans had 8 to 11 segments (24-32 K elements), and 13
+// to 16 segments ran 10-15% slower.
+constexpr int64_t kMinTopkSegment = 24576;
 constexpr int64_t kSegOverhead = 4096;     // fixed cost of a segment, in elements streamed
 constexpr int64_t kMergePerRecord = 32;    // a record merged by a row's last workgroup, in elements streamed
 constexpr int64_t kMaxSplitWork = 8192;    // rows x segments never exceeds max(rows, this)
@@ -30,8 +35,8 @@ struct Plan {
 // workspace can be sized without the device: no segment shorter than
 // kMinSegment, a row's k-record sets must fit one workgroup's merge buffer,
 // and the split never multiplies the work items past kMaxSplitWork.
-int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap) {
-  int64_t b = std::min<int64_t>(kMaxSegments, std::max<int64_t>(1, cdiv(V, kMinSegment)));
+int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap, int64_t min_seg = kMinSegment) {
+  int64_t b = std::min<int64_t>(kMaxSegments, std::max<int64_t>(1, cdiv(V, min_seg)));
   if (k > 0) b = std::min<int64_t>(b, std::max<int64_t>(1, cap / k));
   return std::min<int64_t>(b, std::max<int64_t>(1, cdiv(kMaxSplitWork, rows)));
 }
@@ -48,8 +53,8 @@ int64_t seg_bound(int64_t rows, int64_t V, int64_t k, int cap) {
 constexpr int64_t kSatPerCu = 4;
 int device_cus();
 Plan plan_segments(int64_t rows, int64_t V, int64_t k, int64_t resident, int cap, int64_t granule = 8,
-                   int streams = 1) {
-  const int64_t sb = seg_bound(rows, V, k, cap);
+                   int streams = 1, int64_t min_seg = kMinSegment) {
+  const int64_t sb = seg_bound(rows, V, k, cap, min_seg);
   const int64_t sat = kSatPerCu * device_cus() / streams;
   Plan best{1, cdiv(V, granule) * granule};
   double best_cost = 1e300;
@@ -132,7 +137,7 @@ TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k, bool
   } else {
     resident = resident_topk(dtype, lse, cap);
   }
-  return TopkPlan{plan_segments(rows, V, k, resident, cap, tile), cap};
+  return TopkPlan{plan_segments(rows, V, k, resident, cap, tile, 1, kMinTopkSegment), cap};
 }
 Plan plan_topk_bound(int64_t rows, int64_t V, int64_t k) {
   const int64_t sb = seg_bound(rows, V, k, kCapLarge);
