@@ -17,8 +17,10 @@ constexpr int64_t kMinSegment = 2048;      // elements per workgroup, at least
 // A top-k segment pays a threshold start, an epilogue and its share of the
 // row's merge, so shorter ones lose: on 64 x 202,048 and 3 or 49 x 248,320
 // f32 rows the best plans had 8 to 11 segments (24-32 K elements), and 13
-// to 16 segments ran 10-15% slower.
-constexpr int64_t kMinTopkSegment = 24576;
+// to 16 segments ran 10-15% slower.  The moments pass (float64 pairwise
+// merges of count, mean and M2) shows the same: 8 segments of a 202,048 row
+// beat 16.
+constexpr int64_t kMinMergeSegment = 24576;
 constexpr int64_t kSegOverhead = 4096;     // fixed cost of a segment, in elements streamed
 constexpr int64_t kMergePerRecord = 32;    // a record merged by a row's last workgroup, in elements streamed
 constexpr int64_t kMaxSplitWork = 8192;    // rows x segments never exceeds max(rows, this)
@@ -99,8 +101,8 @@ int64_t resident_topk(int dtype, bool lse, int cap) {
   return (int64_t)(b > 0 ? b : 2) * device_cus();
 }
 
-Plan plan_scan(int dtype, bool lse, int64_t rows, int64_t V, int streams = 1) {
-  return plan_segments(rows, V, 0, resident_scan(dtype, lse), kCapLarge, 8, streams);
+Plan plan_scan(int dtype, bool lse, int64_t rows, int64_t V, int streams = 1, int64_t min_seg = kMinSegment) {
+  return plan_segments(rows, V, 0, resident_scan(dtype, lse), kCapLarge, 8, streams, min_seg);
 }
 Plan plan_scan_bound(int64_t rows, int64_t V) {
   const int64_t sb = seg_bound(rows, V, 0, kCapLarge);
@@ -137,7 +139,7 @@ TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k, bool
   } else {
     resident = resident_topk(dtype, lse, cap);
   }
-  return TopkPlan{plan_segments(rows, V, k, resident, cap, tile, 1, kMinTopkSegment), cap};
+  return TopkPlan{plan_segments(rows, V, k, resident, cap, tile, 1, kMinMergeSegment), cap};
 }
 Plan plan_topk_bound(int64_t rows, int64_t V, int64_t k) {
   const int64_t sb = seg_bound(rows, V, k, kCapLarge);
@@ -571,7 +573,7 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
 
   const double* sigma = nullptr;
   if (top_n_sigma > 0.0f && !greedy) {
-    const Plan p = plan_scan(dtype, false, rows, vocab);
+    const Plan p = plan_scan(dtype, false, rows, vocab, 1, kMinMergeSegment);
     MomArgs m{};
     m.x = logits;
     m.vec = aligned16(logits, ld, elem_size(dtype)) ? 1 : 0;
