@@ -208,7 +208,20 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
 
   const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
   bool first = true;
+  // Fair progress, as in the per-wave top-k kernel: a wave starts at the
+  // highest issue priority and drops one level per quarter of its tiles, so
+  // waves that are ahead yield to those behind (a younger workgroup's
+  // quarters end one tile later per step of age).
+  const uint32_t ntiles = (uint32_t)((e_tiles - e_begin) / TILE);
+  const uint32_t age = (blockIdx.x * 4u) / gridDim.x;
+  const uint32_t q1 = ntiles / 4 + age, q2 = ntiles / 2 + age, q3 = ntiles - ntiles / 4 + age;
+  __builtin_amdgcn_s_setprio(3);
+  uint32_t tix = 0;
   for (int64_t t0 = e_begin; t0 < e_tiles; t0 += TILE) {
+    ++tix;
+    if (tix == q1) __builtin_amdgcn_s_setprio(2);
+    else if (tix == q2) __builtin_amdgcn_s_setprio(1);
+    else if (tix == q3) __builtin_amdgcn_s_setprio(0);
     Group g[SG];
     if constexpr (VEC) load_tile_buf<DT, SG>(g, xr + t0);
     else load_tile_full<DT, SG, false>(g, xr + t0);
