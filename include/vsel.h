@@ -10,6 +10,8 @@
  *                     the reduction, a status word per row
  *   vsel_topk         exact top-k (value, token id) per row, fused with the
  *                     row's argmax and log-sum-exp in one pass over the row
+ *   vsel_topk_noalloc vsel_topk with its scratch in a fixed device array, for
+ *                     callers that cannot allocate
  *   vsel_sample       temperature sampling with top-k then top-p, one caller
  *                     uniform per row
  *   vsel_sample_chain the ordered sampler chain: top-n-sigma, top-k,
@@ -158,6 +160,28 @@ vsel_status vsel_argmax_excluding(const void* logits, int dtype, int64_t rows, i
 vsel_status vsel_topk(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld, int32_t k,
                       float* out_vals, uint32_t* out_ids, uint32_t* out_argmax, float* out_lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* vsel_topk for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and outputs as vsel_topk, with no workspace
+ * argument.  Its scratch is a fixed device array of
+ * VSEL_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the call itself allocates nothing.  Every call on a GPU shares
+ * that GPU's array, so calls that overlap on one GPU (on two streams, or beside
+ * a replay of a graph that captured a call) race; calls ordered on one stream
+ * do not.  A device's first call also launches a small kernel, on `stream`,
+ * that zeroes the array's counters.
+ *   rows        1 <= rows <= VSEL_NOALLOC_MAX_ROWS, else VSEL_EINVAL
+ *   Shapes whose scratch (for the call's own segment plan) exceeds the array
+ *   return VSEL_EWORKSPACE before any launch; the large decode batch
+ *   (1,024 x 202,048, k <= 128) needs about 82 KiB.  VSEL_EDEVICE: no current
+ *   device, or a launch failed.
+ */
+#define VSEL_NOALLOC_MAX_ROWS 16384
+#define VSEL_NOALLOC_SCRATCH_BYTES (8u << 20)
+vsel_status vsel_topk_noalloc(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld, int32_t k,
+                              float* out_vals, uint32_t* out_ids, uint32_t* out_argmax, float* out_lse,
+                              void* stream);
 
 /* Temperature sampling with top-k then top-p and one caller uniform per row.
  * Filtering acts on the untempered distribution and the temperature is applied

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_operations():
     names = declared_functions()
-    for op in ("vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_sample_chain",
+    for op in ("vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_topk_noalloc", "vsel_sample", "vsel_sample_chain",
                "vsel_spec_accept", "vsel_spec_match", "vsel_spec_accept_filtered", "vsel_spec_match_filtered",
                "vsel_workspace_bytes"):
         assert op in names
@@ -90,6 +90,10 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
     assert L.vsel_topk(fake, 0, 4, 100, 100, 101, fake, fake, None, None, ws, 1 << 20, None) == EINVAL
     assert L.vsel_topk(fake, 0, 4, 5000, 5000, 1025, fake, fake, None, None, ws, 1 << 20, None) == EINVAL
     assert L.vsel_topk(fake, 0, 4, 100, 100, 5, None, fake, None, None, ws, 1 << 20, None) == EINVAL
+    # the allocation-free top-k: the row count is checked before any device call
+    assert L.vsel_topk_noalloc(fake, 0, 0, 100, 100, 5, fake, fake, None, None, None) == EINVAL
+    assert L.vsel_topk_noalloc(fake, 0, vsel.NOALLOC_MAX_ROWS + 1, 100, 100, 5, fake, fake, None, None,
+                               None) == EINVAL
     bad_sample = [(-0.5, 20, 0.9), (0.7, -1, 0.9), (0.7, 20, 0.0), (0.7, 20, 1.5), (0.7, 0, 0.9),
                   (0.7, 1025, 0.9), (float("nan"), 20, 0.9), (float("inf"), 20, 0.9)]
     for T, k, p in bad_sample:

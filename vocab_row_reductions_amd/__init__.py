@@ -15,7 +15,7 @@ import os
 
 import torch  # loads the HIP runtime that libvsel.so then shares
 
-__all__ = ["vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_sample", "vsel_sample_chain", "vsel_spec_accept",
+__all__ = ["vsel_argmax", "vsel_argmax_excluding", "vsel_topk", "vsel_topk_noalloc", "vsel_sample", "vsel_sample_chain", "vsel_spec_accept",
            "vsel_spec_match", "vsel_spec_accept_filtered", "vsel_spec_match_filtered",
            "workspace_bytes",
            "VselError", "NONFINITE", "K_MAX", "EXCLUDED_MAX", "library_path"]
@@ -26,6 +26,8 @@ library_path = os.path.join(HERE, "libvsel.so")
 NONFINITE = 0xFFFFFFFF
 K_MAX = 1024
 EXCLUDED_MAX = 256
+NOALLOC_MAX_ROWS = 16384
+NOALLOC_SCRATCH_BYTES = 8 << 20
 F32, BF16 = 0, 1
 OP_ARGMAX, OP_TOPK, OP_SAMPLE, OP_SPEC, OP_SAMPLE_CHAIN, OP_SPEC_FILTERED = 0, 1, 2, 3, 4, 5
 
@@ -47,6 +49,7 @@ def _load():
     L.vsel_argmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, sz, vp]
     L.vsel_argmax_excluding.argtypes = [vp, C.c_int, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.vsel_topk.argtypes = [vp, C.c_int, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.vsel_topk_noalloc.argtypes = [vp, C.c_int, i64, i64, i64, i32, vp, vp, vp, vp, vp]
     L.vsel_sample.argtypes = [vp, C.c_int, i64, i64, i64, f32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.vsel_sample_chain.argtypes = [vp, C.c_int, i64, i64, i64, f32, f32, i32, f32, f32, f32, vp, vp, vp, vp, sz,
                                     vp]
@@ -57,7 +60,7 @@ def _load():
                                             vp, vp, vp, vp, vp, vp, sz, vp]
     L.vsel_spec_match_filtered.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, i32, f32, f32, vp, vp, vp, vp,
                                            vp, vp, sz, vp]
-    for f in (L.vsel_argmax, L.vsel_argmax_excluding, L.vsel_topk, L.vsel_sample, L.vsel_sample_chain,
+    for f in (L.vsel_argmax, L.vsel_argmax_excluding, L.vsel_topk, L.vsel_topk_noalloc, L.vsel_sample, L.vsel_sample_chain,
               L.vsel_spec_accept, L.vsel_spec_match, L.vsel_spec_accept_filtered, L.vsel_spec_match_filtered):
         f.restype = C.c_int
     return L
@@ -173,6 +176,22 @@ def vsel_topk(logits: torch.Tensor, k: int, vocab=None, want_argmax=True, want_l
     _check(lib.vsel_topk(_ptr(logits), dt, rows, V, ld, int(k), _ptr(out["vals"]), _ptr(out["ids"]),
                          _ptr(out.get("argmax")), _ptr(out.get("lse")), _ptr(ws), ws.numel(), _stream(dev)),
            "vsel_topk")
+    return out["vals"], out["ids"], out.get("argmax"), out.get("lse")
+
+
+def vsel_topk_noalloc(logits: torch.Tensor, k: int, vocab=None, want_argmax=True, want_lse=True, out=None):
+    """vsel_topk whose scratch is the library's fixed device array (no workspace
+    is allocated or passed) -> (vals, ids, argmax|None, lse|None)."""
+    rows, V, ld = _rows(logits, vocab)
+    dt = _dtype(logits)
+    dev = logits.device
+    if out is None:
+        out = dict(vals=torch.empty((rows, k), dtype=torch.float32, device=dev),
+                   ids=torch.empty((rows, k), dtype=torch.int32, device=dev),
+                   argmax=torch.empty(rows, dtype=torch.int32, device=dev) if want_argmax else None,
+                   lse=torch.empty(rows, dtype=torch.float32, device=dev) if want_lse else None)
+    _check(lib.vsel_topk_noalloc(_ptr(logits), dt, rows, V, ld, int(k), _ptr(out["vals"]), _ptr(out["ids"]),
+                                 _ptr(out.get("argmax")), _ptr(out.get("lse")), _stream(dev)), "vsel_topk_noalloc")
     return out["vals"], out["ids"], out.get("argmax"), out.get("lse")
 
 

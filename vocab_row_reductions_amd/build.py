@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libvsel.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "scan.hip", "topk.hip", "topk_wave.hip", "spec.hip", "chain.hip", "nucleus.hip"]
+SOURCES = ["api.cpp", "scan.hip", "topk.hip", "topk_wave.hip", "spec.hip", "chain.hip", "nucleus.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Xclang", "-target-feature",
          "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-Wall",

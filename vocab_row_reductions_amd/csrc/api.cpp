@@ -507,16 +507,19 @@ vsel_status vsel_argmax_excluding(const void* logits, int dtype, int64_t rows, i
   return launched(launch_scan(dtype, false, a, (hipStream_t)stream));
 }
 
+// exact_layout: place the buffers for this call's own segment plan rather
+// than for the shape's bound (the plan's segment count never exceeds the
+// bound, so this layout is never larger; the tickets lead either layout).
 static vsel_status topk_common(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                                int32_t k, bool want_lse, TopkArgs& a, void* ws, size_t ws_bytes,
-                               void* stream) {
-  Layout L;
-  const TopkWs w = topk_layout(L, rows, k, plan_topk_bound(rows, vocab, k));
-  if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
+                               void* stream, bool exact_layout = false) {
   const bool vec = aligned16(logits, ld, elem_size(dtype));
   const bool wave = vec && k <= kWaveTopkMax;
   const TopkPlan tp = plan_topk(dtype, want_lse, rows, vocab, k, wave);
   const Plan& p = tp.p;
+  Layout L;
+  const TopkWs w = topk_layout(L, rows, k, exact_layout ? p : plan_topk_bound(rows, vocab, k));
+  if (!ws_ok(ws, ws_bytes, L.off)) return VSEL_EWORKSPACE;
   a.x = logits;
   a.ld = ld;
   a.rows = rows;
@@ -538,16 +541,8 @@ static vsel_status topk_common(const void* logits, int dtype, int64_t rows, int6
 vsel_status vsel_topk(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld, int32_t k,
                       float* out_vals, uint32_t* out_ids, uint32_t* out_argmax, float* out_lse, void* ws,
                       size_t ws_bytes, void* stream) {
-  if (!logits || !out_vals || !out_ids || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
-      !aligned_elem(logits, elem_size(dtype)) || k < 1 || k > VSEL_K_MAX || k > vocab)
-    return VSEL_EINVAL;
-  TopkArgs a{};
-  a.mode = 0;
-  a.out_vals = out_vals;
-  a.out_ids = out_ids;
-  a.out_argmax = out_argmax;
-  a.out_lse = out_lse;
-  return topk_common(logits, dtype, rows, vocab, ld, k, out_lse != nullptr, a, ws, ws_bytes, stream);
+  return (vsel_status)vsel::topk_entry(logits, dtype, rows, vocab, ld, k, out_vals, out_ids, out_argmax, out_lse,
+                                       ws, ws_bytes, stream, false);
 }
 
 // The sampler (vsel_sample) and the ordered chain (vsel_sample_chain): the
@@ -994,3 +989,22 @@ vsel_status vsel_spec_match(const float* target, int64_t ld_t, const float* draf
 }
 
 }  // extern "C"
+
+namespace vsel {
+
+int topk_entry(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld, int32_t k, float* out_vals,
+               uint32_t* out_ids, uint32_t* out_argmax, float* out_lse, void* ws, size_t ws_bytes, void* stream,
+               bool exact_layout) {
+  if (!logits || !out_vals || !out_ids || !elem_ok(dtype) || !rows_ok(rows, vocab, ld) ||
+      !aligned_elem(logits, elem_size(dtype)) || k < 1 || k > VSEL_K_MAX || k > vocab)
+    return VSEL_EINVAL;
+  TopkArgs a{};
+  a.mode = 0;
+  a.out_vals = out_vals;
+  a.out_ids = out_ids;
+  a.out_argmax = out_argmax;
+  a.out_lse = out_lse;
+  return topk_common(logits, dtype, rows, vocab, ld, k, out_lse != nullptr, a, ws, ws_bytes, stream, exact_layout);
+}
+
+}  // namespace vsel

@@ -284,4 +284,12 @@ hipError_t launch_kept_lse(int dtype, const NucArgs& a, hipStream_t s);
 // (row, segment) workgroups (the nucleus arguments, typical_p and jobs).
 hipError_t launch_row_typical(int dtype, const NucArgs& a, hipStream_t s);
 
+// vsel_topk's argument checks, layout and launch, returning a vsel_status.
+// exact_layout places the workspace for the call's own segment plan instead of
+// the shape's bound; the ticket counters lead the layout either way, in
+// max(64 KiB, 4 x rows) bytes.
+int topk_entry(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld, int32_t k, float* out_vals,
+               uint32_t* out_ids, uint32_t* out_argmax, float* out_lse, void* ws, size_t ws_bytes, void* stream,
+               bool exact_layout);
+
 }  // namespace vsel
