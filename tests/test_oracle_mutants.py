@@ -9,6 +9,7 @@ import tests.test_oracle_pins as P
 import tests.test_oracle_pins_match as M
 import tests.test_oracle_pins_chain as C
 import tests.test_oracle_pins_filtered as F
+import tests.test_oracle_pins_exact as E
 from oracle import build as B
 from oracle import oracle as O
 
@@ -27,9 +28,13 @@ MUTANTS = [
      "Z0 += (e[j] = std::exp((static_cast<double>(R.at(r, cand[j])) - z0) / T));",
      [P.test_sample_filter_order_worked_example]),
     ("accept test with p and q transposed", "if (!(lhs <= pt)) {", "if (!(static_cast<double>(u_acc[b * G + i]) * pt <= qt)) {",
-     [P.test_mrs_is_lossless_and_hits_the_ceiling]),
+     [P.test_mrs_is_lossless_and_hits_the_ceiling, E.mrs_exact_pin]),
     ("residual with the wrong sign", "std::max(p_of(L, x) - q_of(L, x), 0.0)", "std::max(q_of(L, x) - p_of(L, x), 0.0)",
-     [P.test_mrs_is_lossless_and_hits_the_ceiling]),
+     [P.test_mrs_is_lossless_and_hits_the_ceiling, E.mrs_exact_pin]),
+    ("residual draw with the accept test's uniform", "      u = u_res[b * G + L];\n", "      u = u_acc[b * G + L];\n",
+     [E.mrs_exact_pin]),
+    ("residual taken from p when q exceeds it nowhere", "      if (W <= 0.0)\n", "      if (W <= 1.0)\n",
+     [E.mrs_exact_pin]),
     ("coupling sum with max instead of min", "s += std::min(p_of(i, x), q_of(i, x));", "s += std::max(p_of(i, x), q_of(i, x));",
      [P.test_spec_invariants_config4_like]),
     ("bonus draw from the wrong target row", "w[x] = p_of(G, x);", "w[x] = p_of(G - 1, x);",
@@ -44,10 +49,11 @@ MUTANTS = [
      [P.test_sample_u_grid_frequencies_and_support]),
     ("sampler-match accepts on a mismatch", "if (i == G || x != draft_tokens[b * G + i]) {",
      "if (i == G || x == draft_tokens[b * G + i]) {",
-     [M.test_sampler_match_accepts_at_sum_pq_and_is_lossless, M.test_sampler_match_draws_follow_the_cumulative_sum]),
+     [M.test_sampler_match_accepts_at_sum_pq_and_is_lossless, M.test_sampler_match_draws_follow_the_cumulative_sum,
+      E.sm_exact_pin]),
     ("sampler-match draws from the draft distribution", "for (int64_t x = 0; x < V; ++x) w[x] = p_of(i, x);",
      "for (int64_t x = 0; x < V; ++x) w[x] = i < G ? q_of(i, x) : p_of(i, x);",
-     [M.test_sampler_match_accepts_at_sum_pq_and_is_lossless]),
+     [M.test_sampler_match_accepts_at_sum_pq_and_is_lossless, E.sm_exact_pin]),
     ("sampler-match emits the drafted token at the mismatch", "      tk[i] = x;\n",
      "      tk[i] = i < G ? draft_tokens[b * G + i] : x;\n",
      [M.test_sampler_match_chi_square_and_power, M.test_sampler_match_draws_follow_the_cumulative_sum]),
@@ -69,6 +75,16 @@ MUTANTS = [
      [F.test_filtered_coupling_sums_match_numpy]),
     ("draft rows left unfiltered", "dq[i] = row_dist(Dr, drow0 + i, V, T, top_k, top_p, min_p, &m);",
      "dq[i] = row_dist(Dr, drow0 + i, V, T, 0, 1.0f, 0.0f, &m);", [F.test_filtered_coupling_sums_match_numpy]),
+    ("filtered top-p on the tempered distribution",
+     "    for (uint32_t x : cand) Z += std::exp(z(x) - zmax);\n    double cum = 0.0;\n"
+     "    for (size_t j = 0; j < cand.size(); ++j) {\n      const double prev = cum;\n"
+     "      cum += std::exp(z(cand[j]) - zmax) / Z;",
+     "    for (uint32_t x : cand) Z += std::exp((z(x) - zmax) / T);\n    double cum = 0.0;\n"
+     "    for (size_t j = 0; j < cand.size(); ++j) {\n      const double prev = cum;\n"
+     "      cum += std::exp((z(cand[j]) - zmax) / T) / Z;",
+     [E.test_filtered_rules_worked_example]),
+    ("filtered min-p in tempered units", "const double thr = zmax + std::log(static_cast<double>(min_p));",
+     "const double thr = zmax + T * std::log(static_cast<double>(min_p));", [E.test_filtered_rules_worked_example]),
     ("filtered nucleus cut on the tempered distribution", "cum += std::exp(z(cand[j]) - zmax) / Z;",
      "cum += std::exp((z(cand[j]) - zmax) / T) / Z;", [F.test_filtered_coupling_sums_match_numpy]),
 ]

@@ -70,8 +70,13 @@ lib = _load()
 _ws_cache: dict = {}
 
 
-def _check(rc: int, what: str):
+def _check(rc: int, what: str, ws=None):
     if rc != 0:
+        if rc == 3 and ws is not None:
+            # a failed launch may leave the workspace's counters nonzero: the
+            # next call of this signature gets a fresh zero-filled workspace
+            for key in [key for key, t in _ws_cache.items() if t is ws]:
+                del _ws_cache[key]
         raise VselError(f"{what}: {lib.vsel_status_string(rc).decode()} (status {rc})")
 
 
@@ -107,17 +112,24 @@ def workspace_bytes(op: int, dtype: int, rows: int, vocab: int, k: int) -> int:
     return int(lib.vsel_workspace_bytes(op, dtype, rows, vocab, k))
 
 
-def workspace(op: int, dtype: int, rows: int, vocab: int, k: int, device) -> torch.Tensor:
-    """Zero-filled workspace for one call signature, cached per device and signature
-    (the kernels leave its counters at zero after every call)."""
+def _ws_key(op: int, dtype: int, rows: int, vocab: int, k: int, device):
     dev = torch.device(device)
-    key = (dev.index, op, dtype, rows, vocab, k)
+    return (dev.index, torch.cuda.current_stream(dev).cuda_stream, op, dtype, rows, vocab, k)
+
+
+def workspace(op: int, dtype: int, rows: int, vocab: int, k: int, device) -> torch.Tensor:
+    """Zero-filled workspace for one call signature, cached per device, stream and
+    signature (the kernels leave its counters at zero after every call; calls that
+    share a workspace must be ordered on one stream).  A graph that captures a call
+    keeps the capture stream's workspace; eager calls on another stream do not
+    touch it."""
+    key = _ws_key(op, dtype, rows, vocab, k, device)
     ws = _ws_cache.get(key)
     if ws is None:
         n = workspace_bytes(op, dtype, rows, vocab, k)
         if n == 0:
             raise VselError("arguments rejected when sizing the workspace")
-        ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(n, dtype=torch.uint8, device=torch.device(device))
         _ws_cache[key] = ws
     return ws
 
@@ -133,7 +145,7 @@ def vsel_argmax(logits: torch.Tensor, vocab=None, out_idx=None, out_val=None, wa
         out_val = torch.empty(rows, dtype=torch.float32, device=dev)
     ws = workspace(OP_ARGMAX, dt, rows, V, 0, dev)
     _check(lib.vsel_argmax(_ptr(logits), dt, rows, V, ld, _ptr(out_idx), _ptr(out_val), _ptr(ws),
-                           ws.numel(), _stream(dev)), "vsel_argmax")
+                           ws.numel(), _stream(dev)), "vsel_argmax", ws)
     return out_idx, out_val
 
 
@@ -158,7 +170,7 @@ def vsel_argmax_excluding(logits: torch.Tensor, excluded: torch.Tensor, vocab=No
     ws = workspace(OP_ARGMAX, dt, rows, V, 0, dev)
     _check(lib.vsel_argmax_excluding(_ptr(logits), dt, rows, V, ld, _ptr(excluded) if n else None, n,
                                      _ptr(out_idx), _ptr(out_status), _ptr(ws), ws.numel(), _stream(dev)),
-           "vsel_argmax_excluding")
+           "vsel_argmax_excluding", ws)
     return out_idx, out_status
 
 
@@ -175,7 +187,7 @@ def vsel_topk(logits: torch.Tensor, k: int, vocab=None, want_argmax=True, want_l
     ws = workspace(OP_TOPK, dt, rows, V, k, dev)
     _check(lib.vsel_topk(_ptr(logits), dt, rows, V, ld, int(k), _ptr(out["vals"]), _ptr(out["ids"]),
                          _ptr(out.get("argmax")), _ptr(out.get("lse")), _ptr(ws), ws.numel(), _stream(dev)),
-           "vsel_topk")
+           "vsel_topk", ws)
     return out["vals"], out["ids"], out.get("argmax"), out.get("lse")
 
 
@@ -210,7 +222,7 @@ def vsel_sample(logits: torch.Tensor, temperature: float, top_k: int, top_p: flo
     ws = workspace(OP_SAMPLE, dt, rows, V, int(top_k), dev)
     _check(lib.vsel_sample(_ptr(logits), dt, rows, V, ld, float(temperature), int(top_k), float(top_p),
                            _ptr(u.contiguous()), _ptr(out_token), _ptr(out_logprob), _ptr(ws), ws.numel(),
-                           _stream(dev)), "vsel_sample")
+                           _stream(dev)), "vsel_sample", ws)
     return out_token, out_logprob
 
 
@@ -230,7 +242,7 @@ def vsel_sample_chain(logits: torch.Tensor, temperature: float, u: torch.Tensor,
     ws = workspace(OP_SAMPLE_CHAIN, dt, rows, V, int(top_k), dev)
     _check(lib.vsel_sample_chain(_ptr(logits), dt, rows, V, ld, float(temperature), float(top_n_sigma), int(top_k),
                                  float(typical_p), float(top_p), float(min_p), _ptr(u.contiguous()), _ptr(out_token),
-                                 _ptr(out_logprob), _ptr(ws), ws.numel(), _stream(dev)), "vsel_sample_chain")
+                                 _ptr(out_logprob), _ptr(ws), ws.numel(), _stream(dev)), "vsel_sample_chain", ws)
     return out_token, out_logprob
 
 
@@ -261,7 +273,7 @@ def vsel_spec_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: to
                                 _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resid), _ptr(u_bonus),
                                 _ptr(out["len_mrs"]), _ptr(out["tok_mrs"]), _ptr(out.get("len_aa")),
                                 _ptr(out.get("tok_aa")), _ptr(out.get("summin")), _ptr(ws), ws.numel(),
-                                _stream(dev)), "vsel_spec_accept")
+                                _stream(dev)), "vsel_spec_accept", ws)
     return out
 
 
@@ -291,7 +303,7 @@ def vsel_spec_match(target: torch.Tensor, draft: torch.Tensor, draft_tokens: tor
     ws = workspace(OP_SPEC, F32, batch, Vt, gamma, dev)
     _check(lib.vsel_spec_match(_ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature),
                                _ptr(draft_tokens), _ptr(u_match), _ptr(out["len_sm"]), _ptr(out["tok_sm"]),
-                               _ptr(out.get("sumprod")), _ptr(ws), ws.numel(), _stream(dev)), "vsel_spec_match")
+                               _ptr(out.get("sumprod")), _ptr(ws), ws.numel(), _stream(dev)), "vsel_spec_match", ws)
     return out
 
 
@@ -322,7 +334,7 @@ def vsel_spec_accept_filtered(target: torch.Tensor, draft: torch.Tensor, draft_t
         _ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature), int(top_k), float(top_p),
         float(min_p), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resid), _ptr(u_bonus), _ptr(out["len_mrs"]),
         _ptr(out["tok_mrs"]), _ptr(out.get("len_aa")), _ptr(out.get("tok_aa")), _ptr(out.get("summin")), _ptr(ws),
-        ws.numel(), _stream(dev)), "vsel_spec_accept_filtered")
+        ws.numel(), _stream(dev)), "vsel_spec_accept_filtered", ws)
     return out
 
 
@@ -352,5 +364,5 @@ def vsel_spec_match_filtered(target: torch.Tensor, draft: torch.Tensor, draft_to
     _check(lib.vsel_spec_match_filtered(
         _ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature), int(top_k), float(top_p),
         float(min_p), _ptr(draft_tokens), _ptr(u_match), _ptr(out["len_sm"]), _ptr(out["tok_sm"]),
-        _ptr(out.get("sumprod")), _ptr(ws), ws.numel(), _stream(dev)), "vsel_spec_match_filtered")
+        _ptr(out.get("sumprod")), _ptr(ws), ws.numel(), _stream(dev)), "vsel_spec_match_filtered", ws)
     return out
