@@ -242,7 +242,9 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
  *   orders it by |z - c| (c = the p-weighted mean of z, since -log p - H =
  *   c - z), then id; top_p < 1 orders it (or the typical set) by value, and
  *   the draw follows the last order (with neither, id order, as in
- *   vsel_sample).  The typical order compares the distances in float32.
+ *   vsel_sample).  The typical order compares the float64 distances with
+ *   their mantissas cut to 30 bits (distances within 2^-30 relative of each
+ *   other tie and fall to the lower id).
  *   u, out_token, out_logprob as vsel_sample; workspace VSEL_OP_SAMPLE_CHAIN
  *   with k = top_k.
  */

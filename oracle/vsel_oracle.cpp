@@ -431,9 +431,10 @@ int oracle_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, in
 // margins (6 per row, +inf when not applicable): the draw margin over W; the
 // distance of typical_p / top_p to the nearer cumulative sum at its cut; the
 // distance of the top-n-sigma and min-p thresholds to the nearest candidate
-// value (logit units); the smallest relative gap between the typicality
-// scores of the typical cut's element, or of the element drawn in typical
-// order, and its neighbours in that order (elements of equal value excluded).
+// value (logit units); the smallest gap between the typicality scores of the
+// typical cut's element, or of the element drawn in typical order, and its
+// neighbours in that order, relative to the larger score or to 1 when both
+// are below 1 (elements of equal value excluded).
 int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                         float temperature, float top_n_sigma, int32_t top_k, float typical_p, float top_p,
                         float min_p, const float* u, uint32_t* out_token, double* out_logp, double* margins,
@@ -509,10 +510,12 @@ int oracle_sample_chain(const void* logits, int dtype, int64_t rows, int64_t voc
     // 3. typical-p
     // tscore: each candidate's typicality score, kept for the near-tie margin
     std::vector<double> tscore;
-    auto tgap = [&](uint32_t a, uint32_t b) {  // relative score gap of two ids (+inf for equal values)
+    // score gap of two ids, relative to the larger score or to one logit unit
+    // when both are smaller (+inf for equal values, which tie exactly)
+    auto tgap = [&](uint32_t a, uint32_t b) {
       if (z(a) == z(b)) return kInf;
       const double sa = tscore[a], sb = tscore[b];
-      return std::fabs(sa - sb) / std::max(std::max(sa, sb), 1e-300);
+      return std::fabs(sa - sb) / std::max(std::max(sa, sb), 1.0);
     };
     if (typical_p < 1.0f) {
       std::vector<double> p;

@@ -51,10 +51,37 @@ constexpr int kMaxLevels = 12;         // key passes (each narrows the key range
 constexpr uint32_t kRun = kCapW / NT;  // sorted window candidates walked per thread
 constexpr int kNG = 4;                 // 16-byte groups per lane per tile
 
+// Typicality keys: the float64 distance |z - c| to the typical centre with its
+// mantissa cut to 30 bits, as 38 bits (an 8-bit exponent for distances in
+// [2^-125, 2^130); smaller ones count as 0, larger ones do not occur), above
+// the complemented id in 26 bits (whole-row calls have vocab <= 2^26).  The
+// cut is monotone, so the key order is the float64 order of the distances
+// except where two differ by less than 2^-30 relative; those tie and fall to
+// the lower id.
+constexpr int kTypIdBits = 26;
+constexpr uint64_t kTypIdMask = (1ull << kTypIdBits) - 1;
+constexpr uint64_t kTypScoreMask = (1ull << 38) - 1;
+__device__ __forceinline__ uint64_t typ_score(double d) {
+  const uint64_t b = (uint64_t)__double_as_longlong(d);
+  const int e = (int)(b >> 52) - 1023;
+  if (e < -125) return 0ull;
+  return ((uint64_t)(e + 126) << 30) | ((b >> 22) & ((1ull << 30) - 1));
+}
+// The distance a score stands for (the cut float64), for the guide bins.
+__device__ __forceinline__ double typ_dist(uint64_t sc) {
+  if (sc == 0ull) return 0.0;
+  const uint64_t e = (sc >> 30) - 126 + 1023;
+  return __longlong_as_double((long long)((e << 52) | ((sc & ((1ull << 30) - 1)) << 22)));
+}
+// The token id a selection key holds.
+__device__ __forceinline__ uint32_t key_id(int order, uint64_t key) {
+  return order == 0 ? ~(uint32_t)key : (uint32_t)(~key & kTypIdMask);
+}
+
 // The candidates of one selection, their order and their weights.
 //   order 0: (value desc, id asc), key comp_key;
-//   order 1: typicality, (|z - c| asc, id asc), key score_key: the distance
-//     to the typical centre c in float32 above the complemented id.
+//   order 1: typicality, (|z - c| asc, id asc), key score_key: the cut
+//     float64 distance to the typical centre c above the complemented id.
 //   A typical set (kT != 0) keeps the elements whose score key is >= kT.
 struct NucSet {
   double m;           // the row maximum
@@ -67,8 +94,8 @@ struct NucSet {
   double span;        // order 1: first-level bins are equal steps of the score over [0, span)
   uint64_t kT;        // typical set: score key >= kT (0: none)
   __device__ __forceinline__ uint64_t score_key(uint32_t bits, uint32_t i) const {
-    const float sc = (float)fabs((double)__uint_as_float(bits) - c);
-    return ((uint64_t)(~__float_as_uint(sc)) << 32) | (uint64_t)(~i);
+    const uint64_t sc = typ_score(fabs((double)__uint_as_float(bits) - c));
+    return ((~sc & kTypScoreMask) << kTypIdBits) | (~(uint64_t)i & kTypIdMask);
   }
   __device__ __forceinline__ uint64_t key(uint32_t bits, uint32_t i) const {
     return order == 0 ? comp_key(bits, i) : score_key(bits, i);
@@ -88,7 +115,7 @@ struct NucSet {
   // or of the score over [0, span) (order 1)
   template <int NB>
   __device__ __forceinline__ uint32_t bin(float z) const {
-    const double d = order == 0 ? -x(z) : fabs((double)z - c) * (kSpan / span);
+    const double d = order == 0 ? -x(z) : typ_dist(typ_score(fabs((double)z - c))) * (kSpan / span);
     return d >= kSpan ? (uint32_t)(NB - 1) : (uint32_t)(d * (NB / kSpan));
   }
 };
@@ -1009,7 +1036,7 @@ __device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
     j.step = 3;
     j.state = 1;
   } else {
-    a.out_token[row] = ~(uint32_t)j.key;
+    a.out_token[row] = key_id(j.order, j.key);
     if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(j.bits) - j.m) / j.T - log(j.tot));
     j.state = 0;
   }
