@@ -2,8 +2,9 @@
 
 Bit-exact: ids, values (the row's own bits) and argmax.  Log-sum-exp within
 1e-5 absolute (p = exp(z - lse), so this is the 1e-5 relative probability
-tolerance) plus the rounding of the float32 output, 2^-23 |lse|.  Full-size batches are compared row by row on a sample the oracle
-computes quickly, and through properties on every row.
+tolerance) plus the rounding of the float32 output, 2^-23 |lse|.  The
+full-size bf16 batch is compared on every row, and checked through
+properties as well.
 """
 import numpy as np
 import pytest
@@ -66,14 +67,17 @@ def test_config5_bf16_batch_full_size(g, oracle, k):
     xd = torch.from_numpy(bits.view(np.int16)).to(g.DEV).view(torch.bfloat16)
     vals, ids, am, lse = g.vsel.vsel_topk(xd, k, vocab=V)
     torch.cuda.synchronize()
-    # oracle on a sample: every row with a copied maximum plus 48 others
-    rng = np.random.default_rng(k)
-    sample = np.unique(np.concatenate([dup_rows, rng.choice(rows, 48, replace=False)]))
-    ov, oi, oam, olse = oracle.topk(bits[sample], k, vocab=V)
-    assert np.array_equal(g.u32(ids)[sample], oi)
-    assert np.array_equal(g.bits(vals)[sample], ov.view(np.uint32))
-    assert np.array_equal(g.u32(am)[sample], oam)
-    assert np.all(lse_ok(lse.cpu().numpy()[sample], olse))
+    # every row against the oracle, in the launch configuration the benchmark
+    # times (the duplicated maxima of 10% of the rows are bf16 ties at the top)
+    ov, oi, oam, olse = oracle.topk(bits, k, vocab=V)
+    gi, gv, ga = g.u32(ids), g.bits(vals), g.u32(am)
+    for name, got, ref in (("ids", gi, oi), ("values", gv, ov.view(np.uint32)), ("argmax", ga, oam)):
+        bad = np.nonzero(np.any((got != ref).reshape(rows, -1), axis=1))[0]
+        assert len(bad) == 0, f"{name} differ on {len(bad)} rows, first {bad[:5]}"
+    assert np.all(lse_ok(lse.cpu().numpy(), olse))
+    # the rows with a copied maximum: a tie at the top, the lower id first
+    assert len(dup_rows) > 0 and np.all(gv[dup_rows, 0] == gv[dup_rows, 1])
+    assert np.all(gi[dup_rows, 0] < gi[dup_rows, 1])
     # properties on every row (float32 on the device, exact comparisons only)
     xf = xd[:, :V].float()
     v = vals
