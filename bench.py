@@ -241,6 +241,7 @@ def main():
 def extras(torch, vsel, W, dev, stream, bufs, out):
     """Microseconds per call for the other configurations (cold: inputs rotated
     over >= 1 GB of copies; warm: one buffer, as right after the LM head)."""
+    from vocab_row_reductions_amd.acceptance import acceptance_counters, summary_line
     ex = {}
     ex["topk_k84_us"] = time_calls(lambda i: vsel.vsel_topk(bufs[i % 3], K, vocab=V, out=out), 50, 5, stream)
     out64 = dict(vals=torch.empty((ROWS, 64), dtype=torch.float32, device=dev),
@@ -317,19 +318,20 @@ def extras(torch, vsel, W, dev, stream, bufs, out):
     so = vsel.vsel_spec_accept(tg, dr, *args)
     ex["spec_accept_32x8_eager_us"] = time_calls(lambda i: vsel.vsel_spec_accept(tg, dr, *args, out=so), 50, 5, stream)
     ex["spec_accept_32x8_device_us"] = time_graph(lambda i: vsel.vsel_spec_accept(tg, dr, *args, out=so), 10, stream)
-    L = so["len_mrs"].cpu().numpy()
-    tested = int(np.minimum(L + 1, 8).sum())
-    ex["spec_accept_32x8_per_position_acceptance"] = float(L.sum() / tested)
-    ex["spec_accept_32x8_mean_summin"] = float(so["summin"].float().mean().item())
+    # the run counters and both closed forms of the same pass, over the tested positions
+    cm = acceptance_counters(so["len_mrs"].cpu().numpy(), 8, so["summin"].cpu().numpy(), so["sumprod"].cpu().numpy())
+    ex["spec_accept_32x8_counters"] = cm
+    print(summary_line(cm), file=sys.stderr, flush=True)
     # the same batch under sampler-match (one uniform per position and the bonus)
     um = g(W.uniforms(32 * 9, seed=2026))
     margs = (args[0], um, 32, 8, 1.0)
     mo = vsel.vsel_spec_match(tg, dr, *margs)
     ex["spec_match_32x8_eager_us"] = time_calls(lambda i: vsel.vsel_spec_match(tg, dr, *margs, out=mo), 50, 5, stream)
     ex["spec_match_32x8_device_us"] = time_graph(lambda i: vsel.vsel_spec_match(tg, dr, *margs, out=mo), 10, stream)
-    Lm = mo["len_sm"].cpu().numpy()
-    ex["spec_match_32x8_per_position_acceptance"] = float(Lm.sum() / int(np.minimum(Lm + 1, 8).sum()))
-    ex["spec_match_32x8_mean_sumprod"] = float(mo["sumprod"].float().mean().item())
+    cs = acceptance_counters(mo["len_sm"].cpu().numpy(), 8, so["summin"].cpu().numpy(), mo["sumprod"].cpu().numpy(),
+                             rule="sampler-match")
+    ex["spec_match_32x8_counters"] = cs
+    print(summary_line(cs), file=sys.stderr, flush=True)
     # both rules with filtered p and q (top-k 50 then top-p 0.95; top-p 0.9 over whole rows)
     for name, kw in (("k50_p095", dict(top_k=50, top_p=0.95)), ("wholerow_p09", dict(top_p=0.9))):
         fo = vsel.vsel_spec_accept_filtered(tg, dr, *args, **kw)

@@ -280,13 +280,17 @@ vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64
  *                 the remaining slots VSEL_NONFINITE
  *   out_len_aa, out_tok_aa: the same for argmax-against-argmax (may be NULL)
  *   out_summin    [batch*gamma] float32 or NULL
+ *   out_sumprod   [batch*gamma] float32 or NULL: sum_x p_i(x) q_i(x), the
+ *                 sampler-match rule's acceptance probability, from the same
+ *                 pass ("Verifying the gain before trusting a throughput
+ *                 number" reads both closed forms for one run)
  */
 vsel_status vsel_spec_accept(const float* target_logits, int64_t ld_t, const float* draft_logits,
                              int64_t ld_d, int64_t batch, int32_t gamma, int64_t vocab,
                              float temperature, const uint32_t* draft_tokens, const float* u_accept,
                              const float* u_resid, const float* u_bonus, int32_t* out_len_mrs,
                              uint32_t* out_tok_mrs, int32_t* out_len_aa, uint32_t* out_tok_aa,
-                             float* out_summin, void* workspace, size_t workspace_bytes,
+                             float* out_summin, float* out_sumprod, void* workspace, size_t workspace_bytes,
                              void* stream);
 
 /* Speculative-decoding acceptance by sampler-match ("speculative-acceptance.md",
@@ -340,7 +344,7 @@ vsel_status vsel_spec_accept_filtered(const float* target_logits, int64_t ld_t, 
                                       const uint32_t* draft_tokens, const float* u_accept,
                                       const float* u_resid, const float* u_bonus, int32_t* out_len_mrs,
                                       uint32_t* out_tok_mrs, int32_t* out_len_aa, uint32_t* out_tok_aa,
-                                      float* out_summin, void* workspace, size_t workspace_bytes,
+                                      float* out_summin, float* out_sumprod, void* workspace, size_t workspace_bytes,
                                       void* stream);
 
 vsel_status vsel_spec_match_filtered(const float* target_logits, int64_t ld_t, const float* draft_logits,

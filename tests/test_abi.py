@@ -112,7 +112,7 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
         a = {**args, **kw}
         return L.vsel_spec_accept(fake, a.get("ld_t", 100), fake, a.get("ld_d", 100), a["batch"], a["gamma"],
                                   a["vocab"], a["T"], fake, fake, fake, fake, fake, fake, None, None, None,
-                                  ws, 1 << 20, None)
+                                  None, ws, 1 << 20, None)
     assert spec(gamma=0) == EINVAL
     assert spec(gamma=257) == EINVAL
     assert spec(batch=0) == EINVAL
@@ -132,7 +132,7 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
     def filt(fn, k=5, p=0.9, mp=0.0, ws_bytes=1 << 20):
         if fn == "accept":
             return L.vsel_spec_accept_filtered(fake, 100, fake, 100, 2, 3, 100, 1.0, k, p, mp, fake, fake, fake,
-                                               fake, fake, fake, None, None, None, ws, ws_bytes, None)
+                                               fake, fake, fake, None, None, None, None, ws, ws_bytes, None)
         return L.vsel_spec_match_filtered(fake, 100, fake, 100, 2, 3, 100, 1.0, k, p, mp, fake, fake, fake, fake,
                                           None, ws, ws_bytes, None)
     for fn in ("accept", "match"):

@@ -3,8 +3,8 @@
 Bit-exact accepted lengths and emitted tokens for both rules, except after an
 accept test whose oracle float64 margin |u*q(t) - p(t)| is below 1e-7 (later
 outputs of that sequence are not compared) and for a draw whose margin to a
-CDF boundary is below 1e-9 of the total.  Coupling sums within 1e-6 absolute
-plus 1e-5 relative.
+CDF boundary is below 1e-9 of the total.  Coupling sums (sum min(p, q) and the
+sum p*q of the same pass) within 1e-6 absolute plus 1e-5 relative.
 """
 import numpy as np
 import pytest
@@ -48,6 +48,12 @@ def compare(g, oracle, d, target=None, draft=None, tokens=None, T=None):
     ok = np.isfinite(ref["summin"])
     assert np.all(np.abs(got["summin"][ok] - ref["summin"][ok]) <= 1e-6 + 1e-5 * np.abs(ref["summin"][ok]))
     assert np.array_equal(np.isnan(got["summin"]), ~ok)
+    # sum p*q from the same pass: the oracle's sampler-match sums of the same p and q
+    rsp = oracle.spec_match(target, draft, tokens, np.full((B, G + 1), 0.5, np.float32), B, G, T)["sumprod"]
+    ok = np.isfinite(rsp)
+    assert np.all(np.abs(got["sumprod"][ok] - rsp[ok]) <= 1e-6 + 1e-5 * np.abs(rsp[ok]))
+    assert np.array_equal(np.isnan(got["sumprod"]), ~ok)
+    assert np.all(got["sumprod"][ok] <= got["summin"][ok] + 1e-6)
     exempt = 0
     for b in range(B):
         am = ref["acc_margin"][b]

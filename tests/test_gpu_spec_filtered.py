@@ -47,6 +47,9 @@ def compare_mrs(g, oracle, d, toks, T, kw):
         g.dev(d["target"]), g.dev(d["draft"]), g.dev(toks), g.dev(d["u_acc"]), g.dev(d["u_res"]), g.dev(d["u_bon"]),
         B, G, T, **kw))
     ref = oracle.spec_accept(d["target"], d["draft"], toks, d["u_acc"], d["u_res"], d["u_bon"], B, G, T, **kw)
+    # sum p*q of the same pass against the oracle's sampler-match sums of the same filtered p and q
+    rsp = oracle.spec_match(d["target"], d["draft"], toks, np.full((B, G + 1), 0.5, np.float32), B, G, T,
+                            **kw)["sumprod"]
     assert np.array_equal(got["len_aa"], ref["len_aa"]) and np.array_equal(got["tok_aa"], ref["tok_aa"])
     skipped = 0
     for b in range(B):
@@ -55,6 +58,7 @@ def compare_mrs(g, oracle, d, toks, T, kw):
             continue
         ok = np.isfinite(ref["summin"][b])
         assert np.all(np.abs(got["summin"][b][ok] - ref["summin"][b][ok]) <= 1e-6 + 1e-5 * ref["summin"][b][ok])
+        assert np.all(np.abs(got["sumprod"][b][ok] - rsp[b][ok]) <= 1e-6 + 1e-5 * rsp[b][ok])
         close = np.nonzero(ref["acc_margin"][b] < ACC_MARGIN)[0]
         if len(close):
             assert np.array_equal(got["tok_mrs"][b, :close[0]], ref["tok_mrs"][b, :close[0]])

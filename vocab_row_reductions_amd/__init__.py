@@ -54,10 +54,10 @@ def _load():
     L.vsel_sample_chain.argtypes = [vp, C.c_int, i64, i64, i64, f32, f32, i32, f32, f32, f32, vp, vp, vp, vp, sz,
                                     vp]
     L.vsel_spec_accept.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                   vp, vp, sz, vp]
+                                   vp, vp, vp, sz, vp]
     L.vsel_spec_match.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.vsel_spec_accept_filtered.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, i32, f32, f32, vp, vp, vp, vp,
-                                            vp, vp, vp, vp, vp, vp, sz, vp]
+                                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.vsel_spec_match_filtered.argtypes = [vp, i64, vp, i64, i64, i32, i64, f32, i32, f32, f32, vp, vp, vp, vp,
                                            vp, vp, sz, vp]
     for f in (L.vsel_argmax, L.vsel_argmax_excluding, L.vsel_topk, L.vsel_topk_noalloc, L.vsel_sample, L.vsel_sample_chain,
@@ -249,7 +249,8 @@ def vsel_sample_chain(logits: torch.Tensor, temperature: float, u: torch.Tensor,
 def vsel_spec_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor, u_accept: torch.Tensor,
                      u_resid: torch.Tensor, u_bonus: torch.Tensor, batch: int, gamma: int, temperature: float,
                      vocab=None, out=None):
-    """Speculative acceptance for batch x gamma drafts -> dict of len_mrs, tok_mrs, len_aa, tok_aa, summin."""
+    """Speculative acceptance for batch x gamma drafts -> dict of len_mrs, tok_mrs, len_aa, tok_aa, summin,
+    sumprod (a caller's `out` may leave out any of the last four)."""
     if target.dtype != torch.float32 or draft.dtype != torch.float32:
         raise TypeError("speculative acceptance takes float32 rows")
     rt, Vt, ld_t = _rows(target, vocab)
@@ -267,12 +268,14 @@ def vsel_spec_accept(target: torch.Tensor, draft: torch.Tensor, draft_tokens: to
                    tok_mrs=torch.empty((batch, gamma + 1), dtype=torch.int32, device=dev),
                    len_aa=torch.empty(batch, dtype=torch.int32, device=dev),
                    tok_aa=torch.empty((batch, gamma + 1), dtype=torch.int32, device=dev),
-                   summin=torch.empty((batch, gamma), dtype=torch.float32, device=dev))
+                   summin=torch.empty((batch, gamma), dtype=torch.float32, device=dev),
+                   sumprod=torch.empty((batch, gamma), dtype=torch.float32, device=dev))
     ws = workspace(OP_SPEC, F32, batch, Vt, gamma, dev)
     _check(lib.vsel_spec_accept(_ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature),
                                 _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resid), _ptr(u_bonus),
                                 _ptr(out["len_mrs"]), _ptr(out["tok_mrs"]), _ptr(out.get("len_aa")),
-                                _ptr(out.get("tok_aa")), _ptr(out.get("summin")), _ptr(ws), ws.numel(),
+                                _ptr(out.get("tok_aa")), _ptr(out.get("summin")), _ptr(out.get("sumprod")), _ptr(ws),
+                                ws.numel(),
                                 _stream(dev)), "vsel_spec_accept", ws)
     return out
 
@@ -328,13 +331,14 @@ def vsel_spec_accept_filtered(target: torch.Tensor, draft: torch.Tensor, draft_t
                    tok_mrs=torch.empty((batch, gamma + 1), dtype=torch.int32, device=dev),
                    len_aa=torch.empty(batch, dtype=torch.int32, device=dev),
                    tok_aa=torch.empty((batch, gamma + 1), dtype=torch.int32, device=dev),
-                   summin=torch.empty((batch, gamma), dtype=torch.float32, device=dev))
+                   summin=torch.empty((batch, gamma), dtype=torch.float32, device=dev),
+                   sumprod=torch.empty((batch, gamma), dtype=torch.float32, device=dev))
     ws = workspace(OP_SPEC_FILTERED, F32, batch, Vt, gamma, dev)
     _check(lib.vsel_spec_accept_filtered(
         _ptr(target), ld_t, _ptr(draft), ld_d, batch, gamma, Vt, float(temperature), int(top_k), float(top_p),
         float(min_p), _ptr(draft_tokens), _ptr(u_accept), _ptr(u_resid), _ptr(u_bonus), _ptr(out["len_mrs"]),
-        _ptr(out["tok_mrs"]), _ptr(out.get("len_aa")), _ptr(out.get("tok_aa")), _ptr(out.get("summin")), _ptr(ws),
-        ws.numel(), _stream(dev)), "vsel_spec_accept_filtered", ws)
+        _ptr(out["tok_mrs"]), _ptr(out.get("len_aa")), _ptr(out.get("tok_aa")), _ptr(out.get("summin")),
+        _ptr(out.get("sumprod")), _ptr(ws), ws.numel(), _stream(dev)), "vsel_spec_accept_filtered", ws)
     return out
 
 

@@ -807,7 +807,8 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
                              int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
                              const float* u_accept, const float* u_resid, const float* u_bonus,
                              int32_t* out_len_mrs, uint32_t* out_tok_mrs, int32_t* out_len_aa,
-                             uint32_t* out_tok_aa, float* out_summin, void* ws, size_t ws_bytes, void* stream) {
+                             uint32_t* out_tok_aa, float* out_summin, float* out_sumprod, void* ws, size_t ws_bytes,
+                             void* stream) {
   if (!u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs) return VSEL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   SpecArgs p;
@@ -822,6 +823,7 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   p.len_aa = out_len_aa;
   p.tok_aa = out_tok_aa;
   p.summin = out_summin;
+  p.sumprod = out_sumprod;
   return launched(launch_spec(p, s));
 }
 
@@ -925,7 +927,8 @@ vsel_status vsel_spec_accept_filtered(const float* target, int64_t ld_t, const f
                                       float top_p, float min_p, const uint32_t* draft_tokens, const float* u_accept,
                                       const float* u_resid, const float* u_bonus, int32_t* out_len_mrs,
                                       uint32_t* out_tok_mrs, int32_t* out_len_aa, uint32_t* out_tok_aa,
-                                      float* out_summin, void* ws, size_t ws_bytes, void* stream) {
+                                      float* out_summin, float* out_sumprod, void* ws, size_t ws_bytes,
+                                      void* stream) {
   if (!u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs) return VSEL_EINVAL;
   if (!filters_ok(top_k, top_p, min_p)) return VSEL_EINVAL;
   SpecFiltWs fw{};
@@ -944,6 +947,7 @@ vsel_status vsel_spec_accept_filtered(const float* target, int64_t ld_t, const f
   p.len_aa = out_len_aa;
   p.tok_aa = out_tok_aa;
   p.summin = out_summin;
+  p.sumprod = out_sumprod;
   return launched(launch_spec(p, s));
 }
 

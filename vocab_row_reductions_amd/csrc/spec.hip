@@ -61,7 +61,10 @@ __device__ __forceinline__ double block_excl_scan_f64(SelShared& sh, double v, d
 }
 
 // ---------------------------------------------------------------- pass 2
-template <bool VEC, bool FILT>
+// SP: also sum p*q per position (the sampler-match acceptance probability,
+// reported beside sum min(p, q) as "Verifying the gain before trusting a
+// throughput number" prints both closed forms), one more FMA per element.
+template <bool VEC, bool FILT, bool SP>
 __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
   constexpr int E = 4, TILE = NT * PG * E;
   __shared__ SelShared sh;
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
 
   // filtered rows: an element below its row's key floor has p (q) = 0
   const uint64_t kz = FILT ? a.kfl[trow] : 0ull, kd = FILT ? a.kfl[nT + drow] : 0ull;
-  double tot = 0.0;
+  double tot = 0.0, tsp = 0.0;
   if (a.T > 0.0f && !bad) {
     const float c = a.lse_c;
     const double Lp = a.st_lse[trow] * (double)kLog2e, Lq = a.st_lse[nT + drow] * (double)kLog2e;
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     // group j of this lane starts at element t0 + (j*NT + tid)*E
     auto pair = [&](const auto& gz, const auto& gd, int64_t t0) {
       constexpr int NGP = (int)(sizeof(gz) / sizeof(Group));
-      float acc = 0.0f;
+      float acc = 0.0f, acc2 = 0.0f;
 #pragma unroll
       for (int j = 0; j < NGP; ++j)
 #pragma unroll
@@ -103,8 +106,10 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
             if (comp_key(gd[j].w[e], x) < kd) q = 0.0f;
           }
           acc += fminf(p, q);
+          if constexpr (SP) acc2 = fmaf(p, q, acc2);
         }
       tot += (double)acc;
+      if constexpr (SP) tsp += (double)acc2;
     };
     const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
     const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
@@ -127,13 +132,19 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
         if (FILT && comp_key(__float_as_uint(zr[x]), (uint32_t)x) < kz) p = 0.0f;
         if (FILT && comp_key(__float_as_uint(dr[x]), (uint32_t)x) < kd) q = 0.0f;
         tot += (double)fminf(p, q);
+        if constexpr (SP) tsp += (double)(p * q);
       }
   }
   tot = block_sum_f64(sh, tot);
+  if constexpr (SP) tsp = block_sum_f64(sh, tsp);
   if (a.S > 1) {
-    if (tid == 0) st_dev(&a.p_summin[pos * a.S + seg], tot);
+    if (tid == 0) {
+      st_dev(&a.p_summin[pos * a.S + seg], tot);
+      if constexpr (SP) st_dev(&a.p_wt[pos * a.S + seg], tsp);
+    }
     if (!last_done(sh, a.tk_pos + pos, (uint32_t)a.S)) return;
     tot = merge_sum(sh, a.p_summin + pos * a.S, a.S);
+    if constexpr (SP) tsp = merge_sum(sh, a.p_wt + pos * a.S, a.S);
   }
   // Position decision (one thread): coupling sum and the accept test.
   if (tid == 0) {
@@ -144,6 +155,7 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     } else if (a.T == 0.0f) {
       flag = (t == a.st_amax[trow]) ? 1u : 0u;
       tot = (a.st_amax[trow] == a.st_amax[nT + drow]) ? 1.0 : 0.0;
+      tsp = tot;
     } else {
       const double Td = a.T;
       double pt = exp((double)zr[t] / Td - a.st_lse[trow]);
@@ -154,6 +166,7 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     }
     st_dev(&a.acc[pos], flag);
     if (a.summin) st_dev(&a.summin[pos], bad ? __builtin_nanf("") : (float)tot);
+    if (SP) st_dev(&a.sumprod[pos], bad ? __builtin_nanf("") : (float)tsp);
   }
   if (!last_done(sh, a.tk_seq + b, (uint32_t)G)) return;
   if (tid < G) sh.hist[tid] = ld_dev(&a.acc[b * G + tid]);
@@ -174,6 +187,8 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     if (a.len_aa) a.len_aa[b] = -1;
     if (a.summin)
       for (int64_t q = 0; q < G; ++q) st_dev(&a.summin[b * G + q], __builtin_nanf(""));
+    if (SP)
+      for (int64_t q = 0; q < G; ++q) st_dev(&a.sumprod[b * G + q], __builtin_nanf(""));
     a.draw_L[b] = -1;
     return;
   }
@@ -707,19 +722,28 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
   }
 }
 
+template <bool VEC, bool FILT>
+static void launch_coupling(bool sp, unsigned npos, const SpecArgs& a, hipStream_t s) {
+  if (sp)
+    hipLaunchKernelGGL((coupling_kernel<VEC, FILT, true>), dim3(npos), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((coupling_kernel<VEC, FILT, false>), dim3(npos), dim3(NT), 0, s, a);
+}
+
 hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
   const bool vec = a.vec_t && a.vec_d;
   const unsigned npos = (unsigned)(a.B * a.gamma * a.S);
+  const bool sp = a.sumprod != nullptr;
   if (a.kfl) {
     if (vec)
-      hipLaunchKernelGGL((coupling_kernel<true, true>), dim3(npos), dim3(NT), 0, s, a);
+      launch_coupling<true, true>(sp, npos, a, s);
     else
-      hipLaunchKernelGGL((coupling_kernel<false, true>), dim3(npos), dim3(NT), 0, s, a);
+      launch_coupling<false, true>(sp, npos, a, s);
   } else {
     if (vec)
-      hipLaunchKernelGGL((coupling_kernel<true, false>), dim3(npos), dim3(NT), 0, s, a);
+      launch_coupling<true, false>(sp, npos, a, s);
     else
-      hipLaunchKernelGGL((coupling_kernel<false, false>), dim3(npos), dim3(NT), 0, s, a);
+      launch_coupling<false, false>(sp, npos, a, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0.0f) return e;
