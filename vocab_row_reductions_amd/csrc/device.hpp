@@ -644,11 +644,13 @@ __device__ __forceinline__ double exp2_split(double a) {
 // is exact for the k that occur); e^r by its Taylor series to r^6 (|r| <=
 // ln2/128, so the truncation is below 1e-19); then 2^(k/64) as a table entry
 // 2^((k mod 64)/64) and an exponent shift.  A few units in the last place,
-// like a library exp.
+// like a library exp.  Host code may call it too (with the table filled by
+// the host's exp2), which is how it is checked against a high-precision
+// exponential.
 constexpr double kL64Hi = 0x1.62e42f0000000p-7;   // ln2/64, high part
 constexpr double kL64Lo = 0x1.df473de6af279p-32;  // ln2/64 - kL64Hi
 constexpr double kInvL64 = 0x1.71547652b82fep+6;  // 64/ln2
-__device__ __forceinline__ double exp_le0(double x, const double* e2) {
+__host__ __device__ __forceinline__ double exp_le0(double x, const double* e2) {
   const double xc = fmax(x, -745.0);
   const double k = rint(xc * kInvL64);
   const double r = fma(-k, kL64Lo, fma(-k, kL64Hi, xc));
