@@ -99,7 +99,7 @@ const char* vsel_status_string(int status);
 /* Workspace bytes an operation needs.
  *   VSEL_OP_ARGMAX:      rows, vocab; k ignored.
  *   VSEL_OP_TOPK:        rows, vocab, k.
- *   VSEL_OP_SAMPLE:      rows, vocab, k = top_k.
+ *   VSEL_OP_SAMPLE:      rows, vocab, k = top_k (the same as VSEL_OP_SAMPLE_CHAIN).
  *   VSEL_OP_SPEC_ACCEPT: rows = batch, vocab, k = gamma.
  *   VSEL_OP_SAMPLE_CHAIN: rows, vocab, k = top_k.
  *   VSEL_OP_SPEC_FILTERED: rows = batch, vocab, k = gamma (any filters).
@@ -193,7 +193,8 @@ vsel_status vsel_topk_noalloc(const void* logits, int dtype, int64_t rows, int64
  *   1. temperature == 0 or top_k == 1: the argmax token, logprob 0 (greedy
  *      draws nothing, "speculative-acceptance.md", "RNG dependency").
  *   2. candidates: the top min(top_k, vocab) elements; top_k == 0 means the
- *      whole row in id order and requires top_p == 1.
+ *      whole row: in id order when top_p == 1, else in (value desc, id asc)
+ *      order for the cut and the draw (vsel_sample_chain with top_p alone).
  *   3. p0_j = exp(z_j - z_0) / sum over candidates (untempered).
  *   4. keep the first n >= 1 candidates, n the smallest with
  *      p0_0 + ... + p0_{n-1} >= top_p (all of them when top_p == 1).
@@ -203,7 +204,8 @@ vsel_status vsel_topk_noalloc(const void* logits, int dtype, int64_t rows, int64
  *   out_logprob = log(w_j / W), the log-probability under the distribution
  *   actually drawn from.
  *   temperature >= 0, 0 <= top_k <= VSEL_K_MAX, 0 < top_p <= 1; with
- *   top_k == 0, vocab <= 67,108,864 (256 segments of 1,024 chunks of 256)
+ *   top_k == 0, vocab <= 67,108,864 (256 segments of 1,024 chunks of 256).
+ *   The workspace (VSEL_OP_SAMPLE) has the layout of VSEL_OP_SAMPLE_CHAIN.
  *   u           [rows] float32 in [0, 1)
  *   out_token   [rows] uint32 (VSEL_NONFINITE for a fail-closed row)
  *   out_logprob [rows] float32 or NULL
@@ -237,7 +239,7 @@ vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t voc
  * filters off except top_k / top_p this is vsel_sample.
  *   temperature >= 0 and finite; top_n_sigma >= 0 and finite;
  *   0 <= top_k <= VSEL_K_MAX; 0 < typical_p <= 1; 0 < top_p <= 1;
- *   0 <= min_p <= 1.  typical_p < 1 needs top_k <= 128.  With top_k == 0,
+ *   0 <= min_p <= 1.  With top_k == 0,
  *   vocab <= 67,108,864, and the filters act on the whole row: typical_p < 1
  *   orders it by |z - c| (c = the p-weighted mean of z, since -log p - H =
  *   c - z), then id; top_p < 1 orders it (or the typical set) by value, and

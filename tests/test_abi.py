@@ -49,9 +49,11 @@ def test_workspace_sizes(vsel):
                   (vsel.OP_SPEC, 8), (vsel.OP_SAMPLE_CHAIN, 0), (vsel.OP_SAMPLE_CHAIN, 128)):
         n = wb(op, vsel.F32, 32, 202048, k)
         assert n > 0 and n % 256 == 0
-    # the chain holds the sampler's workspace and the row moments after it
+    # the sampler is the chain with top-k and top-p only: one layout (the row
+    # moments and, for top_k = 0, the whole-row nucleus after the candidates)
     for k in (0, 1, 50, 1024):
-        assert wb(vsel.OP_SAMPLE_CHAIN, vsel.BF16, 64, 202048, k) > wb(vsel.OP_SAMPLE, vsel.BF16, 64, 202048, k)
+        assert wb(vsel.OP_SAMPLE_CHAIN, vsel.BF16, 64, 202048, k) == wb(vsel.OP_SAMPLE, vsel.BF16, 64, 202048, k)
+    assert wb(vsel.OP_SAMPLE, vsel.F32, 64, 202048, 0) > wb(vsel.OP_SAMPLE, vsel.F32, 64, 202048, 20)
     assert wb(vsel.OP_SAMPLE_CHAIN, vsel.F32, 4, 100, 1025) == 0
     # the filtered rules hold the speculative workspace and the filter pass's after it
     assert wb(vsel.OP_SPEC_FILTERED, vsel.F32, 32, 202048, 8) > wb(vsel.OP_SPEC, vsel.F32, 32, 202048, 8) > 0
@@ -94,7 +96,7 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
     assert L.vsel_topk_noalloc(fake, 0, 0, 100, 100, 5, fake, fake, None, None, None) == EINVAL
     assert L.vsel_topk_noalloc(fake, 0, vsel.NOALLOC_MAX_ROWS + 1, 100, 100, 5, fake, fake, None, None,
                                None) == EINVAL
-    bad_sample = [(-0.5, 20, 0.9), (0.7, -1, 0.9), (0.7, 20, 0.0), (0.7, 20, 1.5), (0.7, 0, 0.9),
+    bad_sample = [(-0.5, 20, 0.9), (0.7, -1, 0.9), (0.7, 20, 0.0), (0.7, 20, 1.5),
                   (0.7, 1025, 0.9), (float("nan"), 20, 0.9), (float("inf"), 20, 0.9)]
     for T, k, p in bad_sample:
         assert L.vsel_sample(fake, 0, 4, 100, 100, T, k, p, fake, fake, None, ws, 1 << 20, None) == EINVAL
@@ -102,7 +104,7 @@ def test_invalid_arguments_return_einval_before_launch(vsel):
         return L.vsel_sample_chain(fake, 0, 4, 100, 100, T, sig, k, typ, p, mp, u, fake, None, ws, ws_bytes, None)
     bad_chain = [dict(sig=-1.0), dict(sig=float("inf")), dict(sig=float("nan")), dict(typ=0.0), dict(typ=1.5),
                  dict(mp=-0.1), dict(mp=1.01), dict(mp=float("nan")),
-                 dict(k=129, typ=0.9), dict(k=-1), dict(k=1025), dict(p=0.0), dict(T=float("inf")),
+                 dict(k=-1), dict(k=1025), dict(p=0.0), dict(T=float("inf")),
                  dict(T=-0.1), dict(u=None)]
     for kw in bad_chain:
         assert chain(**kw) == EINVAL, kw

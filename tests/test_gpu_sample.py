@@ -90,3 +90,20 @@ def test_fail_closed_rows(g, oracle):
         t = g.u32(tok)
         assert t[0] != g.SENT and np.all(t[1:] == g.SENT)
         assert np.all(np.isnan(lp.cpu().numpy()[1:]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_whole_row_top_p(g, oracle, dtype):
+    """top_k = 0 with top_p < 1: the nucleus over the whole row, in (value desc,
+    id asc) order, as the ordered chain with top-p alone defines it."""
+    x, u = W.sampling_rows(rows=64, seed=41)
+    if dtype == "bf16":
+        x = W.f32_to_bf16_bits(x)
+    for T, top_p in ((0.7, 0.95), (1.2, 0.5)):
+        tok, lp = g.vsel.vsel_sample(g.dev_rows(x), T, 0, top_p, g.dev(u), vocab=x.shape[1])
+        otok, olp, om = oracle.sample_chain(x, T, u, top_p=top_p)
+        exempt = np.any(om[:, :3] < MARGIN, axis=1)
+        assert exempt.sum() <= 1
+        gt = g.u32(tok)
+        assert np.array_equal(gt[~exempt], otok[~exempt]), (T, top_p)
+        assert np.all(np.abs(lp.cpu().numpy()[~exempt] - olp[~exempt]) <= 1e-5)

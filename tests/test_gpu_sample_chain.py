@@ -57,6 +57,8 @@ CHAINS = [
     dict(top_k=500, top_n_sigma=1.0, min_p=0.01, top_p=0.9),  # k above the per-wave kernel's range
     dict(top_k=1024, min_p=0.2),
     dict(top_k=20, top_p=0.95),                              # the plain sampler's chain
+    dict(top_k=300, typical_p=0.5),                          # typical-p on the workgroup kernel's candidates
+    dict(top_k=1024, typical_p=0.8, top_p=0.9, min_p=0.01),
 ]
 
 

@@ -129,9 +129,11 @@ struct TopkPlan {
 // Top-k segments are whole tiles (kTopkTile elements of 16 bytes per lane
 // x 8 groups), so only a row's last segment ends in a partial tile.
 // The per-wave variant takes k <= kWaveTopkMax on 16-byte-aligned rows.
-TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k, bool wave) {
+// big_scratch: the chain's typical-p on more than kWaveTopkMax candidates,
+// whose scratch needs the large buffer's free half.
+TopkPlan plan_topk(int dtype, bool lse, int64_t rows, int64_t V, int64_t k, bool wave, bool big_scratch = false) {
   const int64_t tile = (int64_t)kTopkGroups * 256 * (dtype == VSEL_F32 ? 4 : 8);
-  const int cap = (wave || 2 * k <= kCapSmall) ? kCapSmall : kCapLarge;
+  const int cap = (wave || (2 * k <= kCapSmall && !big_scratch)) ? kCapSmall : kCapLarge;
   int64_t resident = 0;
   if (wave) {
     const int b = topk_wave_blocks_per_cu(dtype, lse);
@@ -442,8 +444,7 @@ size_t vsel_workspace_bytes(int op, int dtype, int64_t rows, int64_t vocab, int3
       topk_layout(L, rows, k, plan_topk_bound(rows, vocab, k));
       return L.off;
     }
-    case VSEL_OP_SAMPLE:
-      return sample_ws_bytes(rows, vocab, k);
+    case VSEL_OP_SAMPLE:  // the chain's layout: top_k == 0 with top_p < 1 runs the whole-row nucleus
     case VSEL_OP_SAMPLE_CHAIN: {
       const size_t base = sample_ws_bytes(rows, vocab, k);
       if (base == 0) return 0;
@@ -515,7 +516,7 @@ static vsel_status topk_common(const void* logits, int dtype, int64_t rows, int6
                                void* stream, bool exact_layout = false) {
   const bool vec = aligned16(logits, ld, elem_size(dtype));
   const bool wave = vec && k <= kWaveTopkMax;
-  const TopkPlan tp = plan_topk(dtype, want_lse, rows, vocab, k, wave);
+  const TopkPlan tp = plan_topk(dtype, want_lse, rows, vocab, k, wave, a.mode == 1 && a.typical_p < 1.0f);
   const Plan& p = tp.p;
   Layout L;
   const TopkWs w = topk_layout(L, rows, k, exact_layout ? p : plan_topk_bound(rows, vocab, k));
@@ -561,7 +562,6 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
       !(top_p > 0.0f && top_p <= 1.0f))
     return VSEL_EINVAL;
   if (top_k == 0 && (typical_p < 1.0f || top_p < 1.0f) && !(cw && cw->has_nuc)) return VSEL_EINVAL;
-  if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
   if (top_n_sigma > 0.0f && !cw) return VSEL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   const bool greedy = temperature == 0.0f || top_k == 1;
@@ -699,11 +699,13 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
   return topk_common(logits, dtype, rows, vocab, ld, k, false, a, ws, ws_bytes, stream);
 }
 
+// The sampler is the chain with top_k and top_p only (its workspace has the
+// chain's layout, so top_k == 0 with top_p < 1 takes the whole-row nucleus).
 vsel_status vsel_sample(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
                         float temperature, int32_t top_k, float top_p, const float* u, uint32_t* out_token,
                         float* out_logprob, void* ws, size_t ws_bytes, void* stream) {
-  return sample_impl(logits, dtype, rows, vocab, ld, temperature, top_k, top_p, 0.0f, 1.0f, 0.0f, nullptr, u,
-                     out_token, out_logprob, ws, ws_bytes, stream);
+  return vsel_sample_chain(logits, dtype, rows, vocab, ld, temperature, 0.0f, top_k, 1.0f, top_p, 0.0f, u, out_token,
+                           out_logprob, ws, ws_bytes, stream);
 }
 
 vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64_t vocab, int64_t ld,
@@ -718,7 +720,6 @@ vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64
       !(top_p > 0.0f && top_p <= 1.0f) || !(top_n_sigma >= 0.0f) || std::isinf(top_n_sigma) ||
       !(typical_p > 0.0f && typical_p <= 1.0f) || !(min_p >= 0.0f && min_p <= 1.0f))
     return VSEL_EINVAL;
-  if (typical_p < 1.0f && top_k > kWaveTopkMax) return VSEL_EINVAL;
   const size_t base = sample_ws_bytes(rows, vocab, top_k);
   if (base == 0) return VSEL_EINVAL;
   Layout L;

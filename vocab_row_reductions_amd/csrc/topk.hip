@@ -376,8 +376,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     if (!none && n > 0) {
       double* E = reinterpret_cast<double*>(okey == s_key ? s_key + CAP / 2 : s_key);
       uint32_t* LIST = obits == s_bits ? s_bits + CAP / 2 : s_bits;
-      double* Sc = reinterpret_cast<double*>(&stg[0]);
-      uint32_t* ORD = &stg[1].w[0][0];
+      // the typicality scores after E in the free half when both fit there
+      // (up to 1,024 candidates in the large buffer), else in the staging area
+      const bool in_half = 2 * n <= (uint32_t)(CAP / 2);
+      double* Sc = in_half ? E + n : reinterpret_cast<double*>(&stg[0]);
+      uint32_t* ORD = in_half ? &stg[0].w[0][0] : &stg[1].w[0][0];
       const ChainParams cp{a.temperature, a.top_p,  a.top_n_sigma, a.typical_p, a.min_p,
                            a.mode == 2 ? a.out_kfl + row : nullptr, a.mode == 2 ? a.out_lse_f + row : nullptr};
       chain_tail(okey, obits, n, cp, a.sigma ? a.sigma[row] : 0.0, a.u ? a.u[row] : 0.0f, E, Sc, ORD, LIST, &tok,
