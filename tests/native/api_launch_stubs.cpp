@@ -109,15 +109,15 @@ static void check_spec(const char* what, const SpecArgs& a) {
   if (a.dseg > (int64_t)kChunk * kChunksPerSeg || a.nchunk != (a.V + kChunk - 1) / kChunk) fail(what, "draw plan");
   in_ws(what, "tk_pos", a.tk_pos, B * G);
   in_ws(what, "tk_seq", a.tk_seq, B);
-  in_ws(what, "tk_row", a.tk_row, 2 * B);
   in_ws(what, "tk_draw", a.tk_draw, B);
   in_ws(what, "p_summin", a.p_summin, B * G * a.S);
   in_ws(what, "acc", a.acc, B * G);
   in_ws(what, "draw_L", a.draw_L, B);
   in_ws(what, "p_lse", a.p_lse, B * 2 * a.dS);
-  in_ws(what, "lse64", a.lse64, 2 * B);
   in_ws(what, "p_w", a.p_w, B * a.dS);
   in_ws(what, "p_c", a.p_c, B * a.nchunk);
+  in_ws(what, "p_cb", a.p_cb, B * a.nchunk);
+  in_ws(what, "p_cf", a.p_cf, B * a.nchunk);
   in_ws(what, "p_low", a.p_low, B * G * a.S);
   in_ws(what, "p_wt", a.p_wt, B * G * a.S);
   in_ws(what, "st_amax", a.st_amax, nrows);

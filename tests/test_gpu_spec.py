@@ -142,3 +142,55 @@ def test_chi_square_of_the_emitted_stream(g, oracle):
     assert stat < gold["threshold"]
     counts_aa = np.bincount(got["tok_aa"][:, 0], minlength=V)
     assert float(((counts_aa - n * pf) ** 2 / (n * pf)).sum()) > gold["threshold"]
+
+
+def test_boundary_uniforms_take_the_exact_draw(g, oracle):
+    """The draws run with float32 terms first and stand only far from a CDF
+    boundary.  u placed 3e-6 (relative to the mass) above and below boundaries
+    of the residual normalize(max(p - q, 0)) and of the bonus row's p cannot be
+    decided by float32 terms: the float64 passes must take them, and the
+    tokens must still be the oracle's."""
+    from scipy.special import logsumexp
+    B, G, V = 12, 1, 50000
+    d = W.speculative_batch(batch=B, gamma=G, vocab=V, seed=45)
+    tg, dr = d["target"].astype(np.float64), d["draft"].astype(np.float64)
+    tok = np.zeros(B, np.uint32)
+    ua, ur, ub = np.zeros(B, np.float32), np.full(B, 0.5, np.float32), np.full(B, 0.5, np.float32)
+    for b in range(B):
+        p = np.exp(tg[2 * b] - logsumexp(tg[2 * b]))
+        q = np.exp(dr[b] - logsumexp(dr[b]))
+        side = 3e-6 if b % 2 == 0 else -3e-6
+        if b < 8:   # rejected at position 0: the residual draw
+            cand = np.nonzero(p < 0.5 * q)[0]
+            t = int(cand[np.argmax(q[cand])])
+            tok[b], ua[b] = t, np.float32(0.999)
+            r = np.maximum(p - q, 0.0)
+            c = np.cumsum(r) / r.sum()
+        else:       # accepted (u = 0): the bonus draw from target row 1
+            t = int(np.argmax(q))
+            tok[b] = t
+            pb = np.exp(tg[2 * b + 1] - logsumexp(tg[2 * b + 1]))
+            c = np.cumsum(pb)
+        # a boundary below one of the heavier tokens, with mass on both sides
+        heavy = [x for x in np.argsort(-np.diff(np.concatenate([[0.0], c])))[:16] if 0.05 < c[x - 1] < 0.95]
+        x = int(heavy[b % len(heavy)])
+        u = np.float32(c[x - 1] + side)
+        if b < 8:
+            ur[b] = u
+        else:
+            ub[b] = u
+    dd = dict(d, tokens=tok, u_acc=ua, u_res=ur, u_bon=ub)
+    got, ref, exempt = compare(g, oracle, dd)
+    assert exempt == 0
+    assert list(ref["len_mrs"]) == [0] * 8 + [1] * 4
+
+
+@pytest.mark.parametrize("T", [0.6, 1.7])
+def test_large_logit_offsets(g, oracle, T):
+    """Rows offset by +3000: every float32 exponent is taken relative to the
+    row maximum, so the coupling sums and the draws keep their precision."""
+    d = W.speculative_batch(batch=8, gamma=4, vocab=30000, seed=46, temperature=T)
+    tgt = (d["target"] + np.float32(3000.0)).astype(np.float32)
+    dft = (d["draft"] + np.float32(3000.0)).astype(np.float32)
+    got, ref, exempt = compare(g, oracle, d, target=tgt, draft=dft, T=T)
+    assert exempt <= 1

@@ -154,3 +154,15 @@ def test_chi_square_of_the_gpu_stream(g):
     assert stat < 25.7448
     acc = (got["len_sm"] == 1).mean()
     assert abs(acc - float((pf * (q / q.sum())).sum())) < 4 * np.sqrt(acc * (1 - acc) / n)
+
+
+@pytest.mark.parametrize("T", [0.6, 1.7])
+def test_large_logit_offsets(g, oracle, T):
+    """Rows offset by +3000: the float32 terms are taken relative to the row
+    maximum, so sum p*q and the draws keep their precision."""
+    d = W.speculative_batch(batch=8, gamma=4, vocab=30000, seed=47, temperature=T)
+    tgt = (d["target"] + np.float32(3000.0)).astype(np.float32)
+    dft = (d["draft"] + np.float32(3000.0)).astype(np.float32)
+    um = match_uniforms(8, 4, 47)
+    got, ref, exempt = compare(g, oracle, tgt, dft, d["tokens"], um, 8, 4, T)
+    assert exempt <= 1

@@ -243,20 +243,19 @@ RowDrawWs rowdraw_layout(Layout& L, int64_t rows, int64_t V, const Plan& ps) {
 struct SpecWs {
   ScanWs scan;
   StatsWs st;
-  size_t tk_pos, tk_seq, tk_row, tk_draw;
-  size_t p_summin, acc, draw_L, p_lse, lse64, p_w, p_c;
+  size_t tk_pos, tk_seq, tk_draw;
+  size_t p_summin, acc, draw_L, p_lse, p_w, p_c, p_cb, p_cf;
   size_t p_low, p_wt;  // sampler-match
 };
 SpecWs spec_layout(Layout& L, int64_t B, int64_t G, int64_t V, const Plan& ps, const Plan& pp) {
   SpecWs w{};
   const int64_t nrows = B * (2 * G + 1);
-  const size_t nt = (size_t)(nrows + B * G + B + 2 * B + B);
+  const size_t nt = (size_t)(nrows + B * G + B + B);
   L.reserve_tickets(nt);
   w.scan.tickets = 0;
   w.tk_pos = (size_t)nrows * 4;
   w.tk_seq = w.tk_pos + (size_t)(B * G) * 4;
-  w.tk_row = w.tk_seq + (size_t)B * 4;
-  w.tk_draw = w.tk_row + (size_t)(2 * B) * 4;
+  w.tk_draw = w.tk_seq + (size_t)B * 4;
   w.scan = scan_layout(L, nrows, ps, false);
   w.scan.tickets = 0;
   w.st = stats_layout(L, nrows);
@@ -264,9 +263,10 @@ SpecWs spec_layout(Layout& L, int64_t B, int64_t G, int64_t V, const Plan& ps, c
   w.acc = L.take((size_t)(B * G) * 4);
   w.draw_L = L.take((size_t)B * 4);
   w.p_lse = L.take((size_t)(2 * B * kMaxSegments) * 8);  // per draw segment
-  w.lse64 = L.take((size_t)(2 * B) * 8);
   w.p_w = L.take((size_t)(B * kMaxSegments) * 8);
   w.p_c = L.take((size_t)(B * cdiv(V, kChunk)) * 8);
+  w.p_cb = L.take((size_t)(B * cdiv(V, kChunk)) * 8);
+  w.p_cf = L.take((size_t)(B * cdiv(V, kChunk)) * 4);
   w.p_low = L.take((size_t)(B * G * pp.S) * 8);
   w.p_wt = L.take((size_t)(B * G * pp.S) * 8);
   return w;
@@ -786,19 +786,19 @@ static vsel_status spec_prepare(const float* target, int64_t ld_t, const float* 
   p.st_bad = a.st_bad;
   p.tk_pos = at<uint32_t>(ws, w.tk_pos);
   p.tk_seq = at<uint32_t>(ws, w.tk_seq);
-  p.tk_row = at<uint32_t>(ws, w.tk_row);
   p.tk_draw = at<uint32_t>(ws, w.tk_draw);
   p.p_summin = at<double>(ws, w.p_summin);
   p.acc = at<uint32_t>(ws, w.acc);
   p.draw_L = at<int32_t>(ws, w.draw_L);
   p.p_lse = at<double>(ws, w.p_lse);
-  p.lse64 = at<double>(ws, w.lse64);
   const Plan pd = plan_draw(B, vocab, resident_scan(VSEL_F32, true));
   p.dseg = pd.seg_len;
   p.dS = pd.S;
   p.nchunk = cdiv(vocab, kChunk);
   p.p_w = at<double>(ws, w.p_w);
   p.p_c = at<double>(ws, w.p_c);
+  p.p_cb = at<double>(ws, w.p_cb);
+  p.p_cf = at<uint32_t>(ws, w.p_cf);
   p.p_low = at<double>(ws, w.p_low);
   p.p_wt = at<double>(ws, w.p_wt);
   return VSEL_OK;

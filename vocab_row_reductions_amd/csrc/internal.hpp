@@ -123,19 +123,19 @@ struct SpecArgs {
   // workspace
   uint32_t* tk_pos;     // [B*gamma] per-position tickets
   uint32_t* tk_seq;     // [B]       per-sequence tickets
-  uint32_t* tk_row;     // [B*2]     per draw-row tickets
   uint32_t* tk_draw;    // [B]       per-sequence draw tickets
   double* p_summin;     // [B*gamma*S]
   uint32_t* acc;        // [B*gamma]
   int32_t* draw_L;      // [B]: -1 none, 0..gamma-1 residual at L, gamma bonus
-  double* p_lse;        // [B*2*dS] float64 partial sums for the draw rows
-  double* lse64;        // [B*2]
+  double* p_lse;        // [B*2*dS] residual draw: the segments' float64 sums of P, then of Q
   // the draw: segments of dseg elements (a multiple of kChunk), dS per row
   int64_t dseg;
   int32_t dS;
   int64_t nchunk;       // chunks per row, ceil(V / kChunk)
   double* p_w;          // [B*dS] segment masses
   double* p_c;          // [B*nchunk] chunk masses
+  double* p_cb;         // [B*nchunk] residual draw: the draft row's part of each chunk
+  uint32_t* p_cf;       // [B*nchunk] residual draw: chunks to recompute element by element
   // sampler-match (vsel_spec_match): a fresh draw from p at each position
   int32_t match;
   const float* u_match;  // [B*(gamma+1)]

@@ -5,7 +5,7 @@
 // rejection sampling"; the exact CPU acceptance of "Chapter 21", section
 // 21.9) needs, per verified position, two full-vocabulary reductions (the
 // pages' MLX version pays them as extra passes plus a host sync per
-// position).  Here the whole batch runs in four launches on one stream and
+// position).  Here the whole batch runs in three launches on one stream and
 // nothing returns to the host:
 //   1. row scan (scan.hip) over all target and draft rows: argmax, maximum,
 //      latch, log-sum-exp at T;
@@ -15,12 +15,12 @@
 //      u * q(t) <= p(t) in float64; the last position of a sequence finds the
 //      first rejection L for both rules and writes every emitted token except
 //      the draw;
-//   3. float64 log-sum-exp of the draw rows of sequences that rejected (the
-//      residual mixes p and q, so both must be exact to float64 precision);
-//   4. the draw: float64 masses of each segment of the draw row (residual
+//   3. the draw: float64 masses of each segment of the draw row (residual
 //      max(p - q, 0), or p for the bonus token), then the last workgroup
 //      picks the segment whose prefix crosses u * W and rescans it in id
-//      order.
+//      order.  The residual mixes p and q, so both need float64 log-sum-exps:
+//      the same pass sums them and the residual's parts of each chunk (see
+//      resid_chunks), and the last workgroup combines them.
 //
 // Sampler-match ("speculative-acceptance.md", "The rules", the default rule
 // at T > 0) replaces passes 2-4 by:
@@ -30,7 +30,7 @@
 //      lands on t iff mass(< t) <= u*W < mass(< t) + p(t); the masses come from
 //      float32 terms, so a decision closer to a boundary than they resolve is
 //      taken again with float64 terms over the row;
-//   4. the draw at the first mismatch (or the bonus row), as above from p.
+//   3. the draw at the first mismatch (or the bonus row), as above from p.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -86,8 +86,14 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
   const uint64_t kz = FILT ? a.kfl[trow] : 0ull, kd = FILT ? a.kfl[nT + drow] : 0ull;
   double tot = 0.0, tsp = 0.0;
   if (a.T > 0.0f && !bad) {
+    // p = exp(z/T - lse_p) = exp2((z - m_z) c - (lse_p - m_z/T) log2e), the
+    // exponent relative to the row maximum so that no float32 product carries
+    // a large logit; the offset (at most log V) split in a float part and a
+    // float factor
     const float c = a.lse_c;
-    const double Lp = a.st_lse[trow] * (double)kLog2e, Lq = a.st_lse[nT + drow] * (double)kLog2e;
+    const float mz = a.st_max[trow], md = a.st_max[nT + drow];
+    const double iT = 1.0 / (double)a.T, l2e = 1.4426950408889634;
+    const double Lp = (a.st_lse[trow] - (double)mz * iT) * l2e, Lq = (a.st_lse[nT + drow] - (double)md * iT) * l2e;
     const float Lp_hi = (float)Lp, Lq_hi = (float)Lq;
     const float fp = (float)exp2(-(Lp - (double)Lp_hi)), fq = (float)exp2(-(Lq - (double)Lq_hi));
     // group j of this lane starts at element t0 + (j*NT + tid)*E
@@ -98,8 +104,8 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
       for (int j = 0; j < NGP; ++j)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
-          float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]) - mz, c, -Lp_hi)) * fp;
+          float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]) - md, c, -Lq_hi)) * fq;
           if constexpr (FILT) {
             const uint32_t x = (uint32_t)t0 + (uint32_t)((j * NT + tid) * E + e);
             if (comp_key(gz[j].w[e], x) < kz) p = 0.0f;
@@ -127,8 +133,8 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     }
     if (tid == 0)
       for (int64_t x = e_full; x < e_end; ++x) {
-        float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
-        float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        float p = __builtin_amdgcn_exp2f(fmaf(zr[x] - mz, c, -Lp_hi)) * fp;
+        float q = __builtin_amdgcn_exp2f(fmaf(dr[x] - md, c, -Lq_hi)) * fq;
         if (FILT && comp_key(__float_as_uint(zr[x]), (uint32_t)x) < kz) p = 0.0f;
         if (FILT && comp_key(__float_as_uint(dr[x]), (uint32_t)x) < kd) q = 0.0f;
         tot += (double)fminf(p, q);
@@ -249,8 +255,14 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
   const uint64_t kz = FILT ? a.kfl[trow] : 0ull, kd = FILT ? a.kfl[nT + drow] : 0ull;
   double sp = 0.0, lo = 0.0, ws = 0.0;  // sum p q, mass of p below t, mass of p
   if (a.T > 0.0f && !bad) {
+    // p = exp(z/T - lse_p) = exp2((z - m_z) c - (lse_p - m_z/T) log2e), the
+    // exponent relative to the row maximum so that no float32 product carries
+    // a large logit; the offset (at most log V) split in a float part and a
+    // float factor
     const float c = a.lse_c;
-    const double Lp = a.st_lse[trow] * (double)kLog2e, Lq = a.st_lse[nT + drow] * (double)kLog2e;
+    const float mz = a.st_max[trow], md = a.st_max[nT + drow];
+    const double iT = 1.0 / (double)a.T, l2e = 1.4426950408889634;
+    const double Lp = (a.st_lse[trow] - (double)mz * iT) * l2e, Lq = (a.st_lse[nT + drow] - (double)md * iT) * l2e;
     const float Lp_hi = (float)Lp, Lq_hi = (float)Lq;
     const float fp = (float)exp2(-(Lp - (double)Lp_hi)), fq = (float)exp2(-(Lq - (double)Lq_hi));
     // group j of this lane starts at element t0 + (j*NT + tid)*E
@@ -262,8 +274,8 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const uint32_t x = (uint32_t)t0 + (uint32_t)((j * NT + tid) * E + e);
-          float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]), c, -Lp_hi)) * fp;
-          float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]), c, -Lq_hi)) * fq;
+          float p = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gz[j].w[e]) - mz, c, -Lp_hi)) * fp;
+          float q = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(gd[j].w[e]) - md, c, -Lq_hi)) * fq;
           if constexpr (FILT) {
             if (comp_key(gz[j].w[e], x) < kz) p = 0.0f;
             if (comp_key(gd[j].w[e], x) < kd) q = 0.0f;
@@ -292,8 +304,8 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
     }
     if (tid == 0)
       for (int64_t x = e_full; x < e_end; ++x) {
-        float p = __builtin_amdgcn_exp2f(fmaf(zr[x], c, -Lp_hi)) * fp;
-        float q = __builtin_amdgcn_exp2f(fmaf(dr[x], c, -Lq_hi)) * fq;
+        float p = __builtin_amdgcn_exp2f(fmaf(zr[x] - mz, c, -Lp_hi)) * fp;
+        float q = __builtin_amdgcn_exp2f(fmaf(dr[x] - md, c, -Lq_hi)) * fq;
         if (FILT && comp_key(__float_as_uint(zr[x]), (uint32_t)x) < kz) p = 0.0f;
         if (FILT && comp_key(__float_as_uint(dr[x]), (uint32_t)x) < kd) q = 0.0f;
         sp += (double)(p * q);
@@ -386,48 +398,6 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
 }
 
 // ---------------------------------------------------------------- pass 3
-template <bool VEC>
-__global__ __launch_bounds__(NT) void draw_lse_kernel(SpecArgs a) {
-  constexpr int E = 4;
-  __shared__ SelShared sh;
-  const int tid = threadIdx.x;
-  const Item it = work_item(a.dS);  // the draw segments: few rows, many workgroups
-  const int64_t item = it.row;  // b*2 + which
-  const int seg = (int)it.seg;
-  if (item >= a.B * 2) return;
-  const int64_t b = item >> 1;
-  const int which = (int)(item & 1);
-  const int64_t G = a.gamma;
-  const int32_t L = a.draw_L[b];
-  if (L < 0 || L >= G) return;  // no residual draw for this sequence
-  const int64_t nT = a.B * (G + 1);
-  const int64_t srow = which == 0 ? b * (G + 1) + L : nT + b * G + L;
-  const float* __restrict__ xr = which == 0 ? a.tgt + (b * (G + 1) + L) * a.ld_t : a.dft + (b * G + L) * a.ld_d;
-  const double m = a.st_max[srow];
-  const double Td = a.T, iT = 1.0 / Td;
-  __shared__ double e2[64];
-  init_e2(e2);
-  const int64_t e_begin = (int64_t)seg * a.dseg, e_end = min(a.V, e_begin + a.dseg);
-  double s = 0.0;
-  const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
-  walk_groups<float, PG, VEC>(xr, e_begin, e_full, [&](const auto& g, int64_t) {
-    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
-#pragma unroll
-    for (int j = 0; j < NGP; ++j)
-#pragma unroll
-      for (int e = 0; e < E; ++e) s += exp_le0(((double)__uint_as_float(g[j].w[e]) - m) * iT, e2);
-  });
-  if (tid == 0)
-    for (int64_t x = e_full; x < e_end; ++x) s += exp_le0(((double)xr[x] - m) * iT, e2);
-  s = block_sum_f64(sh, s);
-  if (a.dS > 1) {
-    if (tid == 0) st_dev(&a.p_lse[item * a.dS + seg], s);
-    if (!last_done(sh, a.tk_row + item, (uint32_t)a.dS)) return;
-    s = merge_sum(sh, a.p_lse + item * a.dS, a.dS);
-  }
-  if (tid == 0) a.lse64[item] = m / Td + log(s);
-}
-
 // ---------------------------------------------------------------- pass 4 (and the full-row draw)
 // An inverse-CDF draw in id order over W = sum of weights, in three levels:
 // segment masses, 256-element chunk masses, then one element per thread.
@@ -451,6 +421,7 @@ struct DrawSrc {
   uint64_t kz = 0, kd = 0;
   double iT = 1.0;              // 1 / T
   const double* e2 = nullptr;   // the exp table in LDS (init_e2)
+  bool vz = false, vd = false;  // the rows start and stride on 16 bytes
   __device__ __forceinline__ float zv(int64_t x) const { return __uint_as_float(gbits_at<DT>(z, x)); }
   // (every exponent is at most 0 up to rounding: lp and lq are log-sum-exps
   // of the rows at T, m their maxima)
@@ -466,13 +437,46 @@ struct DrawSrc {
   }
 };
 
+// Elements x .. x+3 of a row as float32 (fill at and past lim): one 16-byte
+// (float32) or 8-byte (bfloat16) load when the row is aligned and all four are
+// in range, else element loads (at `safe`, a valid index, for those past lim).
+struct F4 {
+  float v[4];
+};
+template <typename DT>
+__device__ __forceinline__ F4 row4(const DT* __restrict__ row, int64_t x, int64_t lim, bool vec, float fill,
+                                   int64_t safe) {
+  F4 o;
+  if (vec && x + 3 < lim) {
+    if constexpr (sizeof(DT) == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row + x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.v[e] = __uint_as_float(v[e]);
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(row + x);
+      o.v[0] = __uint_as_float(v.x << 16);
+      o.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+      o.v[2] = __uint_as_float(v.y << 16);
+      o.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = x + e < lim;
+      const float v = __uint_as_float(gbits_at<DT>(row, in ? x + e : safe));
+      o.v[e] = in ? v : fill;
+    }
+  }
+  return o;
+}
+
 // Chunk masses of segment [e_begin, e_end): each wave takes 4 chunks per
 // step (16 loads per lane in flight), reduces each chunk's 256 weights (4 per
 // lane) in float64, and writes the masses to `cm` (LDS) and `pc` (global,
 // indexed from the segment's first chunk).  Returns the segment mass in
 // thread 0: the in-order sum of its chunk masses.
-template <typename DT>
-__device__ double chunk_masses(const DrawSrc<DT>& r, int64_t e_begin, int64_t e_end, double* cm, double* pc) {
+template <class Src>
+__device__ double chunk_masses(const Src& r, int64_t e_begin, int64_t e_end, double* cm, double* pc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int CW = 4;  // chunks per wave per step
   const int nch = (int)((e_end - e_begin + kChunk - 1) / kChunk);
@@ -481,15 +485,14 @@ __device__ double chunk_masses(const DrawSrc<DT>& r, int64_t e_begin, int64_t e_
 #pragma unroll
     for (int j = 0; j < CW; ++j) {
       const int q = q0 + wave * CW + j;
+      const int64_t x0 = e_begin + (int64_t)q * kChunk + lane * 4;
+      const int64_t lim = q < nch ? e_end : x0;  // past the segment: weight 0
+      const F4 fz = row4(r.z, x0, lim, r.vz, -__builtin_inff(), e_begin);
+      const F4 fd = r.d ? row4(r.d, x0, lim, r.vd, 0.0f, e_begin) : F4{{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t x = e_begin + (int64_t)q * kChunk + lane * 4 + e;
-        const bool in = q < nch && x < e_end;
-        const int64_t xs = in ? x : e_begin;
-        const float zx = r.zv(xs);
-        const float dx = r.d ? r.d[xs] : 0.0f;
-        zz[j][e] = in ? zx : -__builtin_inff();  // weight 0
-        dd[j][e] = in ? dx : 0.0f;
+        zz[j][e] = fz.v[e];
+        dd[j][e] = fd.v[e];
       }
     }
 #pragma unroll
@@ -513,13 +516,13 @@ __device__ double chunk_masses(const DrawSrc<DT>& r, int64_t e_begin, int64_t e_
 }
 
 // The draw itself (one workgroup): segment, then chunk, then element.  pw
-// (LDS) holds the S segment masses, pc (global) the row's chunk masses.
+// (LDS) holds the S segment masses, pc (global) the row's chunk masses; cm is
+// LDS room for kChunksPerSeg chunk masses.
 // Returns the token in every thread; *W_out (thread 0) is the total mass.
-template <typename DT>
-__device__ uint32_t draw_pick(SelShared& sh, const DrawSrc<DT>& r, const double* pw, const double* pc, int S,
-                              int64_t seg_len, double u, double* W_out) {
+template <class Src>
+__device__ uint32_t draw_pick(SelShared& sh, const Src& r, const double* pw, const double* pc, int S,
+                              int64_t seg_len, double u, double* W_out, double* cm) {
   const int tid = threadIdx.x;
-  __shared__ double cm[kChunksPerSeg];
   __shared__ int s_seg, s_ch;
   __shared__ double s_in;
   __shared__ uint32_t s_tok;
@@ -601,6 +604,222 @@ __device__ uint32_t draw_pick(SelShared& sh, const DrawSrc<DT>& r, const double*
   return s_tok;
 }
 
+// The residual draw of modified rejection sampling in one pass.  With
+// P = exp((z - m_z)/T) and Q = exp((d - m_d)/T) (m the rows' maxima) and
+// Sp, Sq their float64 row sums, p = P/Sp and q = Q/Sq, so
+//   max(p - q, 0) = P/Sp - Q/Sq   where D = (z - m_z)/T - (d - m_d)/T > log(Sp/Sq),
+// and 0 elsewhere.  The pass sums Sp and Sq and, per 256-element chunk, P and
+// Q over the elements with D above the threshold the row scan's log-sum-exps
+// give (they approximate the rows' sums to within about the rows' entropy in
+// bits times 2^-24, well inside kBand); a chunk holding an element within kBand of it is flagged, and
+// the last workgroup recomputes it element by element once Sp and Sq are
+// exact.  Every other chunk's residual mass is then A/Sp - B/Sq.
+constexpr double kBand = 1e-5;
+
+struct ResidSrc {
+  const float* z;
+  const float* d;
+  double mz, md, iT, iSp, iSq;
+  int64_t V;
+  const double* e2;
+  bool vz, vd;  // the rows start and stride on 16 bytes
+  __device__ __forceinline__ float zv(int64_t x) const { return z[x]; }
+  __device__ __forceinline__ double w(float zx, float dx, int64_t) const {
+    const double p = exp_le0(((double)zx - mz) * iT, e2) * iSp, q = exp_le0(((double)dx - md) * iT, e2) * iSq;
+    return p > q ? p - q : 0.0;
+  }
+};
+
+// Chunk sums of segment [e_begin, e_end) for the residual draw (chunks
+// indexed from the segment's first in pa, pb, pf); returns (every thread) the
+// segment's sums of P and Q.
+__device__ void resid_chunks(SelShared& sh, const ResidSrc& r, double theta, int64_t e_begin, int64_t e_end,
+                             double* pa, double* pb, uint32_t* pf, double* sp_out, double* sq_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int CW = 4;  // chunks per wave per step
+  const int nch = (int)((e_end - e_begin + kChunk - 1) / kChunk);
+  double sp = 0.0, sq = 0.0;
+  for (int q0 = 0; q0 < nch; q0 += NWAVE * CW) {
+    float zz[CW][4], dd[CW][4];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {  // past the segment: P = Q = 0, on neither side
+      const int q = q0 + wave * CW + j;
+      const int64_t x0 = e_begin + (int64_t)q * kChunk + lane * 4;
+      const int64_t lim = q < nch ? e_end : x0;
+      const F4 fz = row4(r.z, x0, lim, r.vz, -__builtin_inff(), e_begin);
+      const F4 fd = row4(r.d, x0, lim, r.vd, -__builtin_inff(), e_begin);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zz[j][e] = fz.v[e];
+        dd[j][e] = fd.v[e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int q = q0 + wave * CW + j;
+      double A = 0.0, B = 0.0;
+      bool near = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double az = ((double)zz[j][e] - r.mz) * r.iT, ad = ((double)dd[j][e] - r.md) * r.iT;
+        const double P = exp_le0(az, r.e2), Q = exp_le0(ad, r.e2);
+        sp += P;
+        sq += Q;
+        const double D = az - ad;  // NaN (both masked) counts on neither side
+        if (D > theta + kBand) {
+          A += P;
+          B += Q;
+        } else if (D >= theta - kBand) {
+          near = true;
+        }
+      }
+      A = wave_sum_f64(A);
+      B = wave_sum_f64(B);
+      const bool flag = __ballot(near) != 0ull;
+      if (lane == 0 && q < nch) {
+        st_dev(&pa[q], A);
+        st_dev(&pb[q], B);
+        st_dev(&pf[q], flag ? 1u : 0u);
+      }
+    }
+  }
+  *sp_out = block_sum_f64(sh, sp);
+  *sq_out = block_sum_f64(sh, sq);
+}
+
+// The residual draw of sequence b at its first rejection L (unfiltered p and
+// q), one workgroup per segment of the row pair; the last one draws.
+__device__ void resid_draw(const SpecArgs& a, SelShared& sh, int64_t b, int seg, int32_t L, const double* e2,
+                           double* cmw) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t G = a.gamma, nT = a.B * (G + 1);
+  const int64_t trow = b * (G + 1) + L, drow = nT + b * G + L;
+  ResidSrc r;
+  r.z = a.tgt + trow * a.ld_t;
+  r.d = a.dft + (b * G + L) * a.ld_d;
+  r.mz = a.st_max[trow];
+  r.md = a.st_max[drow];
+  r.iT = 1.0 / (double)a.T;
+  r.iSp = r.iSq = 1.0;
+  r.V = a.V;
+  r.e2 = e2;
+  r.vz = a.vec_t != 0;
+  r.vd = a.vec_d != 0;
+  // log(Sp/Sq), approximately, from the row scan's log-sum-exps at T
+  const double theta = (a.st_lse[trow] - r.mz * r.iT) - (a.st_lse[drow] - r.md * r.iT);
+  double* pa = a.p_c + b * a.nchunk;
+  double* pb = a.p_cb + b * a.nchunk;
+  uint32_t* pf = a.p_cf + b * a.nchunk;
+  const int64_t e_begin = (int64_t)seg * a.dseg, e_end = min(a.V, e_begin + a.dseg), c0 = e_begin / kChunk;
+  double sp, sq;
+  resid_chunks(sh, r, theta, e_begin, e_end, pa + c0, pb + c0, pf + c0, &sp, &sq);
+  double* ps = a.p_lse + b * 2 * a.dS;  // the segments' Sp, then their Sq
+  if (tid == 0) {
+    st_dev(&ps[seg], sp);
+    st_dev(&ps[a.dS + seg], sq);
+  }
+  if (!last_done(sh, a.tk_draw + b, (uint32_t)a.dS)) return;
+  // ---- the row's last workgroup
+  const double Sp = merge_sum(sh, ps, a.dS), Sq = merge_sum(sh, ps + a.dS, a.dS);
+  r.iSp = 1.0 / Sp;
+  r.iSq = 1.0 / Sq;
+  // each chunk's residual mass: A/Sp - B/Sq, or element by element where
+  // flagged; rows of up to kRcLds chunks also keep them in LDS, so that the
+  // segment sums below read LDS instead of global memory
+  constexpr int kRcPer = 4, kRcLds = kRcPer * NT;
+  static_assert(kRcLds <= kChunksPerSeg, "the chunk masses live in the kernel's chunk buffer");
+  double* rc = cmw;
+  __shared__ uint16_t s_list[kRcLds];
+  __shared__ uint32_t s_n;
+  const int64_t nch = a.nchunk;
+  const bool in_lds = nch <= kRcLds;
+  for (int64_t cb = 0; cb < nch; cb += kRcLds) {
+    if (tid == 0) s_n = 0u;
+    double A[kRcPer], B[kRcPer];
+    uint32_t F[kRcPer];
+#pragma unroll
+    for (int q = 0; q < kRcPer; ++q) {  // every load issued before any is used
+      const int64_t c = cb + q * NT + tid;
+      A[q] = c < nch ? ld_dev(&pa[c]) : 0.0;
+      B[q] = c < nch ? ld_dev(&pb[c]) : 0.0;
+      F[q] = c < nch ? ld_dev(&pf[c]) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kRcPer; ++q) {
+      const int64_t c = cb + q * NT + tid;
+      if (c >= nch) continue;
+      if (F[q]) {
+        s_list[atomicAdd(&s_n, 1u)] = (uint16_t)(c - cb);
+      } else {
+        const double m = fmax(A[q] * r.iSp - B[q] * r.iSq, 0.0);
+        st_dev(&pa[c], m);
+        if (in_lds) rc[c] = m;
+      }
+    }
+    __syncthreads();
+    const uint32_t n = s_n;
+    for (uint32_t k = (uint32_t)wave; k < n; k += NWAVE) {
+      const int64_t cc = cb + s_list[k];
+      double m = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t x = cc * kChunk + lane * 4 + e;
+        if (x < a.V) m += r.w(r.z[x], r.d[x], x);
+      }
+      m = wave_sum_f64(m);
+      if (lane == 0) {
+        st_dev(&pa[cc], m);
+        if (in_lds) rc[cc] = m;
+      }
+    }
+    __syncthreads();
+  }
+  // segment masses: the in-order sums of their chunk masses
+  __shared__ double pw[kMaxSegments];
+  __shared__ int s_degen;
+  if (tid < a.dS) {
+    const int64_t per = a.dseg / kChunk, c_lo = (int64_t)tid * per, c_hi = min(nch, c_lo + per);
+    double t = 0.0;
+    if (in_lds)
+      for (int64_t c = c_lo; c < c_hi; ++c) t += rc[c];
+    else
+      for (int64_t c = c_lo; c < c_hi; ++c) t += ld_dev(&pa[c]);
+    pw[tid] = t;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double W = 0.0;
+    for (int sg = 0; sg < a.dS; ++sg) W += pw[sg];
+    s_degen = W > 0.0 ? 0 : 1;
+  }
+  __syncthreads();
+  double W;
+  uint32_t tok;
+  if (!s_degen) {
+    tok = draw_pick(sh, r, pw, pa, a.dS, a.dseg, (double)a.u_res[b * G + L], &W, cmw);
+  } else {  // the residual sums to 0 (p <= q everywhere): draw from p
+    DrawSrc<float> r2;
+    r2.z = r.z;
+    r2.d = nullptr;
+    r2.lp = r2.lq = 0.0;
+    r2.m = r.mz;
+    r2.T = a.T;
+    r2.iT = r.iT;
+    r2.e2 = e2;
+    r2.V = a.V;
+    r2.vz = r.vz;
+    for (int sg = 0; sg < a.dS; ++sg) {
+      const int64_t eb = (int64_t)sg * a.dseg, ee = min(a.V, eb + a.dseg);
+      const double m2 = chunk_masses(r2, eb, ee, cmw, pa + eb / kChunk);
+      if (tid == 0) pw[sg] = m2;
+      __syncthreads();
+    }
+    tok = draw_pick(sh, r2, pw, pa, a.dS, a.dseg, (double)a.u_res[b * G + L], &W, cmw);
+  }
+  if (tid == 0) a.tok_mrs[b * (G + 1) + L] = tok;
+}
+
 __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   __shared__ SelShared sh;
   __shared__ double cmw[kChunksPerSeg];
@@ -614,11 +833,17 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   if (L < 0) return;
   __shared__ double e2[64];
   init_e2(e2);
+  if (!a.match && L < G && !a.kfl) {  // the residual draw of unfiltered p and q
+    resid_draw(a, sh, b, seg, L, e2, cmw);
+    return;
+  }
   DrawSrc<float> r;
   r.T = a.T;
   r.iT = 1.0 / r.T;
   r.e2 = e2;
   r.V = a.V;
+  r.vz = a.vec_t != 0;
+  r.vd = a.vec_d != 0;
   double u;
   const int64_t nT = a.B * (G + 1);
   if (a.match) {  // sampler-match: a fresh draw from p at row L
@@ -631,8 +856,8 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
     r.z = a.tgt + (b * (G + 1) + L) * a.ld_t;
     r.d = a.dft + (b * G + L) * a.ld_d;
     // filtered: the exact kept-set lse of the filter pass
-    r.lp = a.kfl ? a.st_lse[b * (G + 1) + L] : a.lse64[b * 2];
-    r.lq = a.kfl ? a.st_lse[nT + b * G + L] : a.lse64[b * 2 + 1];
+    r.lp = a.st_lse[b * (G + 1) + L];
+    r.lq = a.st_lse[nT + b * G + L];
     r.m = 0.0;
     u = a.u_res[b * G + L];
   } else {
@@ -673,7 +898,7 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
     }
   }
   double W;
-  const uint32_t tok = draw_pick(sh, r, pw, pc, a.dS, a.dseg, u, &W);
+  const uint32_t tok = draw_pick(sh, r, pw, pc, a.dS, a.dseg, u, &W, cmw);
   if (tid == 0) (a.match ? a.tok_sm : a.tok_mrs)[b * (G + 1) + L] = tok;
 }
 
@@ -704,6 +929,7 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
   r.iT = 1.0 / r.T;
   r.e2 = e2;
   r.V = a.V;
+  r.vz = a.vec != 0;
   if (a.top_n_sigma > 0.0f) r.thr = r.m - (double)a.top_n_sigma * a.sigma[row];
   if (a.min_p > 0.0f) r.thr = fmax(r.thr, r.m + log((double)a.min_p));
   double* pc = a.p_c + row * a.nchunk;
@@ -715,7 +941,7 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
   if (tid < a.S) pw[tid] = ld_dev(&a.p_w[row * a.S + tid]);
   __syncthreads();
   double W;
-  const uint32_t tok = draw_pick(sh, r, pw, pc, a.S, a.seg_len, (double)a.u[row], &W);
+  const uint32_t tok = draw_pick(sh, r, pw, pc, a.S, a.seg_len, (double)a.u[row], &W, cmw);
   if (tid == 0) {
     a.out_token[row] = tok;
     if (a.out_logp) a.out_logp[row] = (float)(((double)r.zv(tok) - r.m) / r.T - log(W));
@@ -747,15 +973,6 @@ hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.T == 0.0f) return e;
-  if (a.kfl) {  // the filter pass already holds the exact lse of every row
-    hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
-    return hipGetLastError();
-  }
-  if (vec)
-    hipLaunchKernelGGL(draw_lse_kernel<true>, dim3((unsigned)(a.B * 2 * a.dS)), dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL(draw_lse_kernel<false>, dim3((unsigned)(a.B * 2 * a.dS)), dim3(NT), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
