@@ -61,17 +61,17 @@ constexpr int kNG = 4;                 // 16-byte groups per lane per tile
 constexpr int kTypIdBits = 26;
 constexpr uint64_t kTypIdMask = (1ull << kTypIdBits) - 1;
 constexpr uint64_t kTypScoreMask = (1ull << 38) - 1;
-__device__ __forceinline__ uint64_t typ_score(double d) {
-  const uint64_t b = (uint64_t)__double_as_longlong(d);
-  const int e = (int)(b >> 52) - 1023;
-  if (e < -125) return 0ull;
-  return ((uint64_t)(e + 126) << 30) | ((b >> 22) & ((1ull << 30) - 1));
+// The cut distance: the float64 d >= 0 with its low 22 mantissa bits cleared
+// (0 below 2^-125), monotone in d.
+__device__ __forceinline__ double typ_cut(double d) {
+  const uint64_t b = (uint64_t)__double_as_longlong(d) & ~((1ull << 22) - 1);
+  return b < ((uint64_t)(1023 - 125) << 52) ? 0.0 : __longlong_as_double((long long)b);
 }
-// The distance a score stands for (the cut float64), for the guide bins.
-__device__ __forceinline__ double typ_dist(uint64_t sc) {
-  if (sc == 0ull) return 0.0;
-  const uint64_t e = (sc >> 30) - 126 + 1023;
-  return __longlong_as_double((long long)((e << 52) | ((sc & ((1ull << 30) - 1)) << 22)));
+// Its 38-bit score: the exponent, biased by 126, above the 30 mantissa bits
+// kept (0 for 0).
+__device__ __forceinline__ uint64_t typ_score(double dc) {
+  const uint64_t b = (uint64_t)__double_as_longlong(dc);
+  return b == 0ull ? 0ull : (b >> 22) - ((uint64_t)(1023 - 126) << 30);
 }
 // The token id a selection key holds.
 __device__ __forceinline__ uint32_t key_id(int order, uint64_t key) {
@@ -93,9 +93,11 @@ struct NucSet {
   double c;           // typical centre (order 1, typical sets)
   double span;        // order 1: first-level bins are equal steps of the score over [0, span)
   uint64_t kT;        // typical set: score key >= kT (0: none)
+  __device__ __forceinline__ uint64_t score_key_of(double dc, uint32_t i) const {
+    return ((~typ_score(dc) & kTypScoreMask) << kTypIdBits) | (~(uint64_t)i & kTypIdMask);
+  }
   __device__ __forceinline__ uint64_t score_key(uint32_t bits, uint32_t i) const {
-    const uint64_t sc = typ_score(fabs((double)__uint_as_float(bits) - c));
-    return ((~sc & kTypScoreMask) << kTypIdBits) | (~(uint64_t)i & kTypIdMask);
+    return score_key_of(typ_cut(fabs((double)__uint_as_float(bits) - c)), i);
   }
   __device__ __forceinline__ uint64_t key(uint32_t bits, uint32_t i) const {
     return order == 0 ? comp_key(bits, i) : score_key(bits, i);
@@ -112,11 +114,29 @@ struct NucSet {
     return __builtin_amdgcn_exp2f((float)(x(z) * 1.4426950408889634));
   }
   // first-level bin: equal steps of (m - z) / T over [0, kSpan) (order 0),
-  // or of the score over [0, span) (order 1)
+  // or of the cut distance over [0, span) (order 1)
+  template <int NB>
+  __device__ __forceinline__ uint32_t bin_of(double d) const {
+    return d >= kSpan ? (uint32_t)(NB - 1) : (uint32_t)(d * (NB / kSpan));
+  }
   template <int NB>
   __device__ __forceinline__ uint32_t bin(float z) const {
-    const double d = order == 0 ? -x(z) : typ_dist(typ_score(fabs((double)z - c))) * (kSpan / span);
-    return d >= kSpan ? (uint32_t)(NB - 1) : (uint32_t)(d * (NB / kSpan));
+    return bin_of<NB>(order == 0 ? -x(z) : typ_cut(fabs((double)z - c)) * (kSpan / span));
+  }
+  // The candidate test, the order key and the first-level bin of element i,
+  // the typicality distance taken once.
+  template <int NB>
+  __device__ __forceinline__ bool look(uint32_t bits, uint32_t i, uint64_t& K, uint32_t& b) const {
+    const float z = __uint_as_float(bits);
+    if (order == 0) {
+      K = comp_key(bits, i);
+      b = bin_of<NB>(-x(z));
+      return in(z, K) && (kT == 0 || score_key(bits, i) >= kT);
+    }
+    const double dc = typ_cut(fabs((double)z - c));
+    K = score_key_of(dc, i);
+    b = bin_of<NB>(dc * (kSpan / span));
+    return in(z, K) && (kT == 0 || K >= kT);
   }
 };
 
@@ -646,6 +666,14 @@ union NucLds {
   } w;
 };
 
+// A pass that stages window candidates while it streams and sorts the row's
+// window only afterwards, in the row's last workgroup, keeps both in the
+// same LDS.
+union StageOrWindow {
+  NucLds L;
+  Stage st;
+};
+
 // Pass 1: guide histogram of exp(z - m) over the candidates and their exact
 // total; the last workgroup places the cut window.
 template <typename DT, bool VEC>
@@ -840,8 +868,9 @@ template <typename DT, bool VEC>
 __global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
   __shared__ SelShared sh;
   __shared__ NucRed r;
-  __shared__ NucLds L;
-  __shared__ Stage st;
+  __shared__ StageOrWindow sw;
+  NucLds& L = sw.L;
+  Stage& st = sw.st;
   __shared__ double e2[64];
   const int tid = threadIdx.x;
   const Item it = work_item(a.S);
@@ -1065,10 +1094,10 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   __syncthreads();
   double t = 0.0;
   for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
-    if (!S.in(bits, (uint32_t)i, S.key(bits, (uint32_t)i))) return;
-    const float z = __uint_as_float(bits);
-    const double w = S.w(z);
-    const uint32_t b = S.bin<kNB>(z);
+    uint64_t K;
+    uint32_t b;
+    if (!S.look<kNB>(bits, (uint32_t)i, K, b)) return;
+    const double w = S.w(__uint_as_float(bits));
     __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     t += w;
@@ -1097,8 +1126,9 @@ template <typename DT, bool VEC>
 __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
   __shared__ SelShared sh;
   __shared__ NucRed r;
-  __shared__ NucLds L;
-  __shared__ Stage st;
+  __shared__ StageOrWindow sw;
+  NucLds& L = sw.L;
+  Stage& st = sw.st;
   __shared__ double e2[64];
   const int tid = threadIdx.x;
   const Item it = work_item(a.S);
@@ -1115,9 +1145,10 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
   uint32_t* lbits = a.lbits + row * kCapW;
   double A = 0.0, zb = -__builtin_inf();  // mass and largest value before the window
   for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
-    if (!S.in(bits, (uint32_t)i, S.key(bits, (uint32_t)i))) return;
+    uint64_t K;
+    uint32_t b;
+    if (!S.look<kNB>(bits, (uint32_t)i, K, b)) return;
     const float z = __uint_as_float(bits);
-    const uint32_t b = S.bin<kNB>(z);
     if (b < jb.b_lo) {
       A += S.w(z);
       zb = fmax(zb, (double)z);
