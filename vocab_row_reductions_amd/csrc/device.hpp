@@ -124,16 +124,28 @@ __device__ __forceinline__ void load_tile(Group (&g)[NG], const DT* __restrict__
 // Walk the whole groups of [e_begin, e_full) of a row: full tiles of NG
 // groups per lane, then the remaining groups one per lane at a time (masked
 // past e_full).  fn(g, t0) gets each tile (a Group[NG] or Group[1]) and its
-// first element index; all threads call it for every tile.
+// first element index; all threads call it for every tile.  The loads of the
+// next full tile are in flight while fn works on the current one.
 template <typename DT, int NG, bool VEC, class Fn>
 __device__ __forceinline__ void walk_groups(const DT* __restrict__ xr, int64_t e_begin, int64_t e_full, Fn&& fn) {
   constexpr int E = Elem<DT>::E;
   constexpr int64_t TILE = (int64_t)NT * NG * E;
   const int64_t e_tiles = e_begin + (e_full - e_begin) / TILE * TILE;
-  for (int64_t t0 = e_begin; t0 < e_tiles; t0 += TILE) {
+  if (e_tiles > e_begin) {
     Group g[NG];
-    load_tile_full<DT, NG, VEC>(g, xr + t0);
-    fn(g, t0);
+    load_tile_full<DT, NG, VEC>(g, xr + e_begin);
+    for (int64_t t0 = e_begin; t0 < e_tiles; t0 += TILE) {
+      Group n[NG];
+      if (t0 + TILE < e_tiles) {
+        load_tile_full<DT, NG, VEC>(n, xr + t0 + TILE);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) n[j] = g[j];
+      }
+      fn(g, t0);
+#pragma unroll
+      for (int j = 0; j < NG; ++j) g[j] = n[j];
+    }
   }
   for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
     Group g1[1];

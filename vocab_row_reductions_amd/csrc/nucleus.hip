@@ -108,8 +108,16 @@ struct NucSet {
   __device__ __forceinline__ bool in(uint32_t bits, uint32_t i, uint64_t K) const {
     return in(__uint_as_float(bits), K) && (kT == 0 || score_key(bits, i) >= kT);
   }
-  __device__ __forceinline__ double x(float z) const { return T == 1.0 ? (double)z - m : ((double)z - m) / T; }
+  // (z - m) / T as a product with 1 / T (loop-invariant)
+  __device__ __forceinline__ double x(float z) const { return T == 1.0 ? (double)z - m : ((double)z - m) * (1.0 / T); }
   __device__ __forceinline__ double w(float z) const { return exp_le0(x(z), e2); }
+  // the weight of an element that passes `ok`, else 0: the exponential is
+  // taken either way, so element loops stay free of branches and the
+  // exponentials of a tile's elements interleave
+  __device__ __forceinline__ double w_if(bool ok, float z) const {
+    const double e = w(z);  // (0 for z = -inf)
+    return ok ? e : 0.0;
+  }
   __device__ __forceinline__ float gw(float z) const {
     return __builtin_amdgcn_exp2f((float)(x(z) * 1.4426950408889634));
   }
@@ -141,6 +149,16 @@ struct NucSet {
 };
 
 // ---------------------------------------------------------------- block helpers
+// last_done, and the finishing workgroup's waves then issue ahead of those of
+// the streaming workgroups that share its CU (its steps are serial, theirs
+// are not).
+__device__ __forceinline__ bool last_of_row(SelShared& sh, uint32_t* ticket, uint32_t n) {
+  if (!last_done(sh, ticket, n)) return false;
+  __builtin_amdgcn_s_setprio(3);
+  return true;
+}
+
+
 struct NucRed {
   double rd[NWAVE * 2];
   uint64_t rk[NWAVE * 2];
@@ -232,82 +250,76 @@ __device__ __forceinline__ double block_ext_f64(NucRed& r, double v) {
   return o;
 }
 
-// Wave 0 chooses the bins [b_lo, b_hi] of nb (<= NB) whose cumulative guide
-// mass (after `base`, the mass above bin 0) first reaches t0 and t1; it counts
-// their candidates (cnt) and those of bins [0, b_hi] (cnt_top).  A target
-// past the last bin takes the last non-empty bin.  All threads call.
+// The bins [b_lo, b_hi] of nb (<= NB) whose cumulative guide mass (after
+// `base`, the mass above bin 0) first reaches t0 and t1; their candidates
+// (cnt) and those of bins [0, b_hi] (cnt_top).  A target past the last bin
+// takes the last non-empty bin.  Each thread holds NB / NT consecutive bins;
+// the thread sums are prefixed in thread order (a fixed order), the thread
+// whose prefix first reaches a target walks its own bins.  All threads call;
+// the results are in r.
 template <int NB>
 __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int nb, double base, double t0,
                           double t1) {
-  const int lane = threadIdx.x & 63;
+  constexpr int PT = NB / NT;
+  static_assert(PT * NT == NB, "bins per thread");
+  const int tid = threadIdx.x, b0 = tid * PT;
   __syncthreads();
-  if (threadIdx.x < 64) {
-    constexpr int PER = NB / 64;
-    double ls = 0.0;
-    int lastnz = -1;
-#pragma unroll 8
-    for (int q = 0; q < PER; ++q) {
-      const int b = lane * PER + q;
-      if (b < nb) {
-        ls += hw[b];
-        if (hc[b]) lastnz = b;
-      }
-    }
-    double incl = ls;
-    for (int d = 1; d < 64; d <<= 1) {
-      const double o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    const double excl = incl - ls;
-    int last = lastnz;
-    for (int d = 1; d < 64; d <<= 1) last = max(last, __shfl_xor(last, d));
-    int b_sel[2];
-    const double tt[2] = {t0, t1};
+  double v[PT];
+  double ls = 0.0;
+  int lastnz = -1;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint64_t hit = __ballot(base + incl >= tt[q]);
-      int b = last < 0 ? 0 : last;
-      if (hit) {
-        const int L = __builtin_ctzll(hit);
-        int cand = 0x7FFFFFFF;
-        if (lane == L) {
-          double c = base + excl;
-#pragma unroll 4
-          for (int j = 0; j < PER; ++j) {
-            const int bb = L * PER + j;
-            if (bb >= nb) break;
-            c += hw[bb];
-            if (c >= tt[q]) {
-              cand = bb;
-              break;
-            }
-          }
-          if (cand == 0x7FFFFFFF) cand = min(L * PER + PER - 1, nb - 1);
-        }
-        b = __shfl(cand, L);
+  for (int q = 0; q < PT; ++q) {
+    const bool in = b0 + q < nb;
+    v[q] = in ? hw[b0 + q] : 0.0;
+    ls += v[q];
+    if (in && hc[b0 + q] != 0u) lastnz = b0 + q;
+  }
+  const double excl = base + block_excl_scan_f64(r, ls);
+  const int last = block_max_i32(r, lastnz);
+  int b_sel[2];
+  const double tt[2] = {t0, t1};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t first = block_min_u32(r, excl + ls >= tt[k] ? (uint32_t)tid : 0xFFFFFFFFu);
+    if (first == 0xFFFFFFFFu) {
+      b_sel[k] = last < 0 ? 0 : last;
+      continue;
+    }
+    __syncthreads();  // (r.ru is read by block_min_u32 until here)
+    if (tid == (int)first) {
+      // the first of its bins whose cumulative mass reaches the target (or
+      // its last bin, where the prefix reached it and this order's rounding
+      // did not)
+      int cand = -1;
+      double c = excl;
+#pragma unroll
+      for (int q = 0; q < PT; ++q) {
+        c += v[q];
+        if (cand < 0 && c >= tt[k]) cand = b0 + q;
       }
-      b_sel[q] = b;
+      r.ru[0] = (uint32_t)(cand < 0 ? min(b0 + PT - 1, nb - 1) : cand);
     }
-    const int lo = b_sel[0], hi = max(b_sel[0], b_sel[1]);
-    uint32_t c = 0, ct = 0;
-#pragma unroll 8
-    for (int q = 0; q < PER; ++q) {
-      const int b = lane * PER + q;
-      if (b <= hi && b < nb) {
-        ct += hc[b];
-        if (b >= lo) c += hc[b];
-      }
+    __syncthreads();
+    b_sel[k] = (int)r.ru[0];
+    __syncthreads();
+  }
+  const int lo = b_sel[0], hi = max(b_sel[0], b_sel[1]);
+  uint32_t c = 0, ct = 0;
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int b = b0 + q;
+    if (b <= hi && b < nb) {
+      ct += hc[b];
+      if (b >= lo) c += hc[b];
     }
-    for (int d = 1; d < 64; d <<= 1) {
-      c += __shfl_xor(c, d);
-      ct += __shfl_xor(ct, d);
-    }
-    if (lane == 0) {
-      r.b_lo = (uint32_t)lo;
-      r.b_hi = (uint32_t)hi;
-      r.cnt = c;
-      r.cnt_top = ct;
-    }
+  }
+  c = block_sum_u32(r, c);
+  ct = block_sum_u32(r, ct);
+  if (tid == 0) {
+    r.b_lo = (uint32_t)lo;
+    r.b_hi = (uint32_t)hi;
+    r.cnt = c;
+    r.cnt_top = ct;
   }
   __syncthreads();
 }
@@ -711,14 +723,15 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   double z0 = 0.0;
   for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
     const float z = __uint_as_float(bits);
-    if (z > -__builtin_inff() && (double)z >= c.thr) {
-      // the exact weight serves the guide too (the total needs it anyway)
+    const bool ok = z > -__builtin_inff() && (double)z >= c.thr;
+    // the exact weight serves the guide too (the total needs it anyway)
+    const double w = S1.w_if(ok, z);
+    if (ok) {
       const uint32_t b = S1.bin<kNB>(z);
-      const double w = S1.w(z);
       __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      z0 += w;
     }
+    z0 += w;
   });
   __syncthreads();
   double* gw = a.h0w + row * kNB;
@@ -726,7 +739,7 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   flush_hist(L.h.hw, L.h.hc, gw, gc);
   z0 = nuc_sum(r, z0, 0);
   if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], z0);
-  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
   const double Z0 = merge_sum(sh, a.p_z0 + row * a.S, a.S);
   take_hist(L.h.hw, L.h.hc, gw, gc);
   const double t = (double)a.top_p * Z0, g = kGuard * Z0;
@@ -779,7 +792,7 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
     const uint64_t K = comp_key(bits, (uint32_t)i);
     const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
     const uint32_t b = cand ? S1.bin<kNB>(z) : (uint32_t)kNB;
-    if (b < b_lo) {
+    if (b < b_lo) {  // (few elements: a branch)
       const double w1 = S1.w(z);
       A += w1;
       if (K >= c.kmp) {
@@ -805,7 +818,7 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
     st_dev(&a.p_a[row * a.S + seg], A);
     st_dev(&a.p_at[row * a.S + seg], AT);
   }
-  if (!last_done(sh, a.tickets + row * 3 + 1, (uint32_t)a.S)) return;
+  if (!last_of_row(sh, a.tickets + row * 3 + 1, (uint32_t)a.S)) return;
   // ---- the row's last workgroup
   const double Atot = merge_sum(sh, a.p_a + row * a.S, a.S);
   const double ATtot = merge_sum(sh, a.p_at + row * a.S, a.S);
@@ -894,13 +907,13 @@ __global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
     // kept candidates above the cut window
     const bool kept = z > -__builtin_inff() && (double)z >= c.thr && S1.bin<kNB>(z) < p.b_lo && K >= p.kfin;
     const uint32_t bt = kept ? S2.bin<kNB>(z) : (uint32_t)kNB;
-    if (bt < p.c_lo) A2 += S2.w(z);
+    if (bt < p.c_lo) A2 += S2.w(z);  // (few elements: a branch)
     if (bt >= p.c_lo && bt <= p.c_hi) stage_window(st, i, c.e_begin);
   });
   flush_window<DT>(st, xr, c.e_begin, &a.lcnt[row], lkey, lbits);
   A2 = nuc_sum(r, A2, 0);
   if (tid == 0) st_dev(&a.p_a2[row * a.S + seg], A2);
-  if (!last_done(sh, a.tickets + row * 3 + 2, (uint32_t)a.S)) return;
+  if (!last_of_row(sh, a.tickets + row * 3 + 2, (uint32_t)a.S)) return;
   const double A2tot = merge_sum(sh, a.p_a2 + row * a.S, a.S);
   const uint32_t n = ld_dev(&a.lcnt[row]);
   __syncthreads();
@@ -998,12 +1011,12 @@ __global__ __launch_bounds__(NT) void typ_moments_kernel(NucArgs a) {
   double z0 = 0.0, y = 0.0, zlo = c.m;
   for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
     const float z = __uint_as_float(bits);
-    if (z > -__builtin_inff() && (double)z >= c.thr) {
-      const double w = exp_le0((double)z - c.m, e2);
-      z0 += w;
-      y += w * (double)z;
-      zlo = fmin(zlo, (double)z);
-    }
+    const bool ok = z > -__builtin_inff() && (double)z >= c.thr;
+    const double e = exp_le0((double)z - c.m, e2);  // taken either way (no branch)
+    const double w = ok ? e : 0.0, zd = ok ? (double)z : 0.0;
+    z0 += w;
+    y += w * zd;
+    zlo = fmin(zlo, ok ? zd : zlo);
   });
   z0 = nuc_sum(r, z0, 0);
   y = nuc_sum(r, y, 1);
@@ -1014,7 +1027,7 @@ __global__ __launch_bounds__(NT) void typ_moments_kernel(NucArgs a) {
     st_dev(&a.p_a[p0 + seg], y);
     st_dev(&a.p_at[p0 + seg], zlo);
   }
-  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
   const double Z0 = merge_sum(sh, a.p_z0 + p0, a.S), Y = merge_sum(sh, a.p_a + p0, a.S);
   const double lo = block_ext_f64<false>(r, tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : c.m);
   if (tid == 0) {
@@ -1096,10 +1109,12 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
     uint64_t K;
     uint32_t b;
-    if (!S.look<kNB>(bits, (uint32_t)i, K, b)) return;
-    const double w = S.w(__uint_as_float(bits));
-    __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const bool ok = S.look<kNB>(bits, (uint32_t)i, K, b);
+    const double w = S.w_if(ok, __uint_as_float(bits));
+    if (ok) {
+      __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     t += w;
   });
   __syncthreads();
@@ -1108,7 +1123,7 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   flush_hist(L.h.hw, L.h.hc, gw, gc);
   t = nuc_sum(r, t, 0);
   if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], t);
-  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
   const double tot = merge_sum(sh, a.p_z0 + row * a.S, a.S);
   take_hist(L.h.hw, L.h.hc, gw, gc);
   const double tg = jb.frac * tot, g = kGuard * tot;
@@ -1147,9 +1162,10 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
   for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
     uint64_t K;
     uint32_t b;
-    if (!S.look<kNB>(bits, (uint32_t)i, K, b)) return;
+    const bool ok = S.look<kNB>(bits, (uint32_t)i, K, b);
     const float z = __uint_as_float(bits);
-    if (b < jb.b_lo) {
+    if (!ok) return;
+    if (b < jb.b_lo) {  // (few elements: a branch)
       A += S.w(z);
       zb = fmax(zb, (double)z);
     } else if (b <= jb.b_hi) {
@@ -1164,7 +1180,7 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
     st_dev(&a.p_a[p0 + seg], A);
     st_dev(&a.p_at[p0 + seg], zb);
   }
-  if (!last_done(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
+  if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
   // ---- the row's last workgroup
   const double Atot = merge_sum(sh, a.p_a + p0, a.S);
   const double zbt = block_ext_f64<true>(r, tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : -__builtin_inf());
@@ -1261,18 +1277,19 @@ __global__ __launch_bounds__(NT) void kept_lse_kernel(NucArgs a) {
   }
   init_e2(e2);
   const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
-  const double m = a.st_max[row], T = a.T;
+  const double m = a.st_max[row], T = a.T, iT = 1.0 / T;
   const double thr = m + log((double)a.min_p);
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
   double w = 0.0;
   for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t) {
     const float z = __uint_as_float(bits);
-    if ((double)z >= thr) w += exp_le0(((double)z - m) / T, e2);
+    const double e = exp_le0(((double)z - m) * iT, e2);  // taken either way (no branch)
+    w += (double)z >= thr ? e : 0.0;
   });
   w = nuc_sum(r, w, 0);
   if (a.S > 1) {
     if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], w);
-    if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
+    if (!last_of_row(sh, a.tickets + row, (uint32_t)a.S)) return;
     w = merge_sum(sh, a.p_z0 + row * a.S, a.S);
   }
   if (tid == 0) {
