@@ -212,7 +212,8 @@ struct NucPlan {                   // per row, written by the last workgroup of 
 // draw): the candidate set and order, the target, and the results.
 struct SelJob {
   double m, thr, T;      // candidates z > -inf, z >= thr; weights exp((z - m) / T)
-  double c, span;        // typical order: the centre and the score span of the bins
+  double c, span;        // the typical centre; the bins' span (value order: of (m - z) / T, typical: of |z - c|)
+  double span_all;       // typical order: the span of every candidate's distance
   double frac;           // target: the first candidate whose cumulative weight reaches frac x total
   uint64_t kfloor, kT;   // order-key floor; typical-set floor on the score key (0: none)
   int32_t order, strict; // 0 value, 1 typicality; strict: cumulative weight must pass the target

@@ -91,7 +91,7 @@ struct NucSet {
   const double* e2;   // the exp table
   int order;          // 0 value, 1 typicality
   double c;           // typical centre (order 1, typical sets)
-  double span;        // order 1: first-level bins are equal steps of the score over [0, span)
+  double span;        // first-level bins are equal steps of the bin coordinate over [0, span)
   uint64_t kT;        // typical set: score key >= kT (0: none)
   __device__ __forceinline__ uint64_t score_key_of(double dc, uint32_t i) const {
     return ((~typ_score(dc) & kTypScoreMask) << kTypIdBits) | (~(uint64_t)i & kTypIdMask);
@@ -121,32 +121,68 @@ struct NucSet {
   __device__ __forceinline__ float gw(float z) const {
     return __builtin_amdgcn_exp2f((float)(x(z) * 1.4426950408889634));
   }
-  // first-level bin: equal steps of (m - z) / T over [0, kSpan) (order 0),
-  // or of the cut distance over [0, span) (order 1)
+  // first-level bin: equal steps over [0, span) of (m - z) / T (order 0) or
+  // of the cut distance (order 1); the last bin also takes everything deeper
   template <int NB>
   __device__ __forceinline__ uint32_t bin_of(double d) const {
     return d >= kSpan ? (uint32_t)(NB - 1) : (uint32_t)(d * (NB / kSpan));
   }
   template <int NB>
   __device__ __forceinline__ uint32_t bin(float z) const {
-    return bin_of<NB>(order == 0 ? -x(z) : typ_cut(fabs((double)z - c)) * (kSpan / span));
+    return bin_of<NB>((order == 0 ? -x(z) : typ_cut(fabs((double)z - c))) * (kSpan / span));
   }
   // The candidate test, the order key and the first-level bin of element i,
-  // the typicality distance taken once.
-  template <int NB>
+  // the typicality distance taken once; ORD is `order` (loops are compiled
+  // per order).
+  template <int NB, int ORD>
   __device__ __forceinline__ bool look(uint32_t bits, uint32_t i, uint64_t& K, uint32_t& b) const {
     const float z = __uint_as_float(bits);
-    if (order == 0) {
+    if constexpr (ORD == 0) {
       K = comp_key(bits, i);
-      b = bin_of<NB>(-x(z));
+      b = bin_of<NB>(-x(z) * (kSpan / span));
       return in(z, K) && (kT == 0 || score_key(bits, i) >= kT);
+    } else {
+      const double dc = typ_cut(fabs((double)z - c));
+      K = score_key_of(dc, i);
+      b = bin_of<NB>(dc * (kSpan / span));
+      return in(z, K) && (kT == 0 || K >= kT);
     }
-    const double dc = typ_cut(fabs((double)z - c));
-    K = score_key_of(dc, i);
-    b = bin_of<NB>(dc * (kSpan / span));
-    return in(z, K) && (kT == 0 || K >= kT);
   }
 };
+
+// Selects a loop body compiled for one order.
+template <int O>
+struct Ord {
+  static constexpr int value = O;
+};
+template <class F>
+__device__ __forceinline__ void by_order(int order, F&& f) {
+  if (order == 0)
+    f(Ord<0>{});
+  else
+    f(Ord<1>{});
+}
+
+// A selection in value order (order 0) with first-level bins over [0, span).
+__device__ __forceinline__ NucSet value_set(double m, double thr, uint64_t kfloor, double T, const double* e2,
+                                            double span = kSpan) {
+  return NucSet{m, thr, kfloor, T, e2, 0, 0.0, span, 0ull};
+}
+
+// How deep a weighted selection's targets can lie, in the units of the bin
+// coordinate.  Every candidate deeper than d weighs at most e^-d, and the
+// heaviest candidate (depth `lead`) at least e^-lead, which bounds the total W
+// from below.  With at most n candidates, those deeper than d hold less than
+// n e^-d; once that is at most (1 - frac - 2 kGuard) W, the mass above d
+// passes both targets of the window, (frac -+ kGuard) W.  The candidates
+// deeper than the bound (plus a margin of 1 for rounding) then share the last
+// guide bin, which keeps most of a peaked row out of the bins the window is
+// placed in.  A bound that failed would only send the row to the one-workgroup
+// fallback (its window would overflow); the selection stays exact.
+__device__ __forceinline__ double crossing_depth(double frac, int64_t n, double lead) {
+  const double rest = 1.0 - frac - 2.0 * kGuard;
+  return rest > 0.0 ? lead + log((double)n / rest) + 1.0 : __builtin_inf();
+}
 
 // ---------------------------------------------------------------- block helpers
 // last_done, and the finishing workgroup's waves then issue ahead of those of
@@ -532,6 +568,7 @@ struct NucCommon {
   int64_t e_begin, e_end;
   double m, thr;
   uint64_t kmp;  // smallest key min_p keeps (0: min_p off)
+  double span1;  // the cut's guide bins (untempered, value order) cover [0, span1)
 };
 
 __device__ __forceinline__ NucCommon nuc_common(const NucArgs& a, int64_t row, int seg) {
@@ -541,6 +578,7 @@ __device__ __forceinline__ NucCommon nuc_common(const NucArgs& a, int64_t row, i
   c.m = a.st_max[row];
   c.thr = a.top_n_sigma > 0.0f ? c.m - (double)a.top_n_sigma * a.sigma[row] : -__builtin_inf();
   c.kmp = a.min_p > 0.0f ? key_floor(c.m + log((double)a.min_p)) : 0ull;
+  c.span1 = fmin(kSpan, crossing_depth((double)a.top_p, a.V, 0.0));
   return c;
 }
 
@@ -548,10 +586,10 @@ __device__ __forceinline__ NucCommon nuc_common(const NucArgs& a, int64_t row, i
 template <typename DT, bool VEC>
 __device__ void row_alone(FbShared& s, NucRed& r, const NucArgs& a, int64_t row, const NucCommon& c,
                           const DT* __restrict__ xr, const double* e2) {
-  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
+  const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
   const SelOut cut = wg_select<DT, VEC>(s, r, xr, a.V, S1, (double)a.top_p, false);
   const uint64_t kfin = max(cut.key, c.kmp);
-  const NucSet S2{c.m, c.thr, kfin, (double)a.T, e2};
+  const NucSet S2 = value_set(c.m, c.thr, kfin, (double)a.T, e2);
   // floor mode: only the kept set's total (a selection at 0 returns it)
   const SelOut d = wg_select<DT, VEC>(s, r, xr, a.V, S2, a.out_kfl ? 0.0 : (double)a.u[row], true);
   if (threadIdx.x == 0) {
@@ -562,6 +600,17 @@ __device__ void row_alone(FbShared& s, NucRed& r, const NucArgs& a, int64_t row,
     }
     a.out_token[row] = ~(uint32_t)d.key;
     if (a.out_logp) a.out_logp[row] = (float)(((double)__uint_as_float(d.bits) - c.m) / (double)a.T - log(d.tot));
+  }
+}
+
+// The last guide bin's mass and count, kept per lane while streaming (most
+// elements of a peaked row land there), added with one LDS atomic per wave.
+__device__ __forceinline__ void add_deep(double* hw, uint32_t* hc, double w, uint32_t n) {
+  w = wave_sum_f64(w);
+  for (int d = 1; d < 64; d <<= 1) n += (uint32_t)__shfl_xor((int)n, d);
+  if ((threadIdx.x & 63) == 0 && n != 0u) {
+    __hip_atomic_fetch_add(&hw[kNB - 1], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(&hc[kNB - 1], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -714,25 +763,30 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, seg);
   const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
-  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
+  const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
   for (int b = tid; b < kNB; b += NT) {
     L.h.hw[b] = 0.0;
     L.h.hc[b] = 0u;
   }
   __syncthreads();
-  double z0 = 0.0;
+  double z0 = 0.0, dw = 0.0;
+  uint32_t dn = 0;
   for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
     const float z = __uint_as_float(bits);
     const bool ok = z > -__builtin_inff() && (double)z >= c.thr;
     // the exact weight serves the guide too (the total needs it anyway)
     const double w = S1.w_if(ok, z);
-    if (ok) {
-      const uint32_t b = S1.bin<kNB>(z);
+    const uint32_t b = S1.bin<kNB>(z);
+    if (ok && b < kNB - 1) {
       __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    const bool deep = ok && b == kNB - 1;
+    dw += deep ? w : 0.0;
+    dn += deep ? 1u : 0u;
     z0 += w;
   });
+  add_deep(L.h.hw, L.h.hc, dw, dn);
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
@@ -774,8 +828,8 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
   const uint32_t b_lo = a.plan[row].b_lo, b_hi = a.plan[row].b_hi;
   const double z0 = a.plan[row].z0;
-  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
-  const NucSet ST{c.m, c.thr, c.kmp, (double)a.T, e2};
+  const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
+  const NucSet ST = value_set(c.m, c.thr, c.kmp, (double)a.T, e2);
   for (int b = tid; b < kNB; b += NT) {
     L.h.hw[b] = 0.0;
     L.h.hc[b] = 0u;
@@ -799,7 +853,7 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
         const double wt = same_t ? w1 : ST.w(z);
         AT += wt;
         if (want_guide) {
-          const uint32_t bt = same_t ? b : ST.bin<kNB>(z);
+          const uint32_t bt = ST.bin<kNB>(z);  // (its own span, also at T = 1)
           __hip_atomic_fetch_add(&L.h.hw[bt], wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           __hip_atomic_fetch_add(&L.h.hc[bt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
@@ -839,7 +893,7 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   uint32_t nk = 0;
   for (uint32_t j = tid; j < n; j += NT) nk += L.w.key[j] >= kfin ? 1u : 0u;
   nk = block_sum_u32(r, nk);
-  const NucSet S2{c.m, c.thr, kfin, (double)a.T, e2};
+  const NucSet S2 = value_set(c.m, c.thr, kfin, (double)a.T, e2);
   const double WT = ATtot + sum_sorted(r, L.w.bits, nk, S2);
   if (a.out_kfl) {  // floor mode: the kept set, nothing drawn
     zero_hist(gw, gc);
@@ -896,8 +950,8 @@ __global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, seg);
   const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
-  const NucSet S1{c.m, c.thr, 0ull, 1.0, e2};
-  const NucSet S2{c.m, c.thr, p.kfin, (double)a.T, e2};
+  const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
+  const NucSet S2 = value_set(c.m, c.thr, p.kfin, (double)a.T, e2);
   uint64_t* lkey = a.lkey + row * kCapW;
   uint32_t* lbits = a.lbits + row * kCapW;
   double A2 = 0.0;
@@ -952,7 +1006,7 @@ __global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
     return;
   }
   const NucPlan p = a.plan[row];
-  const NucSet S2{c.m, c.thr, p.kfin, (double)a.T, e2};
+  const NucSet S2 = value_set(c.m, c.thr, p.kfin, (double)a.T, e2);
   const SelOut d = wg_select<DT, VEC>(fb, r, xr, a.V, S2, (double)a.u[row], true);
   if (threadIdx.x == 0) {
     a.out_token[row] = ~(uint32_t)d.key;
@@ -985,6 +1039,17 @@ __global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
 
 __device__ __forceinline__ NucSet job_set(const SelJob& j, const double* e2) {
   return NucSet{j.m, j.thr, j.kfloor, j.T, e2, j.order, j.c, j.span, j.kT};
+}
+
+// The first-level span of a selection in typical order at target frac over
+// candidates whose largest value is zmax: candidates farther from the centre
+// c than the crossing bound lie below it (once the bound passes m - c), where
+// distance d means weight at most e^((c - d - m) / T) against the heaviest
+// candidate's e^((zmax - m) / T); so the bound in distance is
+// T ln(n / rest) + c - zmax (crossing_depth with that lead, scaled by T).
+__device__ __forceinline__ double typ_span(const SelJob& j, double frac, int64_t n, double zmax) {
+  const double d = j.T * crossing_depth(frac, n, 0.0) + j.c - zmax;
+  return fmin(j.span_all, fmax(d, j.m - j.c));
 }
 
 template <typename DT, bool VEC>
@@ -1037,7 +1102,8 @@ __global__ __launch_bounds__(NT) void typ_moments_kernel(NucArgs a) {
     j.thr = c.thr;
     j.T = 1.0;
     j.c = cen;
-    j.span = fmax(fmax(c.m - cen, cen - lo), 1e-30) * (1.0 + 1e-6);
+    j.span_all = fmax(fmax(c.m - cen, cen - lo), 1e-30) * (1.0 + 1e-6);
+    j.span = typ_span(j, (double)a.typical_p, a.V, c.m);
     j.frac = (double)a.typical_p;
     j.kfloor = 0ull;
     j.kT = 0ull;
@@ -1060,12 +1126,14 @@ __device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
       j.frac = (double)a.top_p;
       j.strict = 0;
       j.step = 2;
+      j.span = fmin(kSpan, crossing_depth(j.frac, a.V, j.m - j.aux));
     } else {
       if (a.min_p > 0.0f) j.thr = fmax(j.thr, j.aux + log((double)a.min_p));
       j.T = (double)a.T;  // the draw in typical order
       j.frac = (double)a.u[row];
       j.strict = 1;
       j.step = 3;
+      j.span = typ_span(j, j.frac, a.V, j.aux);
     }
     j.state = 1;
   } else if (j.step == 2) {
@@ -1076,6 +1144,7 @@ __device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
     j.frac = (double)a.u[row];
     j.strict = 1;
     j.step = 3;
+    j.span = fmin(kSpan, crossing_depth(j.frac, a.V, (j.m - j.aux) / j.T));
     j.state = 1;
   } else {
     a.out_token[row] = key_id(j.order, j.key);
@@ -1105,18 +1174,25 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
     L.h.hc[b] = 0u;
   }
   __syncthreads();
-  double t = 0.0;
-  for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
-    uint64_t K;
-    uint32_t b;
-    const bool ok = S.look<kNB>(bits, (uint32_t)i, K, b);
-    const double w = S.w_if(ok, __uint_as_float(bits));
-    if (ok) {
-      __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    t += w;
+  double t = 0.0, dw = 0.0;
+  uint32_t dn = 0;
+  by_order(S.order, [&](auto ord) {
+    for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+      uint64_t K;
+      uint32_t b;
+      const bool ok = S.look<kNB, decltype(ord)::value>(bits, (uint32_t)i, K, b);
+      const double w = S.w_if(ok, __uint_as_float(bits));
+      if (ok && b < kNB - 1) {
+        __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      const bool deep = ok && b == kNB - 1;
+      dw += deep ? w : 0.0;
+      dn += deep ? 1u : 0u;
+      t += w;
+    });
   });
+  add_deep(L.h.hw, L.h.hc, dw, dn);
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
@@ -1159,18 +1235,20 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
   uint64_t* lkey = a.lkey + row * kCapW;
   uint32_t* lbits = a.lbits + row * kCapW;
   double A = 0.0, zb = -__builtin_inf();  // mass and largest value before the window
-  for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
-    uint64_t K;
-    uint32_t b;
-    const bool ok = S.look<kNB>(bits, (uint32_t)i, K, b);
-    const float z = __uint_as_float(bits);
-    if (!ok) return;
-    if (b < jb.b_lo) {  // (few elements: a branch)
-      A += S.w(z);
-      zb = fmax(zb, (double)z);
-    } else if (b <= jb.b_hi) {
-      stage_window(st, i, e_begin);
-    }
+  by_order(S.order, [&](auto ord) {
+    for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+      uint64_t K;
+      uint32_t b;
+      const bool ok = S.look<kNB, decltype(ord)::value>(bits, (uint32_t)i, K, b);
+      const float z = __uint_as_float(bits);
+      if (!ok) return;
+      if (b < jb.b_lo) {  // (few elements: a branch)
+        A += S.w(z);
+        zb = fmax(zb, (double)z);
+      } else if (b <= jb.b_hi) {
+        stage_window(st, i, e_begin);
+      }
+    });
   });
   flush_window<DT>(st, xr, e_begin, &a.lcnt[row], lkey, lbits, &S);
   A = nuc_sum(r, A, 0);
