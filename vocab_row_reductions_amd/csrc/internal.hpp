@@ -223,6 +223,8 @@ struct SelJob {
   uint32_t bits, pad;    // selected candidate's element bits
   uint64_t key;          // selected candidate's order key
   double tot;            // exact total weight of the candidates
+  double tot_known;      // > 0: that total, known before the guide pass (no exact sums there)
+  double cum;            // exact cumulative weight through the selected candidate
   double zmax;           // largest value among the candidates up to the selected one
   double aux;            // the typical set's largest value (the min_p reference)
 };

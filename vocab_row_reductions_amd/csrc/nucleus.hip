@@ -203,6 +203,7 @@ struct NucRed {
   uint32_t n;
   uint64_t ksel;
   uint32_t bsel;
+  double csel;  // walk_sorted: the cumulative mass through the chosen candidate
 };
 
 // Fixed-order sum over the workgroup (every thread gets it).
@@ -290,15 +291,16 @@ __device__ __forceinline__ double block_ext_f64(NucRed& r, double v) {
 // `base`, the mass above bin 0) first reaches t0 and t1; their candidates
 // (cnt) and those of bins [0, b_hi] (cnt_top).  A target past the last bin
 // takes the last non-empty bin.  Each thread holds NB / NT consecutive bins;
-// the thread sums are prefixed in thread order (a fixed order), the thread
-// whose prefix first reaches a target walks its own bins.  All threads call;
-// the results are in r.
+// the thread sums are prefixed in thread order (a fixed order: within a wave
+// by shuffles, then the wave totals in wave order), the thread whose prefix
+// first reaches a target walks its own bins.  Six barriers.  All threads
+// call; the results are in r.
 template <int NB>
 __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int nb, double base, double t0,
                           double t1) {
   constexpr int PT = NB / NT;
   static_assert(PT * NT == NB, "bins per thread");
-  const int tid = threadIdx.x, b0 = tid * PT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b0 = tid * PT;
   __syncthreads();
   double v[PT];
   double ls = 0.0;
@@ -310,36 +312,55 @@ __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int n
     ls += v[q];
     if (in && hc[b0 + q] != 0u) lastnz = b0 + q;
   }
-  const double excl = base + block_excl_scan_f64(r, ls);
-  const int last = block_max_i32(r, lastnz);
-  int b_sel[2];
-  const double tt[2] = {t0, t1};
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t first = block_min_u32(r, excl + ls >= tt[k] ? (uint32_t)tid : 0xFFFFFFFFu);
-    if (first == 0xFFFFFFFFu) {
-      b_sel[k] = last < 0 ? 0 : last;
-      continue;
-    }
-    __syncthreads();  // (r.ru is read by block_min_u32 until here)
-    if (tid == (int)first) {
-      // the first of its bins whose cumulative mass reaches the target (or
-      // its last bin, where the prefix reached it and this order's rounding
-      // did not)
-      int cand = -1;
-      double c = excl;
-#pragma unroll
-      for (int q = 0; q < PT; ++q) {
-        c += v[q];
-        if (cand < 0 && c >= tt[k]) cand = b0 + q;
-      }
-      r.ru[0] = (uint32_t)(cand < 0 ? min(b0 + PT - 1, nb - 1) : cand);
-    }
-    __syncthreads();
-    b_sel[k] = (int)r.ru[0];
-    __syncthreads();
+  double incl = ls;
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
   }
-  const int lo = b_sel[0], hi = max(b_sel[0], b_sel[1]);
+  const double prev = __shfl_up(incl, 1);
+  int wl = lastnz;
+  for (int d = 1; d < 64; d <<= 1) wl = max(wl, __shfl_xor(wl, d));
+  if (lane == 63) r.rd[wave] = incl;
+  if (lane == 0) r.ru[wave] = (uint32_t)(wl + 1);
+  __syncthreads();
+  double excl = base;
+  int last = -1;
+#pragma unroll
+  for (int q = 0; q < NWAVE; ++q) {
+    if (q < wave) excl += r.rd[q];
+    last = max(last, (int)r.ru[q] - 1);
+  }
+  excl = lane > 0 ? excl + prev : excl;  // this thread's cumulative mass before its bins
+  const uint64_t h0 = __ballot(excl + ls >= t0), h1 = __ballot(excl + ls >= t1);
+  if (lane == 0) {
+    r.rk[wave] = h0 ? (uint64_t)(wave * 64 + __builtin_ctzll(h0)) : ~0ull;
+    r.rk[NWAVE + wave] = h1 ? (uint64_t)(wave * 64 + __builtin_ctzll(h1)) : ~0ull;
+  }
+  __syncthreads();
+  uint64_t f0 = ~0ull, f1 = ~0ull;
+#pragma unroll
+  for (int q = 0; q < NWAVE; ++q) {
+    f0 = min(f0, r.rk[q]);
+    f1 = min(f1, r.rk[NWAVE + q]);
+  }
+  // the first of the owner's bins whose cumulative mass reaches the target
+  // (or its last bin, where the prefix reached it and this order's rounding
+  // did not); no owner: the last non-empty bin
+  auto walk = [&](double tt) {
+    int cand = -1;
+    double c = excl;
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      c += v[q];
+      if (cand < 0 && c >= tt) cand = b0 + q;
+    }
+    return (uint32_t)(cand < 0 ? min(b0 + PT - 1, nb - 1) : cand);
+  };
+  const uint32_t dflt = (uint32_t)(last < 0 ? 0 : last);
+  if (f0 == ~0ull ? tid == 0 : (uint64_t)tid == f0) r.b_lo = f0 == ~0ull ? dflt : walk(t0);
+  if (f1 == ~0ull ? tid == 0 : (uint64_t)tid == f1) r.b_hi = f1 == ~0ull ? dflt : walk(t1);
+  __syncthreads();
+  const int lo = (int)r.b_lo, hi = max(lo, (int)r.b_hi);
   uint32_t c = 0, ct = 0;
 #pragma unroll
   for (int q = 0; q < PT; ++q) {
@@ -349,13 +370,22 @@ __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int n
       if (b >= lo) c += hc[b];
     }
   }
-  c = block_sum_u32(r, c);
-  ct = block_sum_u32(r, ct);
+  for (int d = 1; d < 64; d <<= 1) {
+    c += (uint32_t)__shfl_xor((int)c, d);
+    ct += (uint32_t)__shfl_xor((int)ct, d);
+  }
+  if (lane == 0) r.rk[wave] = ((uint64_t)ct << 32) | c;  // (every read of r.rk above precedes the last barrier)
+  __syncthreads();
   if (tid == 0) {
-    r.b_lo = (uint32_t)lo;
+    uint64_t sc = 0, st = 0;
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) {
+      sc += r.rk[q] & 0xFFFFFFFFull;
+      st += r.rk[q] >> 32;
+    }
     r.b_hi = (uint32_t)hi;
-    r.cnt = c;
-    r.cnt_top = ct;
+    r.cnt = (uint32_t)min<uint64_t>(sc, 0xFFFFFFFFull);
+    r.cnt_top = (uint32_t)min<uint64_t>(st, 0xFFFFFFFFull);
   }
   __syncthreads();
 }
@@ -363,10 +393,37 @@ __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int n
 // Walk n sorted candidates (bits) with weights S.w from a cumulative mass A:
 // the first index whose cumulative c satisfies c >= t (strict = false) or
 // t < c (strict = true); none: the last with a positive weight (or the last).
-// Each thread sums a run of kRun candidates in order, the runs are prefixed
-// in a fixed order, and every thread walks its own run.  All threads call.
+// *cum (if given) gets the cumulative mass through the chosen candidate.  Up
+// to 64 candidates: one per lane of wave 0, prefixed by shuffles; more: each
+// thread sums a run of kRun candidates in order, the runs are prefixed in a
+// fixed order, and every thread walks its own run.  All threads call.
 __device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const NucSet& S, double A, double t,
-                                bool strict) {
+                                bool strict, double* cum = nullptr) {
+  if (n <= 64) {
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const double w = (uint32_t)lane < n ? S.w(__uint_as_float(bits[lane])) : 0.0;
+      double incl = w;
+      for (int d = 1; d < 64; d <<= 1) {
+        const double o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      const double c = A + incl;
+      const bool live = (uint32_t)lane < n;
+      const uint64_t hit = __ballot(live && (strict ? (t < c) : (c >= t)));
+      const uint64_t pos = __ballot(live && w > 0.0);
+      const int j = hit ? __builtin_ctzll(hit) : pos ? 63 - __builtin_clzll(pos) : (n > 0 ? (int)n - 1 : 0);
+      const double cj = __shfl(c, j);
+      if (lane == 0) {
+        r.ru[0] = (uint32_t)j;
+        r.csel = cj;
+      }
+    }
+    __syncthreads();
+    if (cum) *cum = r.csel;
+    return r.ru[0];
+  }
   const uint32_t j0 = threadIdx.x * kRun;
   double wl[kRun];
   double run = 0.0;
@@ -378,23 +435,46 @@ __device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, con
   double c = A + block_excl_scan_f64(r, run);
   uint32_t first = 0xFFFFFFFFu;
   int lastpos = -1;
+  double cfirst = 0.0, clast = 0.0, cend = 0.0;
 #pragma unroll
   for (uint32_t q = 0; q < kRun; ++q) {
     if (j0 + q < n) {
       c += wl[q];
-      if (wl[q] > 0.0) lastpos = (int)(j0 + q);
-      if (first == 0xFFFFFFFFu && (strict ? (t < c) : (c >= t))) first = j0 + q;
+      if (wl[q] > 0.0) {
+        lastpos = (int)(j0 + q);
+        clast = c;
+      }
+      if (first == 0xFFFFFFFFu && (strict ? (t < c) : (c >= t))) {
+        first = j0 + q;
+        cfirst = c;
+      }
+      if (j0 + q == n - 1) cend = c;
     }
   }
-  first = block_min_u32(r, first);
-  lastpos = block_max_i32(r, lastpos);
-  if (first != 0xFFFFFFFFu) return first;
-  if (lastpos >= 0) return (uint32_t)lastpos;
-  return n > 0 ? n - 1 : 0;
+  const uint32_t f = block_min_u32(r, first);
+  const int lp = block_max_i32(r, lastpos);
+  const uint32_t j = f != 0xFFFFFFFFu ? f : lp >= 0 ? (uint32_t)lp : (n > 0 ? n - 1 : 0);
+  if (cum) {
+    // the owner of the chosen candidate's run publishes its cumulative mass
+    __syncthreads();
+    if (j >= j0 && j < j0 + kRun) r.csel = j == first ? cfirst : j == (uint32_t)lastpos ? clast : cend;
+    __syncthreads();
+    *cum = r.csel;
+  }
+  return j;
 }
 
 // Fixed-order sum of S.w over the first n sorted candidates.
 __device__ double sum_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const NucSet& S) {
+  if (n <= 64) {
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const double v = wave_sum_f64(threadIdx.x < n ? S.w(__uint_as_float(bits[threadIdx.x])) : 0.0);
+      if (threadIdx.x == 0) r.csel = v;
+    }
+    __syncthreads();
+    return r.csel;
+  }
   const uint32_t j0 = threadIdx.x * kRun;
   double run = 0.0;
   for (uint32_t q = 0; q < kRun; ++q)
@@ -420,6 +500,7 @@ struct SelOut {
   uint64_t key;   // the selected candidate
   uint32_t bits;  // its element bits
   double tot;     // the candidates' total mass (float64, fixed order)
+  double cum;     // the cumulative mass through the selected candidate
 };
 
 // The weighted selection over the candidates of `S` by one workgroup alone:
@@ -543,13 +624,14 @@ __device__ SelOut wg_select(FbShared& s, NucRed& r, const DT* __restrict__ xr, i
   }
   const uint32_t n = min(r.n, kCapW);
   sort_desc<kCapW>(s.list, lbits, n);
-  const uint32_t j = walk_sorted(r, lbits, n, S, A, frac * tot, strict);
+  double cum = 0.0;
+  const uint32_t j = walk_sorted(r, lbits, n, S, A, frac * tot, strict, &cum);
   if (tid == 0) {
     r.ksel = s.list[j];
     r.bsel = lbits[j];
   }
   __syncthreads();
-  const SelOut o{r.ksel, r.bsel, tot};
+  const SelOut o{r.ksel, r.bsel, tot, cum};
   __syncthreads();
   return o;
 }
@@ -1104,6 +1186,7 @@ __global__ __launch_bounds__(NT) void typ_moments_kernel(NucArgs a) {
     j.c = cen;
     j.span_all = fmax(fmax(c.m - cen, cen - lo), 1e-30) * (1.0 + 1e-6);
     j.span = typ_span(j, (double)a.typical_p, a.V, c.m);
+    j.tot_known = Z0;  // the typical order's weights are these: the guide pass needs no exact sums
     j.frac = (double)a.typical_p;
     j.kfloor = 0ull;
     j.kT = 0ull;
@@ -1127,6 +1210,7 @@ __device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
       j.strict = 0;
       j.step = 2;
       j.span = fmin(kSpan, crossing_depth(j.frac, a.V, j.m - j.aux));
+      j.tot_known = j.cum;  // the typical set's mass
     } else {
       if (a.min_p > 0.0f) j.thr = fmax(j.thr, j.aux + log((double)a.min_p));
       j.T = (double)a.T;  // the draw in typical order
@@ -1134,6 +1218,7 @@ __device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
       j.strict = 1;
       j.step = 3;
       j.span = typ_span(j, j.frac, a.V, j.aux);
+      j.tot_known = a.T == 1.0f && a.min_p == 0.0f ? j.cum : 0.0;  // (the same set and weights)
     }
     j.state = 1;
   } else if (j.step == 2) {
@@ -1145,6 +1230,7 @@ __device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
     j.strict = 1;
     j.step = 3;
     j.span = fmin(kSpan, crossing_depth(j.frac, a.V, (j.m - j.aux) / j.T));
+    j.tot_known = a.T == 1.0f && a.min_p == 0.0f ? j.cum : 0.0;  // (the same set and weights)
     j.state = 1;
   } else {
     a.out_token[row] = key_id(j.order, j.key);
@@ -1176,20 +1262,39 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   __syncthreads();
   double t = 0.0, dw = 0.0;
   uint32_t dn = 0;
+  const bool known = jb.tot_known > 0.0;
   by_order(S.order, [&](auto ord) {
+    if (known) {
+      // the exact total is known: float32 guide weights, and none for the
+      // candidates past the crossing bound (the last bin needs only their count)
+      for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+        uint64_t K;
+        uint32_t b;
+        const bool ok = S.look<kNB, decltype(ord)::value>(bits, (uint32_t)i, K, b);
+        if (ok && b < kNB - 1) {
+          __hip_atomic_fetch_add(&L.h.hw[b], (double)S.gw(__uint_as_float(bits)), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        dn += ok && b == kNB - 1 ? 1u : 0u;
+      });
+      return;
+    }
     for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
       uint64_t K;
       uint32_t b;
       const bool ok = S.look<kNB, decltype(ord)::value>(bits, (uint32_t)i, K, b);
-      const double w = S.w_if(ok, __uint_as_float(bits));
-      if (ok && b < kNB - 1) {
-        __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (ok) {  // (a subset of the row: a branch)
+        const double w = S.w(__uint_as_float(bits));
+        if (b < kNB - 1) {
+          __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
+          dw += w;
+          ++dn;
+        }
+        t += w;
       }
-      const bool deep = ok && b == kNB - 1;
-      dw += deep ? w : 0.0;
-      dn += deep ? 1u : 0u;
-      t += w;
     });
   });
   add_deep(L.h.hw, L.h.hc, dw, dn);
@@ -1197,10 +1302,12 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
   flush_hist(L.h.hw, L.h.hc, gw, gc);
-  t = nuc_sum(r, t, 0);
-  if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], t);
+  if (!known) {
+    t = nuc_sum(r, t, 0);
+    if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], t);
+  }
   if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
-  const double tot = merge_sum(sh, a.p_z0 + row * a.S, a.S);
+  const double tot = known ? jb.tot_known : merge_sum(sh, a.p_z0 + row * a.S, a.S);
   take_hist(L.h.hw, L.h.hc, gw, gc);
   const double tg = jb.frac * tot, g = kGuard * tot;
   pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, tg - g, tg + g);
@@ -1271,7 +1378,8 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
   }
   take_list(L.w.key, L.w.bits, lkey, lbits, n);
   sort_desc<kCapW>(L.w.key, L.w.bits, n);
-  const uint32_t j = walk_sorted(r, L.w.bits, n, S, Atot, jb.frac * jb.tot, jb.strict != 0);
+  double cum = 0.0;
+  const uint32_t j = walk_sorted(r, L.w.bits, n, S, Atot, jb.frac * jb.tot, jb.strict != 0, &cum);
   double zl = -__builtin_inf();  // the window's candidates up to the selected one
   for (uint32_t q = tid; q <= j && q < n; q += NT) zl = fmax(zl, (double)__uint_as_float(L.w.bits[q]));
   zl = block_ext_f64<true>(r, zl);
@@ -1280,6 +1388,7 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
     o.key = L.w.key[j];
     o.bits = L.w.bits[j];
     o.zmax = fmax(zbt, zl);
+    o.cum = cum;
     o.state = 4;
     typ_advance(a, row, o);
   }
@@ -1309,6 +1418,7 @@ __global__ __launch_bounds__(NT) void sel_alone_kernel(NucArgs a) {
     o.bits = d.bits;
     o.tot = d.tot;
     o.zmax = zl;
+    o.cum = d.cum;
     o.state = 4;
     typ_advance(a, row, o);
   }
