@@ -299,7 +299,7 @@ struct MomWs {
 };
 // The whole-row nucleus passes (top_k = 0, top_p < 1).
 struct NucWs {
-  size_t tickets, h0w, h0c, hTw, hTc, lkey, lbits, lcnt, p_z0, p_a, p_at, p_a2, plan, jobs;
+  size_t tickets, h0w, h0c, hTw, hTc, lkey, lbits, lcnt, gcnt, gbits, gidx, p_z0, p_a, p_at, p_a2, plan, jobs;
 };
 NucWs nucleus_layout(Layout& L, int64_t rows, const Plan& p) {
   NucWs w{};
@@ -312,6 +312,9 @@ NucWs nucleus_layout(Layout& L, int64_t rows, const Plan& p) {
   w.lkey = L.take(R * kNucCap * 8);
   w.lbits = L.take(R * kNucCap * 4);
   w.lcnt = L.take(R * 4);
+  w.gcnt = L.take(n * 4);
+  w.gbits = L.take(n * kGatherCap * 4);
+  w.gidx = L.take(n * kGatherCap * 4);
   w.p_z0 = L.take(n * 8);
   w.p_a = L.take(n * 8);
   w.p_at = L.take(n * 8);
@@ -652,6 +655,9 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
       n.lkey = at<uint64_t>(ws, nw.lkey);
       n.lbits = at<uint32_t>(ws, nw.lbits);
       n.lcnt = at<uint32_t>(ws, nw.lcnt);
+      n.gcnt = at<uint32_t>(ws, nw.gcnt);
+      n.gbits = at<uint32_t>(ws, nw.gbits);
+      n.gidx = at<uint32_t>(ws, nw.gidx);
       n.p_z0 = at<double>(ws, nw.p_z0);
       n.p_a = at<double>(ws, nw.p_a);
       n.p_at = at<double>(ws, nw.p_at);
@@ -883,6 +889,9 @@ static vsel_status spec_filter(SpecArgs& p, int32_t top_k, float top_p, float mi
     n.lkey = at<uint64_t>(sub, nw.lkey);
     n.lbits = at<uint32_t>(sub, nw.lbits);
     n.lcnt = at<uint32_t>(sub, nw.lcnt);
+    n.gcnt = at<uint32_t>(sub, nw.gcnt);
+    n.gbits = at<uint32_t>(sub, nw.gbits);
+    n.gidx = at<uint32_t>(sub, nw.gidx);
     n.p_z0 = at<double>(sub, nw.p_z0);
     n.p_a = at<double>(sub, nw.p_a);
     n.p_at = at<double>(sub, nw.p_at);

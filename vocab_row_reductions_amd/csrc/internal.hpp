@@ -198,11 +198,12 @@ struct MomArgs {
 // window).  Histograms, window counters and tickets are zero between calls.
 constexpr int kNucBins = 4096;     // guide bins per row
 constexpr int kNucCap = 4096;      // window candidates per row
+constexpr int kGatherCap = 2048;   // gathered candidates per (row, segment)
 struct NucPlan {                   // per row, written by the last workgroup of a pass
   uint32_t state;                  // 0 cut placed, 1 draw pass needed, 2 done, 3/4 row/draw left to one workgroup
   uint32_t b_lo, b_hi;             // cut window (untempered guide bins)
   uint32_t c_lo, c_hi;             // draw window (tempered guide bins, above the cut window)
-  uint32_t pad;
+  uint32_t listed;                 // 1: every candidate the later passes reach is in the gathered list
   double z0;                       // exact candidate mass, untempered
   double wt;                       // exact kept mass, tempered
   uint64_t kfin;                   // smallest kept composite key
@@ -220,7 +221,8 @@ struct SelJob {
   int32_t state;         // 0 none, 1 guide pass due, 2 window pass due, 3 left to one workgroup, 4 selected
   int32_t step;          // 1 typical cut, 2 top-p within the set, 3 the draw
   uint32_t b_lo, b_hi;   // window (guide bins)
-  uint32_t bits, pad;    // selected candidate's element bits
+  uint32_t bits;         // selected candidate's element bits
+  uint32_t listed;       // 1: every candidate of this and the later selections is in the gathered list
   uint64_t key;          // selected candidate's order key
   double tot;            // exact total weight of the candidates
   double tot_known;      // > 0: that total, known before the guide pass (no exact sums there)
@@ -252,6 +254,12 @@ struct NucArgs {
   uint64_t* lkey;          // [rows*kNucCap] window candidates
   uint32_t* lbits;
   uint32_t* lcnt;          // [rows]
+  // candidates the first guide pass gathered (those within the crossing
+  // bound), per (row, segment) slot in stream order: count (kGatherCap + 1:
+  // overflowed), element bits and indices
+  uint32_t* gcnt;          // [rows*S]
+  uint32_t* gbits;         // [rows*S*kGatherCap]
+  uint32_t* gidx;
   double* p_z0;            // [rows*S] segment partials
   double* p_a;
   double* p_at;

@@ -798,6 +798,82 @@ __device__ __forceinline__ void flush_window(Stage& st, const DT* __restrict__ x
   }
 }
 
+// The candidates a first guide pass gathers (those within the crossing
+// bound): staged without atomics, each wave in a region of its own, placed by
+// a ballot and the lanes' ranks (the wave's count is a uniform register); past
+// a region's end they are only counted.
+struct GatherStage {
+  static constexpr uint32_t kPer = kGatherCap / NWAVE;
+  uint32_t idx[NWAVE][kPer];
+  uint32_t n[NWAVE];
+};
+
+__device__ __forceinline__ void gather(GatherStage& st, uint32_t& cnt, bool take, int64_t i, int64_t e_begin) {
+  const uint64_t m = __ballot(take);
+  if (m != 0ull) {
+    const uint32_t p = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (take && p < GatherStage::kPer) st.idx[threadIdx.x >> 6][p] = (uint32_t)(i - e_begin);
+    cnt += (uint32_t)__builtin_popcountll(m);
+  }
+}
+
+// The workgroup's gathered candidates -> its (row, segment) slot, wave after
+// wave in stream order (a fixed order), with the count (kGatherCap + 1 when
+// a wave's region overflowed; the slot is then left unwritten).  All threads
+// call, each wave with its count.
+template <typename DT>
+__device__ __forceinline__ void flush_gather(GatherStage& st, uint32_t cnt, const DT* __restrict__ xr,
+                                             int64_t e_begin, const NucArgs& a, int64_t row, int seg) {
+  if ((threadIdx.x & 63) == 0) st.n[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  uint32_t off[NWAVE], tot = 0;
+  bool over = false;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    off[w] = tot;
+    tot += min(st.n[w], GatherStage::kPer);
+    over = over || st.n[w] > GatherStage::kPer;
+  }
+  const size_t slot = (size_t)(row * a.S + seg);
+  if (threadIdx.x == 0) st_dev(&a.gcnt[slot], over ? (uint32_t)kGatherCap + 1u : tot);
+  if (over) return;
+  uint32_t* gb = a.gbits + slot * kGatherCap;
+  uint32_t* gi = a.gidx + slot * kGatherCap;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    const uint32_t nw = min(st.n[w], GatherStage::kPer);
+    for (uint32_t j = threadIdx.x; j < nw; j += NT) {
+      const int64_t i = e_begin + st.idx[w][j];
+      gb[off[w] + j] = gbits_at<DT>(xr, i);
+      gi[off[w] + j] = (uint32_t)i;
+    }
+  }
+}
+
+// Whether every segment's gathered candidates fit its slot (the row's last
+// workgroup; all threads call).
+__device__ __forceinline__ bool gathered_all(NucRed& r, const NucArgs& a, int64_t row) {
+  const int v = threadIdx.x < a.S ? (int)ld_dev(&a.gcnt[row * a.S + threadIdx.x]) : 0;
+  return block_max_i32(r, v) <= kGatherCap;
+}
+
+// The elements a pass visits in its (row, segment): the segment itself, or,
+// for a row whose gathered list holds every candidate the pass can reach, the
+// candidates gathered from that segment (fn gets each one's bits and index).
+template <typename DT, bool VEC, class Fn>
+__device__ __forceinline__ void for_each_cand(const NucArgs& a, int64_t row, int seg, bool listed,
+                                              const DT* __restrict__ xr, int64_t e_begin, int64_t e_end, Fn&& fn) {
+  if (listed) {
+    const size_t slot = (size_t)(row * a.S + seg);
+    const uint32_t n = min(a.gcnt[slot], (uint32_t)kGatherCap);
+    const uint32_t* gb = a.gbits + slot * kGatherCap;
+    const uint32_t* gi = a.gidx + slot * kGatherCap;
+    for (uint32_t j = threadIdx.x; j < n; j += NT) fn(gb[j], (int64_t)gi[j]);
+    return;
+  }
+  for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, fn);
+}
+
 union NucLds {
   struct {
     double hw[kNB];
@@ -818,12 +894,16 @@ union StageOrWindow {
 };
 
 // Pass 1: guide histogram of exp(z - m) over the candidates and their exact
-// total; the last workgroup places the cut window.
+// total, and the candidates within the crossing bound (the bins short of the
+// last) gathered per segment; the last workgroup places the cut window.  When
+// every segment's gathered candidates fit and the window stays short of the
+// last bin, the later passes visit only the gathered candidates.
 template <typename DT, bool VEC>
 __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   __shared__ SelShared sh;
   __shared__ NucRed r;
   __shared__ NucLds L;
+  __shared__ GatherStage gs;
   __shared__ double e2[64];
   const int tid = threadIdx.x;
   const Item it = work_item(a.S);
@@ -852,23 +932,26 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   }
   __syncthreads();
   double z0 = 0.0, dw = 0.0;
-  uint32_t dn = 0;
-  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
+  uint32_t dn = 0, ng = 0;
+  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
     const float z = __uint_as_float(bits);
     const bool ok = z > -__builtin_inff() && (double)z >= c.thr;
     // the exact weight serves the guide too (the total needs it anyway)
     const double w = S1.w_if(ok, z);
     const uint32_t b = S1.bin<kNB>(z);
-    if (ok && b < kNB - 1) {
+    const bool shallow = ok && b < kNB - 1;
+    if (shallow) {
       __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    gather(gs, ng, shallow, i, c.e_begin);
     const bool deep = ok && b == kNB - 1;
     dw += deep ? w : 0.0;
     dn += deep ? 1u : 0u;
     z0 += w;
   });
   add_deep(L.h.hw, L.h.hc, dw, dn);
+  flush_gather<DT>(gs, ng, xr, c.e_begin, a, row, seg);
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
@@ -880,11 +963,13 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   take_hist(L.h.hw, L.h.hc, gw, gc);
   const double t = (double)a.top_p * Z0, g = kGuard * Z0;
   pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, t - g, t + g);
+  const bool listed = gathered_all(r, a, row) && r.b_hi < (uint32_t)kNB - 1;
   if (tid == 0) {
     NucPlan& p = a.plan[row];
     p.b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the top of the row when it fits
     p.b_hi = r.b_hi;
     p.z0 = Z0;
+    p.listed = listed ? 1u : 0u;
     p.state = 0u;
   }
 }
@@ -923,7 +1008,7 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   // At T = 1 the tempered weights are the untempered ones; floor mode draws
   // nothing and needs no tempered guide.
   const bool same_t = a.T == 1.0f, want_guide = a.out_kfl == nullptr;
-  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
+  for_each_cand<DT, VEC>(a, row, seg, a.plan[row].listed != 0u, xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
     const float z = __uint_as_float(bits);
     const uint64_t K = comp_key(bits, (uint32_t)i);
     const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
@@ -1037,7 +1122,7 @@ __global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
   uint64_t* lkey = a.lkey + row * kCapW;
   uint32_t* lbits = a.lbits + row * kCapW;
   double A2 = 0.0;
-  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
+  for_each_cand<DT, VEC>(a, row, seg, p.listed != 0u, xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
     const float z = __uint_as_float(bits);
     const uint64_t K = comp_key(bits, (uint32_t)i);
     // kept candidates above the cut window
@@ -1187,6 +1272,7 @@ __global__ __launch_bounds__(NT) void typ_moments_kernel(NucArgs a) {
     j.span_all = fmax(fmax(c.m - cen, cen - lo), 1e-30) * (1.0 + 1e-6);
     j.span = typ_span(j, (double)a.typical_p, a.V, c.m);
     j.tot_known = Z0;  // the typical order's weights are these: the guide pass needs no exact sums
+    j.listed = 0u;
     j.frac = (double)a.typical_p;
     j.kfloor = 0ull;
     j.kT = 0ull;
@@ -1239,11 +1325,17 @@ __device__ void typ_advance(const NucArgs& a, int64_t row, SelJob& j) {
   }
 }
 
+// The guide pass of a selection.  The first selection (the typical cut) also
+// gathers its candidates within the crossing bound per segment; when they all
+// fit and its window stays short of the last bin, they hold every candidate
+// of the later selections too (the typical set precedes the selected
+// candidate in the typical order), and the later passes visit only them.
 template <typename DT, bool VEC>
 __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   __shared__ SelShared sh;
   __shared__ NucRed r;
   __shared__ NucLds L;
+  __shared__ GatherStage gs;
   __shared__ double e2[64];
   const int tid = threadIdx.x;
   const Item it = work_item(a.S);
@@ -1261,26 +1353,28 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   }
   __syncthreads();
   double t = 0.0, dw = 0.0;
-  uint32_t dn = 0;
-  const bool known = jb.tot_known > 0.0;
+  uint32_t dn = 0, ng = 0;
+  const bool known = jb.tot_known > 0.0, first = jb.step == 1, listed = !first && jb.listed != 0u;
   by_order(S.order, [&](auto ord) {
     if (known) {
       // the exact total is known: float32 guide weights, and none for the
       // candidates past the crossing bound (the last bin needs only their count)
-      for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+      for_each_cand<DT, VEC>(a, row, seg, listed, xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
         uint64_t K;
         uint32_t b;
         const bool ok = S.look<kNB, decltype(ord)::value>(bits, (uint32_t)i, K, b);
-        if (ok && b < kNB - 1) {
+        const bool shallow = ok && b < kNB - 1;
+        if (shallow) {
           __hip_atomic_fetch_add(&L.h.hw[b], (double)S.gw(__uint_as_float(bits)), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
           __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        if (first) gather(gs, ng, shallow, i, e_begin);
         dn += ok && b == kNB - 1 ? 1u : 0u;
       });
       return;
     }
-    for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+    for_each_cand<DT, VEC>(a, row, seg, listed, xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
       uint64_t K;
       uint32_t b;
       const bool ok = S.look<kNB, decltype(ord)::value>(bits, (uint32_t)i, K, b);
@@ -1295,9 +1389,11 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
         }
         t += w;
       }
+      if (first) gather(gs, ng, ok && b < kNB - 1, i, e_begin);
     });
   });
   add_deep(L.h.hw, L.h.hc, dw, dn);
+  if (first) flush_gather<DT>(gs, ng, xr, e_begin, a, row, seg);
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
@@ -1311,11 +1407,13 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   take_hist(L.h.hw, L.h.hc, gw, gc);
   const double tg = jb.frac * tot, g = kGuard * tot;
   pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, tg - g, tg + g);
+  const bool now_listed = first ? gathered_all(r, a, row) && r.b_hi < (uint32_t)kNB - 1 : jb.listed != 0u;
   if (tid == 0) {
     SelJob& j = a.jobs[row];
     j.b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the front of the order when it fits
     j.b_hi = r.b_hi;
     j.tot = tot;
+    j.listed = now_listed ? 1u : 0u;
     j.state = 2;
   }
 }
@@ -1343,7 +1441,7 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
   uint32_t* lbits = a.lbits + row * kCapW;
   double A = 0.0, zb = -__builtin_inf();  // mass and largest value before the window
   by_order(S.order, [&](auto ord) {
-    for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
+    for_each_cand<DT, VEC>(a, row, seg, jb.listed != 0u, xr, e_begin, e_end, [&](uint32_t bits, int64_t i) {
       uint64_t K;
       uint32_t b;
       const bool ok = S.look<kNB, decltype(ord)::value>(bits, (uint32_t)i, K, b);

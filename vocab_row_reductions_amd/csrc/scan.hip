@@ -237,17 +237,21 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
     lse_check(g, tmax);
     fold();
   }
-  // the row's last partial tile: one group per lane at a time (pads -inf)
-  for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
-    Group g1[1];
-    load_tile<DT, 1, VEC>(g1, xr, t0, e_full);
-    if constexpr (EXCL) exclude(g1, (uint32_t)t0, (uint32_t)(NT * E));
+  // the segment's last partial tile, its loads issued together (groups past
+  // e_full read as -inf)
+  if (e_tiles < e_full) {
+    Group g[SG];
+    load_tile<DT, SG, VEC>(g, xr, e_tiles, e_full);
+    if constexpr (EXCL) exclude(g, (uint32_t)e_tiles, (uint32_t)(e_full - e_tiles));
     if (first) {
-      seed(g1);
+      seed(g);
       first = false;
     }
-    const float m1 = group(g1[0], (uint32_t)t0 + (uint32_t)tid * E);
-    lse_check(g1, m1);
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < SG; ++j) tmax = fmax_nan(tmax, group(g[j], (uint32_t)e_tiles + (uint32_t)(j * NT + tid) * E));
+    if constexpr (WANT_LSE) asm volatile("" ::"v"(ls), "v"(tmax));
+    lse_check(g, tmax);
     fold();
   }
   // the row's last few elements (fewer than one group): one lane, after
