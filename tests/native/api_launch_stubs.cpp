@@ -182,6 +182,9 @@ static void check_nuc(const char* what, const NucArgs& a, bool full) {
   in_ws(what, "lkey", a.lkey, R * kNucCap);
   in_ws(what, "lbits", a.lbits, R * kNucCap);
   in_ws(what, "lcnt", a.lcnt, R);
+  in_ws(what, "gcnt", a.gcnt, n);
+  in_ws(what, "gbits", a.gbits, n * kGatherCap);
+  in_ws(what, "gidx", a.gidx, n * kGatherCap);
   in_ws(what, "p_a", a.p_a, n);
   in_ws(what, "p_at", a.p_at, n);
   in_ws(what, "p_a2", a.p_a2, n);

@@ -204,6 +204,7 @@ struct NucPlan {                   // per row, written by the last workgroup of 
   uint32_t b_lo, b_hi;             // cut window (untempered guide bins)
   uint32_t c_lo, c_hi;             // draw window (tempered guide bins, above the cut window)
   uint32_t listed;                 // 1: every candidate the later passes reach is in the gathered list
+  uint32_t h0top, hTtop;           // highest non-empty bins (short of the last) of the row's two histograms
   double z0;                       // exact candidate mass, untempered
   double wt;                       // exact kept mass, tempered
   uint64_t kfin;                   // smallest kept composite key
@@ -223,6 +224,7 @@ struct SelJob {
   uint32_t b_lo, b_hi;   // window (guide bins)
   uint32_t bits;         // selected candidate's element bits
   uint32_t listed;       // 1: every candidate of this and the later selections is in the gathered list
+  uint32_t htop, pad;    // highest non-empty bin (short of the last) of the row's histogram
   uint64_t key;          // selected candidate's order key
   double tot;            // exact total weight of the candidates
   double tot_known;      // > 0: that total, known before the guide pass (no exact sums there)

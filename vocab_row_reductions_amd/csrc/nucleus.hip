@@ -395,8 +395,9 @@ __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int n
 // t < c (strict = true); none: the last with a positive weight (or the last).
 // *cum (if given) gets the cumulative mass through the chosen candidate.  Up
 // to 64 candidates: one per lane of wave 0, prefixed by shuffles; more: each
-// thread sums a run of kRun candidates in order, the runs are prefixed in a
-// fixed order, and every thread walks its own run.  All threads call.
+// thread sums a run of ceil(n / NT) candidates in order, the runs are
+// prefixed in a fixed order, and every thread walks its own run.  All threads
+// call.
 __device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const NucSet& S, double A, double t,
                                 bool strict, double* cum = nullptr) {
   if (n <= 64) {
@@ -424,12 +425,14 @@ __device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, con
     if (cum) *cum = r.csel;
     return r.ru[0];
   }
-  const uint32_t j0 = threadIdx.x * kRun;
+  const uint32_t R = (n + NT - 1) / NT;  // (<= kRun) candidates per thread
+  const uint32_t j0 = threadIdx.x * R;
   double wl[kRun];
   double run = 0.0;
 #pragma unroll
   for (uint32_t q = 0; q < kRun; ++q) {
-    wl[q] = (j0 + q < n) ? S.w(__uint_as_float(bits[j0 + q])) : 0.0;
+    wl[q] = 0.0;
+    if (q < R && j0 + q < n) wl[q] = S.w(__uint_as_float(bits[j0 + q]));
     run += wl[q];
   }
   double c = A + block_excl_scan_f64(r, run);
@@ -438,7 +441,7 @@ __device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, con
   double cfirst = 0.0, clast = 0.0, cend = 0.0;
 #pragma unroll
   for (uint32_t q = 0; q < kRun; ++q) {
-    if (j0 + q < n) {
+    if (q < R && j0 + q < n) {
       c += wl[q];
       if (wl[q] > 0.0) {
         lastpos = (int)(j0 + q);
@@ -457,11 +460,77 @@ __device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, con
   if (cum) {
     // the owner of the chosen candidate's run publishes its cumulative mass
     __syncthreads();
-    if (j >= j0 && j < j0 + kRun) r.csel = j == first ? cfirst : j == (uint32_t)lastpos ? clast : cend;
+    if (j >= j0 && j < j0 + R) r.csel = j == first ? cfirst : j == (uint32_t)lastpos ? clast : cend;
     __syncthreads();
     *cum = r.csel;
   }
   return j;
+}
+
+// ---------------------------------------------------------------- one-wave windows
+// A window of up to 64 candidates, one per lane of the calling wave (lanes
+// from n on hold nothing), put in (key desc) order: each lane's rank is the
+// number of larger keys (keys are distinct), then the lanes trade places
+// through the wave's own LDS scratch (sk, sb: 64 entries).
+__device__ __forceinline__ uint64_t lane_key(uint64_t v, uint32_t j) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), (int)j) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, (int)j);
+}
+__device__ __forceinline__ void wave_sort(uint64_t& key, uint32_t& bits, uint32_t n, uint64_t* sk, uint32_t* sb) {
+  const uint32_t lane = threadIdx.x & 63;
+  uint32_t rank = 0;
+  for (uint32_t j = 0; j < n; ++j) rank += lane_key(key, j) > key ? 1u : 0u;
+  if (lane < n) {
+    sk[rank] = key;
+    sb[rank] = bits;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  key = lane < n ? sk[lane] : 0ull;
+  bits = lane < n ? sb[lane] : 0u;
+}
+// Inclusive prefix sum over the wave in lane order (fixed order).
+__device__ __forceinline__ double wave_incl_f64(double v) {
+  const int lane = threadIdx.x & 63;
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+// The first lane (< n) whose flag is set; else the last (< n) with a positive
+// weight; else n - 1 (0 for none): walk_sorted's choice over one wave.
+__device__ __forceinline__ uint32_t wave_pick(bool hit, bool pos, uint32_t n) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t h = __ballot(hit && lane < n), p = __ballot(pos && lane < n);
+  return h ? (uint32_t)__builtin_ctzll(h) : p ? (uint32_t)(63 - __builtin_clzll(p)) : (n > 0 ? n - 1 : 0u);
+}
+
+// The window's n candidates in LDS put in (key desc) order.  Up to NT of
+// them: each thread ranks its own candidate against all n (keys are distinct;
+// broadcast reads) and moves it to its place through scratch past the
+// window's first half; more: the bitonic network.
+__device__ __forceinline__ void sort_window(uint64_t* key, uint32_t* bits, uint32_t n) {
+  if (n > (uint32_t)NT) {
+    sort_desc<kCapW>(key, bits, n);
+    return;
+  }
+  const uint32_t t = threadIdx.x;
+  uint64_t* sk = key + kCapW / 2;
+  uint32_t* sb = bits + kCapW / 2;
+  const uint64_t mine = t < n ? key[t] : 0ull;
+  const uint32_t mb = t < n ? bits[t] : 0u;
+  uint32_t rank = 0;
+  for (uint32_t j = 0; j < n; ++j) rank += key[j] > mine ? 1u : 0u;
+  if (t < n) {
+    sk[rank] = mine;
+    sb[rank] = mb;
+  }
+  __syncthreads();
+  if (t < n) {
+    key[t] = sk[t];
+    bits[t] = sb[t];
+  }
+  __syncthreads();
 }
 
 // Fixed-order sum of S.w over the first n sorted candidates.
@@ -475,9 +544,10 @@ __device__ double sum_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const 
     __syncthreads();
     return r.csel;
   }
-  const uint32_t j0 = threadIdx.x * kRun;
+  const uint32_t R = (n + NT - 1) / NT;  // (<= kRun) candidates per thread
+  const uint32_t j0 = threadIdx.x * R;
   double run = 0.0;
-  for (uint32_t q = 0; q < kRun; ++q)
+  for (uint32_t q = 0; q < R; ++q)
     if (j0 + q < n) run += S.w(__uint_as_float(bits[j0 + q]));
   return nuc_sum(r, run, 0);
 }
@@ -696,21 +766,29 @@ __device__ __forceinline__ void add_deep(double* hw, uint32_t* hc, double w, uin
   }
 }
 
-// LDS histogram -> the row's global histogram (device-scope atomics that
-// return, so they are complete when the workgroup arrives at its ticket).
-__device__ __forceinline__ void flush_hist(const double* hw, const uint32_t* hc, double* gw, uint32_t* gc) {
+// LDS histogram -> the row's global histogram (device-scope atomics,
+// complete when the workgroup arrives at its ticket).  The highest non-empty
+// bin short of the last goes to *top (an atomic max per wave), so that the
+// row's last workgroup clears only the bins up to it.
+__device__ __forceinline__ void flush_hist(const double* hw, const uint32_t* hc, double* gw, uint32_t* gc,
+                                           uint32_t* top) {
+  int hi = -1;
   for (int b = threadIdx.x; b < kNB; b += NT) {
     const uint32_t c = hc[b];
     if (c) {
       (void)__hip_atomic_fetch_add(&gw[b], hw[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       (void)__hip_atomic_fetch_add(&gc[b], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (b < kNB - 1) hi = b;
     }
   }
+  for (int d = 1; d < 64; d <<= 1) hi = max(hi, __shfl_xor(hi, d));
+  if ((threadIdx.x & 63) == 0 && hi >= 0)
+    (void)__hip_atomic_fetch_max(top, (uint32_t)hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The row's global histogram -> LDS, leaving zeros behind.  Each thread
-// issues all of its loads before it waits for any.
-__device__ __forceinline__ void take_hist(double* hw, uint32_t* hc, double* gw, uint32_t* gc) {
+// The row's global histogram -> LDS.  Each thread issues all of its loads
+// before it waits for any.  (clear_hist zeroes it afterwards.)
+__device__ __forceinline__ void take_hist(double* hw, uint32_t* hc, const double* gw, const uint32_t* gc) {
   constexpr int Q = kNB / NT;
   __syncthreads();
   double v[Q];
@@ -725,8 +803,57 @@ __device__ __forceinline__ void take_hist(double* hw, uint32_t* hc, double* gw, 
     const int b = q * NT + threadIdx.x;
     hw[b] = v[q];
     hc[b] = c[q];
-    st_dev(&gw[b], 0.0);
-    st_dev(&gc[b], 0u);
+  }
+  __syncthreads();
+}
+
+// The same in two halves, so that a tail can issue these loads together with
+// others: load_hist into registers, put_hist into LDS (then a barrier).
+constexpr int kHQ = kNB / NT;
+__device__ __forceinline__ void load_hist(const double* gw, const uint32_t* gc, double (&v)[kHQ],
+                                          uint32_t (&c)[kHQ]) {
+#pragma unroll
+  for (int q = 0; q < kHQ; ++q) {
+    v[q] = ld_dev(&gw[q * NT + threadIdx.x]);
+    c[q] = ld_dev(&gc[q * NT + threadIdx.x]);
+  }
+}
+__device__ __forceinline__ void put_hist(double* hw, uint32_t* hc, const double (&v)[kHQ], const uint32_t (&c)[kHQ]) {
+#pragma unroll
+  for (int q = 0; q < kHQ; ++q) {
+    hw[q * NT + threadIdx.x] = v[q];
+    hc[q * NT + threadIdx.x] = c[q];
+  }
+  __syncthreads();
+}
+
+// The row's n (<= kCapW) window candidates -> LDS, all loads issued first;
+// (k0, b0) is this thread's first candidate, loaded earlier (before n was
+// known, together with the tail's other loads).
+__device__ __forceinline__ void take_list_pf(uint64_t* key, uint32_t* bits, const uint64_t* lkey,
+                                             const uint32_t* lbits, uint32_t n, uint64_t k0, uint32_t b0) {
+  constexpr int Q = kCapW / NT;
+  uint64_t k[Q];
+  uint32_t b[Q];
+#pragma unroll
+  for (int q = 1; q < Q; ++q) {
+    const uint32_t j = q * NT + threadIdx.x;
+    if (j < n) {
+      k[q] = ld_dev(&lkey[j]);
+      b[q] = ld_dev(&lbits[j]);
+    }
+  }
+  if (threadIdx.x < n) {
+    key[threadIdx.x] = k0;
+    bits[threadIdx.x] = b0;
+  }
+#pragma unroll
+  for (int q = 1; q < Q; ++q) {
+    const uint32_t j = q * NT + threadIdx.x;
+    if (j < n) {
+      key[j] = k[q];
+      bits[j] = b[q];
+    }
   }
   __syncthreads();
 }
@@ -756,10 +883,19 @@ __device__ __forceinline__ void take_list(uint64_t* key, uint32_t* bits, const u
   __syncthreads();
 }
 
-__device__ __forceinline__ void zero_hist(double* gw, uint32_t* gc) {
-  for (int b = threadIdx.x; b < kNB; b += NT) {
+// The row's global histogram back to zero: the bins up to *top and the last
+// (no others were written), and *top itself.  Called where no barrier
+// follows, so no wave waits for these stores.
+__device__ __forceinline__ void clear_hist(double* gw, uint32_t* gc, uint32_t* top) {
+  const uint32_t t = ld_dev(top);
+  for (uint32_t b = threadIdx.x; b <= t; b += NT) {
     st_dev(&gw[b], 0.0);
     st_dev(&gc[b], 0u);
+  }
+  if (threadIdx.x == 0) {
+    st_dev(&gw[kNB - 1], 0.0);
+    st_dev(&gc[kNB - 1], 0u);
+    st_dev(top, 0u);
   }
 }
 
@@ -848,13 +984,6 @@ __device__ __forceinline__ void flush_gather(GatherStage& st, uint32_t cnt, cons
       gi[off[w] + j] = (uint32_t)i;
     }
   }
-}
-
-// Whether every segment's gathered candidates fit its slot (the row's last
-// workgroup; all threads call).
-__device__ __forceinline__ bool gathered_all(NucRed& r, const NucArgs& a, int64_t row) {
-  const int v = threadIdx.x < a.S ? (int)ld_dev(&a.gcnt[row * a.S + threadIdx.x]) : 0;
-  return block_max_i32(r, v) <= kGatherCap;
 }
 
 // The elements a pass visits in its (row, segment): the segment itself, or,
@@ -955,15 +1084,23 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
-  flush_hist(L.h.hw, L.h.hc, gw, gc);
+  flush_hist(L.h.hw, L.h.hc, gw, gc, &a.plan[row].h0top);
   z0 = nuc_sum(r, z0, 0);
   if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], z0);
   if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
-  const double Z0 = merge_sum(sh, a.p_z0 + row * a.S, a.S);
-  take_hist(L.h.hw, L.h.hc, gw, gc);
+  // ---- the row's last workgroup: its global loads issued together
+  const int64_t p0 = row * a.S;
+  const double vz = tid < a.S ? ld_dev(&a.p_z0[p0 + tid]) : 0.0;
+  const int vg = tid < a.S ? (int)ld_dev(&a.gcnt[p0 + tid]) : 0;
+  double hv[kHQ];
+  uint32_t hcv[kHQ];
+  load_hist(gw, gc, hv, hcv);
+  const double Z0 = block_sum_f64(sh, vz);
+  const bool fit = block_max_i32(r, vg) <= kGatherCap;
+  put_hist(L.h.hw, L.h.hc, hv, hcv);
   const double t = (double)a.top_p * Z0, g = kGuard * Z0;
   pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, t - g, t + g);
-  const bool listed = gathered_all(r, a, row) && r.b_hi < (uint32_t)kNB - 1;
+  const bool listed = fit && r.b_hi < (uint32_t)kNB - 1;
   if (tid == 0) {
     NucPlan& p = a.plan[row];
     p.b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the top of the row when it fits
@@ -972,6 +1109,7 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
     p.listed = listed ? 1u : 0u;
     p.state = 0u;
   }
+  clear_hist(gw, gc, &a.plan[row].h0top);
 }
 
 // Pass 2: the exact mass above the cut window and the window's candidates; the
@@ -1032,7 +1170,8 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   __syncthreads();
   double* gw = a.hTw + row * kNB;
   uint32_t* gc = a.hTc + row * kNB;
-  flush_hist(L.h.hw, L.h.hc, gw, gc);
+  uint32_t* htop = &a.plan[row].hTtop;
+  flush_hist(L.h.hw, L.h.hc, gw, gc, htop);
   A = nuc_sum(r, A, 0);
   AT = nuc_sum(r, AT, 1);
   if (tid == 0) {
@@ -1040,40 +1179,110 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
     st_dev(&a.p_at[row * a.S + seg], AT);
   }
   if (!last_of_row(sh, a.tickets + row * 3 + 1, (uint32_t)a.S)) return;
-  // ---- the row's last workgroup
-  const double Atot = merge_sum(sh, a.p_a + row * a.S, a.S);
-  const double ATtot = merge_sum(sh, a.p_at + row * a.S, a.S);
+  // ---- the row's last workgroup: its first global loads issued together
+  const int64_t p0 = row * a.S;
+  const double va = tid < a.S ? ld_dev(&a.p_a[p0 + tid]) : 0.0;
+  const double vat = tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : 0.0;
   const uint32_t n = ld_dev(&a.lcnt[row]);
-  __syncthreads();
+  const uint64_t k0 = ld_dev(&lkey[tid]);
+  const uint32_t b0 = ld_dev(&lbits[tid]);
+  const double Atot = block_sum_f64(sh, va);
+  const double ATtot = block_sum_f64(sh, vat);
   if (tid == 0) st_dev(&a.lcnt[row], 0u);
   if (n > kCapW) {
     // the window is too crowded for LDS: the row is left to nuc_alone
-    zero_hist(gw, gc);
     if (tid == 0) a.plan[row].state = 3u;
+    clear_hist(gw, gc, htop);
     return;
   }
-  take_list(L.w.key, L.w.bits, lkey, lbits, n);
-  sort_desc<kCapW>(L.w.key, L.w.bits, n);
-  // the cut, then min_p: the kept candidates of the window are its first nk
-  const uint32_t jc = walk_sorted(r, L.w.bits, n, S1, Atot, (double)a.top_p * z0, false);
-  const uint64_t kfin = max(L.w.key[jc], c.kmp);
-  uint32_t nk = 0;
-  for (uint32_t j = tid; j < n; j += NT) nk += L.w.key[j] >= kfin ? 1u : 0u;
-  nk = block_sum_u32(r, nk);
-  const NucSet S2 = value_set(c.m, c.thr, kfin, (double)a.T, e2);
-  const double WT = ATtot + sum_sorted(r, L.w.bits, nk, S2);
-  if (a.out_kfl) {  // floor mode: the kept set, nothing drawn
-    zero_hist(gw, gc);
-    if (tid == 0) {
-      a.out_kfl[row] = kfin;
-      a.out_lse_f[row] = c.m / (double)a.T + log(WT);
-      a.plan[row].state = 2u;
+  const double tcut = (double)a.top_p * z0;
+  uint64_t kfin;
+  double WT;
+  if (n <= 64) {
+    // a small window: the cut, min_p and the draw by wave 0 alone, the window
+    // in its lanes (no barriers); the others wait for the outcome
+    if (tid < 64) {
+      uint64_t key = (uint32_t)tid < n ? k0 : 0ull;
+      uint32_t bits = (uint32_t)tid < n ? b0 : 0u;
+      wave_sort(key, bits, n, L.w.key, L.w.bits);
+      const bool live = (uint32_t)tid < n;
+      const double w1 = live ? S1.w(__uint_as_float(bits)) : 0.0;
+      const uint32_t jc = wave_pick(Atot + wave_incl_f64(w1) >= tcut, w1 > 0.0, n);
+      const uint64_t kf = max(lane_key(key, jc), c.kmp);
+      const uint32_t nk = (uint32_t)__builtin_popcountll(__ballot(live && key >= kf));
+      const NucSet S2 = value_set(c.m, c.thr, kf, (double)a.T, e2);
+      const double w2 = (uint32_t)tid < nk ? S2.w(__uint_as_float(bits)) : 0.0;
+      const double wt = ATtot + wave_sum_f64(w2);
+      uint32_t above = 0u;
+      if (a.out_kfl) {  // floor mode: the kept set, nothing drawn
+        if (tid == 0) {
+          a.out_kfl[row] = kf;
+          a.out_lse_f[row] = c.m / (double)a.T + log(wt);
+          a.plan[row].state = 2u;
+        }
+      } else {
+        const double t2 = (double)a.u[row] * wt;
+        if (t2 < ATtot) {
+          above = 1u;
+        } else {
+          const uint32_t jd = wave_pick(t2 < ATtot + wave_incl_f64(w2), w2 > 0.0, nk);
+          if ((uint32_t)tid == jd) {
+            a.out_token[row] = ~(uint32_t)key;
+            if (a.out_logp)
+              a.out_logp[row] = (float)(((double)__uint_as_float(bits) - c.m) / (double)a.T - log(wt));
+            a.plan[row].state = 2u;
+          }
+        }
+      }
+      if (tid == 0) {
+        r.ru[0] = above;
+        r.ksel = kf;
+        r.csel = wt;
+      }
     }
-    return;
+    __syncthreads();
+    if (r.ru[0] == 0u) {
+      clear_hist(gw, gc, htop);
+      return;
+    }
+    kfin = r.ksel;
+    WT = r.csel;
+  } else {
+    take_list_pf(L.w.key, L.w.bits, lkey, lbits, n, k0, b0);
+    sort_window(L.w.key, L.w.bits, n);
+    // the cut, then min_p: the kept candidates of the window are its first nk
+    const uint32_t jc = walk_sorted(r, L.w.bits, n, S1, Atot, tcut, false);
+    kfin = max(L.w.key[jc], c.kmp);
+    uint32_t nk = 0;
+    for (uint32_t j = tid; j < n; j += NT) nk += L.w.key[j] >= kfin ? 1u : 0u;
+    nk = block_sum_u32(r, nk);
+    const NucSet S2 = value_set(c.m, c.thr, kfin, (double)a.T, e2);
+    WT = ATtot + sum_sorted(r, L.w.bits, nk, S2);
+    if (a.out_kfl) {  // floor mode: the kept set, nothing drawn
+      if (tid == 0) {
+        a.out_kfl[row] = kfin;
+        a.out_lse_f[row] = c.m / (double)a.T + log(WT);
+        a.plan[row].state = 2u;
+      }
+      clear_hist(gw, gc, htop);
+      return;
+    }
+    const double t2 = (double)a.u[row] * WT;
+    if (t2 >= ATtot) {
+      const uint32_t jd = walk_sorted(r, L.w.bits, nk, S2, ATtot, t2, true);
+      if (tid == 0) {
+        a.out_token[row] = ~(uint32_t)L.w.key[jd];
+        if (a.out_logp)
+          a.out_logp[row] = (float)(((double)__uint_as_float(L.w.bits[jd]) - c.m) / (double)a.T - log(WT));
+        a.plan[row].state = 2u;
+      }
+      clear_hist(gw, gc, htop);
+      return;
+    }
   }
-  const double t2 = (double)a.u[row] * WT;
-  if (t2 < ATtot) {
+  {
     // the draw falls above the window: place the draw window
+    const double t2 = (double)a.u[row] * WT;
     take_hist(L.h.hw, L.h.hc, gw, gc);
     pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, t2 - kGuard * WT, t2 + kGuard * WT);
     if (tid == 0) {
@@ -1084,15 +1293,7 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
       q.kfin = kfin;
       q.state = 1u;
     }
-    return;
-  }
-  zero_hist(gw, gc);
-  const uint32_t jd = walk_sorted(r, L.w.bits, nk, S2, ATtot, t2, true);
-  if (tid == 0) {
-    a.out_token[row] = ~(uint32_t)L.w.key[jd];
-    if (a.out_logp)
-      a.out_logp[row] = (float)(((double)__uint_as_float(L.w.bits[jd]) - c.m) / (double)a.T - log(WT));
-    a.plan[row].state = 2u;
+    clear_hist(gw, gc, htop);
   }
 }
 
@@ -1145,7 +1346,7 @@ __global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
     return;
   }
   take_list(L.w.key, L.w.bits, lkey, lbits, n);
-  sort_desc<kCapW>(L.w.key, L.w.bits, n);
+  sort_window(L.w.key, L.w.bits, n);
   const uint32_t jd = walk_sorted(r, L.w.bits, n, S2, A2tot, (double)a.u[row] * p.wt, true);
   if (tid == 0) {
     a.out_token[row] = ~(uint32_t)L.w.key[jd];
@@ -1397,17 +1598,26 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
-  flush_hist(L.h.hw, L.h.hc, gw, gc);
+  uint32_t* htop = &a.jobs[row].htop;
+  flush_hist(L.h.hw, L.h.hc, gw, gc, htop);
   if (!known) {
     t = nuc_sum(r, t, 0);
     if (tid == 0) st_dev(&a.p_z0[row * a.S + seg], t);
   }
   if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
-  const double tot = known ? jb.tot_known : merge_sum(sh, a.p_z0 + row * a.S, a.S);
-  take_hist(L.h.hw, L.h.hc, gw, gc);
+  // ---- the row's last workgroup: its global loads issued together
+  const int64_t p0 = row * a.S;
+  const double vt = !known && tid < a.S ? ld_dev(&a.p_z0[p0 + tid]) : 0.0;
+  const int vg = first && tid < a.S ? (int)ld_dev(&a.gcnt[p0 + tid]) : 0;
+  double hv[kHQ];
+  uint32_t hcv[kHQ];
+  load_hist(gw, gc, hv, hcv);
+  const double tot = known ? jb.tot_known : block_sum_f64(sh, vt);
+  const bool fit = block_max_i32(r, vg) <= kGatherCap;
+  put_hist(L.h.hw, L.h.hc, hv, hcv);
   const double tg = jb.frac * tot, g = kGuard * tot;
   pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, tg - g, tg + g);
-  const bool now_listed = first ? gathered_all(r, a, row) && r.b_hi < (uint32_t)kNB - 1 : jb.listed != 0u;
+  const bool now_listed = first ? fit && r.b_hi < (uint32_t)kNB - 1 : jb.listed != 0u;
   if (tid == 0) {
     SelJob& j = a.jobs[row];
     j.b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the front of the order when it fits
@@ -1416,6 +1626,7 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
     j.listed = now_listed ? 1u : 0u;
     j.state = 2;
   }
+  clear_hist(gw, gc, htop);
 }
 
 template <typename DT, bool VEC>
@@ -1464,18 +1675,46 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
     st_dev(&a.p_at[p0 + seg], zb);
   }
   if (!last_of_row(sh, a.tickets + row * 3, (uint32_t)a.S)) return;
-  // ---- the row's last workgroup
-  const double Atot = merge_sum(sh, a.p_a + p0, a.S);
-  const double zbt = block_ext_f64<true>(r, tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : -__builtin_inf());
+  // ---- the row's last workgroup: its first global loads issued together
+  const double va = tid < a.S ? ld_dev(&a.p_a[p0 + tid]) : 0.0;
+  const double vb = tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : -__builtin_inf();
   const uint32_t n = ld_dev(&a.lcnt[row]);
-  __syncthreads();
+  const uint64_t k0 = ld_dev(&lkey[tid]);
+  const uint32_t b0 = ld_dev(&lbits[tid]);
+  const double Atot = block_sum_f64(sh, va);
+  const double zbt = block_ext_f64<true>(r, vb);
   if (tid == 0) st_dev(&a.lcnt[row], 0u);
   if (n > kCapW) {
     if (tid == 0) a.jobs[row].state = 3;  // too crowded for LDS: left to sel_alone
     return;
   }
-  take_list(L.w.key, L.w.bits, lkey, lbits, n);
-  sort_desc<kCapW>(L.w.key, L.w.bits, n);
+  if (n <= 64) {
+    // a small window: the selection by wave 0 alone, the window in its lanes
+    if (tid < 64) {
+      uint64_t key = (uint32_t)tid < n ? k0 : 0ull;
+      uint32_t bits = (uint32_t)tid < n ? b0 : 0u;
+      wave_sort(key, bits, n, L.w.key, L.w.bits);
+      const bool live = (uint32_t)tid < n;
+      const double w = live ? S.w(__uint_as_float(bits)) : 0.0;
+      const double cw = Atot + wave_incl_f64(w), tg = jb.frac * jb.tot;
+      const uint32_t j = wave_pick(jb.strict ? (tg < cw) : (cw >= tg), w > 0.0, n);
+      // the largest value among the window's candidates up to the selected one
+      double zl = live && (uint32_t)tid <= j ? (double)__uint_as_float(bits) : -__builtin_inf();
+      for (int d = 1; d < 64; d <<= 1) zl = fmax(zl, __shfl_xor(zl, d));
+      if ((uint32_t)tid == j) {
+        SelJob& o = a.jobs[row];
+        o.key = key;
+        o.bits = bits;
+        o.zmax = fmax(zbt, zl);
+        o.cum = cw;
+        o.state = 4;
+        typ_advance(a, row, o);
+      }
+    }
+    return;
+  }
+  take_list_pf(L.w.key, L.w.bits, lkey, lbits, n, k0, b0);
+  sort_window(L.w.key, L.w.bits, n);
   double cum = 0.0;
   const uint32_t j = walk_sorted(r, L.w.bits, n, S, Atot, jb.frac * jb.tot, jb.strict != 0, &cum);
   double zl = -__builtin_inf();  // the window's candidates up to the selected one
