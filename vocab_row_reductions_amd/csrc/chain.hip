@@ -77,11 +77,18 @@ __global__ __launch_bounds__(NT) void moments_kernel(MomArgs a) {
       st_dev(&a.p_m2[row * a.S + seg], v.m2);
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
+    // the segments' partials loaded at once (one per thread), then merged in
+    // segment order by one thread
+    __shared__ double pn[kMaxSegments], pmean[kMaxSegments], pm2[kMaxSegments];
+    if (tid < a.S) {
+      pn[tid] = ld_dev(&a.p_n[row * a.S + tid]);
+      pmean[tid] = ld_dev(&a.p_mean[row * a.S + tid]);
+      pm2[tid] = ld_dev(&a.p_m2[row * a.S + tid]);
+    }
+    __syncthreads();
     if (tid == 0) {
       Mom w{0.0, 0.0, 0.0};
-      for (int sg = 0; sg < a.S; ++sg)
-        w = mom_merge(w, Mom{ld_dev(&a.p_n[row * a.S + sg]), ld_dev(&a.p_mean[row * a.S + sg]),
-                             ld_dev(&a.p_m2[row * a.S + sg])});
+      for (int sg = 0; sg < a.S; ++sg) w = mom_merge(w, Mom{pn[sg], pmean[sg], pm2[sg]});
       v = w;
     }
   }

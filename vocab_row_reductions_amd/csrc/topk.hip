@@ -300,10 +300,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
     const int64_t s0 = row * a.S;
-    // record counts of all segments at once, then their offsets (wave 0)
-    if (tid < a.S) sh.hist[tid] = ld_dev(&a.rec_cnt[s0 + tid]);
+    // record counts of all segments at once (in flight with the (max, sum)
+    // partials), then their offsets (wave 0)
+    const uint32_t cnt_t = tid < a.S ? ld_dev(&a.rec_cnt[s0 + tid]) : 0u;
     uint64_t unusedP;
     merge_key_lse(sh, nullptr, a.p_m + s0, a.p_s + s0, a.S, c, unusedP, r);
+    if (tid < a.S) sh.hist[tid] = cnt_t;
+    __syncthreads();
     if (tid < 64) {
       uint32_t cv[4], loc = 0;
 #pragma unroll
@@ -321,12 +324,35 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
     __syncthreads();
     n = sh.cnt2;
-    for (int sg = 0; sg < a.S; ++sg) {
-      const uint32_t off = sh.hist[sg];
-      const uint32_t cs = (sg + 1 < a.S ? sh.hist[sg + 1] : n) - off;
-      for (uint32_t i = tid; i < cs; i += NT) {
-        s_key[off + i] = ld_dev(&a.rec_key[(s0 + sg) * k + i]);
-        s_bits[off + i] = ld_dev(&a.rec_bits[(s0 + sg) * k + i]);
+    // every record of the row in rounds of loads: record f of the
+    // concatenation is record f - off[sg] of segment sg (sg found by a binary
+    // search of the offsets), kMergeQ per thread in flight at once
+    constexpr int kMergeQ = 4;
+    for (uint32_t f0 = 0; f0 < n; f0 += NT * kMergeQ) {
+      uint64_t v[kMergeQ];
+      uint32_t vb[kMergeQ];
+#pragma unroll
+      for (int q = 0; q < kMergeQ; ++q) {
+        const uint32_t f = f0 + (uint32_t)(q * NT) + tid;
+        if (f < n) {
+          int lo = 0, hi = a.S - 1;  // the last segment whose offset is <= f
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh.hist[mid] <= f) lo = mid;
+            else hi = mid - 1;
+          }
+          const int64_t src = (s0 + lo) * k + (f - sh.hist[lo]);
+          v[q] = ld_dev(&a.rec_key[src]);
+          vb[q] = ld_dev(&a.rec_bits[src]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kMergeQ; ++q) {
+        const uint32_t f = f0 + (uint32_t)(q * NT) + tid;
+        if (f < n) {
+          s_key[f] = v[q];
+          s_bits[f] = vb[q];
+        }
       }
     }
     __syncthreads();
