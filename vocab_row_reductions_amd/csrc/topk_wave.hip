@@ -717,8 +717,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
     const int64_t s0 = row * a.S;
-    // the segments' counts in flight with their (max, sum) partials
+    // one round of loads: the segments' counts, their (max, sum) partials and
+    // every record slot (a segment's slots past its count hold stale keys,
+    // dropped below)
     const uint32_t cnt_t = tid < a.S ? ld_dev(&a.rec_cnt[s0 + tid]) : 0u;
+    constexpr int kSlotQ = kCapSmall / NT;
+    const uint32_t nslots = (uint32_t)a.S * k;  // <= kCapSmall (the segment plan)
+    uint64_t v[kSlotQ];
+#pragma unroll
+    for (int q = 0; q < kSlotQ; ++q) {
+      const uint32_t f = (uint32_t)(q * NT) + tid;
+      if (f < nslots) v[q] = ld_dev(&a.rec_key[s0 * k + f]);
+    }
     uint64_t unusedP;
     merge_key_lse(sh, nullptr, a.p_m + s0, a.p_s + s0, a.S, c, unusedP, r);
     if (tid < a.S) sh.hist[tid] = cnt_t;
@@ -740,29 +750,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
     __syncthreads();
     n = sh.cnt2;
-    // every record of the row in one round of loads: record f of the
-    // concatenation is record f - off[sg] of segment sg (sg found by a binary
-    // search of the offsets), up to kMergeQ per thread in flight at once
-    constexpr int kMergeQ = 4;
-    for (uint32_t f0 = 0; f0 < n; f0 += NT * kMergeQ) {
-      uint64_t v[kMergeQ];
+    // slot (segment sg, index i) -> the concatenation, if i is below sg's count
 #pragma unroll
-      for (int q = 0; q < kMergeQ; ++q) {
-        const uint32_t f = f0 + (uint32_t)(q * NT) + tid;
-        if (f < n) {
-          int lo = 0, hi = a.S - 1;  // the last segment whose offset is <= f
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sh.hist[mid] <= f) lo = mid;
-            else hi = mid - 1;
-          }
-          v[q] = ld_dev(&a.rec_key[(s0 + lo) * k + (f - sh.hist[lo])]);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < kMergeQ; ++q) {
-        const uint32_t f = f0 + (uint32_t)(q * NT) + tid;
-        if (f < n) s_key[f] = v[q];
+    for (int q = 0; q < kSlotQ; ++q) {
+      const uint32_t f = (uint32_t)(q * NT) + tid;
+      if (f < nslots) {
+        const uint32_t sg = f / k, i = f - sg * k;
+        const uint32_t o = sh.hist[sg], e = (int)sg + 1 < a.S ? sh.hist[sg + 1] : n;
+        if (o + i < e) s_key[o + i] = v[q];
       }
     }
     __syncthreads();
