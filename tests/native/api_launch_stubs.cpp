@@ -88,11 +88,17 @@ static hipError_t check_topk(const TopkArgs& a, int cap) {
   in_ws("topk", "rec_cnt", a.rec_cnt, n);
   in_ws("topk", "p_m", a.p_m, n);
   in_ws("topk", "p_s", a.p_s, n);
+  in_ws("topk", "m_n", a.m_n, n);
+  in_ws("topk", "m_mean", a.m_mean, n);
+  in_ws("topk", "m_m2", a.m_m2, n);
   disjoint("topk");
   return hipSuccess;
 }
 
-hipError_t launch_topk(int, bool, int cap, const TopkArgs& a, hipStream_t) { return check_topk(a, cap); }
+hipError_t launch_topk(int, bool, int cap, const TopkArgs& a, hipStream_t) {
+  if (a.m_n) fail("topk", "row moments outside the per-wave kernel");
+  return check_topk(a, cap);
+}
 hipError_t launch_topk_wave(int, bool, const TopkArgs& a, hipStream_t) {
   if (a.k > kWaveTopkMax || !a.vec) fail("topk_wave", "k or alignment");
   return check_topk(a, kCapSmall);

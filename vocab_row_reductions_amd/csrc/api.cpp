@@ -570,7 +570,11 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
   const bool greedy = temperature == 0.0f || top_k == 1;
 
   const double* sigma = nullptr;
-  if (top_n_sigma > 0.0f && !greedy) {
+  // the per-wave top-k kernel takes the row moments in its own pass
+  const bool fused_moments = top_n_sigma > 0.0f && !greedy && top_k > 0 &&
+                             aligned16(logits, ld, elem_size(dtype)) &&
+                             std::min<int64_t>(top_k, vocab) <= kWaveTopkMax;
+  if (top_n_sigma > 0.0f && !greedy && !fused_moments) {
     const Plan p = plan_scan(dtype, false, rows, vocab, 1, kMinMergeSegment);
     MomArgs m{};
     m.x = logits;
@@ -699,6 +703,11 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
   a.typical_p = typical_p;
   a.min_p = min_p;
   a.sigma = sigma;
+  if (fused_moments) {
+    a.m_n = at<double>(ws, cw->mom.p_n);
+    a.m_mean = at<double>(ws, cw->mom.p_mean);
+    a.m_m2 = at<double>(ws, cw->mom.p_m2);
+  }
   a.u = u;
   a.out_token = out_token;
   a.out_logp = out_logprob;

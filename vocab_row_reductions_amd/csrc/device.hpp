@@ -753,6 +753,30 @@ __device__ __forceinline__ bool last_done(SelShared& sh, uint32_t* ticket, uint3
   return sh.last != 0;
 }
 
+// ---------------------------------------------------------------- moments
+// (count, mean, squared deviations) of a set of values; two sets merge by the
+// pairwise update of Chan, Golub and LeVeque.
+struct Mom {
+  double n, mean, m2;
+};
+
+__device__ __forceinline__ Mom mom_merge(Mom a, Mom b) {
+  if (b.n == 0.0) return a;
+  if (a.n == 0.0) return b;
+  const double n = a.n + b.n, d = b.mean - a.mean;
+  return Mom{n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
+}
+
+// Lanes folded into lane 0 in a fixed order (lane l takes lane l + 2^s).
+__device__ __forceinline__ Mom wave_mom(Mom v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const Mom o{__shfl_down(v.n, d), __shfl_down(v.mean, d), __shfl_down(v.m2, d)};
+    if (((int)(threadIdx.x & 63) & (2 * d - 1)) == 0) v = mom_merge(v, o);
+  }
+  return v;  // lane 0
+}
+
 // ---------------------------------------------------------------- merges
 // Reductions over per-segment partials, loaded in parallel (one thread per
 // segment) so that their device-scope load latencies overlap.  S <= NT.

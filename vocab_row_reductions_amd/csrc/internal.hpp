@@ -76,6 +76,12 @@ struct TopkArgs {
   float typical_p;      // 1: off (needs k <= kWaveTopkMax)
   float min_p;          // 0: off
   const double* sigma;  // [rows] standard deviation of each row (top_n_sigma > 0)
+  // or (per-wave kernel) the row moments taken in the same pass: per
+  // (row, segment) count, mean and squared deviations of the values above
+  // -inf (non-null: the kernel computes sigma itself)
+  double* m_n;
+  double* m_mean;
+  double* m_m2;
   // mode 2 (filtered speculative acceptance): per row, the smallest kept
   // composite key and the kept set's log sum of exp(z/T); nothing is drawn
   uint64_t* out_kfl;

@@ -139,7 +139,7 @@ __device__ __forceinline__ uint32_t wave_cut(uint64_t* wb, uint32_t n, uint64_t 
 // LDS use (about 33 KB) allows four workgroups per CU, i.e. four waves per
 // SIMD; the attribute lets the compiler use the 128 VGPRs that occupancy
 // leaves instead of spilling to reach a higher one.
-template <typename DT, bool WANT_LSE>
+template <typename DT, bool WANT_LSE, bool MOM = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void topk_wave_kernel(TopkArgs a) {
   constexpr int E = Elem<DT>::E;
   constexpr int64_t TILE = (int64_t)NT * WTG * E;
@@ -208,6 +208,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     huge = !(__builtin_fabsf(m) <= 0x1p25f);
   };
 
+  // Row moments for top-n-sigma (MOM): each lane's values above -inf, shifted
+  // by its first such value, in float64 (as the moments pass takes them).
+  double mn = 0.0, mr = 0.0, ms1 = 0.0, ms2 = 0.0;
+  auto mom_add = [&](const float (&x)[E]) {
+    if constexpr (MOM) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool ok = x[e] > -__builtin_inff();
+        const double xd = (double)x[e];
+        mr = (mn == 0.0 && ok) ? xd : mr;
+        const double d = ok ? xd - mr : 0.0;
+        mn += ok ? 1.0 : 0.0;
+        ms1 += d;
+        ms2 = fma(d, d, ms2);
+      }
+    }
+  };
+
   auto group_max = [&](const Group& g, float (&x)[E]) {
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = __uint_as_float(gbits<DT>(g, e));
@@ -274,6 +292,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   auto lse_group = [&](const Group& g) {
     float x[E];
     const float gm = group_max(g, x);
+    mom_add(x);
     if constexpr (WANT_LSE) {
       float acc = __builtin_amdgcn_exp2f(fmaf(x[0], c, noff));
 #pragma unroll
@@ -578,6 +597,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const uint32_t b = has ? gbits_at<DT>(xr, i) : kNegInfBits;
     const float x = __uint_as_float(b);
     lm = fmax_nan(lm, x);
+    if constexpr (MOM) {
+      float x1[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) x1[e] = e == 0 ? x : -__builtin_inff();
+      mom_add(x1);
+    }
     if constexpr (WANT_LSE) {
       if (x > trig && x < __builtin_inff()) set_offset(x);
       LS += huge ? (double)__builtin_amdgcn_exp2f((x - om) * c)
@@ -707,6 +732,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   };
   rank_order(n, n <= kRank);
 
+  // Row moments (MOM): the lanes' sums folded per wave, then the waves in
+  // order; then the segments (below), in a fixed order too.
+  __shared__ double s_mom[3 * NWAVE];
+  Mom mv{0.0, 0.0, 0.0};
+  auto fold_waves = [&](Mom v) {
+    v = wave_mom(v);
+    __syncthreads();
+    if (lane == 0) {
+      s_mom[wave] = v.n;
+      s_mom[NWAVE + wave] = v.mean;
+      s_mom[2 * NWAVE + wave] = v.m2;
+    }
+    __syncthreads();
+    Mom w{0.0, 0.0, 0.0};
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) w = mom_merge(w, Mom{s_mom[q], s_mom[NWAVE + q], s_mom[2 * NWAVE + q]});
+    return w;
+  };
+  if constexpr (MOM) {
+    Mom v{mn, 0.0, 0.0};
+    if (mn > 0.0) v = Mom{mn, mr + ms1 / mn, ms2 - ms1 * ms1 / mn};
+    mv = fold_waves(v);
+  }
+
   if (a.S > 1) {
     const int64_t slot = row * a.S + seg;
     for (uint32_t i = tid; i < n; i += NT) st_dev(&a.rec_key[slot * k + i], okey[i]);
@@ -714,9 +763,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       st_dev(&a.rec_cnt[slot], n);
       st_dev(&a.p_m[slot], r.m);
       st_dev(&a.p_s[slot], r.s);
+      if constexpr (MOM) {
+        st_dev(&a.m_n[slot], mv.n);
+        st_dev(&a.m_mean[slot], mv.mean);
+        st_dev(&a.m_m2[slot], mv.m2);
+      }
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
     const int64_t s0 = row * a.S;
+    Mom ms{0.0, 0.0, 0.0};  // this thread's segment's moments (MOM)
+    if constexpr (MOM) {
+      if (tid < a.S) ms = Mom{ld_dev(&a.m_n[s0 + tid]), ld_dev(&a.m_mean[s0 + tid]), ld_dev(&a.m_m2[s0 + tid])};
+    }
     // one round of loads: the segments' counts, their (max, sum) partials and
     // every record slot (a segment's slots past its count hold stale keys,
     // dropped below)
@@ -762,7 +820,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
     __syncthreads();
     rank_order(n, false);
+    if constexpr (MOM) mv = fold_waves(ms);
   }
+  double sigma = a.sigma ? a.sigma[row] : 0.0;
+  if constexpr (MOM) sigma = mv.n > 0.0 ? sqrt(fmax(mv.m2, 0.0) / mv.n) : 0.0;
 
   const bool bad = (r.m != r.m) || (r.m == __builtin_inff());
   const bool none = bad || r.m == -__builtin_inff();
@@ -800,7 +861,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       uint32_t* LIST = ORD + kWStage;
       const ChainParams cp{a.temperature, a.top_p,  a.top_n_sigma, a.typical_p, a.min_p,
                            a.mode == 2 ? a.out_kfl + row : nullptr, a.mode == 2 ? a.out_lse_f + row : nullptr};
-      chain_tail(okey, obits, n, cp, a.sigma ? a.sigma[row] : 0.0, a.u ? a.u[row] : 0.0f, E, Sc, ORD, LIST, &tok,
+      chain_tail(okey, obits, n, cp, sigma, a.u ? a.u[row] : 0.0f, E, Sc, ORD, LIST, &tok,
                  &lp);
     }
     if (tid == 0) {
@@ -815,13 +876,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   }
 }
 
-template <typename DT, bool L>
+template <typename DT, bool L, bool M = false>
 static hipError_t go_wave(const TopkArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((topk_wave_kernel<DT, L>), dim3((unsigned)(a.rows * a.S)), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((topk_wave_kernel<DT, L, M>), dim3((unsigned)(a.rows * a.S)), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_wave(int dtype, bool want_lse, const TopkArgs& a, hipStream_t s) {
+  if (a.m_n)  // row moments in the same pass (the sampler chain's top-n-sigma; no log-sum-exp)
+    return dtype == 0 ? go_wave<float, false, true>(a, s) : go_wave<uint16_t, false, true>(a, s);
   if (dtype == 0) return want_lse ? go_wave<float, true>(a, s) : go_wave<float, false>(a, s);
   return want_lse ? go_wave<uint16_t, true>(a, s) : go_wave<uint16_t, false>(a, s);
 }
