@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_919_009
+TRAFFIC_BYTES = 414_926_537
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "273c3bc0f19aca0facf691f1774b7639249408d845f8a1e0ff51c8b899ea507b"
+TRAFFIC_SHA256 = "618d9aab8f19b21c4e1f195ad12c27d0cda15ac3d78d03ee4619e3ca62b0bb52"
 
 
 def sources_digest():
@@ -115,6 +115,60 @@ def time_graph(fn, n, stream):
     return ev0.elapsed_time(ev1) * 1e3 / (reps * n)
 
 
+def _only_rows(torch, W, dev):
+    x, u = W.sampling_rows()
+    return torch.from_numpy(x).to(dev), torch.from_numpy(u).to(dev)
+
+
+def _only_spec(torch, W, dev):
+    d = W.speculative_batch()
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return g(d["target"]), g(d["draft"]), (g(d["tokens"].view(np.int32)), g(d["u_acc"]), g(d["u_res"]),
+                                            g(d["u_bon"]), 32, 8, 1.0)
+
+
+def _only_topp(torch, vsel, W, dev):
+    x, u = _only_rows(torch, W, dev)
+    return lambda i: vsel.vsel_sample_chain(x, 0.7, u, top_p=0.95)
+
+
+def _only_typical(torch, vsel, W, dev):
+    x, u = _only_rows(torch, W, dev)
+    return lambda i: vsel.vsel_sample_chain(x, 0.7, u, typical_p=0.9)
+
+
+def _only_sample(torch, vsel, W, dev):
+    x, u = _only_rows(torch, W, dev)
+    return lambda i: vsel.vsel_sample(x, 0.7, 20, 0.95, u)
+
+
+def _only_chain(torch, vsel, W, dev):
+    x, u = _only_rows(torch, W, dev)
+    return lambda i: vsel.vsel_sample_chain(x, 0.7, u, top_n_sigma=1.0, top_k=50, typical_p=0.9, top_p=0.95,
+                                            min_p=0.05)
+
+
+def _only_spec_accept(torch, vsel, W, dev):
+    tg, dr, args = _only_spec(torch, W, dev)
+    return lambda i: vsel.vsel_spec_accept(tg, dr, *args)
+
+
+def _only_spec_filtered(torch, vsel, W, dev):
+    tg, dr, args = _only_spec(torch, W, dev)
+    return lambda i: vsel.vsel_spec_accept_filtered(tg, dr, *args, top_p=0.9)
+
+
+def _only_verify(torch, vsel, W, dev):
+    x = torch.from_numpy(W.verify_topk_rows(rows=3)).to(dev)
+    return lambda i: vsel.vsel_topk(x, 84)
+
+
+# --only: one configuration, for profiling its kernels
+ONLY = {"wholerow-topp": _only_topp, "wholerow-typical": _only_typical, "sample": _only_sample,
+        "chain": _only_chain, "spec-accept": _only_spec_accept, "spec-filtered-wholerow": _only_spec_filtered,
+        "verify3": _only_verify}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +179,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=40)
+    ap.add_argument("--only", choices=sorted(ONLY),
+                    help="profiling: run --steps calls of one other configuration (after --warmup calls) and print "
+                         "its time per call instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the selection path has no multi-GPU leg); got --gpus {args.gpus}",
@@ -137,6 +194,20 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.only:
+        fn = ONLY[args.only](torch, vsel, W, dev)
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "steps": args.steps, "warmup": args.warmup,
+                          "us_per_call": ev0.elapsed_time(ev1) * 1e3 / max(1, args.steps)}), flush=True)
+        return
     print(f"bench: generating {ROWS} x {V} bf16 rows (ld {LD})", file=sys.stderr, flush=True)
     bits, _ = W.decode_batch_bf16(rows=ROWS, vocab=V, ld=LD)
     base = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)

@@ -121,15 +121,19 @@ struct NucSet {
   __device__ __forceinline__ float gw(float z) const {
     return __builtin_amdgcn_exp2f((float)(x(z) * 1.4426950408889634));
   }
-  // first-level bin: equal steps over [0, span) of (m - z) / T (order 0) or
-  // of the cut distance (order 1); the last bin also takes everything deeper
+  // First-level bins: NB equal steps over [0, span) of (m - z) / T (order 0)
+  // or of the cut distance (order 1); the last bin also takes everything
+  // deeper.  bin_of takes the coordinate already scaled by NB / span (order
+  // 0: z - m times the loop-invariant vscale, one product).
   template <int NB>
-  __device__ __forceinline__ uint32_t bin_of(double d) const {
-    return d >= kSpan ? (uint32_t)(NB - 1) : (uint32_t)(d * (NB / kSpan));
+  __device__ __forceinline__ static uint32_t bin_of(double v) {
+    return (uint32_t)fmin(v, (double)(NB - 1));
   }
   template <int NB>
+  __device__ __forceinline__ double vscale() const { return -((double)NB / span) / T; }
+  template <int NB>
   __device__ __forceinline__ uint32_t bin(float z) const {
-    return bin_of<NB>((order == 0 ? -x(z) : typ_cut(fabs((double)z - c))) * (kSpan / span));
+    return bin_of<NB>(order == 0 ? ((double)z - m) * vscale<NB>() : typ_cut(fabs((double)z - c)) * ((double)NB / span));
   }
   // The candidate test, the order key and the first-level bin of element i,
   // the typicality distance taken once; ORD is `order` (loops are compiled
@@ -139,16 +143,40 @@ struct NucSet {
     const float z = __uint_as_float(bits);
     if constexpr (ORD == 0) {
       K = comp_key(bits, i);
-      b = bin_of<NB>(-x(z) * (kSpan / span));
+      b = bin_of<NB>(((double)z - m) * vscale<NB>());
       return in(z, K) && (kT == 0 || score_key(bits, i) >= kT);
     } else {
       const double dc = typ_cut(fabs((double)z - c));
       K = score_key_of(dc, i);
-      b = bin_of<NB>(dc * (kSpan / span));
+      b = bin_of<NB>(dc * ((double)NB / span));
       return in(z, K) && (kT == 0 || K >= kT);
     }
   }
 };
+
+// The elements of for_each_elem, a tile at a time: fn(b, at) gets an array b
+// of the lane's N element bits (N = NG * E for a whole tile, E for a short
+// tile, 1 for each element of the tail) and at(q), the index of b[q].  A body
+// can so issue one kind of work for every element of the tile before the next
+// kind (the elements' exponentials interleave ahead of their branches).
+template <typename DT, int NG, bool VEC, class Fn>
+__device__ __forceinline__ void for_each_batch(const DT* __restrict__ xr, int64_t e_begin, int64_t e_end, Fn&& fn) {
+  constexpr int E = Elem<DT>::E;
+  const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
+  walk_groups<DT, NG, VEC>(xr, e_begin, e_full, [&](const auto& g, int64_t t0) {
+    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+    uint32_t b[NGP * E];
+#pragma unroll
+    for (int j = 0; j < NGP; ++j)
+#pragma unroll
+      for (int e = 0; e < E; ++e) b[j * E + e] = gbits<DT>(g[j], e);
+    fn(b, [&](int q) { return t0 + (int64_t)(((q / E) * NT + (int)threadIdx.x) * E + q % E); });
+  });
+  for (int64_t i = e_full + threadIdx.x; i < e_end; i += NT) {
+    const uint32_t b[1] = {gbits_at<DT>(xr, i)};
+    fn(b, [&](int) { return i; });
+  }
+}
 
 // Selects a loop body compiled for one order.
 template <int O>
@@ -299,18 +327,31 @@ template <int NB>
 __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int nb, double base, double t0,
                           double t1) {
   constexpr int PT = NB / NT;
-  static_assert(PT * NT == NB, "bins per thread");
+  static_assert(PT * NT == NB && (PT & (PT - 1)) == 0, "bins per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b0 = tid * PT;
+  // Neighbouring threads' bins start PT bins apart: the q-th bin of every
+  // lane of a wave would lie in the same LDS banks.  Each thread reads its
+  // bins from a starting point of its own instead, (q + tid) mod PT.
+  auto bin_q = [&](int q) { return b0 + ((q + tid) & (PT - 1)); };
+  // (every loop below issues all of its LDS reads before it uses any: bins
+  // past nb read the last one and are dropped)
   __syncthreads();
   double v[PT];
+  uint32_t n[PT];
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int b = min(bin_q(q), nb - 1);
+    v[q] = hw[b];
+    n[q] = hc[b];
+  }
   double ls = 0.0;
   int lastnz = -1;
 #pragma unroll
   for (int q = 0; q < PT; ++q) {
-    const bool in = b0 + q < nb;
-    v[q] = in ? hw[b0 + q] : 0.0;
-    ls += v[q];
-    if (in && hc[b0 + q] != 0u) lastnz = b0 + q;
+    const int b = bin_q(q);
+    const bool in = b < nb;
+    ls += in ? v[q] : 0.0;
+    if (in && n[q] != 0u) lastnz = max(lastnz, b);
   }
   double incl = ls;
   for (int d = 1; d < 64; d <<= 1) {
@@ -347,11 +388,14 @@ __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int n
   // (or its last bin, where the prefix reached it and this order's rounding
   // did not); no owner: the last non-empty bin
   auto walk = [&](double tt) {
+    double w[PT];
+#pragma unroll
+    for (int q = 0; q < PT; ++q) w[q] = hw[min(b0 + q, nb - 1)];
     int cand = -1;
     double c = excl;
 #pragma unroll
     for (int q = 0; q < PT; ++q) {
-      c += v[q];
+      c += b0 + q < nb ? w[q] : 0.0;
       if (cand < 0 && c >= tt) cand = b0 + q;
     }
     return (uint32_t)(cand < 0 ? min(b0 + PT - 1, nb - 1) : cand);
@@ -364,10 +408,10 @@ __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int n
   uint32_t c = 0, ct = 0;
 #pragma unroll
   for (int q = 0; q < PT; ++q) {
-    const int b = b0 + q;
+    const int b = bin_q(q);
     if (b <= hi && b < nb) {
-      ct += hc[b];
-      if (b >= lo) c += hc[b];
+      ct += n[q];
+      if (b >= lo) c += n[q];
     }
   }
   for (int d = 1; d < 64; d <<= 1) {
@@ -772,12 +816,21 @@ __device__ __forceinline__ void add_deep(double* hw, uint32_t* hc, double w, uin
 // row's last workgroup clears only the bins up to it.
 __device__ __forceinline__ void flush_hist(const double* hw, const uint32_t* hc, double* gw, uint32_t* gc,
                                            uint32_t* top) {
+  constexpr int Q = kNB / NT;
+  uint32_t c[Q];
+  double w[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {  // (all LDS reads first)
+    c[q] = hc[q * NT + threadIdx.x];
+    w[q] = hw[q * NT + threadIdx.x];
+  }
   int hi = -1;
-  for (int b = threadIdx.x; b < kNB; b += NT) {
-    const uint32_t c = hc[b];
-    if (c) {
-      (void)__hip_atomic_fetch_add(&gw[b], hw[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      (void)__hip_atomic_fetch_add(&gc[b], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int b = q * NT + (int)threadIdx.x;
+    if (c[q]) {
+      (void)__hip_atomic_fetch_add(&gw[b], w[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      (void)__hip_atomic_fetch_add(&gc[b], c[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (b < kNB - 1) hi = b;
     }
   }
@@ -937,18 +990,24 @@ __device__ __forceinline__ void flush_window(Stage& st, const DT* __restrict__ x
 // The candidates a first guide pass gathers (those within the crossing
 // bound): staged without atomics, each wave in a region of its own, placed by
 // a ballot and the lanes' ranks (the wave's count is a uniform register); past
-// a region's end they are only counted.
+// a region's end they are only counted.  Their bits are staged with them, so
+// the flush reads nothing back from the row.
 struct GatherStage {
   static constexpr uint32_t kPer = kGatherCap / NWAVE;
   uint32_t idx[NWAVE][kPer];
+  uint32_t bits[NWAVE][kPer];
   uint32_t n[NWAVE];
 };
 
-__device__ __forceinline__ void gather(GatherStage& st, uint32_t& cnt, bool take, int64_t i, int64_t e_begin) {
+__device__ __forceinline__ void gather(GatherStage& st, uint32_t& cnt, bool take, int64_t i, int64_t e_begin,
+                                       uint32_t bits) {
   const uint64_t m = __ballot(take);
   if (m != 0ull) {
     const uint32_t p = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (take && p < GatherStage::kPer) st.idx[threadIdx.x >> 6][p] = (uint32_t)(i - e_begin);
+    if (take && p < GatherStage::kPer) {
+      st.idx[threadIdx.x >> 6][p] = (uint32_t)(i - e_begin);
+      st.bits[threadIdx.x >> 6][p] = bits;
+    }
     cnt += (uint32_t)__builtin_popcountll(m);
   }
 }
@@ -957,9 +1016,8 @@ __device__ __forceinline__ void gather(GatherStage& st, uint32_t& cnt, bool take
 // wave in stream order (a fixed order), with the count (kGatherCap + 1 when
 // a wave's region overflowed; the slot is then left unwritten).  All threads
 // call, each wave with its count.
-template <typename DT>
-__device__ __forceinline__ void flush_gather(GatherStage& st, uint32_t cnt, const DT* __restrict__ xr,
-                                             int64_t e_begin, const NucArgs& a, int64_t row, int seg) {
+__device__ __forceinline__ void flush_gather(GatherStage& st, uint32_t cnt, int64_t e_begin, const NucArgs& a,
+                                             int64_t row, int seg) {
   if ((threadIdx.x & 63) == 0) st.n[threadIdx.x >> 6] = cnt;
   __syncthreads();
   uint32_t off[NWAVE], tot = 0;
@@ -979,9 +1037,8 @@ __device__ __forceinline__ void flush_gather(GatherStage& st, uint32_t cnt, cons
   for (int w = 0; w < NWAVE; ++w) {
     const uint32_t nw = min(st.n[w], GatherStage::kPer);
     for (uint32_t j = threadIdx.x; j < nw; j += NT) {
-      const int64_t i = e_begin + st.idx[w][j];
-      gb[off[w] + j] = gbits_at<DT>(xr, i);
-      gi[off[w] + j] = (uint32_t)i;
+      gb[off[w] + j] = st.bits[w][j];
+      gi[off[w] + j] = (uint32_t)(e_begin + st.idx[w][j]);
     }
   }
 }
@@ -1060,27 +1117,38 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
     L.h.hc[b] = 0u;
   }
   __syncthreads();
-  double z0 = 0.0, dw = 0.0;
+  double z0 = 0.0;
   uint32_t dn = 0, ng = 0;
-  for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
-    const float z = __uint_as_float(bits);
-    const bool ok = z > -__builtin_inff() && (double)z >= c.thr;
-    // the exact weight serves the guide too (the total needs it anyway)
-    const double w = S1.w_if(ok, z);
-    const uint32_t b = S1.bin<kNB>(z);
-    const bool shallow = ok && b < kNB - 1;
-    if (shallow) {
-      __hip_atomic_fetch_add(&L.h.hw[b], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for_each_batch<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](const auto& bits, auto at) {
+    constexpr int N = (int)(sizeof(bits) / sizeof(bits[0]));
+    // the exact weights first, every element's (free of branches, so that
+    // the tile's exponentials interleave); they serve the guide too
+    double w[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float z = __uint_as_float(bits[q]);
+      w[q] = S1.w_if(z > -__builtin_inff() && (double)z >= c.thr, z);
     }
-    gather(gs, ng, shallow, i, c.e_begin);
-    const bool deep = ok && b == kNB - 1;
-    dw += deep ? w : 0.0;
-    dn += deep ? 1u : 0u;
-    z0 += w;
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float z = __uint_as_float(bits[q]);
+      const bool ok = z > -__builtin_inff() && (double)z >= c.thr;
+      const uint32_t b = S1.bin<kNB>(z);
+      const bool shallow = ok && b < kNB - 1;
+      if (shallow) {
+        __hip_atomic_fetch_add(&L.h.hw[b], w[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      gather(gs, ng, shallow, at(q), c.e_begin, bits[q]);
+      dn += ok && b == kNB - 1 ? 1u : 0u;
+      z0 += w[q];
+    }
   });
-  add_deep(L.h.hw, L.h.hc, dw, dn);
-  flush_gather<DT>(gs, ng, xr, c.e_begin, a, row, seg);
+  // The last bin gets the deep candidates' count but not their mass: a target
+  // past the other bins' mass falls to the last non-empty bin, which is the
+  // last bin whenever it holds candidates, as it would with the mass.
+  add_deep(L.h.hw, L.h.hc, 0.0, dn);
+  flush_gather(gs, ng, c.e_begin, a, row, seg);
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
@@ -1570,7 +1638,7 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
           __hip_atomic_fetch_add(&L.h.hc[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        if (first) gather(gs, ng, shallow, i, e_begin);
+        if (first) gather(gs, ng, shallow, i, e_begin, bits);
         dn += ok && b == kNB - 1 ? 1u : 0u;
       });
       return;
@@ -1590,11 +1658,11 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
         }
         t += w;
       }
-      if (first) gather(gs, ng, ok && b < kNB - 1, i, e_begin);
+      if (first) gather(gs, ng, ok && b < kNB - 1, i, e_begin, bits);
     });
   });
   add_deep(L.h.hw, L.h.hc, dw, dn);
-  if (first) flush_gather<DT>(gs, ng, xr, e_begin, a, row, seg);
+  if (first) flush_gather(gs, ng, e_begin, a, row, seg);
   __syncthreads();
   double* gw = a.h0w + row * kNB;
   uint32_t* gc = a.h0c + row * kNB;
