@@ -1001,6 +1001,7 @@ struct GatherStage {
 
 __device__ __forceinline__ void gather(GatherStage& st, uint32_t& cnt, bool take, int64_t i, int64_t e_begin,
                                        uint32_t bits) {
+  if (cnt > GatherStage::kPer) return;  // the region overflowed: its count stays past the end
   const uint64_t m = __ballot(take);
   if (m != 0ull) {
     const uint32_t p = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -1058,6 +1059,27 @@ __device__ __forceinline__ void for_each_cand(const NucArgs& a, int64_t row, int
     return;
   }
   for_each_elem<DT, kNG, VEC>(xr, e_begin, e_end, fn);
+}
+
+// for_each_cand a tile at a time, as for_each_batch (a gathered list one
+// candidate at a time).
+template <typename DT, bool VEC, class Fn>
+__device__ __forceinline__ void for_each_cand_batch(const NucArgs& a, int64_t row, int seg, bool listed,
+                                                    const DT* __restrict__ xr, int64_t e_begin, int64_t e_end,
+                                                    Fn&& fn) {
+  if (listed) {
+    const size_t slot = (size_t)(row * a.S + seg);
+    const uint32_t n = min(a.gcnt[slot], (uint32_t)kGatherCap);
+    const uint32_t* gb = a.gbits + slot * kGatherCap;
+    const uint32_t* gi = a.gidx + slot * kGatherCap;
+    for (uint32_t j = threadIdx.x; j < n; j += NT) {
+      const uint32_t b[1] = {gb[j]};
+      const int64_t i = (int64_t)gi[j];
+      fn(b, [&](int) { return i; });
+    }
+    return;
+  }
+  for_each_batch<DT, kNG, VEC>(xr, e_begin, e_end, fn);
 }
 
 union NucLds {
@@ -1214,25 +1236,45 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   // At T = 1 the tempered weights are the untempered ones; floor mode draws
   // nothing and needs no tempered guide.
   const bool same_t = a.T == 1.0f, want_guide = a.out_kfl == nullptr;
-  for_each_cand<DT, VEC>(a, row, seg, a.plan[row].listed != 0u, xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t i) {
-    const float z = __uint_as_float(bits);
-    const uint64_t K = comp_key(bits, (uint32_t)i);
-    const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
-    const uint32_t b = cand ? S1.bin<kNB>(z) : (uint32_t)kNB;
-    if (b < b_lo) {  // (few elements: a branch)
-      const double w1 = S1.w(z);
-      A += w1;
-      if (K >= c.kmp) {
-        const double wt = same_t ? w1 : ST.w(z);
-        AT += wt;
-        if (want_guide) {
-          const uint32_t bt = ST.bin<kNB>(z);  // (its own span, also at T = 1)
-          __hip_atomic_fetch_add(&L.h.hw[bt], wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          __hip_atomic_fetch_add(&L.h.hc[bt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // A tile's bins first; a tile with an element above the window anywhere in
+  // the wave takes the untempered weights of all its elements at once (0 for
+  // those not above it, free of branches so that they interleave), a tile
+  // without one none.
+  for_each_cand_batch<DT, VEC>(a, row, seg, a.plan[row].listed != 0u, xr, c.e_begin, c.e_end,
+                               [&](const auto& bits, auto at) {
+    constexpr int N = (int)(sizeof(bits) / sizeof(bits[0]));
+    uint32_t b[N];
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float z = __uint_as_float(bits[q]);
+      const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
+      b[q] = cand ? S1.bin<kNB>(z) : (uint32_t)kNB;
+      any = any || b[q] < b_lo;
+    }
+    if (__ballot(any) != 0ull) {
+      double w1[N];
+#pragma unroll
+      for (int q = 0; q < N; ++q) w1[q] = S1.w_if(b[q] < b_lo, __uint_as_float(bits[q]));
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        A += w1[q];
+        const uint64_t K = comp_key(bits[q], (uint32_t)at(q));
+        if (b[q] < b_lo && K >= c.kmp) {
+          const float z = __uint_as_float(bits[q]);
+          const double wt = same_t ? w1[q] : ST.w(z);
+          AT += wt;
+          if (want_guide) {
+            const uint32_t bt = ST.bin<kNB>(z);  // (its own span, also at T = 1)
+            __hip_atomic_fetch_add(&L.h.hw[bt], wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(&L.h.hc[bt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
         }
       }
     }
-    if (b >= b_lo && b <= b_hi) stage_window(st, i, c.e_begin);
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (b[q] >= b_lo && b[q] <= b_hi) stage_window(st, at(q), c.e_begin);
   });
   flush_window<DT>(st, xr, c.e_begin, &a.lcnt[row], lkey, lbits);
   __syncthreads();
