@@ -11,28 +11,37 @@
 //      the first at which the cumulative tempered mass exp((z - max) / T)
 //      passes u times the kept total.
 // The row is never sorted.  A guide histogram of the masses (summed in
-// float64 in the order the LDS atomics land, bins of equal steps of
-// (max - z) / T; the parallel passes add the exact weights, the one-workgroup
-// refinement float32 exponentials) places a window of candidates around the
-// crossing, wider than the guide's error.
+// float64 in the order the LDS atomics land; 4,096 bins of equal steps of
+// (max - z) / T over [0, span), span the crossing bound below, deeper
+// candidates sharing the last bin; the parallel passes add the exact weights,
+// the one-workgroup refinement float32 exponentials) places a window of
+// candidates around the crossing, wider than the guide's error.
 // An exact pass then sums the float64 masses above the window and the totals
 // in a fixed order and gathers the window's candidates; they are sorted in LDS
 // and walked in order.
 //
-// Three launches, each over (row, segment) workgroups, the last workgroup of
-// a row finishing it:
+// Four launches, the first three over (row, segment) workgroups, the last
+// workgroup of a row finishing it:
 //   nuc_hist:    guide histogram of the untempered masses and their exact
-//                total; the last workgroup places the cut window (from the
-//                top of the row when everything above the crossing fits LDS).
+//                total, and every segment's candidates short of the last bin
+//                gathered into a list of the (row, segment); the last
+//                workgroup places the cut window (from the top of the row when
+//                everything above the crossing fits LDS) and marks the row
+//                "listed" when every list is whole and the window stays short
+//                of the last bin.  The later passes of a listed row visit its
+//                lists instead of the row.
 //   nuc_collect: the exact mass above the window and the window's candidates,
 //                and the guide histogram and exact mass of the tempered
 //                weights above it; the last workgroup cuts, applies min_p,
 //                totals the kept mass and draws when the draw falls in the
 //                window, else places the draw window.
 //   nuc_draw:    for the remaining rows, the same over the draw window.
-// A window with more candidates than LDS holds is left to the row's last
-// workgroup alone, which narrows it by guide passes over equal steps of the
-// composite key (value, then id); these also separate tied values.
+//   nuc_alone:   one workgroup per row, for a window with more candidates than
+//                LDS holds: it narrows the window by guide passes over equal
+//                steps of the composite key (value, then id); these also
+//                separate tied values.
+// A window of at most 64 candidates is sorted and walked by one wave in its
+// lanes, one of at most 256 by ranks, one per thread.
 //
 // Typical-p over whole rows (further down) uses the same guide / window /
 // fallback scheme for each of its selections, in the typical order or in
