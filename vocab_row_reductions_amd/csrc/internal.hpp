@@ -201,7 +201,8 @@ struct MomArgs {
 
 // The sampler chain over whole rows with a top-p cut: three passes over
 // (row, segment) workgroups (a guide histogram, the cut window, the draw
-// window).  Histograms, window counters and tickets are zero between calls.
+// window) and a one-workgroup fallback.  Histograms, window counters and
+// tickets are zero between calls.
 constexpr int kNucBins = 4096;     // guide bins per row
 constexpr int kNucCap = 4096;      // window candidates per row
 constexpr int kGatherCap = 2048;   // gathered candidates per (row, segment)
@@ -212,6 +213,7 @@ struct NucPlan {                   // per row, written by the last workgroup of 
   uint32_t listed;                 // 1: every candidate the later passes reach is in the gathered list
   uint32_t h0top, hTtop;           // highest non-empty bins (short of the last) of the row's two histograms
   double z0;                       // exact candidate mass, untempered
+  double a_above;                  // exact untempered mass of the candidates above the cut window
   double wt;                       // exact kept mass, tempered
   uint64_t kfin;                   // smallest kept composite key
 };

@@ -1200,11 +1200,23 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   const double t = (double)a.top_p * Z0, g = kGuard * Z0;
   pick_bins<kNB>(r, L.h.hw, L.h.hc, kNB, 0.0, t - g, t + g);
   const bool listed = fit && r.b_hi < (uint32_t)kNB - 1;
+  const uint32_t b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the top of the row when it fits
+  // The exact mass above the window: the bins above it hold the exact weights
+  // of their candidates (summed in the order the atomics landed, like the
+  // guide that placed the window), taken here in bin order.
+  double av = 0.0;
+#pragma unroll
+  for (int q = 0; q < kNB / NT; ++q) {
+    const uint32_t b = (uint32_t)tid * (kNB / NT) + q;
+    av += b < b_lo ? L.h.hw[b] : 0.0;
+  }
+  const double above = nuc_sum(r, av, 0);
   if (tid == 0) {
     NucPlan& p = a.plan[row];
-    p.b_lo = r.cnt_top <= kCapW ? 0u : r.b_lo;  // from the top of the row when it fits
+    p.b_lo = b_lo;
     p.b_hi = r.b_hi;
     p.z0 = Z0;
+    p.a_above = above;
     p.listed = listed ? 1u : 0u;
     p.state = 0u;
   }
@@ -1241,41 +1253,43 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   __syncthreads();
   uint64_t* lkey = a.lkey + row * kCapW;
   uint32_t* lbits = a.lbits + row * kCapW;
-  double A = 0.0, AT = 0.0;
-  // At T = 1 the tempered weights are the untempered ones; floor mode draws
-  // nothing and needs no tempered guide.
+  // The exact mass above the window comes from the guide pass.  The kept
+  // candidates above it need their tempered weights here only for the draw's
+  // guide, at T != 1 or with min_p; otherwise their mass is that one.
   const bool same_t = a.T == 1.0f, want_guide = a.out_kfl == nullptr;
-  // A tile's bins first; a tile with an element above the window anywhere in
-  // the wave takes the untempered weights of all its elements at once (0 for
-  // those not above it, free of branches so that they interleave), a tile
+  const bool need_wt = want_guide || !same_t || c.kmp != 0ull;
+  double AT = 0.0;
+  // A tile's bins first; a tile with a kept candidate above the window
+  // anywhere in the wave takes the tempered weights of all its elements at
+  // once (0 for the others, free of branches so that they interleave), a tile
   // without one none.
   for_each_cand_batch<DT, VEC>(a, row, seg, a.plan[row].listed != 0u, xr, c.e_begin, c.e_end,
                                [&](const auto& bits, auto at) {
     constexpr int N = (int)(sizeof(bits) / sizeof(bits[0]));
     uint32_t b[N];
-    bool any = false;
 #pragma unroll
     for (int q = 0; q < N; ++q) {
       const float z = __uint_as_float(bits[q]);
       const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
       b[q] = cand ? S1.bin<kNB>(z) : (uint32_t)kNB;
-      any = any || b[q] < b_lo;
     }
-    if (__ballot(any) != 0ull) {
-      double w1[N];
-#pragma unroll
-      for (int q = 0; q < N; ++q) w1[q] = S1.w_if(b[q] < b_lo, __uint_as_float(bits[q]));
+    if (need_wt) {
+      bool kept[N], any = false;
 #pragma unroll
       for (int q = 0; q < N; ++q) {
-        A += w1[q];
-        const uint64_t K = comp_key(bits[q], (uint32_t)at(q));
-        if (b[q] < b_lo && K >= c.kmp) {
-          const float z = __uint_as_float(bits[q]);
-          const double wt = same_t ? w1[q] : ST.w(z);
-          AT += wt;
-          if (want_guide) {
-            const uint32_t bt = ST.bin<kNB>(z);  // (its own span, also at T = 1)
-            __hip_atomic_fetch_add(&L.h.hw[bt], wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        kept[q] = b[q] < b_lo && comp_key(bits[q], (uint32_t)at(q)) >= c.kmp;
+        any = any || kept[q];
+      }
+      if (__ballot(any) != 0ull) {
+        double wt[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q) wt[q] = ST.w_if(kept[q], __uint_as_float(bits[q]));
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+          AT += wt[q];
+          if (want_guide && kept[q]) {
+            const uint32_t bt = ST.bin<kNB>(__uint_as_float(bits[q]));  // (its own span, also at T = 1)
+            __hip_atomic_fetch_add(&L.h.hw[bt], wt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_fetch_add(&L.h.hc[bt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
         }
@@ -1291,22 +1305,19 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   uint32_t* gc = a.hTc + row * kNB;
   uint32_t* htop = &a.plan[row].hTtop;
   flush_hist(L.h.hw, L.h.hc, gw, gc, htop);
-  A = nuc_sum(r, A, 0);
-  AT = nuc_sum(r, AT, 1);
-  if (tid == 0) {
-    st_dev(&a.p_a[row * a.S + seg], A);
-    st_dev(&a.p_at[row * a.S + seg], AT);
+  if (need_wt) {
+    AT = nuc_sum(r, AT, 1);
+    if (tid == 0) st_dev(&a.p_at[row * a.S + seg], AT);
   }
   if (!last_of_row(sh, a.tickets + row * 3 + 1, (uint32_t)a.S)) return;
   // ---- the row's last workgroup: its first global loads issued together
   const int64_t p0 = row * a.S;
-  const double va = tid < a.S ? ld_dev(&a.p_a[p0 + tid]) : 0.0;
-  const double vat = tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : 0.0;
+  const double vat = need_wt && tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : 0.0;
   const uint32_t n = ld_dev(&a.lcnt[row]);
   const uint64_t k0 = ld_dev(&lkey[tid]);
   const uint32_t b0 = ld_dev(&lbits[tid]);
-  const double Atot = block_sum_f64(sh, va);
-  const double ATtot = block_sum_f64(sh, vat);
+  const double Atot = a.plan[row].a_above;
+  const double ATtot = need_wt ? block_sum_f64(sh, vat) : Atot;
   if (tid == 0) st_dev(&a.lcnt[row], 0u);
   if (n > kCapW) {
     // the window is too crowded for LDS: the row is left to nuc_alone
