@@ -120,6 +120,34 @@ Plan plan_draw(int64_t rows, int64_t V, int64_t resident) {
   return Plan{(int32_t)cdiv(V, seg), seg};
 }
 
+// The whole-row passes (nucleus and typical-p): two workgroups per CU (LDS
+// bound), each bound by its own float64 work rather than by HBM.  A CU's time
+// is then its workgroups' segments plus a fixed cost per workgroup (the
+// histogram flush and the row's tail, about kNucSegCost elements' worth), and
+// a CU left with a single workgroup runs it at about 0.6 of the CU's rate.  S
+// minimises the busiest CU's time.  (Measured on 288 speculative rows: 3
+// segments 537 us per filtered call, 7 segments 558 us; 256 rows: 2 segments
+// 583 us, 1 segment 633 us.)
+constexpr int64_t kNucSegCost = 24576;
+Plan plan_nucleus(int64_t rows, int64_t V) {
+  const int64_t sb = seg_bound(rows, V, 0, kCapLarge);  // (the workspace's bound)
+  const int64_t cus = device_cus();
+  Plan best{1, cdiv(V, 8) * 8};
+  double best_cost = 1e300;
+  for (int64_t S = 1; S <= sb; ++S) {
+    const int64_t seg = cdiv(cdiv(V, S), 8) * 8;
+    const int64_t Sx = cdiv(V, seg);
+    if (Sx != S) continue;
+    const int64_t per_cu = cdiv(rows * Sx, cus);
+    const double cost = (double)per_cu * (double)(seg + kNucSegCost) / (per_cu >= 2 ? 1.0 : 0.6);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = Plan{(int32_t)Sx, seg};
+    }
+  }
+  return best;
+}
+
 // Top-k: the small candidate buffer whenever it can hold the merge, which
 // keeps four workgroups per CU.
 struct TopkPlan {
@@ -645,8 +673,7 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
       n.u = u;
       n.out_token = out_token;
       n.out_logp = out_logprob;
-      // the passes keep two workgroups per CU resident (LDS bound)
-      const Plan pn = plan_segments(rows, vocab, 0, 2 * (int64_t)device_cus(), kCapLarge);
+      const Plan pn = plan_nucleus(rows, vocab);
       n.seg_len = pn.seg_len;
       n.S = pn.S;
       n.vec = a.vec1;
@@ -909,7 +936,7 @@ static vsel_status spec_filter(SpecArgs& p, int32_t top_k, float top_p, float mi
     n.out_kfl = kfl + off;
     n.out_lse_f = lse + off;
     if (top_p < 1.0f) {
-      const Plan pn = plan_segments(rows, p.V, 0, 2 * (int64_t)device_cus(), kCapLarge);
+      const Plan pn = plan_nucleus(rows, p.V);
       n.seg_len = pn.seg_len;
       n.S = pn.S;
       if (launch_row_nucleus(VSEL_F32, n, s) != hipSuccess) return VSEL_EDEVICE;
