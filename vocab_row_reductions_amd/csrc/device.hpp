@@ -808,22 +808,34 @@ __device__ __forceinline__ void merge_key_lse(SelShared& sh, const uint64_t* pk,
     if (pk) k = ld_dev(&pk[tid]);
     v = LSE{ld_dev(&pm[tid]), ld_dev(&ps[tid])};
   }
+  // The maximum first (NaN-propagating), then every partial rescaled to it at
+  // once (one float64 exp2 per lane, not a chain of pairwise merges) and
+  // summed in a fixed order.
   k = wave_max_u64(k);
-  v = wave_lse(v, c);
+  float M = wave_max_nan(v.m);
   __syncthreads();
   if (lane == 0) {
     sh.wk[wave] = k;
-    sh.wm[wave] = v.m;
-    sh.ws[wave] = v.s;
+    sh.wm[wave] = M;
   }
   __syncthreads();
   P = sh.wk[0];
-  r = LSE{sh.wm[0], sh.ws[0]};
+  M = sh.wm[0];
 #pragma unroll
   for (int q = 1; q < NWAVE; ++q) {
     P = sh.wk[q] > P ? sh.wk[q] : P;
-    r = lse_merge(r, LSE{sh.wm[q], sh.ws[q]}, c);
+    M = fmax_nan(M, sh.wm[q]);
   }
+  double t = 0.0;
+  if (v.m == M) t = v.s;
+  else if (v.m != -__builtin_inff()) t = v.s * exp2((double)(v.m - M) * (double)c);
+  t = wave_sum_f64(t);
+  if (lane == 0) sh.ws[wave] = t;
+  __syncthreads();
+  double sum = sh.ws[0];
+#pragma unroll
+  for (int q = 1; q < NWAVE; ++q) sum += sh.ws[q];
+  r = (M != M) ? LSE{M, __builtin_nan("")} : LSE{M, sum};
 }
 
 // Work index of this workgroup, remapped so that consecutive work items run

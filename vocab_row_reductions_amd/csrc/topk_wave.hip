@@ -771,14 +771,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
     const int64_t s0 = row * a.S;
-    Mom ms{0.0, 0.0, 0.0};  // this thread's segment's moments (MOM)
-    if constexpr (MOM) {
-      if (tid < a.S) ms = Mom{ld_dev(&a.m_n[s0 + tid]), ld_dev(&a.m_mean[s0 + tid]), ld_dev(&a.m_m2[s0 + tid])};
-    }
     // one round of loads: the segments' counts, their (max, sum) partials and
     // every record slot (a segment's slots past its count hold stale keys,
-    // dropped below)
-    const uint32_t cnt_t = tid < a.S ? ld_dev(&a.rec_cnt[s0 + tid]) : 0u;
+    // dropped below); threads past the segments load segment 0's words and
+    // drop them, so no load waits on a branch
+    const int64_t s_t = s0 + (tid < a.S ? tid : 0);
+    const uint32_t cnt_l = ld_dev(&a.rec_cnt[s_t]);
     constexpr int kSlotQ = kCapSmall / NT;
     const uint32_t nslots = (uint32_t)a.S * k;  // <= kCapSmall (the segment plan)
     uint64_t v[kSlotQ];
@@ -787,6 +785,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       const uint32_t f = (uint32_t)(q * NT) + tid;
       if (f < nslots) v[q] = ld_dev(&a.rec_key[s0 * k + f]);
     }
+    Mom ms{0.0, 0.0, 0.0};  // this thread's segment's moments (MOM)
+    if constexpr (MOM) {
+      const Mom ml{ld_dev(&a.m_n[s_t]), ld_dev(&a.m_mean[s_t]), ld_dev(&a.m_m2[s_t])};
+      if (tid < a.S) ms = ml;
+    }
+    const uint32_t cnt_t = tid < a.S ? cnt_l : 0u;
     uint64_t unusedP;
     merge_key_lse(sh, nullptr, a.p_m + s0, a.p_s + s0, a.S, c, unusedP, r);
     if (tid < a.S) sh.hist[tid] = cnt_t;
