@@ -475,10 +475,161 @@ struct ChainParams {
   uint64_t* kfl_out;
   double* lse_out;
 };
+// Lane l's float64 v, in every lane (l uniform).
+__device__ __forceinline__ double readlane_f64(double v, uint32_t l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, (int)l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), (int)l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Lane src's value (a gather within the wave).
+__device__ __forceinline__ uint32_t from_lane_u32(uint32_t v, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)v);
+}
+__device__ __forceinline__ double from_lane_f64(double v, uint32_t src) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = from_lane_u32((uint32_t)b, src), hi = from_lane_u32((uint32_t)(b >> 32), src);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// The lane whose dst is this lane (dst a permutation of the wave's lanes).
+__device__ __forceinline__ uint32_t lane_sending_here(uint32_t dst) {
+  return (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)(threadIdx.x & 63));
+}
+
+// chain_tail (below) for n <= 64 candidates, by wave 0 alone with candidate
+// (or list place) l in lane l: the same arithmetic in the same order, every
+// in-order sum a loop over the lanes' values read out one by one, so no step
+// waits on LDS.  Called by wave 0 only, all its lanes active.
+__device__ inline void chain_tail_wave(const uint64_t* key, const uint32_t* bits, uint32_t n, const ChainParams& cp,
+                                       double sigma, float u, uint32_t* tok, float* logp) {
+  const uint32_t lane = threadIdx.x & 63;
+  const bool live = lane < n;
+  const double z = live ? (double)__uint_as_float(bits[lane]) : 0.0;
+  const double z0 = readlane_f64(z, 0);
+  const double e = live ? exp(z - z0) : 0.0;  // E[j]
+  uint32_t cnt = n;
+  if (cp.top_n_sigma > 0.0f) {
+    const double thr = z0 - (double)cp.top_n_sigma * sigma;
+    const uint64_t stop = __ballot(lane >= 1 && live && !(z >= thr));
+    cnt = stop ? (uint32_t)__builtin_ctzll(stop) : n;
+  }
+  // the list: place l holds candidate li, its E and its value
+  uint32_t li = lane;
+  double el = e, zl = z;
+  bool value_order = true;
+  if (cp.typical_p < 1.0f) {
+    const bool in = lane < cnt;
+    double Z = 0.0;
+    for (uint32_t j = 0; j < cnt; ++j) Z += readlane_f64(e, j);
+    const double sj = in && e > 0.0 ? log(e / Z) : -__builtin_inf();
+    const double term = (e / Z) * sj;
+    double H = 0.0;
+    for (uint32_t j = 0; j < cnt; ++j)
+      if (readlane_f64(e, j) > 0.0) H -= readlane_f64(term, j);
+    const double sc = in && e > 0.0 ? fabs(-sj - H) : __builtin_inf();
+    uint32_t r = 0;
+    for (uint32_t i = 0; i < cnt; ++i) {
+      const double si = readlane_f64(sc, i);
+      r += (si < sc || (si == sc && i < lane)) ? 1u : 0u;
+    }
+    const uint32_t ord = lane_sending_here(in ? r : lane);  // ORD[place]
+    const double qv = from_lane_f64(e, ord) / Z;
+    double cum = 0.0;
+    uint32_t m = cnt;
+    for (uint32_t rr = 0; rr < cnt; ++rr) {
+      cum += readlane_f64(qv, rr);
+      if (cum >= (double)cp.typical_p) {
+        m = rr + 1;
+        break;
+      }
+    }
+    li = ord;
+    el = from_lane_f64(e, ord);
+    zl = from_lane_f64(z, ord);
+    cnt = m;
+    value_order = false;
+  }
+  if (cp.top_p < 1.0f) {
+    if (!value_order) {  // back to value order: candidate indices ascending
+      uint32_t rk = 0;
+      for (uint32_t i = 0; i < cnt; ++i) rk += (uint32_t)__builtin_amdgcn_readlane((int)li, (int)i) < li ? 1u : 0u;
+      const uint32_t src = lane_sending_here(lane < cnt ? rk : lane);
+      li = from_lane_u32(li, src);
+      el = from_lane_f64(el, src);
+      zl = from_lane_f64(zl, src);
+      value_order = true;
+    }
+    double Z = 0.0;
+    for (uint32_t i = 0; i < cnt; ++i) Z += readlane_f64(el, i);
+    const double qv = el / Z;
+    double cum = 0.0;
+    for (uint32_t i = 0; i < cnt; ++i) {
+      cum += readlane_f64(qv, i);
+      if (cum >= (double)cp.top_p) {
+        cnt = i + 1;
+        break;
+      }
+    }
+  }
+  if (cp.min_p > 0.0f) {
+    double cmax = readlane_f64(zl, 0);
+    if (!value_order)
+      for (uint32_t i = 1; i < cnt; ++i) cmax = fmax(cmax, readlane_f64(zl, i));
+    const double thr = cmax + log((double)cp.min_p);
+    const bool keep = lane < cnt && zl >= thr;
+    const uint64_t km = __ballot(keep);
+    const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+    const uint32_t nk = (uint32_t)__builtin_popcountll(km);
+    const uint32_t src = lane_sending_here(keep ? pos : nk + (lane - pos));  // kept first, in order
+    li = from_lane_u32(li, src);
+    zl = from_lane_f64(zl, src);
+    cnt = nk;
+  }
+  // the tempered weights, then the draw in list order
+  const double T = cp.temperature;
+  const double et = lane < cnt ? exp((zl - z0) / T) : 0.0;
+  double W = 0.0;
+  for (uint32_t i = 0; i < cnt; ++i) W += readlane_f64(et, i);
+  if (cp.kfl_out) {
+    if (lane == 0) {
+      *cp.kfl_out = key[(uint32_t)__builtin_amdgcn_readlane((int)li, (int)(cnt - 1))];
+      *cp.lse_out = z0 / T + log(W);
+    }
+    return;
+  }
+  const double target = (double)u * W;
+  double c = 0.0;
+  int pick = -1;
+  for (uint32_t i = 0; i < cnt; ++i) {
+    c += readlane_f64(et, i);
+    if (target < c) {
+      pick = (int)i;
+      break;
+    }
+  }
+  if (pick < 0) {
+    for (int i = (int)cnt - 1; i >= 0; --i)
+      if (readlane_f64(et, (uint32_t)i) > 0.0) {
+        pick = i;
+        break;
+      }
+    if (pick < 0) pick = 0;
+  }
+  if (lane == 0) {
+    const uint32_t j = (uint32_t)__builtin_amdgcn_readlane((int)li, pick);
+    *tok = ~(uint32_t)key[j];
+    *logp = (float)(((double)__uint_as_float(bits[j]) - z0) / T - log(W));
+  }
+}
+
 __device__ inline void chain_tail(const uint64_t* key, const uint32_t* bits, uint32_t n, const ChainParams& cp,
                                   double sigma, float u, double* E, double* S, uint32_t* ORD, uint32_t* LIST,
                                   uint32_t* tok, float* logp) {
   const int tid = threadIdx.x;
+  if (n <= 64) {  // (n is uniform) one wave in its lanes; the others are done
+    if (tid < 64) chain_tail_wave(key, bits, n, cp, sigma, u, tok, logp);
+    return;
+  }
   __shared__ uint32_t c_cnt;
   __shared__ double c_Z, c_H;
   auto zv = [&](uint32_t j) { return (double)__uint_as_float(bits[j]); };

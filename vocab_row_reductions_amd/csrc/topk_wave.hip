@@ -785,11 +785,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       const uint32_t f = (uint32_t)(q * NT) + tid;
       if (f < nslots) v[q] = ld_dev(&a.rec_key[s0 * k + f]);
     }
-    Mom ms{0.0, 0.0, 0.0};  // this thread's segment's moments (MOM)
-    if constexpr (MOM) {
-      const Mom ml{ld_dev(&a.m_n[s_t]), ld_dev(&a.m_mean[s_t]), ld_dev(&a.m_m2[s_t])};
-      if (tid < a.S) ms = ml;
-    }
+    // this thread's segment's moments (MOM; masked where they are used, so
+    // that nothing waits for them before)
+    Mom ms{0.0, 0.0, 0.0};
+    if constexpr (MOM) ms = Mom{ld_dev(&a.m_n[s_t]), ld_dev(&a.m_mean[s_t]), ld_dev(&a.m_m2[s_t])};
     const uint32_t cnt_t = tid < a.S ? cnt_l : 0u;
     uint64_t unusedP;
     merge_key_lse(sh, nullptr, a.p_m + s0, a.p_s + s0, a.S, c, unusedP, r);
@@ -824,7 +823,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
     __syncthreads();
     rank_order(n, false);
-    if constexpr (MOM) mv = fold_waves(ms);
+    if constexpr (MOM) mv = fold_waves(tid < a.S ? ms : Mom{0.0, 0.0, 0.0});
   }
   double sigma = a.sigma ? a.sigma[row] : 0.0;
   if constexpr (MOM) sigma = mv.n > 0.0 ? sqrt(fmax(mv.m2, 0.0) / mv.n) : 0.0;
