@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_926_537
+TRAFFIC_BYTES = 414_932_363
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "618d9aab8f19b21c4e1f195ad12c27d0cda15ac3d78d03ee4619e3ca62b0bb52"
+TRAFFIC_SHA256 = "82aff54851da2d10febff32ca8bebf7444ce11d4243dbb5df641c9ce188346ce"
 
 
 def sources_digest():
