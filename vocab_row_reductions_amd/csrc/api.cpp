@@ -120,6 +120,19 @@ Plan plan_draw(int64_t rows, int64_t V, int64_t resident) {
   return Plan{(int32_t)cdiv(V, seg), seg};
 }
 
+// The draws of modified rejection sampling share pass 2's launch:
+// about two draw workgroups per CU in all (16 segments per row for 32
+// sequences), so that their float64 work spreads over the CUs beside pass 2's
+// stream.  (The 32 x 8 batch: 12, 16, 24 and 32 segments per row took 158.5,
+// 157.0, 171.4 and 175.8 us per call.)
+Plan plan_draw_fused(int64_t B, int64_t V) {
+  const int64_t want = std::min<int64_t>(kMaxSegments, std::max<int64_t>(1, cdiv(2 * device_cus(), B)));
+  int64_t seg = cdiv(cdiv(V, want), kChunk) * kChunk;
+  seg = std::min<int64_t>(seg, (int64_t)kChunk * kChunksPerSeg);
+  seg = std::max<int64_t>(seg, cdiv(cdiv(V, kMaxSegments), kChunk) * kChunk);
+  return Plan{(int32_t)cdiv(V, seg), seg};
+}
+
 // The whole-row passes (nucleus and typical-p): two workgroups per CU (LDS
 // bound), each bound by its own float64 work rather than by HBM.  A CU's time
 // is then its workgroups' segments plus a fixed cost per workgroup (the
@@ -773,10 +786,12 @@ vsel_status vsel_sample_chain(const void* logits, int dtype, int64_t rows, int64
 }
 
 // Argument checks, pass 1 (row statistics of every target and draft row)
-// and the common kernel arguments of both speculative entry points.
+// and the common kernel arguments of the speculative entry points.
+// fused_draw: the draws will run in pass 2's launch (modified rejection
+// sampling at T > 0), which sets their segments.
 static vsel_status spec_prepare(const float* target, int64_t ld_t, const float* draft, int64_t ld_d, int64_t batch,
                                 int32_t gamma, int64_t vocab, float temperature, const uint32_t* draft_tokens,
-                                void* ws, size_t ws_bytes, hipStream_t s, SpecArgs& p) {
+                                void* ws, size_t ws_bytes, hipStream_t s, SpecArgs& p, bool fused_draw = false) {
   if (!target || !draft || !draft_tokens) return VSEL_EINVAL;
   if (batch < 1 || gamma < 1 || gamma > kMaxSegments || vocab < 1 || vocab >= (int64_t(1) << 31) || ld_t < vocab ||
       ld_d < vocab)
@@ -833,7 +848,7 @@ static vsel_status spec_prepare(const float* target, int64_t ld_t, const float* 
   p.acc = at<uint32_t>(ws, w.acc);
   p.draw_L = at<int32_t>(ws, w.draw_L);
   p.p_lse = at<double>(ws, w.p_lse);
-  const Plan pd = plan_draw(B, vocab, resident_scan(VSEL_F32, true));
+  const Plan pd = fused_draw ? plan_draw_fused(B, vocab) : plan_draw(B, vocab, resident_scan(VSEL_F32, true));
   p.dseg = pd.seg_len;
   p.dS = pd.S;
   p.nchunk = cdiv(vocab, kChunk);
@@ -855,8 +870,8 @@ vsel_status vsel_spec_accept(const float* target, int64_t ld_t, const float* dra
   if (!u_accept || !u_resid || !u_bonus || !out_len_mrs || !out_tok_mrs) return VSEL_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   SpecArgs p;
-  const vsel_status st =
-      spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws, ws_bytes, s, p);
+  const vsel_status st = spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws,
+                                      ws_bytes, s, p, temperature > 0.0f);
   if (st != VSEL_OK) return st;
   p.u_acc = u_accept;
   p.u_res = u_resid;
@@ -981,8 +996,8 @@ vsel_status vsel_spec_accept_filtered(const float* target, int64_t ld_t, const f
   if (!spec_filtered_ws(batch, gamma, vocab, ws, ws_bytes, fw)) return VSEL_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   SpecArgs p;
-  vsel_status st =
-      spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws, ws_bytes, s, p);
+  vsel_status st = spec_prepare(target, ld_t, draft, ld_d, batch, gamma, vocab, temperature, draft_tokens, ws,
+                                ws_bytes, s, p, temperature > 0.0f);
   if (st != VSEL_OK) return st;
   if ((st = spec_filter(p, top_k, top_p, min_p, ws, fw, s)) != VSEL_OK) return st;
   p.u_acc = u_accept;

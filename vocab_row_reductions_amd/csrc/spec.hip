@@ -5,7 +5,7 @@
 // rejection sampling"; the exact CPU acceptance of "Chapter 21", section
 // 21.9) needs, per verified position, two full-vocabulary reductions (the
 // pages' MLX version pays them as extra passes plus a host sync per
-// position).  Here the whole batch runs in three launches on one stream and
+// position).  Here the whole batch runs in two launches on one stream and
 // nothing returns to the host:
 //   1. row scan (scan.hip) over all target and draft rows: argmax, maximum,
 //      latch, log-sum-exp at T;
@@ -15,15 +15,18 @@
 //      u * q(t) <= p(t) in float64; the last position of a sequence finds the
 //      first rejection L for both rules and writes every emitted token except
 //      the draw;
-//   3. the draw: float64 masses of each segment of the draw row (residual
-//      max(p - q, 0), or p for the bonus token), then the last workgroup
-//      picks the segment whose prefix crosses u * W and rescans it in id
-//      order.  The residual mixes p and q, so both need float64 log-sum-exps:
-//      the same pass sums them and the residual's parts of each chunk (see
-//      resid_chunks), and the last workgroup combines them.
+//   and in the same launch, the draw: the accept tests need only pass 1's
+//   log-sum-exps, so the draw's workgroups find L themselves and run beside
+//   the coupling pass.  They take float64 masses of each segment of the draw
+//   row (residual max(p - q, 0), or p for the bonus token), then the last
+//   one picks the segment whose prefix crosses u * W and rescans it in id
+//   order.  The residual mixes p and q, so both need float64 log-sum-exps:
+//   the same pass sums them and the residual's parts of each chunk (see
+//   resid_chunks), and the last workgroup combines them.
+// The filtered rules run the filter passes between 1 and 2.
 //
 // Sampler-match ("speculative-acceptance.md", "The rules", the default rule
-// at T > 0) replaces passes 2-4 by:
+// at T > 0) replaces pass 2 and the draw by:
 //   2. match pass, one workgroup per (position, segment): the masses of p
 //      below the drafted token t and in all, and sum p*q (the rule's
 //      acceptance probability, "Verifying the gain").  The fresh draw from p
@@ -61,15 +64,39 @@ __device__ __forceinline__ double block_excl_scan_f64(SelShared& sh, double v, d
 }
 
 // ---------------------------------------------------------------- pass 2
+// The accept test u * q(t) <= p(t) of one position in float64, from the row
+// scan's log-sum-exps (kill_p / kill_q: the drafted token lies outside the
+// filtered target / draft row).  Out of line, so that pass 2's position
+// decision and the draws of the fused launch, which find the first rejection
+// themselves, run the same code and take the same decision bit for bit.
+__device__ __noinline__ uint32_t mrs_accept(float zt, float dt, double lp, double lq, float T, float u, bool kill_p,
+                                            bool kill_q) {
+  const double Td = T;
+  double pt = exp((double)zt / Td - lp);
+  double qt = exp((double)dt / Td - lq);
+  if (kill_p) pt = 0.0;
+  if (kill_q) qt = 0.0;
+  return ((double)u * qt <= pt) ? 1u : 0u;
+}
+
+// (row, segment) of work item `l` of `n` items (a launch's items after its
+// first ones), consecutive items on one XCD when n and the items before are
+// whole multiples of the 8 XCDs (workgroups are dealt round-robin over them).
+__device__ __forceinline__ Item work_item_at(uint32_t l, uint32_t n, bool xcd, int32_t S) {
+  const uint32_t w = xcd ? (l & 7u) * (n >> 3) + (l >> 3) : l;
+  const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(w / (uint32_t)S);
+  return Item{row, (uint32_t)__builtin_amdgcn_readfirstlane(w - row * (uint32_t)S)};
+}
+
 // SP: also sum p*q per position (the sampler-match acceptance probability,
 // reported beside sum min(p, q) as "Verifying the gain before trusting a
 // throughput number" prints both closed forms), one more FMA per element.
-template <bool VEC, bool FILT, bool SP>
-__global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
+// FUSED: the draws run in the same launch (coupling_draw_kernel) and own the
+// emitted token at the first rejection L (or the bonus token).
+template <bool VEC, bool FILT, bool SP, bool FUSED>
+__device__ __forceinline__ void coupling_body(const SpecArgs& a, SelShared& sh, Item it) {
   constexpr int E = 4, TILE = NT * PG * E;
-  __shared__ SelShared sh;
   const int tid = threadIdx.x;
-  const Item it = work_item(a.S);
   const int64_t pos = it.row;
   const int seg = (int)it.seg;
   const int64_t G = a.gamma;
@@ -163,12 +190,9 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
       tot = (a.st_amax[trow] == a.st_amax[nT + drow]) ? 1.0 : 0.0;
       tsp = tot;
     } else {
-      const double Td = a.T;
-      double pt = exp((double)zr[t] / Td - a.st_lse[trow]);
-      double qt = exp((double)dr[t] / Td - a.st_lse[nT + drow]);
-      if (FILT && comp_key(__float_as_uint(zr[t]), t) < kz) pt = 0.0;
-      if (FILT && comp_key(__float_as_uint(dr[t]), t) < kd) qt = 0.0;
-      flag = ((double)a.u_acc[pos] * qt <= pt) ? 1u : 0u;
+      const float zt = zr[t], dt = dr[t];
+      flag = mrs_accept(zt, dt, a.st_lse[trow], a.st_lse[nT + drow], a.T, a.u_acc[pos],
+                        FILT && comp_key(__float_as_uint(zt), t) < kz, FILT && comp_key(__float_as_uint(dt), t) < kd);
     }
     st_dev(&a.acc[pos], flag);
     if (a.summin) st_dev(&a.summin[pos], bad ? __builtin_nanf("") : (float)tot);
@@ -179,13 +203,21 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
   __syncthreads();
   if (tid != 0) return;
 
-  // Sequence decision.
+  // Sequence decision.  Fused with the draws, the token at the first
+  // rejection (or the bonus token) is the draw's alone to write: this thread
+  // leaves it, and a failed sequence has no draw.
   uint32_t* tm = a.tok_mrs + b * (G + 1);
   uint32_t* ta = a.tok_aa ? a.tok_aa + b * (G + 1) : nullptr;
   bool fail = a.st_bad[b * (G + 1) + G] != 0;
   for (int64_t q = 0; q < G; ++q) fail |= sh.hist[q] == 2u;
+  int64_t L = G;
+  for (int64_t q = 0; q < G; ++q)
+    if (sh.hist[q] == 0u) {
+      L = q;
+      break;
+    }
   for (int64_t q = 0; q <= G; ++q) {
-    tm[q] = kFail;
+    if (!FUSED || fail || q != L) tm[q] = kFail;
     if (ta) ta[q] = kFail;
   }
   if (fail) {
@@ -216,15 +248,15 @@ __global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
     a.draw_L[b] = -1;
     return;
   }
-  int64_t L = G;
-  for (int64_t q = 0; q < G; ++q)
-    if (sh.hist[q] == 0u) {
-      L = q;
-      break;
-    }
   a.len_mrs[b] = (int32_t)L;
   for (int64_t q = 0; q < L; ++q) tm[q] = a.tokens[b * G + q];
   a.draw_L[b] = (int32_t)L;
+}
+
+template <bool VEC, bool FILT, bool SP>
+__global__ __launch_bounds__(NT) void coupling_kernel(SpecArgs a) {
+  __shared__ SelShared sh;
+  coupling_body<VEC, FILT, SP, false>(a, sh, work_item(a.S));
 }
 
 // ---------------------------------------------------------------- sampler-match pass
@@ -470,15 +502,15 @@ __device__ __forceinline__ F4 row4(const DT* __restrict__ row, int64_t x, int64_
   return o;
 }
 
-// Chunk masses of segment [e_begin, e_end): each wave takes 4 chunks per
-// step (16 loads per lane in flight), reduces each chunk's 256 weights (4 per
-// lane) in float64, and writes the masses to `cm` (LDS) and `pc` (global,
+// Chunk masses of segment [e_begin, e_end): each wave takes CW chunks per
+// step (4 CW loads per lane in flight), reduces each chunk's 256 weights (4
+// per lane) in float64, and writes the masses to `cm` (LDS) and `pc` (global,
 // indexed from the segment's first chunk).  Returns the segment mass in
-// thread 0: the in-order sum of its chunk masses.
-template <class Src>
+// thread 0: the in-order sum of its chunk masses.  (CW = 2 in the launch that
+// shares its workgroups' registers with pass 2, 4 in launches of their own.)
+template <int CW, class Src>
 __device__ double chunk_masses(const Src& r, int64_t e_begin, int64_t e_end, double* cm, double* pc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int CW = 4;  // chunks per wave per step
   const int nch = (int)((e_end - e_begin + kChunk - 1) / kChunk);
   for (int q0 = 0; q0 < nch; q0 += NWAVE * CW) {
     float zz[CW][4], dd[CW][4];
@@ -636,7 +668,7 @@ struct ResidSrc {
 __device__ void resid_chunks(SelShared& sh, const ResidSrc& r, double theta, int64_t e_begin, int64_t e_end,
                              double* pa, double* pb, uint32_t* pf, double* sp_out, double* sq_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int CW = 4;  // chunks per wave per step
+  constexpr int CW = 2;  // chunks per wave per step (the registers of pass 2's workgroups bound it)
   const int nch = (int)((e_end - e_begin + kChunk - 1) / kChunk);
   double sp = 0.0, sq = 0.0;
   for (int q0 = 0; q0 < nch; q0 += NWAVE * CW) {
@@ -811,7 +843,7 @@ __device__ void resid_draw(const SpecArgs& a, SelShared& sh, int64_t b, int seg,
     r2.vz = r.vz;
     for (int sg = 0; sg < a.dS; ++sg) {
       const int64_t eb = (int64_t)sg * a.dseg, ee = min(a.V, eb + a.dseg);
-      const double m2 = chunk_masses(r2, eb, ee, cmw, pa + eb / kChunk);
+      const double m2 = chunk_masses<2>(r2, eb, ee, cmw, pa + eb / kChunk);
       if (tid == 0) pw[sg] = m2;
       __syncthreads();
     }
@@ -820,20 +852,19 @@ __device__ void resid_draw(const SpecArgs& a, SelShared& sh, int64_t b, int seg,
   if (tid == 0) a.tok_mrs[b * (G + 1) + L] = tok;
 }
 
-__global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
-  __shared__ SelShared sh;
+// One workgroup's share of sequence b's draw at L (L < gamma: the residual
+// at the first rejection, or the sampler-match draw at the first mismatch;
+// L = gamma: the bonus token), segment seg of the draw row.  FUSED: the draws
+// of unfiltered modified rejection sampling in pass 2's launch.
+template <bool FUSED>
+__device__ __forceinline__ void draw_item(const SpecArgs& a, SelShared& sh, int64_t b, int seg, int32_t L) {
+  constexpr int CW = FUSED ? 2 : 4;
   __shared__ double cmw[kChunksPerSeg];
   const int tid = threadIdx.x;
-  const Item it = work_item(a.dS);
-  const int64_t b = it.row;
-  const int seg = (int)it.seg;
-  if (b >= a.B) return;
   const int64_t G = a.gamma;
-  const int32_t L = a.draw_L[b];
-  if (L < 0) return;
   __shared__ double e2[64];
   init_e2(e2);
-  if (!a.match && L < G && !a.kfl) {  // the residual draw of unfiltered p and q
+  if (FUSED && L < G && !a.kfl) {  // the residual draw of unfiltered p and q
     resid_draw(a, sh, b, seg, L, e2, cmw);
     return;
   }
@@ -873,7 +904,7 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   }
   double* pc = a.p_c + b * a.nchunk;
   const int64_t e_begin = (int64_t)seg * a.dseg, e_end = min(a.V, e_begin + a.dseg);
-  const double ms = chunk_masses(r, e_begin, e_end, cmw, pc + e_begin / kChunk);
+  const double ms = chunk_masses<CW>(r, e_begin, e_end, cmw, pc + e_begin / kChunk);
   if (tid == 0) st_dev(&a.p_w[b * a.dS + seg], ms);
   if (!last_done(sh, a.tk_draw + b, (uint32_t)a.dS)) return;
   __shared__ double pw[kMaxSegments];
@@ -892,7 +923,7 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
     r.m = a.st_max[b * (G + 1) + L];
     for (int sg = 0; sg < a.dS; ++sg) {
       const int64_t eb = (int64_t)sg * a.dseg, ee = min(a.V, eb + a.dseg);
-      const double m2 = chunk_masses(r, eb, ee, cmw, pc + eb / kChunk);
+      const double m2 = chunk_masses<CW>(r, eb, ee, cmw, pc + eb / kChunk);
       if (tid == 0) pw[sg] = m2;
       __syncthreads();
     }
@@ -900,6 +931,74 @@ __global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
   double W;
   const uint32_t tok = draw_pick(sh, r, pw, pc, a.dS, a.dseg, u, &W, cmw);
   if (tid == 0) (a.match ? a.tok_sm : a.tok_mrs)[b * (G + 1) + L] = tok;
+}
+
+// The draw as a launch of its own, after pass 2 has decided L: sampler-match,
+// whose first mismatch needs pass 2's masses (modified rejection sampling
+// draws in pass 2's launch).
+__global__ __launch_bounds__(NT) void spec_draw_kernel(SpecArgs a) {
+  __shared__ SelShared sh;
+  const Item it = work_item(a.dS);
+  const int64_t b = it.row;
+  if (b >= a.B) return;
+  const int32_t L = a.draw_L[b];
+  if (L < 0) return;
+  draw_item<false>(a, sh, b, (int)it.seg, L);
+}
+
+// First rejection of sequence b under modified rejection sampling (gamma:
+// every draft accepted), or -1 where the sequence fails closed: pass 2's
+// position and sequence decisions, taken again from the row scan's results
+// (and the filter pass's, FILT) with the same accept function (T > 0).
+template <bool FILT>
+__device__ __forceinline__ int32_t first_reject(const SpecArgs& a, SelShared& sh, int64_t b) {
+  const int tid = threadIdx.x;
+  const int64_t G = a.gamma, nT = a.B * (G + 1);
+  __shared__ int32_t s_L;
+  if (tid < G) {
+    const int64_t pos = b * G + tid, trow = b * (G + 1) + tid, drow = b * G + tid;
+    const uint32_t t = a.tokens[pos];
+    uint32_t flag = 2u;
+    if (!a.st_bad[trow] && !a.st_bad[nT + drow] && t < (uint64_t)a.V) {
+      const float zt = a.tgt[trow * a.ld_t + t], dt = a.dft[drow * a.ld_d + t];
+      const bool kill_p = FILT && comp_key(__float_as_uint(zt), t) < a.kfl[trow];
+      const bool kill_q = FILT && comp_key(__float_as_uint(dt), t) < a.kfl[nT + drow];
+      flag = mrs_accept(zt, dt, a.st_lse[trow], a.st_lse[nT + drow], a.T, a.u_acc[pos], kill_p, kill_q);
+    }
+    sh.hist[tid] = flag;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    bool fail = a.st_bad[b * (G + 1) + G] != 0;
+    int32_t L = (int32_t)G;
+    for (int64_t q = 0; q < G; ++q) fail |= sh.hist[q] == 2u;
+    for (int64_t q = 0; q < G; ++q)
+      if (sh.hist[q] == 0u) {
+        L = (int32_t)q;
+        break;
+      }
+    s_L = fail ? -1 : L;
+  }
+  __syncthreads();
+  return s_L;
+}
+
+// Pass 2 and the draws of modified rejection sampling (T > 0) in one launch.  The first B * dS workgroups are the draws (dispatched first,
+// so that their float64 work overlaps the coupling pass's stream); each finds
+// its sequence's first rejection itself, so it need not wait for pass 2.  The
+// rest are pass 2's (position, segment) items.
+template <bool VEC, bool FILT, bool SP>
+__global__ __launch_bounds__(NT) void coupling_draw_kernel(SpecArgs a) {
+  __shared__ SelShared sh;
+  const uint32_t nd = (uint32_t)(a.B * a.dS);
+  if (blockIdx.x < nd) {
+    const uint32_t b = blockIdx.x / (uint32_t)a.dS;
+    const int32_t L = first_reject<FILT>(a, sh, b);
+    if (L >= 0) draw_item<true>(a, sh, b, (int)(blockIdx.x - b * (uint32_t)a.dS), L);
+    return;
+  }
+  const uint32_t n = gridDim.x - nd;
+  coupling_body<VEC, FILT, SP, true>(a, sh, work_item_at(blockIdx.x - nd, n, (nd & 7u) == 0 && (n & 7u) == 0, a.S));
 }
 
 template <typename DT>
@@ -934,7 +1033,7 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
   if (a.min_p > 0.0f) r.thr = fmax(r.thr, r.m + log((double)a.min_p));
   double* pc = a.p_c + row * a.nchunk;
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
-  const double ms = chunk_masses(r, e_begin, e_end, cmw, pc + e_begin / kChunk);
+  const double ms = chunk_masses<4>(r, e_begin, e_end, cmw, pc + e_begin / kChunk);
   if (tid == 0) st_dev(&a.p_w[row * a.S + seg], ms);
   if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
   __shared__ double pw[kMaxSegments];
@@ -948,32 +1047,38 @@ __global__ __launch_bounds__(NT) void row_draw_kernel(DrawArgs a) {
   }
 }
 
+// Pass 2: at T > 0 with the draws in the same launch (their workgroups
+// first), at T = 0 (no draw) alone.
 template <bool VEC, bool FILT>
-static void launch_coupling(bool sp, unsigned npos, const SpecArgs& a, hipStream_t s) {
-  if (sp)
+static void launch_coupling(bool sp, const SpecArgs& a, hipStream_t s) {
+  const unsigned npos = (unsigned)(a.B * a.gamma * a.S);
+  if (a.T > 0.0f) {
+    const dim3 grid((unsigned)(a.B * a.dS) + npos);
+    if (sp)
+      hipLaunchKernelGGL((coupling_draw_kernel<VEC, FILT, true>), grid, dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((coupling_draw_kernel<VEC, FILT, false>), grid, dim3(NT), 0, s, a);
+  } else if (sp) {
     hipLaunchKernelGGL((coupling_kernel<VEC, FILT, true>), dim3(npos), dim3(NT), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((coupling_kernel<VEC, FILT, false>), dim3(npos), dim3(NT), 0, s, a);
+  }
 }
 
 hipError_t launch_spec(const SpecArgs& a, hipStream_t s) {
   const bool vec = a.vec_t && a.vec_d;
-  const unsigned npos = (unsigned)(a.B * a.gamma * a.S);
   const bool sp = a.sumprod != nullptr;
   if (a.kfl) {
     if (vec)
-      launch_coupling<true, true>(sp, npos, a, s);
+      launch_coupling<true, true>(sp, a, s);
     else
-      launch_coupling<false, true>(sp, npos, a, s);
+      launch_coupling<false, true>(sp, a, s);
   } else {
     if (vec)
-      launch_coupling<true, false>(sp, npos, a, s);
+      launch_coupling<true, false>(sp, a, s);
     else
-      launch_coupling<false, false>(sp, npos, a, s);
+      launch_coupling<false, false>(sp, a, s);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.T == 0.0f) return e;
-  hipLaunchKernelGGL(spec_draw_kernel, dim3((unsigned)(a.B * a.dS)), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
