@@ -180,6 +180,7 @@ static void check_nuc(const char* what, const NucArgs& a, bool full) {
   in_ws(what, "st_bad", a.st_bad, R);
   in_ws(what, "out_kfl", a.out_kfl, R);
   in_ws(what, "out_lse_f", a.out_lse_f, R);
+  if (a.x2 && (a.rows1 < 1 || a.rows1 >= R)) fail(what, "second batch");
   if (!full) return disjoint(what);
   in_ws(what, "h0w", a.h0w, R * kNucBins);
   in_ws(what, "h0c", a.h0c, R * kNucBins);

@@ -179,3 +179,26 @@ def test_fail_closed(g, oracle):
     um = W.uniforms(3 * 3, seed=651).reshape(3, 3)
     got, _, _ = compare_sm(g, oracle, d, toks, um, 1.0, dict(top_p=0.8))
     assert list(got["len_sm"][1:]) == [-1, -1]
+
+
+@pytest.mark.parametrize("kw", [dict(top_p=0.9), dict(top_p=0.5, min_p=0.02)],
+                         ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_wholerow_nucleus_windows(g, oracle, kw, T):
+    """The whole-row nucleus of the filtered rules over rows from flat to
+    peaked (each sequence's rows scaled by its own factor, 0.05 to 8), so
+    that the cut windows of the floor-mode window pass differ widely in size:
+    a handful of candidates in the peaked rows, thousands in the flat ones."""
+    B, G, V = 6, 3, 50000
+    d = W.speculative_batch(batch=B, gamma=G, vocab=V, seed=640)
+    scale = np.array([0.05, 0.3, 1.0, 2.0, 4.0, 8.0], np.float32)
+    tgt = (d["target"].reshape(B, G + 1, V) * scale[:, None, None]).reshape(B * (G + 1), V)
+    dft = (d["draft"].reshape(B, G, V) * scale[:, None, None]).reshape(B * G, V)
+    d = dict(d, target=np.ascontiguousarray(tgt, np.float32), draft=np.ascontiguousarray(dft, np.float32))
+    T = float(np.float32(T))
+    toks = filtered_drafts(d, T, kw, 641)
+    _, _, skipped = compare_mrs(g, oracle, d, toks, T, kw)
+    assert skipped <= 1
+    um = W.uniforms(B * (G + 1), seed=642).reshape(B, G + 1)
+    _, _, skipped = compare_sm(g, oracle, d, toks, um, T, kw)
+    assert skipped <= 1

@@ -394,12 +394,13 @@ ChainWs chain_layout(Layout& L, int64_t rows, int64_t vocab, int32_t top_k) {
 // Filtered speculative acceptance: after the speculative workspace, per row
 // the smallest kept key and the kept set's lse (target rows, then draft
 // rows), then the filter pass's scratch: a top-k workspace, used by the
-// target rows and then the draft rows, and two nucleus workspaces (also used
-// by the min-p threshold pass), one per part, each at its own 256-byte
-// aligned base.  All are disjoint where it matters, so calls with any
-// filters can share one workspace: each keeps its own counters at zero.
+// target rows and then the draft rows, and a nucleus workspace (also used by
+// the min-p threshold pass) for the target and draft rows together, at its
+// own 256-byte aligned base.  All are disjoint where it matters, so calls
+// with any filters can share one workspace: each keeps its own counters at
+// zero.
 struct SpecFiltWs {
-  size_t kfl, lse, sub_topk, topk_bytes, sub_nuc[2], end;
+  size_t kfl, lse, sub_topk, topk_bytes, sub_nuc, end;
 };
 SpecFiltWs spec_filter_layout(size_t spec_end, int64_t B, int64_t G, int64_t V) {
   SpecFiltWs w{};
@@ -411,9 +412,9 @@ SpecFiltWs spec_filter_layout(size_t spec_end, int64_t B, int64_t G, int64_t V) 
   // The top-k passes of the two parts (target rows, draft rows) share one
   // region: its only zero-required words, the tickets, lead every top-k
   // layout, so each part's tickets lie in the other's.  The nucleus passes
-  // need their window counters zero as well, which sit behind row-sized
-  // regions: each part gets a region of its own.
-  size_t tk = 0, nu[2] = {0, 0};
+  // (and the min-p threshold pass) run over both parts in one set of
+  // launches, with a region of their own.
+  size_t tk = 0;
   const int64_t part_rows[2] = {nT, B * G};
   for (int part = 0; part < 2; ++part) {
     const int64_t rows = part_rows[part];
@@ -422,14 +423,12 @@ SpecFiltWs spec_filter_layout(size_t spec_end, int64_t B, int64_t G, int64_t V) 
       topk_layout(b, rows, k, plan_topk_bound(rows, V, k));
       tk = std::max(tk, b.off);
     }
-    Layout b;
-    nucleus_layout(b, rows, plan_scan_bound(rows, V));
-    nu[part] = b.off;
   }
+  Layout nb;
+  nucleus_layout(nb, nrows, plan_scan_bound(nrows, V));
   w.sub_topk = L.take(tk);
   w.topk_bytes = tk;
-  w.sub_nuc[0] = L.take(nu[0]);
-  w.sub_nuc[1] = L.take(nu[1]);
+  w.sub_nuc = L.take(nb.off);
   w.end = L.off;
   return w;
 }
@@ -896,12 +895,11 @@ static vsel_status spec_filter(SpecArgs& p, int32_t top_k, float top_p, float mi
   const int64_t G = p.gamma, nT = p.B * (G + 1), nD = p.B * G;
   uint64_t* kfl = at<uint64_t>(ws, fw.kfl);
   double* lse = at<double>(ws, fw.lse);
-  for (int part = 0; part < 2; ++part) {
-    void* sub = at<char>(ws, fw.sub_nuc[part]);
-    const float* x = part == 0 ? p.tgt : p.dft;
-    const int64_t ld = part == 0 ? p.ld_t : p.ld_d;
-    const int64_t rows = part == 0 ? nT : nD, off = part == 0 ? 0 : nT;
-    if (top_k >= 1) {
+  if (top_k >= 1) {  // the top-k passes, per part
+    for (int part = 0; part < 2; ++part) {
+      const float* x = part == 0 ? p.tgt : p.dft;
+      const int64_t ld = part == 0 ? p.ld_t : p.ld_d;
+      const int64_t rows = part == 0 ? nT : nD, off = part == 0 ? 0 : nT;
       TopkArgs a{};
       a.mode = 2;
       a.temperature = p.T;
@@ -915,18 +913,23 @@ static vsel_status spec_filter(SpecArgs& p, int32_t top_k, float top_p, float mi
       const vsel_status st =
           topk_common(x, VSEL_F32, rows, p.V, ld, k, false, a, at<char>(ws, fw.sub_topk), fw.topk_bytes, s);
       if (st != VSEL_OK) return st;
-      continue;
     }
+  } else {  // the whole-row passes over the target rows and then the draft rows, in one set of launches
+    void* sub = at<char>(ws, fw.sub_nuc);
+    const int64_t rows = nT + nD;
     Layout L;
     const NucWs nw = nucleus_layout(L, rows, plan_scan_bound(rows, p.V));
     NucArgs n{};
-    n.x = x;
-    n.ld = ld;
+    n.x = p.tgt;
+    n.ld = p.ld_t;
+    n.x2 = p.dft;
+    n.ld2 = p.ld_d;
+    n.rows1 = nT;
     n.rows = rows;
     n.V = p.V;
-    n.vec = aligned16(x, ld, 4) ? 1 : 0;
-    n.st_max = p.st_max + off;
-    n.st_bad = p.st_bad + off;
+    n.vec = aligned16(p.tgt, p.ld_t, 4) && aligned16(p.dft, p.ld_d, 4) ? 1 : 0;
+    n.st_max = p.st_max;
+    n.st_bad = p.st_bad;
     n.sigma = nullptr;
     n.top_n_sigma = 0.0f;
     n.top_p = top_p;
@@ -948,8 +951,8 @@ static vsel_status spec_filter(SpecArgs& p, int32_t top_k, float top_p, float mi
     n.p_at = at<double>(sub, nw.p_at);
     n.p_a2 = at<double>(sub, nw.p_a2);
     n.plan = at<NucPlan>(sub, nw.plan);
-    n.out_kfl = kfl + off;
-    n.out_lse_f = lse + off;
+    n.out_kfl = kfl;
+    n.out_lse_f = lse;
     if (top_p < 1.0f) {
       const Plan pn = plan_nucleus(rows, p.V);
       n.seg_len = pn.seg_len;

@@ -243,11 +243,15 @@ struct SelJob {
 struct NucArgs {
   const void* x;
   int64_t ld;
+  // rows1 > 0 and x2: rows from rows1 on are rows of x2 (stride ld2), so
+  // that two batches (speculative target and draft rows) run in one launch
+  const void* x2;
+  int64_t ld2, rows1;
   int64_t rows;
   int64_t V;
   int64_t seg_len;         // a multiple of 8 elements
   int32_t S;
-  int32_t vec;             // rows start and stride 16-byte aligned
+  int32_t vec;             // rows start and stride 16-byte aligned (both batches)
   const float* st_max;     // [rows] row maxima (scan)
   const uint32_t* st_bad;  // [rows] fail-closed rows (scan)
   const double* sigma;     // [rows] standard deviations (top_n_sigma > 0)

@@ -51,6 +51,13 @@
 
 namespace vsel {
 
+// Row `row` of the launch's rows: rows past rows1 belong to the second batch.
+template <typename DT>
+__device__ __forceinline__ const DT* nuc_row(const NucArgs& a, int64_t row) {
+  if (a.x2 != nullptr && row >= a.rows1) return reinterpret_cast<const DT*>(a.x2) + (row - a.rows1) * a.ld2;
+  return reinterpret_cast<const DT*>(a.x) + row * a.ld;
+}
+
 constexpr int kNB = kNucBins;          // guide bins of the parallel passes
 constexpr int kFbNB = 2048;            // guide bins of the one-workgroup refinement
 constexpr double kSpan = 40.0;         // (max - z) / T in [0, 40) in equal steps; lower values share the last bin
@@ -451,7 +458,8 @@ __device__ void pick_bins(NucRed& r, const double* hw, const uint32_t* hc, int n
 // thread sums a run of ceil(n / NT) candidates in order, the runs are
 // prefixed in a fixed order, and every thread walks its own run.  All threads
 // call.
-__device__ uint32_t walk_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const NucSet& S, double A, double t,
+template <class Bits>
+__device__ uint32_t walk_sorted(NucRed& r, const Bits& bits, uint32_t n, const NucSet& S, double A, double t,
                                 bool strict, double* cum = nullptr) {
   if (n <= 64) {
     __syncthreads();
@@ -587,7 +595,8 @@ __device__ __forceinline__ void sort_window(uint64_t* key, uint32_t* bits, uint3
 }
 
 // Fixed-order sum of S.w over the first n sorted candidates.
-__device__ double sum_sorted(NucRed& r, const uint32_t* bits, uint32_t n, const NucSet& S) {
+template <class Bits>
+__device__ double sum_sorted(NucRed& r, const Bits& bits, uint32_t n, const NucSet& S) {
   if (n <= 64) {
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -1141,7 +1150,7 @@ __global__ __launch_bounds__(NT) void nuc_hist_kernel(NucArgs a) {
   }
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, seg);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
   for (int b = tid; b < kNB; b += NT) {
     L.h.hw[b] = 0.0;
@@ -1241,7 +1250,7 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   if (tid == 0) st.n = 0u;
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, seg);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   const uint32_t b_lo = a.plan[row].b_lo, b_hi = a.plan[row].b_hi;
   const double z0 = a.plan[row].z0;
   const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
@@ -1427,6 +1436,183 @@ __global__ __launch_bounds__(NT) void nuc_collect_kernel(NucArgs a) {
   }
 }
 
+// Pass 2 in floor mode (the kept set of filtered speculative acceptance, no
+// draw): nothing needs the tempered guide, so the workgroup's LDS is the
+// window's staging while the segment streams and the row's window keys in
+// the row's last workgroup, one union of 32 KB (four workgroups per CU where
+// the drawing pass fits two).  A window candidate's key gives back its
+// weight (+0 and -0, which keys fold together, weigh the same), so the
+// window is sorted as keys alone.  Same decisions, in the same order, as
+// nuc_collect_kernel's floor mode.
+struct KeyBits {
+  const uint64_t* k;
+  __device__ __forceinline__ uint32_t operator[](uint32_t j) const { return key_bits((uint32_t)(k[j] >> 32)); }
+};
+union FloorLds {
+  Stage st;
+  uint64_t key[kCapW];
+};
+
+// key[0..n) (distinct keys, n <= kCapW) put in descending order: ranks
+// through scratch past the first half for up to NT keys, else the bitonic
+// network (zero padding, never above a real key).
+__device__ __forceinline__ void sort_keys_desc(uint64_t* key, uint32_t n) {
+  const uint32_t t = threadIdx.x;
+  if (n <= (uint32_t)NT) {
+    uint64_t* sk = key + kCapW / 2;
+    const uint64_t mine = t < n ? key[t] : 0ull;
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < n; ++j) rank += key[j] > mine ? 1u : 0u;
+    if (t < n) sk[rank] = mine;
+    __syncthreads();
+    if (t < n) key[t] = sk[t];
+    __syncthreads();
+    return;
+  }
+  uint32_t P = 1;
+  while (P < n) P <<= 1;
+  for (uint32_t i = n + t; i < P; i += NT) key[i] = 0ull;
+  for (uint32_t size = 2; size <= P; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (uint32_t i = t; i < P / 2; i += NT) {
+        const uint32_t lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        const uint64_t x = key[lo], y = key[hi];
+        if ((lo & size) == 0 ? (x < y) : (x > y)) {
+          key[lo] = y;
+          key[hi] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(NT) void nuc_collect_floor_kernel(NucArgs a) {
+  __shared__ SelShared sh;
+  __shared__ NucRed r;
+  __shared__ FloorLds F;
+  __shared__ uint32_t s_bits[64];
+  __shared__ double e2[64];
+  const int tid = threadIdx.x;
+  const Item it = work_item(a.S);
+  const int64_t row = it.row;
+  const int seg = (int)it.seg;
+  if (row >= a.rows || a.st_bad[row]) return;
+  if (tid == 0) F.st.n = 0u;
+  init_e2(e2);
+  const NucCommon c = nuc_common(a, row, seg);
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
+  const uint32_t b_lo = a.plan[row].b_lo, b_hi = a.plan[row].b_hi;
+  const double z0 = a.plan[row].z0;
+  const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
+  const NucSet ST = value_set(c.m, c.thr, c.kmp, (double)a.T, e2);
+  uint64_t* lkey = a.lkey + row * kCapW;
+  uint32_t* lbits = a.lbits + row * kCapW;
+  // The kept mass above the window: the guide pass's exact mass at T = 1
+  // without min_p, else the tempered weights of the kept candidates there.
+  const bool need_wt = a.T != 1.0f || c.kmp != 0ull;
+  double AT = 0.0;
+  for_each_cand_batch<DT, VEC>(a, row, seg, a.plan[row].listed != 0u, xr, c.e_begin, c.e_end,
+                               [&](const auto& bits, auto at) {
+    constexpr int N = (int)(sizeof(bits) / sizeof(bits[0]));
+    uint32_t b[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float z = __uint_as_float(bits[q]);
+      const bool cand = z > -__builtin_inff() && (double)z >= c.thr;
+      b[q] = cand ? S1.bin<kNB>(z) : (uint32_t)kNB;
+    }
+    if (need_wt) {
+      bool kept[N], any = false;
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        kept[q] = b[q] < b_lo && comp_key(bits[q], (uint32_t)at(q)) >= c.kmp;
+        any = any || kept[q];
+      }
+      if (__ballot(any) != 0ull) {
+#pragma unroll
+        for (int q = 0; q < N; ++q) AT += ST.w_if(kept[q], __uint_as_float(bits[q]));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (b[q] >= b_lo && b[q] <= b_hi) stage_window(F.st, at(q), c.e_begin);
+  });
+  flush_window<DT>(F.st, xr, c.e_begin, &a.lcnt[row], lkey, lbits);
+  if (need_wt) {
+    AT = nuc_sum(r, AT, 1);
+    if (tid == 0) st_dev(&a.p_at[row * a.S + seg], AT);
+  }
+  if (!last_of_row(sh, a.tickets + row * 3 + 1, (uint32_t)a.S)) return;
+  // ---- the row's last workgroup: its first global loads issued together
+  const int64_t p0 = row * a.S;
+  const double vat = need_wt && tid < a.S ? ld_dev(&a.p_at[p0 + tid]) : 0.0;
+  const uint32_t n = ld_dev(&a.lcnt[row]);
+  const uint64_t k0 = ld_dev(&lkey[tid]);
+  const double Atot = a.plan[row].a_above;
+  const double ATtot = need_wt ? block_sum_f64(sh, vat) : Atot;
+  if (tid == 0) st_dev(&a.lcnt[row], 0u);
+  if (n > kCapW) {  // the window is too crowded for LDS: the row is left to nuc_alone
+    if (tid == 0) a.plan[row].state = 3u;
+    return;
+  }
+  const double tcut = (double)a.top_p * z0;
+  if (n <= 64) {  // wave 0 alone, the window in its lanes
+    if (tid < 64) {
+      uint64_t key = (uint32_t)tid < n ? k0 : 0ull;
+      uint32_t bits = (uint32_t)tid < n ? key_bits((uint32_t)(key >> 32)) : 0u;
+      wave_sort(key, bits, n, F.key, s_bits);
+      const bool live = (uint32_t)tid < n;
+      const double w1 = live ? S1.w(__uint_as_float(bits)) : 0.0;
+      const uint32_t jc = wave_pick(Atot + wave_incl_f64(w1) >= tcut, w1 > 0.0, n);
+      const uint64_t kf = max(lane_key(key, jc), c.kmp);
+      const uint32_t nk = (uint32_t)__builtin_popcountll(__ballot(live && key >= kf));
+      const NucSet S2 = value_set(c.m, c.thr, kf, (double)a.T, e2);
+      const double w2 = (uint32_t)tid < nk ? S2.w(__uint_as_float(bits)) : 0.0;
+      const double wt = ATtot + wave_sum_f64(w2);
+      if (tid == 0) {
+        a.out_kfl[row] = kf;
+        a.out_lse_f[row] = c.m / (double)a.T + log(wt);
+        a.plan[row].state = 2u;
+      }
+    }
+    return;
+  }
+  {  // the keys into LDS, all loads issued first
+    constexpr int Q = kCapW / NT;
+    uint64_t k[Q];
+#pragma unroll
+    for (int q = 1; q < Q; ++q) {
+      const uint32_t j = q * NT + tid;
+      if (j < n) k[q] = ld_dev(&lkey[j]);
+    }
+    if ((uint32_t)tid < n) F.key[tid] = k0;
+#pragma unroll
+    for (int q = 1; q < Q; ++q) {
+      const uint32_t j = q * NT + tid;
+      if (j < n) F.key[j] = k[q];
+    }
+    __syncthreads();
+  }
+  sort_keys_desc(F.key, n);
+  const KeyBits kb{F.key};
+  // the cut, then min_p: the kept candidates of the window are its first nk
+  const uint32_t jc = walk_sorted(r, kb, n, S1, Atot, tcut, false);
+  const uint64_t kfin = max(F.key[jc], c.kmp);
+  uint32_t nk = 0;
+  for (uint32_t j = tid; j < n; j += NT) nk += F.key[j] >= kfin ? 1u : 0u;
+  nk = block_sum_u32(r, nk);
+  const NucSet S2 = value_set(c.m, c.thr, kfin, (double)a.T, e2);
+  const double WT = ATtot + sum_sorted(r, kb, nk, S2);
+  if (tid == 0) {
+    a.out_kfl[row] = kfin;
+    a.out_lse_f[row] = c.m / (double)a.T + log(WT);
+    a.plan[row].state = 2u;
+  }
+}
+
 // Pass 3 (rows whose draw falls above the cut window): the exact tempered mass
 // above the draw window and its candidates; the last workgroup draws.
 template <typename DT, bool VEC>
@@ -1447,7 +1633,7 @@ __global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
   if (tid == 0) st.n = 0u;
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, seg);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   const NucSet S1 = value_set(c.m, c.thr, 0ull, 1.0, e2, c.span1);
   const NucSet S2 = value_set(c.m, c.thr, p.kfin, (double)a.T, e2);
   uint64_t* lkey = a.lkey + row * kCapW;
@@ -1498,7 +1684,7 @@ __global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
   if (state != 3u && state != 4u) return;
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, 0);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   if (state == 3u) {
     row_alone<DT, VEC>(fb, r, a, row, c, xr, e2);
     return;
@@ -1570,7 +1756,7 @@ __global__ __launch_bounds__(NT) void typ_moments_kernel(NucArgs a) {
   }
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, seg);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   double z0 = 0.0, y = 0.0, zlo = c.m;
   for_each_elem<DT, kNG, VEC>(xr, c.e_begin, c.e_end, [&](uint32_t bits, int64_t) {
     const float z = __uint_as_float(bits);
@@ -1677,7 +1863,7 @@ __global__ __launch_bounds__(NT) void sel_hist_kernel(NucArgs a) {
   init_e2(e2);
   const NucSet S = job_set(jb, e2);
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   for (int b = tid; b < kNB; b += NT) {
     L.h.hw[b] = 0.0;
     L.h.hc[b] = 0u;
@@ -1777,7 +1963,7 @@ __global__ __launch_bounds__(NT) void sel_collect_kernel(NucArgs a) {
   init_e2(e2);
   const NucSet S = job_set(jb, e2);
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   uint64_t* lkey = a.lkey + row * kCapW;
   uint32_t* lbits = a.lbits + row * kCapW;
   double A = 0.0, zb = -__builtin_inf();  // mass and largest value before the window
@@ -1871,7 +2057,7 @@ __global__ __launch_bounds__(NT) void sel_alone_kernel(NucArgs a) {
   const SelJob jb = a.jobs[row];
   init_e2(e2);
   const NucSet S = job_set(jb, e2);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   const SelOut d = wg_select<DT, VEC>(fb, r, xr, a.V, S, jb.frac, jb.strict != 0);
   double zl = -__builtin_inf();
   for_each_elem<DT, kNG, VEC>(xr, 0, a.V, [&](uint32_t bits, int64_t i) {
@@ -1931,7 +2117,7 @@ __global__ __launch_bounds__(NT) void kept_lse_kernel(NucArgs a) {
     return;
   }
   init_e2(e2);
-  const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
+  const DT* __restrict__ xr = nuc_row<DT>(a, row);
   const double m = a.st_max[row], T = a.T, iT = 1.0 / T;
   const double thr = m + log((double)a.min_p);
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
@@ -1973,7 +2159,10 @@ template <typename DT, bool VEC>
 static void go_nucleus(const NucArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.rows * a.S));
   hipLaunchKernelGGL((nuc_hist_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
-  hipLaunchKernelGGL((nuc_collect_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+  if (a.out_kfl)
+    hipLaunchKernelGGL((nuc_collect_floor_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((nuc_collect_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
   hipLaunchKernelGGL((nuc_draw_kernel<DT, VEC>), grid, dim3(NT), 0, s, a);
   hipLaunchKernelGGL((nuc_alone_kernel<DT, VEC>), dim3((unsigned)a.rows), dim3(NT), 0, s, a);
 }
