@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_932_363
+TRAFFIC_BYTES = 414_929_225
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "82aff54851da2d10febff32ca8bebf7444ce11d4243dbb5df641c9ce188346ce"
+TRAFFIC_SHA256 = "eef98d90a271929b6c809ac6c2384e3f8fe4e66458364a1ac50e57fb726e40b9"
 
 
 def sources_digest():
