@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_929_225
+TRAFFIC_BYTES = 414_934_835
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "eef98d90a271929b6c809ac6c2384e3f8fe4e66458364a1ac50e57fb726e40b9"
+TRAFFIC_SHA256 = "67edf901195fcc25d6cb366a7747cf342d97a4c98dd59c9eb4817c7981566bab"
 
 
 def sources_digest():
@@ -153,6 +153,12 @@ def _only_spec_accept(torch, vsel, W, dev):
     return lambda i: vsel.vsel_spec_accept(tg, dr, *args)
 
 
+def _only_spec_match(torch, vsel, W, dev):
+    tg, dr, args = _only_spec(torch, W, dev)
+    um = torch.from_numpy(W.uniforms(32 * 9, seed=W.BASE_SEED + 930)).to(dev)
+    return lambda i: vsel.vsel_spec_match(tg, dr, args[0], um, 32, 8, 1.0)
+
+
 def _only_spec_filtered(torch, vsel, W, dev):
     tg, dr, args = _only_spec(torch, W, dev)
     return lambda i: vsel.vsel_spec_accept_filtered(tg, dr, *args, top_p=0.9)
@@ -165,7 +171,8 @@ def _only_verify(torch, vsel, W, dev):
 
 # --only: one configuration, for profiling its kernels
 ONLY = {"wholerow-topp": _only_topp, "wholerow-typical": _only_typical, "sample": _only_sample,
-        "chain": _only_chain, "spec-accept": _only_spec_accept, "spec-filtered-wholerow": _only_spec_filtered,
+        "chain": _only_chain, "spec-accept": _only_spec_accept, "spec-match": _only_spec_match,
+        "spec-filtered-wholerow": _only_spec_filtered,
         "verify3": _only_verify}
 
 

@@ -210,16 +210,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 
   // Row moments for top-n-sigma (MOM): each lane's values above -inf, shifted
   // by its first such value, in float64 (as the moments pass takes them).
-  double mn = 0.0, mr = 0.0, ms1 = 0.0, ms2 = 0.0;
+  // The shift is settled once per group, in the rare groups a lane meets
+  // before its first such value, and the count is an integer, so an element
+  // costs a conversion, a subtraction, a select, an add and an FMA.
+  uint32_t mcnt = 0;
+  double mr = 0.0, ms1 = 0.0, ms2 = 0.0;
   auto mom_add = [&](const float (&x)[E]) {
     if constexpr (MOM) {
+      if (mcnt == 0u) {
+        float first = -__builtin_inff();
+#pragma unroll
+        for (int e = E - 1; e >= 0; --e) first = x[e] > -__builtin_inff() ? x[e] : first;
+        if (first > -__builtin_inff()) mr = (double)first;
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const bool ok = x[e] > -__builtin_inff();
-        const double xd = (double)x[e];
-        mr = (mn == 0.0 && ok) ? xd : mr;
-        const double d = ok ? xd - mr : 0.0;
-        mn += ok ? 1.0 : 0.0;
+        const double d = ok ? (double)x[e] - mr : 0.0;
+        mcnt += ok ? 1u : 0u;
         ms1 += d;
         ms2 = fma(d, d, ms2);
       }
@@ -751,6 +759,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     return w;
   };
   if constexpr (MOM) {
+    const double mn = (double)mcnt;
     Mom v{mn, 0.0, 0.0};
     if (mn > 0.0) v = Mom{mn, mr + ms1 / mn, ms2 - ms1 * ms1 / mn};
     mv = fold_waves(v);
