@@ -137,6 +137,11 @@ def _only_typical(torch, vsel, W, dev):
     return lambda i: vsel.vsel_sample_chain(x, 0.7, u, typical_p=0.9)
 
 
+def _only_threshold(torch, vsel, W, dev):
+    x, u = _only_rows(torch, W, dev)
+    return lambda i: vsel.vsel_sample_chain(x, 0.7, u, top_n_sigma=1.0, min_p=0.05)
+
+
 def _only_sample(torch, vsel, W, dev):
     x, u = _only_rows(torch, W, dev)
     return lambda i: vsel.vsel_sample(x, 0.7, 20, 0.95, u)
@@ -170,7 +175,8 @@ def _only_verify(torch, vsel, W, dev):
 
 
 # --only: one configuration, for profiling its kernels
-ONLY = {"wholerow-topp": _only_topp, "wholerow-typical": _only_typical, "sample": _only_sample,
+ONLY = {"wholerow-topp": _only_topp, "wholerow-typical": _only_typical, "wholerow-threshold": _only_threshold,
+        "sample": _only_sample,
         "chain": _only_chain, "spec-accept": _only_spec_accept, "spec-match": _only_spec_match,
         "spec-filtered-wholerow": _only_spec_filtered,
         "verify3": _only_verify}

@@ -25,17 +25,48 @@ __global__ __launch_bounds__(NT) void moments_kernel(MomArgs a) {
   if (row >= a.rows) return;
   const DT* __restrict__ xr = reinterpret_cast<const DT*>(a.x) + row * a.ld;
   const int64_t e_begin = (int64_t)seg * a.seg_len, e_end = min(a.V, e_begin + a.seg_len);
-  // this thread's values, in the order the tiles give them
-  double n = 0.0, s1 = 0.0, s2 = 0.0, r = 0.0;
-  for_each_elem<DT, 4, VEC>(xr, e_begin, e_end, [&](uint32_t bits, int64_t) {
-    const float z = __uint_as_float(bits);
-    if (!(z > -__builtin_inff())) return;  // -inf (a mask) takes no part; NaN rows fail closed elsewhere
-    if (n == 0.0) r = z;
-    const double d = (double)z - r;
-    n += 1.0;
-    s1 += d;
-    s2 += d * d;
+  // this thread's values, in the order the tiles give them; -inf (a mask)
+  // takes no part (NaN rows fail closed elsewhere).  The shift r is settled
+  // once per group, in the groups a lane meets before its first value above
+  // -inf, and the count is an integer: per element a select, a conversion,
+  // a subtraction, an add and an FMA.
+  constexpr int E = Elem<DT>::E;
+  uint32_t cnt = 0;
+  double s1 = 0.0, s2 = 0.0, r = 0.0;
+  auto add = [&](const float (&x)[E]) {
+    if (cnt == 0u) {
+      float first = -__builtin_inff();
+#pragma unroll
+      for (int e = E - 1; e >= 0; --e) first = x[e] > -__builtin_inff() ? x[e] : first;
+      if (first > -__builtin_inff()) r = (double)first;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = x[e] > -__builtin_inff();
+      const double d = ok ? (double)x[e] - r : 0.0;
+      cnt += ok ? 1u : 0u;
+      s1 += d;
+      s2 = fma(d, d, s2);
+    }
+  };
+  const int64_t e_full = e_begin + (e_end - e_begin) / E * E;
+  walk_groups<DT, 4, VEC>(xr, e_begin, e_full, [&](const auto& g, int64_t) {
+    constexpr int NGP = (int)(sizeof(g) / sizeof(Group));
+#pragma unroll
+    for (int j = 0; j < NGP; ++j) {
+      float x[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = __uint_as_float(gbits<DT>(g[j], e));
+      add(x);
+    }
   });
+  for (int64_t i = e_full + tid; i < e_end; i += NT) {  // the last few elements, one per lane
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = e == 0 ? __uint_as_float(gbits_at<DT>(xr, i)) : -__builtin_inff();
+    add(x);
+  }
+  const double n = (double)cnt;
   Mom v{n, 0.0, 0.0};
   if (n > 0.0) v = Mom{n, r + s1 / n, s2 - s1 * s1 / n};
   v = wave_mom(v);
