@@ -71,6 +71,11 @@ static hipError_t check_scan(const ScanArgs& a) {
   for (const uint32_t* p : {a.st_amax, a.st_bad}) in_ws("scan", "row stats", p, rows);
   in_ws("scan", "st_max", a.st_max, rows);
   in_ws("scan", "st_lse", a.st_lse, rows);
+  in_ws("scan", "m_n", a.m_n, n);
+  in_ws("scan", "m_mean", a.m_mean, n);
+  in_ws("scan", "m_m2", a.m_m2, n);
+  in_ws("scan", "sigma", a.sigma, rows);
+  if (a.sigma && (a.n_excl > 0 || !a.m_n || !a.m_mean || !a.m_m2)) fail("scan", "row moments");
   disjoint("scan");
   return hipSuccess;
 }

@@ -614,7 +614,9 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
   const bool fused_moments = top_n_sigma > 0.0f && !greedy && top_k > 0 &&
                              aligned16(logits, ld, elem_size(dtype)) &&
                              std::min<int64_t>(top_k, vocab) <= kWaveTopkMax;
-  if (top_n_sigma > 0.0f && !greedy && !fused_moments) {
+  // over whole rows (top_k = 0) the row scan takes them in its pass
+  const bool scan_moments = top_n_sigma > 0.0f && !greedy && top_k == 0;
+  if (top_n_sigma > 0.0f && !greedy && !fused_moments && !scan_moments) {
     const Plan p = plan_scan(dtype, false, rows, vocab, 1, kMinMergeSegment);
     MomArgs m{};
     m.x = logits;
@@ -664,6 +666,13 @@ static vsel_status sample_impl(const void* logits, int dtype, int64_t rows, int6
     a.st_amax = at<uint32_t>(ws, w.st.amax);
     a.st_max = at<float>(ws, w.st.mx);
     a.st_bad = at<uint32_t>(ws, w.st.bad);
+    if (scan_moments) {
+      a.m_n = at<double>(ws, cw->mom.p_n);
+      a.m_mean = at<double>(ws, cw->mom.p_mean);
+      a.m_m2 = at<double>(ws, cw->mom.p_m2);
+      a.sigma = at<double>(ws, cw->mom.sigma);
+      sigma = a.sigma;
+    }
     hipError_t e = launch_scan(dtype, false, a, s);
     if (e != hipSuccess) return VSEL_EDEVICE;
     if (typical_p < 1.0f || top_p < 1.0f) {

@@ -51,6 +51,14 @@ struct ScanArgs {
   const uint32_t* excl;
   int32_t n_excl;      // 0 .. kMaxExcluded
   uint32_t* out_status;
+  // row moments in the same pass (the sampler chain's top-n-sigma over whole
+  // rows; no log-sum-exp, no excluded ids): per (row, segment) count, mean
+  // and squared deviations of the values above -inf, and each row's
+  // standard deviation (null: no moments)
+  double* m_n;
+  double* m_mean;
+  double* m_m2;
+  double* sigma;
 };
 constexpr int kMaxExcluded = 256;
 

@@ -21,7 +21,7 @@ namespace vsel {
 constexpr int SG = 8;            // 16-byte groups per lane per tile
 constexpr float kLazyScan = 64.0f; // the exp2 offset moves when a maximum passes it by this
 
-template <typename DT, bool WANT_LSE, bool VEC, bool EXCL = false>
+template <typename DT, bool WANT_LSE, bool VEC, bool EXCL = false, bool MOM = false>
 __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
   constexpr int E = Elem<DT>::E;
   constexpr int64_t TILE = (int64_t)NT * SG * E;
@@ -123,10 +123,36 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
     }
   };
 
+  // Row moments (MOM): each lane's values above -inf shifted by its first
+  // such value (in stream order), in float64, as the moments pass takes
+  // them; the shift is settled once per group, in the groups a lane meets
+  // before that value, and the count is an integer.
+  uint32_t mcnt = 0;
+  double mr = 0.0, ms1 = 0.0, ms2 = 0.0;
+  auto mom_add = [&](const float (&x)[E]) {
+    if constexpr (MOM) {
+      if (mcnt == 0u) {
+        float first = -__builtin_inff();
+#pragma unroll
+        for (int e = E - 1; e >= 0; --e) first = x[e] > -__builtin_inff() ? x[e] : first;
+        if (first > -__builtin_inff()) mr = (double)first;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool ok = x[e] > -__builtin_inff();
+        const double d = ok ? (double)x[e] - mr : 0.0;
+        mcnt += ok ? 1u : 0u;
+        ms1 += d;
+        ms2 = fma(d, d, ms2);
+      }
+    }
+  };
+
   auto group = [&](const Group& g, uint32_t pos) {
     float x[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) x[e] = __uint_as_float(gbits<DT>(g, e));
+    mom_add(x);
     float m0 = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) m0 = fmax_nan(m0, x[e]);
@@ -282,6 +308,12 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
         from_tail = true;
       }
       lm = fmax_nan(lm, x);
+      if constexpr (MOM) {
+        float x1[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) x1[e] = e == 0 ? x : -__builtin_inff();
+        mom_add(x1);
+      }
       if constexpr (WANT_LSE) {
         if (x > trig && x < __builtin_inff()) set_offset(x);
         LS += huge ? (double)__builtin_amdgcn_exp2f((x - om) * c)
@@ -311,18 +343,55 @@ __global__ __launch_bounds__(NT) void scan_kernel(ScanArgs a) {
 #pragma unroll
   for (int q = 1; q < NWAVE; ++q) P = sh.wk[q] > P ? sh.wk[q] : P;
 
+  // Moments (MOM): the lanes folded per wave, then the waves in order, then
+  // (below) the segments, each in a fixed order.
+  __shared__ double s_mom[3 * NWAVE];
+  auto fold_waves = [&](Mom v) {
+    v = wave_mom(v);
+    __syncthreads();
+    if (lane == 0) {
+      s_mom[wave] = v.n;
+      s_mom[NWAVE + wave] = v.mean;
+      s_mom[2 * NWAVE + wave] = v.m2;
+    }
+    __syncthreads();
+    Mom w{0.0, 0.0, 0.0};
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) w = mom_merge(w, Mom{s_mom[q], s_mom[NWAVE + q], s_mom[2 * NWAVE + q]});
+    return w;
+  };
+  Mom mv{0.0, 0.0, 0.0};
+  if constexpr (MOM) {
+    const double mn = (double)mcnt;
+    Mom v{mn, 0.0, 0.0};
+    if (mn > 0.0) v = Mom{mn, mr + ms1 / mn, ms2 - ms1 * ms1 / mn};
+    mv = fold_waves(v);
+  }
+
   if (a.S > 1) {
     const int64_t slot = row * a.S + seg;
     if (tid == 0) {
       st_dev(&a.p_key[slot], P);
       st_dev(&a.p_m[slot], r.m);
       st_dev(&a.p_s[slot], r.s);
+      if constexpr (MOM) {
+        st_dev(&a.m_n[slot], mv.n);
+        st_dev(&a.m_mean[slot], mv.mean);
+        st_dev(&a.m_m2[slot], mv.m2);
+      }
     }
     if (!last_done(sh, a.tickets + row, (uint32_t)a.S)) return;
     const int64_t s0 = row * a.S;
+    // this thread's segment's moments, loaded with the partials below
+    Mom ms{0.0, 0.0, 0.0};
+    if constexpr (MOM) {
+      if (tid < a.S) ms = Mom{ld_dev(&a.m_n[s0 + tid]), ld_dev(&a.m_mean[s0 + tid]), ld_dev(&a.m_m2[s0 + tid])};
+    }
     merge_key_lse(sh, a.p_key + s0, a.p_m + s0, a.p_s + s0, a.S, c, P, r);
+    if constexpr (MOM) mv = fold_waves(ms);
   }
   if (tid != 0) return;
+  if constexpr (MOM) a.sigma[row] = mv.n > 0.0 ? sqrt(fmax(mv.m2, 0.0) / mv.n) : 0.0;
 
   const bool bad = (r.m != r.m) || (r.m == __builtin_inff());
   const bool none = bad || P == 0;
@@ -350,6 +419,15 @@ static hipError_t go(const ScanArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((scan_kernel<DT, false, true, true>), grid, dim3(NT), 0, s, a);
       else
         hipLaunchKernelGGL((scan_kernel<DT, false, false, true>), grid, dim3(NT), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (!L) {
+    if (a.sigma) {  // the row moments in the same pass
+      if (vec)
+        hipLaunchKernelGGL((scan_kernel<DT, false, true, false, true>), grid, dim3(NT), 0, s, a);
+      else
+        hipLaunchKernelGGL((scan_kernel<DT, false, false, false, true>), grid, dim3(NT), 0, s, a);
       return hipGetLastError();
     }
   }
