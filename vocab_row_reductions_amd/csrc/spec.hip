@@ -547,6 +547,59 @@ __device__ double chunk_masses(const Src& r, int64_t e_begin, int64_t e_end, dou
   return tot;
 }
 
+// The first of n masses v[0..n) (LDS) whose running sum passes t (t <
+// cum + v[i]), by wave 0: each lane sums a run of ceil(n / 64) consecutive
+// masses in order, the runs are prefixed across the lanes (float64, a fixed
+// order), and the lane holding the crossing walks its run.  Returns the
+// index in every lane of wave 0 and sets *rem to the part of t past the
+// masses before it; with no crossing (rounding at the very top) the last
+// positive mass (index 0 if none), *rem its mass.  total: the sum of the
+// runs, for callers that need W before choosing t (then t = scale * W).
+__device__ __forceinline__ int wave_pick_mass(const double* v, int n, double scale, bool scale_by_total, double t,
+                                              double* rem, double* total) {
+  const int lane = threadIdx.x & 63;
+  const int R = (n + 63) / 64;
+  const int lo = min(n, lane * R), hi = min(n, lo + R);
+  double run = 0.0;
+  for (int i = lo; i < hi; ++i) run += v[i];
+  double incl = run;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  const double W = __shfl(incl, 63);
+  if (scale_by_total) t = scale * W;
+  double c = __shfl_up(incl, 1);
+  if (lane == 0) c = 0.0;
+  int found = -1, lastpos = -1;
+  double r = 0.0;
+  for (int i = lo; i < hi; ++i) {
+    if (found < 0 && t < c + v[i]) {
+      found = i;
+      r = t - c;
+    }
+    if (v[i] > 0.0) lastpos = i;
+    c += v[i];
+  }
+  const uint64_t hit = __ballot(found >= 0);
+  int pick;
+  double rr;
+  if (hit) {
+    const int l = __builtin_ctzll(hit);
+    pick = __shfl(found, l);
+    rr = __shfl(r, l);
+  } else {
+    const uint64_t pos = __ballot(lastpos >= 0);
+    const int l = pos ? 63 - __builtin_clzll(pos) : 0;
+    pick = pos ? __shfl(lastpos, l) : 0;
+    rr = v[pick];
+  }
+  *rem = rr;
+  *total = W;
+  return pick;
+}
+
 // The draw itself (one workgroup): segment, then chunk, then element.  pw
 // (LDS) holds the S segment masses, pc (global) the row's chunk masses; cm is
 // LDS room for kChunksPerSeg chunk masses.
@@ -558,62 +611,28 @@ __device__ uint32_t draw_pick(SelShared& sh, const Src& r, const double* pw, con
   __shared__ int s_seg, s_ch;
   __shared__ double s_in;
   __shared__ uint32_t s_tok;
-  if (tid == 0) {
-    double W = 0.0;
-    for (int sg = 0; sg < S; ++sg) W += pw[sg];
-    const double target = u * W;
-    double cum = 0.0;
-    int pick = -1;
-    for (int sg = 0; sg < S; ++sg) {
-      if (target < cum + pw[sg]) {
-        pick = sg;
-        break;
-      }
-      cum += pw[sg];
+  if (tid < 64) {
+    double rem, W;
+    const int pick = wave_pick_mass(pw, S, u, true, 0.0, &rem, &W);
+    if (tid == 0) {
+      s_seg = pick;
+      s_in = rem;
+      s_tok = kFail;
+      *W_out = W;
     }
-    double tin = target - cum;
-    if (pick < 0) {  // rounding at the very top: the last segment with mass
-      for (int sg = S - 1; sg >= 0; --sg)
-        if (pw[sg] > 0.0) {
-          pick = sg;
-          break;
-        }
-      if (pick < 0) pick = 0;
-      tin = pw[pick];
-    }
-    s_seg = pick;
-    s_in = tin;
-    s_tok = kFail;
-    *W_out = W;
   }
   __syncthreads();
   const int64_t e_begin = (int64_t)s_seg * seg_len, e_end = min(r.V, e_begin + seg_len);
   const int nch = (int)((e_end - e_begin + kChunk - 1) / kChunk);
   for (int q = tid; q < nch; q += NT) cm[q] = ld_dev(&pc[e_begin / kChunk + q]);
   __syncthreads();
-  if (tid == 0) {
-    const double tin = s_in;
-    double cum = 0.0;
-    int pick = -1;
-    for (int q = 0; q < nch; ++q) {
-      if (tin < cum + cm[q]) {
-        pick = q;
-        break;
-      }
-      cum += cm[q];
+  if (tid < 64) {
+    double rem, unused;
+    const int pick = wave_pick_mass(cm, nch, 0.0, false, s_in, &rem, &unused);
+    if (tid == 0) {
+      s_ch = pick;
+      s_in = rem;
     }
-    double t2 = tin - cum;
-    if (pick < 0) {
-      for (int q = nch - 1; q >= 0; --q)
-        if (cm[q] > 0.0) {
-          pick = q;
-          break;
-        }
-      if (pick < 0) pick = 0;
-      t2 = cm[pick];
-    }
-    s_ch = pick;
-    s_in = t2;
   }
   __syncthreads();
   const int64_t c0 = e_begin + (int64_t)s_ch * kChunk;
