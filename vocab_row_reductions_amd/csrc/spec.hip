@@ -600,6 +600,16 @@ __device__ __forceinline__ int wave_pick_mass(const double* v, int n, double sca
   return pick;
 }
 
+// Whether any of v[0..n) (LDS, n <= 4 * 64) is positive, by wave 0 (a sum of
+// such nonnegative masses is positive exactly then).
+__device__ __forceinline__ bool wave_any_positive(const double* v, int n) {
+  const int lane = threadIdx.x & 63;
+  bool any = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) any = any || (q * 64 + lane < n && v[q * 64 + lane] > 0.0);
+  return __ballot(any) != 0ull;
+}
+
 // The draw itself (one workgroup): segment, then chunk, then element.  pw
 // (LDS) holds the S segment masses, pc (global) the row's chunk masses; cm is
 // LDS room for kChunksPerSeg chunk masses.
@@ -839,10 +849,9 @@ __device__ void resid_draw(const SpecArgs& a, SelShared& sh, int64_t b, int seg,
     pw[tid] = t;
   }
   __syncthreads();
-  if (tid == 0) {
-    double W = 0.0;
-    for (int sg = 0; sg < a.dS; ++sg) W += pw[sg];
-    s_degen = W > 0.0 ? 0 : 1;
+  if (tid < 64) {
+    const bool pos = wave_any_positive(pw, a.dS);
+    if (tid == 0) s_degen = pos ? 0 : 1;
   }
   __syncthreads();
   double W;
@@ -931,10 +940,9 @@ __device__ __forceinline__ void draw_item(const SpecArgs& a, SelShared& sh, int6
   __syncthreads();
   // Degenerate residual (p <= q everywhere): draw from p instead.
   __shared__ int s_degen;
-  if (tid == 0) {
-    double W = 0.0;
-    for (int sg = 0; sg < a.dS; ++sg) W += pw[sg];
-    s_degen = (r.d != nullptr && !(W > 0.0)) ? 1 : 0;
+  if (tid < 64) {
+    const bool degen = r.d != nullptr && !wave_any_positive(pw, a.dS);
+    if (tid == 0) s_degen = degen ? 1 : 0;
   }
   __syncthreads();
   if (s_degen) {
