@@ -1627,8 +1627,11 @@ __global__ __launch_bounds__(NT) void nuc_draw_kernel(NucArgs a) {
   const Item it = work_item(a.S);
   const int64_t row = it.row;
   const int seg = (int)it.seg;
-  if (row >= a.rows || a.st_bad[row]) return;
-  if (a.plan[row].state != 1u) return;
+  if (row >= a.rows) return;
+  {  // both words loaded at once: most rows need nothing from this pass
+    const uint32_t bad = a.st_bad[row], state = a.plan[row].state;
+    if (bad || state != 1u) return;
+  }
   const NucPlan p = a.plan[row];
   if (tid == 0) st.n = 0u;
   init_e2(e2);
@@ -1679,9 +1682,9 @@ __global__ __launch_bounds__(NT) void nuc_alone_kernel(NucArgs a) {
   __shared__ FbShared fb;
   __shared__ double e2[64];
   const int64_t row = blockIdx.x;
-  if (row >= a.rows || a.st_bad[row]) return;
-  const uint32_t state = a.plan[row].state;
-  if (state != 3u && state != 4u) return;
+  if (row >= a.rows) return;
+  const uint32_t bad = a.st_bad[row], state = a.plan[row].state;  // loaded at once
+  if (bad || (state != 3u && state != 4u)) return;
   init_e2(e2);
   const NucCommon c = nuc_common(a, row, 0);
   const DT* __restrict__ xr = nuc_row<DT>(a, row);
