@@ -677,7 +677,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   uint64_t held[kPer];
   uint32_t place[kPer];
   {
-    const uint64_t Tb = s_T > T ? s_T : T;
+    uint64_t Tb = s_T > T ? s_T : T;
+    // When the four lists can each be cut to their k largest and still fit the
+    // direct ranking (4 k <= kRank), a wave holding more than k records above
+    // the shared threshold cuts to its own k largest (a wave-level select, no
+    // barrier): the workgroup's k largest lie among the waves' k largest, and
+    // the radix select of more than kRank records is avoided.
+    if (4u * k <= kRank) {
+      uint32_t above = 0;
+#pragma unroll
+      for (uint32_t q = 0; q < kPer; ++q) {
+        const uint32_t i = q * 64 + lane;
+        above += (uint32_t)__popcll(__ballot(i < wcnt && wb[i] >= Tb));
+      }
+      if (above > k) {
+        const uint64_t Tw = wave_kth(wb, wcnt, k, area.hist);
+        Tb = Tw > Tb ? Tw : Tb;
+      }
+    }
     uint32_t kept = 0;
 #pragma unroll
     for (uint32_t q = 0; q < kPer; ++q) {
