@@ -1010,9 +1010,10 @@ __device__ __forceinline__ int32_t first_reject(const SpecArgs& a, SelShared& sh
   return s_L;
 }
 
-// Pass 2 and the draws of modified rejection sampling (T > 0) in one launch.  The first B * dS workgroups are the draws (dispatched first,
-// so that their float64 work overlaps the coupling pass's stream); each finds
-// its sequence's first rejection itself, so it need not wait for pass 2.  The
+// Pass 2 and the draws of modified rejection sampling (T > 0) in one launch.
+// The first B * dS workgroups are the draws (dispatched first, so that their
+// float64 work overlaps the coupling pass's stream); each finds its
+// sequence's first rejection itself, so it need not wait for pass 2.  The
 // rest are pass 2's (position, segment) items.
 template <bool VEC, bool FILT, bool SP>
 __global__ __launch_bounds__(NT) void coupling_draw_kernel(SpecArgs a) {
