@@ -94,9 +94,13 @@ __device__ __forceinline__ void load_tile(Group (&g)[NG], const DT* __restrict__
     }
     return;
   }
+  // (the lane offsets of a partial tile are formed here, from a thread index
+  // the compiler cannot hoist, so none of them stays live through a loop)
+  uint32_t ptid = tid;
+  asm volatile("" : "+v"(ptid));
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    const uint32_t o = (uint32_t)(j * NT + tid) * E;
+    const uint32_t o = (uint32_t)(j * NT + ptid) * E;
     const bool full = o < lim;
     const uint32_t src = full ? o : 0u;
     if constexpr (VEC) {
@@ -791,6 +795,33 @@ __device__ __forceinline__ void load_tile_buf(Group (&g)[NG], const DT* __restri
     g[j].w[0] = v.x; g[j].w[1] = v.y; g[j].w[2] = v.z; g[j].w[3] = v.w;
   }
   (void)E;
+}
+
+// A row's last, partial tile by the same buffer loads, all issued together:
+// lim (uniform) is the number of elements left from tb, a multiple of E and
+// at least E.  Groups at or past lim read as -inf; their lanes re-read the
+// tile's first group, so every address lies inside the row.  (The lane
+// offsets are formed here, from a thread index the compiler cannot hoist,
+// so no per-lane constant of this rare tile stays live through the loop.)
+template <typename DT, int NG>
+__device__ __forceinline__ void load_tile_buf_part(Group (&g)[NG], const DT* __restrict__ tb, uint32_t lim) {
+  constexpr int E = Elem<DT>::E;
+  constexpr uint32_t pad = (E == 4) ? kNegInfBits : 0xFF80FF80u;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)tb, 0, (int)(lim * (uint32_t)sizeof(DT)), 0x00020000);
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const uint32_t o = ((uint32_t)j * NT + tid) * E;
+    const bool full = o < lim;
+    const u32x4 v =
+        __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((full ? o : 0u) * (uint32_t)sizeof(DT)), 0, 2 /* nontemporal */);
+    g[j].w[0] = full ? v.x : pad;
+    g[j].w[1] = full ? v.y : pad;
+    g[j].w[2] = full ? v.z : pad;
+    g[j].w[3] = full ? v.w : pad;
+  }
 }
 
 // 2^a in float64 for a finite a, to float precision (the fraction through

@@ -152,11 +152,11 @@ __device__ __forceinline__ void coupling_body(const SpecArgs& a, SelShared& sh, 
       load_tile_full<float, PG, VEC>(gd, dr + t0);
       pair(gz, gd, t0);
     }
-    for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
-      Group gz[1], gd[1];
-      load_tile<float, 1, VEC>(gz, zr, t0, e_full);
-      load_tile<float, 1, VEC>(gd, dr, t0, e_full);
-      pair(gz, gd, t0);
+    if (e_tiles < e_full) {  // the last partial tile, its loads issued together
+      Group gz[PG], gd[PG];
+      load_tile<float, PG, VEC>(gz, zr, e_tiles, e_full);  // past e_full: -inf, so p = q = 0
+      load_tile<float, PG, VEC>(gd, dr, e_tiles, e_full);
+      pair(gz, gd, e_tiles);
     }
     if (tid == 0)
       for (int64_t x = e_full; x < e_end; ++x) {
@@ -328,11 +328,11 @@ __global__ __launch_bounds__(NT) void match_kernel(SpecArgs a) {
       load_tile_full<float, PG, VEC>(gd, dr + t0);
       pair(gz, gd, t0);
     }
-    for (int64_t t0 = e_tiles; t0 < e_full; t0 += (int64_t)NT * E) {
-      Group gz[1], gd[1];
-      load_tile<float, 1, VEC>(gz, zr, t0, e_full);  // past e_full: -inf, so p = q = 0
-      load_tile<float, 1, VEC>(gd, dr, t0, e_full);
-      pair(gz, gd, t0);
+    if (e_tiles < e_full) {  // the last partial tile, its loads issued together
+      Group gz[PG], gd[PG];
+      load_tile<float, PG, VEC>(gz, zr, e_tiles, e_full);  // past e_full: -inf, so p = q = 0
+      load_tile<float, PG, VEC>(gd, dr, e_tiles, e_full);
+      pair(gz, gd, e_tiles);
     }
     if (tid == 0)
       for (int64_t x = e_full; x < e_end; ++x) {

@@ -510,7 +510,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   __builtin_amdgcn_s_setprio(3);
   int64_t t0 = e_begin;
   int64_t ov_t0 = 0;
-  int ovj = WTG;  // next group of an overflowed tile to take again (WTG: none)
+  uint32_t ov_lim = 0;  // elements of the overflowed tile inside the segment (a multiple of E)
+  int ovj = WTG;        // next group of an overflowed tile to take again (WTG: none)
   bool first = true, want_flush = false;
   uint32_t tix = 0;  // full tiles so far (the histogram scan rotates over the waves)
   for (;;) {
@@ -519,13 +520,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       want_flush = false;
     }
     if (ovj < WTG) {
+      // (groups of a partial tile past the segment's end read as -inf and
+      // are not loaded; ovj stops at the first group no lane reaches)
       const uint32_t o = (uint32_t)(ovj * NT + tid) * E;
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + ov_t0 + o));
+      const bool full = o < ov_lim;
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + ov_t0 + (full ? o : 0u)));
+      constexpr uint32_t pad = (E == 4) ? kNegInfBits : 0xFF80FF80u;
       Group g1;
-      g1.w[0] = v.x; g1.w[1] = v.y; g1.w[2] = v.z; g1.w[3] = v.w;
+      g1.w[0] = full ? v.x : pad;
+      g1.w[1] = full ? v.y : pad;
+      g1.w[2] = full ? v.z : pad;
+      g1.w[3] = full ? v.w : pad;
       float x[E];
       stage(g1, group_max(g1, x), (uint32_t)ov_t0 + o);
       ++ovj;
+      if ((uint32_t)(ovj * NT) * E >= ov_lim) ovj = WTG;
       want_flush = true;
       continue;
     }
@@ -565,6 +574,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       if (sn > kWStage) {
         sn = sn0;  // open the earlier groups, then take this tile again
         ov_t0 = t0;
+        ov_lim = (uint32_t)TILE;
         ovj = 0;
         want_flush = true;
       } else if (sn >= kFlushAt) {
@@ -574,22 +584,72 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       continue;
     }
     if (t0 < e_full) {
-      // the row's last partial tile: one group per lane at a time (at most
-      // 63 staged groups wait, so these never overflow the staging list)
-      Group g1[1];
-      load_tile<DT, 1, true>(g1, xr, t0, e_full);
-      if (first) {
-        first_tile(g1, t0);
-        first = false;
+      if constexpr (!WANT_LSE && !MOM) {
+        // the segment's last partial tile in one memory round trip instead
+        // of one per group: all its loads issued together (groups past
+        // e_full read as -inf), then the same steps as a full tile on the
+        // ngr groups that hold real elements only
+        const uint32_t lim = (uint32_t)(e_full - t0);
+        const uint32_t ngr = (lim + (uint32_t)(NT * E) - 1u) / (uint32_t)(NT * E);  // uniform, 1..WTG
+        Group g[WTG];
+        load_tile_buf_part<DT, WTG>(g, xr + t0, lim);
+        if (first) {
+          first_tile(g, t0);
+          first = false;
+        }
+        const uint64_t Ts = uniform_u64(__hip_atomic_load(&s_T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        const uint32_t sn0 = sn;
+        float gm[WTG];
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < WTG; ++j) {
+          gm[j] = -__builtin_inff();
+          if ((uint32_t)j < ngr) {
+            gm[j] = lse_group(g[j]);
+            tmax = fmax_nan(tmax, gm[j]);
+          }
+        }
+        lse_check(g, tmax);
+        if (Ts > T) {
+          T = Ts;
+          tf = thr_float(T);
+        }
+#pragma unroll
+        for (int j = 0; j < WTG; ++j)
+          if ((uint32_t)j < ngr) stage(g[j], gm[j], (uint32_t)t0 + (uint32_t)(j * NT + tid) * E);
+        if ((uint32_t)tid * E < lim) count_max(tmax);  // lanes holding a real group
+        fold();
+        if (sn > kWStage) {
+          sn = sn0;  // open the earlier groups, then take this tile again
+          ov_t0 = t0;
+          ov_lim = lim;
+          ovj = 0;
+          want_flush = true;
+        } else if (sn >= kFlushAt) {
+          want_flush = true;
+        }
+        t0 = e_full;
+        continue;
+      } else {
+        // the row's last partial tile, one group per lane at a time: with
+        // float work on every element, the tile at once measured slower (at
+        // most 63 staged groups wait, so these never overflow the staging
+        // list)
+        Group g1[1];
+        load_tile<DT, 1, true>(g1, xr, t0, e_full);
+        if (first) {
+          first_tile(g1, t0);
+          first = false;
+        }
+        const float gm1 = lse_group(g1[0]);
+        lse_check(g1, gm1);
+        stage(g1[0], gm1, (uint32_t)t0 + (uint32_t)tid * E);
+        if (t0 + (int64_t)tid * E < e_full) count_max(gm1);  // real groups only
+        fold();
+        if (sn >= kFlushAt) want_flush = true;
+        t0 += (int64_t)NT * E;
+        continue;
       }
-      const float gm1 = lse_group(g1[0]);
-      lse_check(g1, gm1);
-      stage(g1[0], gm1, (uint32_t)t0 + (uint32_t)tid * E);
-      if (t0 + (int64_t)tid * E < e_full) count_max(gm1);  // real groups only
-      fold();
-      if (sn >= kFlushAt) want_flush = true;
-      t0 += (int64_t)NT * E;
-      continue;
     }
     if (sn) {
       want_flush = true;
