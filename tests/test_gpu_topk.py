@@ -153,3 +153,43 @@ def test_back_to_back_calls_reuse_workspace(g, oracle):
         k = int(rng.choice([1, 20, 64, 84, 200]))
         x = (np.round(rng.normal(0, 3, (rows, V)) * 32) / 32).astype(np.float32)
         compare(g, oracle, x, min(k, V))
+
+
+def compare_no_lse(g, oracle, x, k, ld=None):
+    """vsel_topk without a log-sum-exp output: the plain fused kernel, whose
+    segment-final partial tile is loaded in one round trip."""
+    xd = g.dev_rows(x, ld)
+    vals, ids, am, lse = g.vsel.vsel_topk(xd, k, vocab=x.shape[1], want_lse=False)
+    assert lse is None
+    ov, oi, oam, _ = oracle.topk(x, k)
+    gi, gv = g.u32(ids), g.bits(vals)
+    bad = oi[:, 0] == g.SENT
+    assert np.array_equal(gi[bad, 0], oi[bad, 0])
+    assert np.array_equal(gi[~bad], oi[~bad]), "top-k ids differ"
+    assert np.array_equal(gv[~bad], ov[~bad].view(np.uint32)), "top-k values differ"
+    assert np.array_equal(g.u32(am), oam), "argmax differs"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_partial_tiles_without_lse(g, oracle, dtype):
+    """Rows whose segments end in partial tiles of every size, through the
+    kernel without log-sum-exp: constant rows stage every group of that tile
+    (the staging list overflows and the tile is read again, bounded by the
+    row's end), ascending rows keep their largest elements in it, and few rows
+    of 248,320 make the last segment a partial tile alone."""
+    rng = np.random.default_rng(77)
+    for V in (4099, 50003, 202045, 202048, 248320):
+        x = rng.normal(0, 1, (6, V)).astype(np.float32)
+        x[0, :] = 1.5
+        x[1, :] = np.arange(V, dtype=np.float32)
+        tail = min(5000, V // 2)
+        x[2, -tail:] = 50.0 + np.arange(tail, dtype=np.float32)  # the winners in the partial tile
+        x[3, :] = np.round(x[3, :])
+        x[4, ::2] = -np.inf
+        if dtype == "bf16":
+            x = W.f32_to_bf16_bits(x)
+        for k in (1, 20, 84, 128):
+            compare_no_lse(g, oracle, x, min(k, V), ld=(V + 7) // 8 * 8)
+    x = W.verify_topk_rows(rows=3)
+    for k in (20, 84):
+        compare_no_lse(g, oracle, x, k)
