@@ -520,21 +520,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       want_flush = false;
     }
     if (ovj < WTG) {
-      // (groups of a partial tile past the segment's end read as -inf and
-      // are not loaded; ovj stops at the first group no lane reaches)
       const uint32_t o = (uint32_t)(ovj * NT + tid) * E;
-      const bool full = o < ov_lim;
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + ov_t0 + (full ? o : 0u)));
-      constexpr uint32_t pad = (E == 4) ? kNegInfBits : 0xFF80FF80u;
       Group g1;
-      g1.w[0] = full ? v.x : pad;
-      g1.w[1] = full ? v.y : pad;
-      g1.w[2] = full ? v.z : pad;
-      g1.w[3] = full ? v.w : pad;
+      if constexpr (!WANT_LSE && !MOM) {
+        // (a partial tile can overflow in this variant: its groups past the
+        // segment's end read as -inf and are not loaded, and ovj stops at
+        // the first group no lane reaches)
+        const bool full = o < ov_lim;
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + ov_t0 + (full ? o : 0u)));
+        constexpr uint32_t pad = (E == 4) ? kNegInfBits : 0xFF80FF80u;
+        g1.w[0] = full ? v.x : pad;
+        g1.w[1] = full ? v.y : pad;
+        g1.w[2] = full ? v.z : pad;
+        g1.w[3] = full ? v.w : pad;
+      } else {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + ov_t0 + o));
+        g1.w[0] = v.x; g1.w[1] = v.y; g1.w[2] = v.z; g1.w[3] = v.w;
+      }
       float x[E];
       stage(g1, group_max(g1, x), (uint32_t)ov_t0 + o);
       ++ovj;
-      if ((uint32_t)(ovj * NT) * E >= ov_lim) ovj = WTG;
+      if constexpr (!WANT_LSE && !MOM)
+        if ((uint32_t)(ovj * NT) * E >= ov_lim) ovj = WTG;
       want_flush = true;
       continue;
     }
@@ -574,7 +581,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       if (sn > kWStage) {
         sn = sn0;  // open the earlier groups, then take this tile again
         ov_t0 = t0;
-        ov_lim = (uint32_t)TILE;
+        if constexpr (!WANT_LSE && !MOM) ov_lim = (uint32_t)TILE;
         ovj = 0;
         want_flush = true;
       } else if (sn >= kFlushAt) {
