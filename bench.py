@@ -29,10 +29,10 @@ METRIC = "logit rows/sec + achieved HBM GB/s, fused argmax+top-k(k=84), V=202048
 # HBM bytes per launch of the fused kernel from two rocprofv3 counter runs
 # (FETCH_SIZE, WRITE_SIZE; scaled by the counters' reading for a plain copy of
 # known size), valid for the kernel sources they were taken on.
-TRAFFIC_BYTES = 414_935_825
+TRAFFIC_BYTES = 414_951_184
 TRAFFIC_SOURCES = ("vocab_row_reductions_amd/csrc/topk_wave.hip", "vocab_row_reductions_amd/csrc/device.hpp",
                    "vocab_row_reductions_amd/csrc/internal.hpp")
-TRAFFIC_SHA256 = "86aa8982166f6db167274131e40cdf1702fa86bc25a94e0f7c7c90f98d951e4c"
+TRAFFIC_SHA256 = "4a19aa6b07f632779c5b8a3d1c580bce36736571e55b8bc3ed892956a3f878e7"
 
 
 def sources_digest():
